@@ -1,0 +1,172 @@
+/*
+ * FLARE / FLARE++ forward operator: plain fp64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this file's library. The GPU library
+ * never calls it, and the two share no code.
+ *
+ * Every function works on one (batch, head) problem with fp64 inputs that the
+ * caller has widened exactly from the stored fp32 or bf16 values. Loops are
+ * written in the order of the definitions; OpenMP only spreads independent
+ * rows (latents in the encode, tokens in the decode) over threads, and every
+ * sum runs sequentially over its index.
+ *
+ * Definitions followed (FLARE pages):
+ *  - Encode ("2. Implement Encode Stage" of the FLARE skill page; "4. Combine
+ *    Encode-Decode into Attention Layer", its encode half): the M latent
+ *    queries of a head attend to the N tokens,
+ *        l[m][n] = s * <Q[m], K[n]>,  s = 1/sqrt(D),
+ *        A_enc[m][n] = softmax over n of l[m][n],
+ *        Z[m] = sum_n A_enc[m][n] V[n].
+ *  - Decode: the tokens attend back to the latents through the transpose of
+ *    the same logits (the "encode-decode factorization" with a token-mixing
+ *    matrix of rank at most M, FLARE arXiv abstract),
+ *        A_dec[n][m] = softmax over m of l[m][n],
+ *        Y[n] = sum_m A_dec[n][m] Z[m].
+ *    The FLARE skill page's step 3 instead decodes with separately projected
+ *    token queries against Z as keys; this oracle follows the transposed-
+ *    logit reading (see the readings list of the design notes).
+ *  - FLARE++ (FLARE++ skill page, "Core Mechanism"; FLARE++ arXiv abstract:
+ *    the encoder's output corrects the learned queries):
+ *        Q' = Q + encode(Q, K, V);  Z = encode(Q', K, V);  Y = decode(Q', K, Z).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double dot(const double* a, const double* b, int64_t D) {
+    double s = 0.0;
+    for (int64_t d = 0; d < D; ++d) s += a[d] * b[d];
+    return s;
+}
+
+/* Encode of one head: Z[M][D] from Q[M][D], K[N][D], V[N][D].
+ * Returns 0, or -1 when scratch memory cannot be allocated. */
+int flare_oracle_encode(const double* Q, const double* K, const double* V,
+                        int64_t N, int64_t M, int64_t D, double* Z) {
+    const double s = 1.0 / sqrt((double)D);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* logit = (double*)malloc((size_t)N * sizeof(double));
+        if (!logit) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t m = 0; m < M; ++m) {
+            if (!logit) continue;
+            /* logits of latent m against every token, and their maximum */
+            double mx = -INFINITY;
+            for (int64_t n = 0; n < N; ++n) {
+                logit[n] = s * dot(Q + m * D, K + n * D, D);
+                if (logit[n] > mx) mx = logit[n];
+            }
+            /* softmax over the tokens, applied to V */
+            double den = 0.0;
+            double* z = Z + m * D;
+            for (int64_t d = 0; d < D; ++d) z[d] = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double e = exp(logit[n] - mx);
+                den += e;
+                const double* v = V + n * D;
+                for (int64_t d = 0; d < D; ++d) z[d] += e * v[d];
+            }
+            for (int64_t d = 0; d < D; ++d) z[d] /= den;
+        }
+        free(logit);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Decode of one head for R selected tokens: Y[R][D] from Q[M][D], K[N][D],
+ * Z[M][D]; rows[i] names the token of output row i (rows == NULL means all
+ * N tokens, R = N). Returns 0, -1 on allocation failure, -2 on a bad row. */
+int flare_oracle_decode(const double* Q, const double* K, const double* Z,
+                        int64_t N, int64_t M, int64_t D,
+                        const int64_t* rows, int64_t R, double* Y) {
+    const double s = 1.0 / sqrt((double)D);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* logit = (double*)malloc((size_t)M * sizeof(double));
+        if (!logit) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < R; ++i) {
+            if (!logit) continue;
+            int64_t n = rows ? rows[i] : i;
+            if (n < 0 || n >= N) {
+#pragma omp atomic write
+                failed = 2;
+                continue;
+            }
+            const double* k = K + n * D;
+            /* the same logits as the encode, read along the latent axis */
+            double mx = -INFINITY;
+            for (int64_t m = 0; m < M; ++m) {
+                logit[m] = s * dot(Q + m * D, k, D);
+                if (logit[m] > mx) mx = logit[m];
+            }
+            double den = 0.0;
+            double* y = Y + i * D;
+            for (int64_t d = 0; d < D; ++d) y[d] = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                double e = exp(logit[m] - mx);
+                den += e;
+                const double* z = Z + m * D;
+                for (int64_t d = 0; d < D; ++d) y[d] += e * z[d];
+            }
+            for (int64_t d = 0; d < D; ++d) y[d] /= den;
+        }
+        free(logit);
+    }
+    return failed == 1 ? -1 : (failed == 2 ? -2 : 0);
+}
+
+/* FLARE forward of one head: Z = encode(Q, K, V); Y = decode(Q, K, Z).
+ * Z_out[M][D] receives Z. */
+int flare_oracle_forward(const double* Q, const double* K, const double* V,
+                         int64_t N, int64_t M, int64_t D,
+                         const int64_t* rows, int64_t R, double* Y, double* Z_out) {
+    int rc = flare_oracle_encode(Q, K, V, N, M, D, Z_out);
+    if (rc) return rc;
+    return flare_oracle_decode(Q, K, Z_out, N, M, D, rows, R, Y);
+}
+
+/* FLARE++ forward of one head: Q' = Q + encode(Q, K, V), then the FLARE
+ * forward with Q' in place of Q. Qp_out[M][D] receives Q', Z_out[M][D] the
+ * second encode's Z. */
+int flare_oracle_pp_forward(const double* Q, const double* K, const double* V,
+                            int64_t N, int64_t M, int64_t D,
+                            const int64_t* rows, int64_t R, double* Y,
+                            double* Qp_out, double* Z_out) {
+    int rc = flare_oracle_encode(Q, K, V, N, M, D, Qp_out);
+    if (rc) return rc;
+    for (int64_t i = 0; i < M * D; ++i) Qp_out[i] += Q[i];
+    return flare_oracle_forward(Qp_out, K, V, N, M, D, rows, R, Y, Z_out);
+}
+
+/* Number of OpenMP threads a parallel region uses (1 without OpenMP). */
+int flare_oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void flare_oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

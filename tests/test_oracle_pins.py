@@ -1,0 +1,248 @@
+"""Pins of the fp64 CPU oracle against facts fixed outside the oracle itself.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped scale,
+a softmax over the wrong axis, a transposed operand, values instead of Z in
+the decode, a missing FLARE++ residual) fails at least one test:
+
+* library routine: the FLARE pages state that both stages are standard
+  scaled-dot-product attention calls (FLARE arXiv abstract; FLARE++ arXiv
+  abstract), so encode, decode, FLARE and FLARE++ are compared with torch's
+  float64 ``scaled_dot_product_attention`` on the CPU;
+* closed forms: one token, one latent, zero queries, and two-token sigmoid
+  cases worked out by hand below;
+* invariants of the token-mixing matrix W = A_dec A_enc, which the FLARE
+  abstract says has rank at most M: row-stochastic, non-negative, rank <= M,
+  reversible (detailed balance) with real eigenvalues in [0, 1], Y = W V;
+* equivariance under token permutations, constant V, and linearity in V
+  (FLARE only; FLARE++ is not linear in V).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from flare_inputs import f32_to_bf16_bits, make_inputs
+
+RNG = np.random.default_rng(1234)
+
+
+def rand(*shape, scale=1.0):
+    return RNG.standard_normal(shape) * scale
+
+
+def sdpa(q, k, v):
+    """torch float64 SDPA with its default scale 1/sqrt(head width)."""
+    out = F.scaled_dot_product_attention(torch.from_numpy(np.array(q, dtype=np.float64)),
+                                         torch.from_numpy(np.array(k, dtype=np.float64)),
+                                         torch.from_numpy(np.array(v, dtype=np.float64)))
+    return out.numpy()
+
+
+# ------------------------------------------------------------ library routine
+@pytest.mark.parametrize("B,H,N,M,D", [(2, 3, 37, 5, 8), (1, 2, 130, 17, 16), (1, 1, 1, 1, 4)])
+def test_encode_is_sdpa_of_latents_over_tokens(B, H, N, M, D):
+    Q, K, V = rand(H, M, D), rand(B, H, N, D), rand(B, H, N, D)
+    Z = oracle.encode(Q, K, V)
+    ref = sdpa(np.broadcast_to(Q, (B, H, M, D)), K, V)
+    np.testing.assert_allclose(Z, ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("B,H,N,M,D", [(2, 3, 37, 5, 8), (1, 2, 65, 33, 16)])
+def test_decode_is_sdpa_of_tokens_over_latents(B, H, N, M, D):
+    Q, K, Z = rand(H, M, D), rand(B, H, N, D), rand(B, H, M, D)
+    Y = oracle.decode(Q, K, Z)
+    ref = sdpa(K, np.broadcast_to(Q, (B, H, M, D)), Z)
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_forward_is_two_sdpa_calls():
+    B, H, N, M, D = 2, 2, 50, 7, 8
+    Q, K, V = rand(H, M, D, scale=0.7), rand(B, H, N, D), rand(B, H, N, D)
+    Y, Z = oracle.forward(Q, K, V)
+    Qb = np.broadcast_to(Q, (B, H, M, D))
+    Zr = sdpa(Qb, K, V)
+    np.testing.assert_allclose(Z, Zr, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Y, sdpa(K, Qb, Zr), rtol=1e-12, atol=1e-13)
+
+
+def test_pp_forward_is_residual_then_two_sdpa_calls():
+    B, H, N, M, D = 2, 2, 40, 6, 8
+    Q, K, V = rand(H, M, D, scale=0.5), rand(B, H, N, D), rand(B, H, N, D)
+    Y, Qp, Z = oracle.pp_forward(Q, K, V)
+    Qb = np.broadcast_to(Q, (B, H, M, D))
+    Qp_ref = Qb + sdpa(Qb, K, V)
+    Z_ref = sdpa(Qp_ref, K, V)
+    np.testing.assert_allclose(Qp, Qp_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Z, Z_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Y, sdpa(K, Qp_ref, Z_ref), rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- closed forms
+def test_single_token_encode_returns_that_token():
+    Q, K, V = rand(3, 9, 8), rand(1, 3, 1, 8), rand(1, 3, 1, 8)
+    Z = oracle.encode(Q, K, V)
+    np.testing.assert_array_equal(Z, np.broadcast_to(V, (1, 3, 9, 8)))
+    Y, _ = oracle.forward(Q, K, V)
+    np.testing.assert_allclose(Y, V, rtol=0, atol=1e-15)
+
+
+def test_zero_queries_give_token_means():
+    B, H, N, M, D = 1, 2, 33, 4, 8
+    K, V = rand(B, H, N, D), rand(B, H, N, D)
+    Q = np.zeros((H, M, D))
+    Y, Z = oracle.forward(Q, K, V)
+    mean = V.mean(axis=2, keepdims=True)
+    np.testing.assert_allclose(Z, np.broadcast_to(mean, Z.shape), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Y, np.broadcast_to(mean, Y.shape), rtol=1e-13, atol=1e-14)
+
+
+def test_single_latent_decode_copies_z():
+    Q, K, Z = rand(2, 1, 8), rand(1, 2, 21, 8), rand(1, 2, 1, 8)
+    Y = oracle.decode(Q, K, Z)
+    np.testing.assert_array_equal(Y, np.broadcast_to(Z, Y.shape))
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + math.exp(-x))
+
+
+@pytest.mark.parametrize("q", [-2.0, -0.3, 0.0, 0.9, 3.0])
+def test_two_token_closed_forms(q):
+    # D=4 (s=1/2). Tokens k0 = 0 and k1 = e0; one latent q*e0. The encode is a
+    # two-way softmax of logits 0 and q/2, so with values v0 = 0, v1 = e1 it
+    # gives Z = sigmoid(q/2) e1 (e1 keeps K and V apart), and with one latent
+    # every token decodes to Z. For FLARE++ take v1 = e0: the first encode
+    # gives sigmoid(q/2) e0, the corrected latent is q' = q + sigmoid(q/2)
+    # along e0, and the result is sigmoid(q'/2) e0 for every token.
+    D = 4
+    K = np.zeros((1, 1, 2, D)); K[0, 0, 1, 0] = 1.0
+    V = np.zeros((1, 1, 2, D)); V[0, 0, 1, 1] = 1.0
+    Q = np.zeros((1, 1, D)); Q[0, 0, 0] = q
+    Y, Z = oracle.forward(Q, K, V)
+    z = sigmoid(q / 2.0)
+    exp_z = np.zeros(D); exp_z[1] = z
+    np.testing.assert_allclose(Z[0, 0, 0], exp_z, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(Y[0, 0], np.broadcast_to(exp_z, (2, D)), rtol=1e-14, atol=1e-15)
+
+    Vpp = np.zeros((1, 1, 2, D)); Vpp[0, 0, 1, 0] = 1.0
+    Ypp, Qp, Zpp = oracle.pp_forward(Q, K, Vpp)
+    qp = q + sigmoid(q / 2.0)
+    np.testing.assert_allclose(Qp[0, 0, 0, 0], qp, rtol=1e-14)
+    np.testing.assert_allclose(Ypp[0, 0, :, 0], [sigmoid(qp / 2.0)] * 2, rtol=1e-14)
+    # without the residual the answer would be sigmoid(sigmoid(q/2)/2); the two
+    # readings coincide only at q = 0
+    if q != 0.0:
+        assert abs(sigmoid(qp / 2.0) - sigmoid(sigmoid(q / 2.0) / 2.0)) > 1e-3
+
+
+@pytest.mark.parametrize("a,b", [(1.0, -1.0), (0.2, 2.5)])
+def test_two_latent_decode_closed_form(a, b):
+    # D=1 (s=1): token k attends to latents a and b with logits a*k and b*k,
+    # so its weight on latent a is sigmoid((a - b) k).
+    ks = np.array([-1.5, 0.0, 0.4, 2.0])
+    Q = np.array([[[a], [b]]])
+    K = ks.reshape(1, 1, 4, 1)
+    Z = np.array([[[[3.0], [-1.0]]]])
+    Y = oracle.decode(Q, K, Z)
+    w = np.array([sigmoid((a - b) * k) for k in ks])
+    np.testing.assert_allclose(Y[0, 0, :, 0], w * 3.0 + (1 - w) * -1.0, rtol=1e-14, atol=1e-15)
+
+
+# -------------------------------------------------------- mixing-matrix facts
+def mixing_matrix(Q, K):
+    """W (N x N) read off the oracle: Y columns are W applied to V columns."""
+    N, D = K.shape
+    assert D >= N
+    V = np.zeros((N, D))
+    V[:, :N] = np.eye(N)
+    Z = oracle.encode_head(Q, K, V)
+    Y = oracle.decode_head(Q, K, Z)
+    return Y[:, :N]
+
+
+@pytest.mark.parametrize("N,M", [(12, 3), (16, 5), (10, 1)])
+def test_mixing_matrix_is_reversible_stochastic_and_low_rank(N, M):
+    D = 16
+    Q, K = rand(M, D, scale=0.8), rand(N, D)
+    W = mixing_matrix(Q, K)
+    assert (W >= 0).all()
+    np.testing.assert_allclose(W.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    sv = np.linalg.svd(W, compute_uv=False)
+    assert sv[M] / sv[0] < 1e-12 if M < N else True
+    assert sv[M - 1] / sv[0] > 1e-8  # rank exactly M for generic inputs
+    # stationary distribution pi (left eigenvector of eigenvalue 1)
+    evals, evecs = np.linalg.eig(W.T)
+    i = np.argmin(abs(evals - 1.0))
+    pi = np.real(evecs[:, i]); pi = pi / pi.sum()
+    assert (pi > 0).all()
+    F_ = pi[:, None] * W
+    np.testing.assert_allclose(F_, F_.T, rtol=0, atol=1e-14)
+    assert np.max(abs(np.imag(evals))) < 1e-10
+    ev = np.real(evals)
+    assert ev.min() > -1e-10 and ev.max() < 1 + 1e-10
+    # Y = W V for an arbitrary V
+    V = rand(N, D)
+    Y = oracle.decode_head(Q, K, oracle.encode_head(Q, K, V))
+    np.testing.assert_allclose(Y, W @ V, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- invariants
+@pytest.mark.parametrize("pp", [False, True])
+def test_token_permutation_permutes_output(pp):
+    B, H, N, M, D = 1, 2, 45, 6, 8
+    Q, K, V = rand(H, M, D, scale=0.6), rand(B, H, N, D), rand(B, H, N, D)
+    perm = RNG.permutation(N)
+    f = (lambda *a: oracle.pp_forward(*a)[0]) if pp else (lambda *a: oracle.forward(*a)[0])
+    Y = f(Q, K, V)
+    Yp = f(Q, K[:, :, perm], V[:, :, perm])
+    np.testing.assert_allclose(Yp, Y[:, :, perm], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("pp", [False, True])
+def test_constant_values_give_constant_output(pp):
+    B, H, N, M, D = 2, 2, 30, 5, 8
+    Q, K = rand(H, M, D), rand(B, H, N, D)
+    c = rand(B, H, 1, D)
+    V = np.broadcast_to(c, (B, H, N, D)).copy()
+    Y = oracle.pp_forward(Q, K, V)[0] if pp else oracle.forward(Q, K, V)[0]
+    np.testing.assert_allclose(Y, np.broadcast_to(c, Y.shape), rtol=1e-13, atol=1e-14)
+
+
+def test_flare_is_linear_in_values_and_flarepp_is_not():
+    B, H, N, M, D = 1, 1, 40, 4, 8
+    Q, K = rand(H, M, D), rand(B, H, N, D)
+    V1, V2 = rand(B, H, N, D), rand(B, H, N, D)
+    a, b = 0.7, -1.3
+    Y = lambda V: oracle.forward(Q, K, V)[0]
+    np.testing.assert_allclose(Y(a * V1 + b * V2), a * Y(V1) + b * Y(V2), rtol=1e-11, atol=1e-12)
+    P = lambda V: oracle.pp_forward(Q, K, V)[0]
+    assert np.max(abs(P(a * V1 + b * V2) - (a * P(V1) + b * P(V2)))) > 1e-3
+
+
+def test_sampled_rows_match_full_decode():
+    Q, K, V = rand(2, 5, 8), rand(1, 2, 50, 8), rand(1, 2, 50, 8)
+    Y, Z = oracle.forward(Q, K, V)
+    rows = np.array([49, 0, 17, 17, 3])
+    Ys, _ = oracle.forward(Q, K, V, rows=rows)
+    np.testing.assert_array_equal(Ys, Y[:, :, rows])
+
+
+# ------------------------------------------------------- input widening / gen
+def test_bf16_widening_matches_torch():
+    x = RNG.standard_normal(4096).astype(np.float32) * 3
+    bits = f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.widen(bits), ref)
+
+
+def test_generator_is_deterministic_and_shaped():
+    a = make_inputs(2, 3, 100, 7, 16, "bf16", 0.5, 1.0, seed=9)
+    b = make_inputs(2, 3, 100, 7, 16, "bf16", 0.5, 1.0, seed=9)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    assert a[0].shape == (3, 7, 16) and a[1].shape == (2, 3, 100, 16) and a[0].dtype == np.uint16
+    q32 = make_inputs(1, 1, 8, 4, 16, "f32", 2.0, 1.0, seed=3)[0]
+    assert q32.dtype == np.float32 and 1.0 < q32.std() < 3.0
