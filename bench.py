@@ -1,0 +1,188 @@
+"""Benchmark of the FLARE forward hot path on one MI355X.
+
+One step = one full pass of the operator over one batch of synthetic inputs
+that are already resident in HBM: split-N encode -> combine -> decode (FLARE),
+or the five-launch FLARE++ sequence, through the C ABI's caller-workspace
+entry point. Default workload: the PDE-mesh shape B=4, H=8, N=65536, M=128,
+D=32 in bf16 (the throughput metric is quoted on N=65536, M=128).
+
+Prints one JSON line with throughput (tokens*heads/s), the roofline position
+of the dominant kernel (its average duration measured with HIP events on the
+launch stream during the timed steps), and the fp64 CPU oracle's throughput
+on a bounded sample of the same workload as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+KERNEL_SOURCES = {
+    "encode_partial": ["rank_latent_attention_flare_amd/csrc/kernels_bf16.hip"],
+    "decode": ["rank_latent_attention_flare_amd/csrc/kernels_bf16.hip"],
+    "combine": ["rank_latent_attention_flare_amd/csrc/kernels_common.hip"],
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", type=int, default=2, help="workload number 1-5 (default 2)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy-mib", type=int, default=512,
+                   help="size of the plain copy kernel run once before the timed steps (counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this "
+              "build: the kernels shard by (batch, head) or by tokens, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from flare_inputs import WORKLOADS, recipe, workload_inputs
+    from rank_latent_attention_flare_amd import flare as F
+
+    if not os.path.exists(F.LIB_PATH):
+        from rank_latent_attention_flare_amd.build import build
+        build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = WORKLOADS[args.workload]
+    op = F.FLARE_OP_PP_FORWARD if w.op == "pp_forward" else F.FLARE_OP_FORWARD
+    fn = F.flare_pp_forward if op == F.FLARE_OP_PP_FORWARD else F.flare_forward
+
+    Qh, Kh, Vh = workload_inputs(w)
+
+    def dev(a):
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+        return t.view(torch.bfloat16) if a.dtype == np.uint16 else t
+
+    Q, K, V = dev(Qh), dev(Kh), dev(Vh)
+    Y = torch.empty_like(K)
+    ws = F.workspace_for(op, Q, K)
+    stream = torch.cuda.current_stream()
+
+    # plain copy of known size (scales hardware memory counters to bytes)
+    if args.calib_copy_mib > 0:
+        nb = args.calib_copy_mib << 20
+        a = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        F.flare_copy_kernel(a, b)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        fn(Q, K, V, out=Y, workspace=ws)
+    torch.cuda.synchronize()
+
+    F.flare_timing_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        fn(Q, K, V, out=Y, workspace=ws)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    kt = F.flare_timing_read()
+    F.flare_timing_enable(False)
+    if not torch.isfinite(Y.float()).all():
+        print("non-finite output", file=sys.stderr)
+        sys.exit(1)
+
+    ms_step = total_ms / args.steps
+    tok_heads = w.B * w.H * w.N
+    value = tok_heads / (ms_step * 1e-3)
+    e = 2 if w.dtype == "bf16" else 4
+    kv_bytes = w.B * w.H * w.N * w.D * e
+    passes = 2 if op == F.FLARE_OP_PP_FORWARD else 1
+    flops_step = (12 if passes == 2 else 8) * w.B * w.H * w.N * w.M * w.D
+    kern = {}
+    for kind, (ms, cnt) in kt.items():
+        if cnt:
+            kern[kind] = {"avg_us": 1e3 * ms / cnt, "launches_per_step": cnt / args.steps,
+                          "share": ms / total_ms}
+    # algorithmic bytes per launch: encode reads K and V; decode reads K and writes Y
+    alg_bytes = {"encode_partial": 2 * kv_bytes, "decode": 2 * kv_bytes}
+    dominant = max(("encode_partial", "decode"), key=lambda k: kern[k]["avg_us"] * kern[k]["launches_per_step"])
+    avg_s = kern[dominant]["avg_us"] * 1e-6
+    achieved = alg_bytes[dominant] / avg_s / 1e9
+    traffic = None
+    pmc_path = os.path.join(ROOT, "profiles", f"{dominant}_{w.name}_pmc.json")
+    if os.path.exists(pmc_path):
+        with open(pmc_path) as f:
+            pmc = json.load(f)
+        if pmc.get("source_hash") == source_hash(dominant):
+            traffic = pmc.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "alg_bytes_per_launch": alg_bytes[dominant],
+                "mfma_tflops_step": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
+                "mfma_frac_step": round(flops_step / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                "hbm_frac_step": round((4 if passes == 1 else 6) * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        t0 = time.perf_counter()
+        done = 0
+        for (b, h) in heads:
+            q = Qh[h]
+            if op == F.FLARE_OP_PP_FORWARD:
+                oracle.pp_forward_head(oracle.widen(q), oracle.widen(Kh[b, h]), oracle.widen(Vh[b, h]))
+            else:
+                qq, kk = oracle.widen(q), oracle.widen(Kh[b, h])
+                z = oracle.encode_head(qq, kk, oracle.widen(Vh[b, h]))
+                oracle.decode_head(qq, kk, z)
+            done += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        cpu = {"value": round(done * w.N / el, 1), "unit": "tokens*heads/s", "cores": oracle.threads(),
+               "kind": "oracle", "sample": f"{done} of {len(heads)} heads of {w.name}, full N={w.N}, "
+                                            f"fp64 {w.op}, {el:.1f} s"}
+
+    line = {
+        "metric": "FLARE fwd tokens*heads/s (N=65536, M=128) + roofline fraction",
+        "value": round(value, 1), "unit": "tokens*heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (" + recipe() + ")",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "op": w.op,
+                   "plan": F.flare_describe_plan(op, w.B, w.H, w.N, w.M, w.D, Q.dtype)},
+        "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kern.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * libflare: FLARE / FLARE++ low-rank attention routing, forward pass, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operator (per batch item b and head h; heads are independent and each owns
+ * its own latent slice, FLARE arXiv abstract):
+ *   logits   l[m][n] = s * <Q[h][m], K[b][h][n]>,  s = 1/sqrt(D)
+ *   encode   Z[m]    = sum_n softmax_n(l[m][.])[n] * V[b][h][n]
+ *            (latents attend to tokens: FLARE skill page, "2. Implement
+ *             Encode Stage")
+ *   decode   Y[n]    = sum_m softmax_m(l[.][n])[m] * Z[m]
+ *            (tokens attend back through the transposed logits; the
+ *             encode-decode factorization of the FLARE arXiv abstract)
+ *   FLARE++  Q' = Q + encode(Q, K, V), then encode and decode with Q'
+ *            (FLARE++ arXiv abstract: the encoder's output corrects the
+ *             learned queries)
+ *
+ * Conventions shared by every entry point
+ *   Layout    Q is [H][M][D] (one latent set per head, shared over the batch).
+ *             K, V and Y are [B][H][N][D]. Z is [B][H][M][D]. All row-major,
+ *             contiguous, D innermost.
+ *   Memory    All tensor pointers are device pointers on the current HIP
+ *             device, 16-byte aligned. The caller owns every tensor; the
+ *             library neither frees nor retains them.
+ *   Types     dtype selects the element type of Q, K, V, Z and Y alike.
+ *             FLARE_F32 computes in fp32 throughout. FLARE_BF16 feeds bf16
+ *             MFMA and keeps every accumulator, softmax statistic and Z in
+ *             fp32; probabilities, Z and Q' are rounded to nearest-even bf16
+ *             where they become MFMA operands, and outputs are rounded to
+ *             nearest-even bf16.
+ *   Sizes     B, H, N, M, D >= 1. Supported: FLARE_F32 with D <= 128 and
+ *             M <= 512; FLARE_BF16 with D in {32, 64, 128} and M <= 256.
+ *   Async     Work is enqueued on `stream` (0 = the legacy default stream)
+ *             and the call returns; inputs must stay unchanged until the
+ *             stream passes the call. Device faults surface at the caller's
+ *             next synchronisation.
+ *   Errors    A call returns FLARE_OK or an error status and never aborts.
+ *             Arguments are validated before any launch, so an error status
+ *             other than FLARE_ERR_HIP means nothing was enqueued.
+ *             flare_last_error() describes the last failure of the calling
+ *             thread.
+ *   Workspace The plain entry points allocate stream-ordered scratch memory
+ *             (hipMallocAsync/hipFreeAsync on `stream`). The *_ws variants
+ *             take caller-owned scratch memory of at least
+ *             flare_workspace_size() bytes instead; concurrent calls must not
+ *             share one workspace.
+ */
+#ifndef LIBFLARE_FLARE_H
+#define LIBFLARE_FLARE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FLARE_F32 = 0, FLARE_BF16 = 1 } flare_dtype;
+
+typedef enum {
+    FLARE_OK = 0,
+    FLARE_ERR_INVALID_ARG = 1, /* null pointer, size < 1, misaligned or aliased tensors, small workspace */
+    FLARE_ERR_UNSUPPORTED = 2, /* (dtype, D, M) outside the supported set */
+    FLARE_ERR_NO_MEMORY = 3,   /* scratch allocation failed */
+    FLARE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} flare_status;
+
+typedef enum { FLARE_OP_ENCODE = 0, FLARE_OP_DECODE = 1, FLARE_OP_FORWARD = 2, FLARE_OP_PP_FORWARD = 3 } flare_op;
+
+/* Encode: Y := Z[B][H][M][D] = softmax_n(s Q K^T) V for every (b, h).
+ * FLARE skill page, "2. Implement Encode Stage"; encode half of step 4.
+ * Inputs Q [H][M][D], K and V [B][H][N][D]; output Y is the Z tensor. */
+flare_status flare_encode(const void* Q, const void* K, const void* V, void* Y,
+                          int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                          flare_dtype dtype, hipStream_t stream);
+
+/* Decode: Y[B][H][N][D] = softmax_m(s K Q^T) Z for every (b, h), with the
+ * latents Z passed in the V argument as [B][H][M][D]. The decode half of the
+ * FLARE encode-decode factorization (FLARE arXiv abstract). K is [B][H][N][D]. */
+flare_status flare_decode(const void* Q, const void* K, const void* V, void* Y,
+                          int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                          flare_dtype dtype, hipStream_t stream);
+
+/* FLARE forward: Y = decode(Q, K, encode(Q, K, V)). Z stays fp32 between the
+ * two stages and is rounded once when it becomes an MFMA operand, so the
+ * result equals flare_decode(flare_encode(.)) for the same shapes.
+ * FLARE skill page, step 4; FLARE arXiv abstract ("two SDPA calls"). */
+flare_status flare_forward(const void* Q, const void* K, const void* V, void* Y,
+                           int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                           flare_dtype dtype, hipStream_t stream);
+
+/* FLARE++ forward: Q'[b][h] = Q[h] + encode(Q, K, V)[b][h] (rounded to dtype),
+ * then Y = decode(Q', K, encode(Q', K, V)). FLARE++ skill page, "Core
+ * Mechanism"; FLARE++ arXiv abstract. */
+flare_status flare_pp_forward(const void* Q, const void* K, const void* V, void* Y,
+                              int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                              flare_dtype dtype, hipStream_t stream);
+
+/* Scratch bytes the *_ws variant of `op` needs for these sizes (0 when the
+ * sizes or type are invalid or unsupported). */
+size_t flare_workspace_size(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                            flare_dtype dtype);
+
+/* Variants taking caller-owned scratch memory (device pointer, 256-byte
+ * aligned, at least flare_workspace_size(op, ...) bytes). Same results as the
+ * plain entry points; nothing is allocated. */
+flare_status flare_encode_ws(const void* Q, const void* K, const void* V, void* Y,
+                             int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                             flare_dtype dtype, hipStream_t stream, void* workspace, size_t ws_bytes);
+flare_status flare_decode_ws(const void* Q, const void* K, const void* V, void* Y,
+                             int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                             flare_dtype dtype, hipStream_t stream, void* workspace, size_t ws_bytes);
+flare_status flare_forward_ws(const void* Q, const void* K, const void* V, void* Y,
+                              int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                              flare_dtype dtype, hipStream_t stream, void* workspace, size_t ws_bytes);
+flare_status flare_pp_forward_ws(const void* Q, const void* K, const void* V, void* Y,
+                                 int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                 flare_dtype dtype, hipStream_t stream, void* workspace, size_t ws_bytes);
+
+/* Static text for a status code. */
+const char* flare_status_string(flare_status s);
+
+/* Detail of the calling thread's last non-OK status ("" if none). The
+ * pointer stays valid until the thread's next libflare call. */
+const char* flare_last_error(void);
+
+/* ---------------------------------------------------------- measurement
+ * Kernel timing with HIP events recorded on the launch stream around every
+ * kernel the library enqueues. Kernel kinds: 0 = encode partial (split-N
+ * online softmax), 1 = combine, 2 = decode. */
+#define FLARE_KERNEL_KINDS 3
+
+/* Turn event recording on (1) or off (0) for the calling process, and drop
+ * every recorded event. */
+flare_status flare_timing_enable(int on);
+
+/* Wait for the recorded events, add the elapsed milliseconds of each kernel
+ * kind into ms[kind] and the number of launches into count[kind] (arrays of
+ * FLARE_KERNEL_KINDS entries), then drop them. */
+flare_status flare_timing_read(double* ms, int64_t* count);
+
+/* Plain device-to-device copy of `bytes` bytes (multiple of 16, 16-byte
+ * aligned pointers) on `stream`: a kernel of known traffic, used to scale
+ * hardware memory counters to bytes. */
+flare_status flare_copy_kernel(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+/* Launch plan the library would use (for logs): writes a short text into
+ * buf (up to len bytes incl. the terminator). */
+flare_status flare_describe_plan(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                 flare_dtype dtype, char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFLARE_FLARE_H */

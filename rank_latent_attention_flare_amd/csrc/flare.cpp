@@ -1,0 +1,469 @@
+// libflare host runtime: argument validation, launch planning, workspace
+// layout, kernel dispatch and the C ABI declared in include/flare.h.
+//
+// Launch sequences (all on the caller's stream):
+//   encode      K1 encode partials -> K2 combine (Z in dtype)
+//   decode      K3 decode (Z given)
+//   forward     K1 -> K2 (fp32 Z) -> K3
+//   pp_forward  K1(Q) -> K2 (Q' = Q + Z0) -> K1(Q') -> K2 (fp32 Z) -> K3(Q')
+// FLARE skill page steps 2-4 and FLARE arXiv abstract (encode/decode);
+// FLARE++ skill page "Core Mechanism" and FLARE++ arXiv abstract (Q').
+#include "flare.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+using flare::CombineArgs;
+using flare::DecodeArgs;
+using flare::EncodeArgs;
+
+thread_local std::string g_last_error;
+
+flare_status fail(flare_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+flare_status hip_fail(hipError_t e, const char* what) {
+    return fail(FLARE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+constexpr int kTargetEncWaves = 2048;  // waves over all encode workgroups
+constexpr int kTargetDecWgs = 1024;    // decode workgroups
+constexpr int64_t kMaxGridY = 65535;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Plan {
+    flare_dtype dt;
+    int64_t B, H, N, M, D;
+    int BH, Mp;
+    int C, chunk_len;  // encode split over N
+    int G;             // decode workgroups per (b, h)
+    size_t esize;
+    size_t off_acc, off_mu, off_sig, off_z, off_qp, total[4];
+    float c;
+};
+
+bool supported(flare_dtype dt, int64_t D, int64_t M, std::string* why) {
+    if (dt == FLARE_BF16) {
+        if (!(D == 32 || D == 64 || D == 128)) {
+            *why = "bf16 supports D in {32, 64, 128}";
+            return false;
+        }
+        if (M > 256) {
+            *why = "bf16 supports M <= 256";
+            return false;
+        }
+        return true;
+    }
+    if (!(D == 8 || D == 16 || D == 24 || D == 32 || D == 48 || D == 64 || D == 96 || D == 128)) {
+        *why = "fp32 supports D in {8, 16, 24, 32, 48, 64, 96, 128}";
+        return false;
+    }
+    if (M > 4096) {
+        *why = "fp32 supports M <= 4096";
+        return false;
+    }
+    return true;
+}
+
+// Sizes and type only (no pointers). Returns OK and fills the plan.
+flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dt, Plan* p) {
+    if (dt != FLARE_F32 && dt != FLARE_BF16) return fail(FLARE_ERR_INVALID_ARG, "dtype must be FLARE_F32 or FLARE_BF16");
+    if (B < 1 || H < 1 || N < 1 || M < 1 || D < 1)
+        return fail(FLARE_ERR_INVALID_ARG, "B, H, N, M and D must all be >= 1");
+    std::string why;
+    if (!supported(dt, D, M, &why)) return fail(FLARE_ERR_UNSUPPORTED, why);
+    if (B * H > kMaxGridY) return fail(FLARE_ERR_UNSUPPORTED, "B*H must be <= 65535");
+    if (N > (int64_t(1) << 30)) return fail(FLARE_ERR_UNSUPPORTED, "N must be <= 2^30");
+    const int64_t esz = dt == FLARE_BF16 ? 2 : 4;
+    // every tensor byte count must fit comfortably in 63 bits
+    const double kv = double(B) * double(H) * double(N) * double(D) * double(esz);
+    if (kv > 4.0e18) return fail(FLARE_ERR_INVALID_ARG, "tensor sizes overflow");
+
+    p->dt = dt;
+    p->B = B; p->H = H; p->N = N; p->M = M; p->D = D;
+    p->BH = int(B * H);
+    p->esize = size_t(esz);
+    p->c = float((1.0 / std::sqrt(double(D))) * 1.4426950408889634);
+    int tile, waves_per_wg;
+    if (dt == FLARE_BF16) {
+        p->Mp = int((M + 31) / 32 * 32);
+        const flare::EncCfg cfg = flare::enc_cfg_bf16(int(D), p->Mp / 32);
+        tile = flare::enc_tile_tokens_bf16(cfg);
+        waves_per_wg = flare::enc_threads_bf16(cfg) / 64;
+    } else {
+        p->Mp = int(M);
+        tile = 64;
+        waves_per_wg = 4 * int((M + 255) / 256);
+    }
+    // Split over N: enough workgroups to fill the chip, but chunks of at least
+    // 32*Mp tokens so that the partials stay a few percent of the K/V bytes.
+    const int64_t target_wgs = std::max<int64_t>(1, kTargetEncWaves / waves_per_wg);
+    int64_t C = std::max<int64_t>(1, (target_wgs + p->BH - 1) / p->BH);
+    const int64_t cmax = std::max<int64_t>(1, N / (32 * int64_t(p->Mp)));
+    C = std::min(C, cmax);
+    if (const char* e = std::getenv("FLARE_TEST_CHUNKS")) {
+        const long v = std::strtol(e, nullptr, 10);
+        if (v > 0) C = v;
+    }
+    int64_t chunk = (N + C - 1) / C;
+    chunk = (chunk + tile - 1) / tile * tile;
+    C = (N + chunk - 1) / chunk;
+    p->C = int(C);
+    p->chunk_len = int(chunk);
+    // decode workgroups per (b, h)
+    const int64_t per_wg = 32 * flare::kDecTB * flare::kDecWaves;
+    int64_t G = std::max<int64_t>(1, (kTargetDecWgs + p->BH - 1) / p->BH);
+    G = std::min<int64_t>(G, (N + per_wg - 1) / per_wg);
+    p->G = int(G);
+    // workspace layout
+    const size_t parts = size_t(p->BH) * size_t(C) * size_t(p->Mp);
+    size_t off = 0;
+    p->off_acc = off; off = align256(off + parts * size_t(D) * 4);
+    p->off_mu = off;  off = align256(off + parts * 4);
+    p->off_sig = off; off = align256(off + parts * 4);
+    const size_t enc_total = off;
+    p->off_z = off;   off = align256(off + size_t(p->BH) * size_t(M) * size_t(D) * 4);
+    const size_t fwd_total = off;
+    p->off_qp = off;  off = align256(off + size_t(p->BH) * size_t(M) * size_t(D) * p->esize);
+    p->total[FLARE_OP_ENCODE] = enc_total;
+    p->total[FLARE_OP_DECODE] = 0;
+    p->total[FLARE_OP_FORWARD] = fwd_total;
+    p->total[FLARE_OP_PP_FORWARD] = off;
+    return FLARE_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = uintptr_t(a), y = uintptr_t(b);
+    return x < y + nb && y < x + na;
+}
+
+flare_status check_ptrs(const Plan& p, flare_op op, const void* Q, const void* K, const void* V, void* Y) {
+    if (!Q || !K || !Y || (op != FLARE_OP_DECODE && !V) || (op == FLARE_OP_DECODE && !V))
+        return fail(FLARE_ERR_INVALID_ARG, "null tensor pointer");
+    const void* ptrs[4] = {Q, K, V, Y};
+    for (const void* q : ptrs)
+        if (uintptr_t(q) % 16 != 0) return fail(FLARE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const size_t e = p.esize;
+    const size_t nq = size_t(p.H) * p.M * p.D * e;
+    const size_t nkv = size_t(p.BH) * p.N * p.D * e;
+    const size_t nz = size_t(p.BH) * p.M * p.D * e;
+    const size_t nv = op == FLARE_OP_DECODE ? nz : nkv;
+    const size_t ny = op == FLARE_OP_ENCODE ? nz : nkv;
+    if (overlaps(Y, ny, Q, nq) || overlaps(Y, ny, K, nkv) || overlaps(Y, ny, V, nv))
+        return fail(FLARE_ERR_INVALID_ARG, "output overlaps an input");
+    return FLARE_OK;
+}
+
+// ------------------------------------------------------------------ timing
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    struct Rec {
+        int kind;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> pool;
+};
+Timing g_timing;
+
+hipEvent_t take_event() {
+    if (!g_timing.pool.empty()) {
+        hipEvent_t e = g_timing.pool.back();
+        g_timing.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F&& launch) {
+    std::unique_lock<std::mutex> lk(g_timing.mu);
+    if (!g_timing.on) {
+        lk.unlock();
+        return launch();
+    }
+    hipEvent_t a = take_event(), b = take_event();
+    if (!a || !b) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(a, s);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(b, s);
+    if (e != hipSuccess) return e;
+    g_timing.recs.push_back({kind, a, b});
+    return hipSuccess;
+}
+
+// --------------------------------------------------------------- launchers
+hipError_t run_encode_partial(const Plan& p, const void* Q, int64_t q_bstride, const void* K, const void* V,
+                              char* ws, hipStream_t s) {
+    EncodeArgs a{};
+    a.Q = Q;
+    a.q_bstride = q_bstride;
+    a.K = K;
+    a.V = V;
+    a.BH = p.BH; a.H = int(p.H); a.N = int(p.N); a.M = int(p.M); a.Mp = p.Mp; a.D = int(p.D);
+    a.C = p.C;
+    a.chunk_len = p.chunk_len;
+    a.c = p.c;
+    a.out.acc = (float*)(ws + p.off_acc);
+    a.out.mu = (float*)(ws + p.off_mu);
+    a.out.sig = (float*)(ws + p.off_sig);
+    return timed(0, s, [&] {
+        return p.dt == FLARE_BF16 ? flare::launch_encode_bf16(a, s) : flare::launch_encode_f32(a, s);
+    });
+}
+
+hipError_t run_combine(const Plan& p, int mode, const void* Q, void* out, char* ws, hipStream_t s) {
+    CombineArgs a{};
+    a.in.acc = (float*)(ws + p.off_acc);
+    a.in.mu = (float*)(ws + p.off_mu);
+    a.in.sig = (float*)(ws + p.off_sig);
+    a.BH = p.BH; a.H = int(p.H); a.M = int(p.M); a.Mp = p.Mp; a.D = int(p.D); a.C = p.C;
+    a.mode = mode;
+    a.bf16 = p.dt == FLARE_BF16;
+    a.Q = Q;
+    a.out = out;
+    return timed(1, s, [&] { return flare::launch_combine(a, s); });
+}
+
+hipError_t run_decode(const Plan& p, const void* Q, int64_t q_bstride, const void* K, const void* Z, bool z_f32,
+                      void* Y, hipStream_t s) {
+    DecodeArgs a{};
+    a.Q = Q;
+    a.q_bstride = q_bstride;
+    a.K = K;
+    a.Z = Z;
+    a.z_f32 = z_f32;
+    a.Y = Y;
+    a.BH = p.BH; a.H = int(p.H); a.N = int(p.N); a.M = int(p.M); a.Mp = p.Mp; a.D = int(p.D);
+    a.G = p.G;
+    a.c = p.c;
+    return timed(2, s, [&] {
+        return p.dt == FLARE_BF16 ? flare::launch_decode_bf16(a, s) : flare::launch_decode_f32(a, s);
+    });
+}
+
+flare_status prepare(flare_op op, const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H,
+                     int64_t N, int64_t M, int64_t D, flare_dtype dt, void* ws, size_t ws_bytes, Plan* p) {
+    g_last_error.clear();
+    flare_status st = make_plan(B, H, N, M, D, dt, p);
+    if (st != FLARE_OK) return st;
+    st = check_ptrs(*p, op, Q, K, V, Y);
+    if (st != FLARE_OK) return st;
+    const size_t need = p->total[op];
+    if (need > 0) {
+        if (!ws) return fail(FLARE_ERR_INVALID_ARG, "workspace pointer is null");
+        if (uintptr_t(ws) % 256 != 0) return fail(FLARE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(FLARE_ERR_INVALID_ARG,
+                        "workspace too small: need " + std::to_string(need) + " bytes, got " + std::to_string(ws_bytes));
+    }
+    return FLARE_OK;
+}
+
+flare_status exec(flare_op op, const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H,
+                  int64_t N, int64_t M, int64_t D, flare_dtype dt, hipStream_t s, void* wsv, size_t ws_bytes) {
+    Plan p;
+    flare_status st = prepare(op, Q, K, V, Y, B, H, N, M, D, dt, wsv, ws_bytes, &p);
+    if (st != FLARE_OK) return st;
+    char* ws = (char*)wsv;
+    hipError_t e = hipSuccess;
+    switch (op) {
+        case FLARE_OP_ENCODE:
+            e = run_encode_partial(p, Q, 0, K, V, ws, s);
+            if (e == hipSuccess) e = run_combine(p, flare::COMBINE_Z_DTYPE, Q, Y, ws, s);
+            break;
+        case FLARE_OP_DECODE:
+            e = run_decode(p, Q, 0, K, V, dt == FLARE_F32, Y, s);
+            break;
+        case FLARE_OP_FORWARD:
+            e = run_encode_partial(p, Q, 0, K, V, ws, s);
+            if (e == hipSuccess) e = run_combine(p, flare::COMBINE_Z_F32, Q, ws + p.off_z, ws, s);
+            if (e == hipSuccess) e = run_decode(p, Q, 0, K, ws + p.off_z, true, Y, s);
+            break;
+        case FLARE_OP_PP_FORWARD: {
+            void* qp = ws + p.off_qp;
+            const int64_t qstride = H * M * D;
+            e = run_encode_partial(p, Q, 0, K, V, ws, s);
+            if (e == hipSuccess) e = run_combine(p, flare::COMBINE_QPRIME, Q, qp, ws, s);
+            if (e == hipSuccess) e = run_encode_partial(p, qp, qstride, K, V, ws, s);
+            if (e == hipSuccess) e = run_combine(p, flare::COMBINE_Z_F32, Q, ws + p.off_z, ws, s);
+            if (e == hipSuccess) e = run_decode(p, qp, qstride, K, ws + p.off_z, true, Y, s);
+            break;
+        }
+    }
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    return FLARE_OK;
+}
+
+flare_status exec_alloc(flare_op op, const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H,
+                        int64_t N, int64_t M, int64_t D, flare_dtype dt, hipStream_t s) {
+    Plan p;
+    g_last_error.clear();
+    flare_status st = make_plan(B, H, N, M, D, dt, &p);
+    if (st != FLARE_OK) return st;
+    st = check_ptrs(p, op, Q, K, V, Y);
+    if (st != FLARE_OK) return st;
+    const size_t need = p.total[op];
+    void* ws = nullptr;
+    if (need > 0) {
+        const char* f = std::getenv("FLARE_TEST_FAIL_ALLOC");
+        if (f && std::strcmp(f, "1") == 0) return fail(FLARE_ERR_NO_MEMORY, "allocation failure injected by FLARE_TEST_FAIL_ALLOC");
+        hipError_t e = hipMallocAsync(&ws, need, s);
+        if (e != hipSuccess || !ws) return fail(FLARE_ERR_NO_MEMORY, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+    }
+    st = exec(op, Q, K, V, Y, B, H, N, M, D, dt, s, ws, need);
+    if (ws) {
+        hipError_t e = hipFreeAsync(ws, s);
+        if (e != hipSuccess && st == FLARE_OK) return hip_fail(e, "hipFreeAsync");
+    }
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+flare_status flare_encode(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
+                          int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {
+    return exec_alloc(FLARE_OP_ENCODE, Q, K, V, Y, B, H, N, M, D, dtype, stream);
+}
+flare_status flare_decode(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
+                          int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {
+    return exec_alloc(FLARE_OP_DECODE, Q, K, V, Y, B, H, N, M, D, dtype, stream);
+}
+flare_status flare_forward(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
+                           int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {
+    return exec_alloc(FLARE_OP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, stream);
+}
+flare_status flare_pp_forward(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
+                              int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {
+    return exec_alloc(FLARE_OP_PP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, stream);
+}
+
+size_t flare_workspace_size(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype) {
+    if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_FORWARD) return 0;
+    Plan p;
+    if (make_plan(B, H, N, M, D, dtype, &p) != FLARE_OK) return 0;
+    return p.total[op];
+}
+
+flare_status flare_encode_ws(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
+                             int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws, size_t n) {
+    return exec(FLARE_OP_ENCODE, Q, K, V, Y, B, H, N, M, D, dtype, stream, ws, n);
+}
+flare_status flare_decode_ws(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
+                             int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws, size_t n) {
+    return exec(FLARE_OP_DECODE, Q, K, V, Y, B, H, N, M, D, dtype, stream, ws, n);
+}
+flare_status flare_forward_ws(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
+                              int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws, size_t n) {
+    return exec(FLARE_OP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, stream, ws, n);
+}
+flare_status flare_pp_forward_ws(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H,
+                                 int64_t N, int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws,
+                                 size_t n) {
+    return exec(FLARE_OP_PP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, stream, ws, n);
+}
+
+const char* flare_status_string(flare_status s) {
+    switch (s) {
+        case FLARE_OK: return "FLARE_OK";
+        case FLARE_ERR_INVALID_ARG: return "FLARE_ERR_INVALID_ARG";
+        case FLARE_ERR_UNSUPPORTED: return "FLARE_ERR_UNSUPPORTED";
+        case FLARE_ERR_NO_MEMORY: return "FLARE_ERR_NO_MEMORY";
+        case FLARE_ERR_HIP: return "FLARE_ERR_HIP";
+    }
+    return "FLARE_ERR_UNKNOWN";
+}
+
+const char* flare_last_error(void) { return g_last_error.c_str(); }
+
+flare_status flare_timing_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    for (auto& r : g_timing.recs) {
+        g_timing.pool.push_back(r.a);
+        g_timing.pool.push_back(r.b);
+    }
+    g_timing.recs.clear();
+    g_timing.on = on != 0;
+    return FLARE_OK;
+}
+
+flare_status flare_timing_read(double* ms, int64_t* count) {
+    if (!ms || !count) return fail(FLARE_ERR_INVALID_ARG, "null output array");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    flare_status st = FLARE_OK;
+    for (auto& r : g_timing.recs) {
+        float t = 0.0f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+        if (e != hipSuccess) {
+            st = hip_fail(e, "event timing");
+        } else if (r.kind >= 0 && r.kind < FLARE_KERNEL_KINDS) {
+            ms[r.kind] += double(t);
+            count[r.kind] += 1;
+        }
+        g_timing.pool.push_back(r.a);
+        g_timing.pool.push_back(r.b);
+    }
+    g_timing.recs.clear();
+    return st;
+}
+
+flare_status flare_copy_kernel(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+    g_last_error.clear();
+    if (!src || !dst) return fail(FLARE_ERR_INVALID_ARG, "null pointer");
+    if (bytes % 16 || uintptr_t(src) % 16 || uintptr_t(dst) % 16)
+        return fail(FLARE_ERR_INVALID_ARG, "copy needs 16-byte aligned pointers and size");
+    if (overlaps(src, bytes, dst, bytes)) return fail(FLARE_ERR_INVALID_ARG, "copy ranges overlap");
+    hipError_t e = flare::launch_copy(src, dst, bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "copy kernel");
+    return FLARE_OK;
+}
+
+flare_status flare_describe_plan(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                 flare_dtype dtype, char* buf, size_t len) {
+    g_last_error.clear();
+    if (!buf || len == 0) return fail(FLARE_ERR_INVALID_ARG, "null buffer");
+    if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_FORWARD) return fail(FLARE_ERR_INVALID_ARG, "bad op");
+    Plan p;
+    flare_status st = make_plan(B, H, N, M, D, dtype, &p);
+    if (st != FLARE_OK) return st;
+    std::string enc;
+    if (dtype == FLARE_BF16) {
+        const flare::EncCfg cfg = flare::enc_cfg_bf16(int(D), p.Mp / 32);
+        enc = "encode grid (" + std::to_string(p.C) + "," + std::to_string(p.BH) + ") waves " +
+              std::to_string(cfg.wm) + "x" + std::to_string(cfg.wt) + " latent-blocks/wave " + std::to_string(cfg.mbw) +
+              " tile " + std::to_string(flare::enc_tile_tokens_bf16(cfg));
+    } else {
+        enc = "encode grid (" + std::to_string(p.C) + "," + std::to_string(p.BH) + "," + std::to_string((M + 255) / 256) +
+              ") threads 256";
+    }
+    std::string txt = enc + " chunk " + std::to_string(p.chunk_len) + "; decode grid (" +
+                      (dtype == FLARE_BF16 ? std::to_string(p.G) : std::to_string((N + 255) / 256)) + "," +
+                      std::to_string(p.BH) + "); workspace " + std::to_string(p.total[op]) + " bytes";
+    std::snprintf(buf, len, "%s", txt.c_str());
+    return FLARE_OK;
+}
+
+}  // extern "C"

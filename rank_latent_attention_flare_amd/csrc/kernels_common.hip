@@ -1,0 +1,237 @@
+// FLARE forward kernels shared by both storage types, and the fp32 path.
+//
+//  combine           merges the split-N encode partials into Z (or Q' = Q + Z
+//                    for FLARE++), in a fixed chunk order (deterministic).
+//  encode_partial_f32, decode_f32
+//                    fp32 storage and arithmetic throughout (no reduced-
+//                    precision operands): one lane per latent in the encode,
+//                    one lane per token in the decode, each with an exact
+//                    online softmax (running maximum, rescaled sums).
+//  copy_kernel       plain 16-byte-per-lane copy of known traffic.
+//
+// Operator (FLARE skill page, steps 2 and 4; FLARE arXiv abstract):
+// Z[m] = softmax_n(s <Q[m], K[n]>) V, Y[n] = softmax_m(s <Q[m], K[n]>) Z, with
+// s = 1/sqrt(D); exponentials in base 2 on logits scaled by c = s log2(e).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace flare {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Combine (FLARE++ residual included). One thread per (b, h, m, d):
+//   mu* = max_c mu_c,  w_c = 2^(mu_c - mu*),
+//   Z = sum_c w_c acc_c / sum_c w_c sig_c
+// which is exactly the softmax over all N tokens (log-sum-exp merge).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+    const int bh = blockIdx.y;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= a.M * a.D) return;
+    const int m = idx / a.D, d = idx - m * a.D;
+    const int C = a.C, Mp = a.Mp, D = a.D;
+    const int64_t base = (int64_t)bh * C * Mp;
+    float mx = -INFINITY;
+    for (int c = 0; c < C; ++c) mx = fmaxf(mx, a.in.mu[base + (int64_t)c * Mp + m]);
+    float num = 0.0f, den = 0.0f;
+    for (int c = 0; c < C; ++c) {
+        const int64_t r = base + (int64_t)c * Mp + m;
+        const float mc = a.in.mu[r];
+        const float w = (mc == -INFINITY) ? 0.0f : exp2f(mc - mx);
+        num = fmaf(w, a.in.acc[r * D + d], num);
+        den = fmaf(w, a.in.sig[r], den);
+    }
+    const float z = num / den;
+    const int64_t o = (int64_t)bh * a.M * D + idx;
+    if (a.mode == COMBINE_Z_F32) {
+        ((float*)a.out)[o] = z;
+    } else if (a.mode == COMBINE_Z_DTYPE) {
+        if (a.bf16)
+            ((uint16_t*)a.out)[o] = f32_to_bf16_rne(z);
+        else
+            ((float*)a.out)[o] = z;
+    } else {
+        const int h = bh % a.H;
+        const int64_t qi = (int64_t)h * a.M * D + idx;
+        if (a.bf16) {
+            const uint16_t qb = ((const uint16_t*)a.Q)[qi];
+            const float q = __uint_as_float((uint32_t)qb << 16);
+            ((uint16_t*)a.out)[o] = f32_to_bf16_rne(q + z);
+        } else {
+            ((float*)a.out)[o] = ((const float*)a.Q)[qi] + z;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 encode partials: grid (C, BH, latent groups of 256); thread = latent.
+// K/V tiles of 64 tokens go through LDS; each thread keeps its latent's exact
+// running maximum, sum and accumulator.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
+    constexpr int T = 64;
+    __shared__ float kt[T * D], vt[T * D];
+    const int tid = threadIdx.x;
+    const int chunk = blockIdx.x, bh = blockIdx.y;
+    const int m = blockIdx.z * 256 + tid;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int N = a.N, M = a.M;
+    const int n0 = chunk * a.chunk_len, n1 = min(N, n0 + a.chunk_len);
+    const float c = a.c;
+    const float* Kb = (const float*)a.K + (int64_t)bh * N * D;
+    const float* Vb = (const float*)a.V + (int64_t)bh * N * D;
+    const float* Qb = (const float*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
+    const bool active = m < M;
+    float q[D], acc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        q[d] = active ? Qb[(int64_t)m * D + d] : 0.0f;
+        acc[d] = 0.0f;
+    }
+    float mu = -INFINITY, sig = 0.0f;
+    for (int t0 = n0; t0 < n1; t0 += T) {
+        const int nt = min(T, n1 - t0);
+        for (int e = tid; e < nt * D; e += 256) {
+            kt[e] = Kb[(int64_t)t0 * D + e];
+            vt[e] = Vb[(int64_t)t0 * D + e];
+        }
+        __syncthreads();
+        if (active) {
+            for (int t = 0; t < nt; ++t) {
+                float s = 0.0f;
+#pragma unroll
+                for (int d = 0; d < D; ++d) s = fmaf(q[d], kt[t * D + d], s);
+                const float x = s * c;
+                if (x > mu) {
+                    const float alpha = (mu == -INFINITY) ? 0.0f : exp2f(mu - x);
+                    sig *= alpha;
+#pragma unroll
+                    for (int d = 0; d < D; ++d) acc[d] *= alpha;
+                    mu = x;
+                }
+                const float p = exp2f(x - mu);
+                sig += p;
+#pragma unroll
+                for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vt[t * D + d], acc[d]);
+            }
+        }
+        __syncthreads();
+    }
+    if (active) {
+        const int64_t r = ((int64_t)bh * gridDim.x + chunk) * a.Mp + m;
+        a.out.mu[r] = mu;
+        a.out.sig[r] = sig;
+#pragma unroll
+        for (int d = 0; d < D; ++d) a.out.acc[r * D + d] = acc[d];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 decode: grid (token blocks of 256, BH); thread = token. Exact online
+// softmax over the latents; Q and Z rows are read with wave-uniform addresses.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void decode_f32(DecodeArgs a) {
+    const int bh = blockIdx.y;
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int N = a.N, M = a.M;
+    if (n >= N) return;
+    const float c = a.c;
+    const float* Qb = (const float*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
+    const float* Zb = (const float*)a.Z + (int64_t)bh * M * D;
+    const float* kr = (const float*)a.K + ((int64_t)bh * N + n) * D;
+    float k[D], y[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        k[d] = kr[d];
+        y[d] = 0.0f;
+    }
+    float nu = -INFINITY, tau = 0.0f;
+    for (int m = 0; m < M; ++m) {
+        float s = 0.0f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) s = fmaf(Qb[(int64_t)m * D + d], k[d], s);
+        const float x = s * c;
+        if (x > nu) {
+            const float alpha = (nu == -INFINITY) ? 0.0f : exp2f(nu - x);
+            tau *= alpha;
+#pragma unroll
+            for (int d = 0; d < D; ++d) y[d] *= alpha;
+            nu = x;
+        }
+        const float p = exp2f(x - nu);
+        tau += p;
+#pragma unroll
+        for (int d = 0; d < D; ++d) y[d] = fmaf(p, Zb[(int64_t)m * D + d], y[d]);
+    }
+    float* yr = (float*)a.Y + ((int64_t)bh * N + n) * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) yr[d] = y[d] / tau;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                    size_t n16) {
+    for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+        dst[i] = src[i];
+}
+
+template <int D>
+hipError_t enc_f32(const EncodeArgs& a, hipStream_t s) {
+    dim3 grid(a.C, a.BH, (a.M + 255) / 256), block(256);
+    hipLaunchKernelGGL((encode_partial_f32<D>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t dec_f32(const DecodeArgs& a, hipStream_t s) {
+    dim3 grid((a.N + 255) / 256, a.BH), block(256);
+    hipLaunchKernelGGL((decode_f32<D>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// fp32 kernels are instantiated for head widths that are multiples of 8.
+#define FLARE_F32_DISPATCH(FN, a, s)     \
+    switch ((a).D) {                     \
+        case 8: return FN<8>(a, s);      \
+        case 16: return FN<16>(a, s);    \
+        case 24: return FN<24>(a, s);    \
+        case 32: return FN<32>(a, s);    \
+        case 48: return FN<48>(a, s);    \
+        case 64: return FN<64>(a, s);    \
+        case 96: return FN<96>(a, s);    \
+        case 128: return FN<128>(a, s);  \
+        default: return hipErrorInvalidValue; \
+    }
+
+hipError_t launch_encode_f32(const EncodeArgs& a, hipStream_t s) { FLARE_F32_DISPATCH(enc_f32, a, s) }
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { FLARE_F32_DISPATCH(dec_f32, a, s) }
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+    dim3 grid((a.M * a.D + 255) / 256, a.BH), block(256);
+    hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return hipSuccess;
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4*)src, (u32x4*)dst, n16);
+    return hipGetLastError();
+}
+
+}  // namespace flare

@@ -1,0 +1,75 @@
+// Internal interface between the host runtime (flare.cpp) and the gfx950
+// kernels (kernels_bf16.hip, kernels_f32.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flare {
+
+// Where the split-N encode writes its per-chunk online-softmax state.
+struct Partials {
+    float* acc;  // [BH][C][Mp][D] unnormalised sums of p * V
+    float* mu;   // [BH][C][Mp]    offsets (log2 units) the sums are taken against
+    float* sig;  // [BH][C][Mp]    sums of p
+};
+
+struct EncodeArgs {
+    const void* Q;       // [H][M][D] or, with q_bstride > 0, [B][H][M][D]
+    int64_t q_bstride;   // elements between batch entries of Q (0: shared)
+    const void* K;       // [B][H][N][D]
+    const void* V;       // [B][H][N][D]
+    int BH, H, N, M, Mp, D;
+    int C, chunk_len;    // chunks per (b, h) and tokens per chunk
+    float c;             // (1/sqrt(D)) * log2(e)
+    Partials out;
+};
+
+// What the combine writes.
+enum CombineMode {
+    COMBINE_Z_F32 = 0,    // fp32 Z [BH][M][D]
+    COMBINE_Z_DTYPE = 1,  // Z in the operator dtype [BH][M][D]
+    COMBINE_QPRIME = 2    // Q' = Q + Z in the operator dtype [BH][M][D]
+};
+
+struct CombineArgs {
+    Partials in;
+    int BH, H, M, Mp, D, C;
+    int mode;
+    bool bf16;           // operator dtype (for modes 1 and 2)
+    const void* Q;       // mode 2: learned queries [H][M][D]
+    void* out;
+};
+
+struct DecodeArgs {
+    const void* Q;       // as in EncodeArgs
+    int64_t q_bstride;
+    const void* K;       // [B][H][N][D]
+    const void* Z;       // [BH][M][D], fp32 or operator dtype
+    bool z_f32;
+    void* Y;             // [B][H][N][D]
+    int BH, H, N, M, Mp, D;
+    int G;               // workgroups per (b, h)
+    float c;
+};
+
+// Encode tile configuration for bf16 (waves over latent blocks x waves over tokens).
+struct EncCfg {
+    int mbw, wm, wt;
+};
+EncCfg enc_cfg_bf16(int D, int Mb);
+int enc_tile_tokens_bf16(EncCfg cfg);
+int enc_threads_bf16(EncCfg cfg);
+
+constexpr int kDecWaves = 4;  // waves per decode workgroup
+constexpr int kDecTB = 2;     // 32-token blocks per wave per step
+int dec_lds_bytes_bf16(int Mp, int D);
+
+hipError_t launch_encode_bf16(const EncodeArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_encode_f32(const EncodeArgs& a, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace flare

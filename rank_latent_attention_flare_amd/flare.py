@@ -1,0 +1,181 @@
+"""Python binding of libflare: argument marshalling only.
+
+Each function has the name of the C entry point it calls (include/flare.h)
+and passes device pointers, sizes, the dtype code and the current torch
+stream. No arithmetic of the operator happens here; PyTorch provides device
+memory and streams. If libflare.so has not been built the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflare.so")
+
+FLARE_F32, FLARE_BF16 = 0, 1
+FLARE_OP_ENCODE, FLARE_OP_DECODE, FLARE_OP_FORWARD, FLARE_OP_PP_FORWARD = 0, 1, 2, 3
+FLARE_KERNEL_KINDS = 3
+KERNEL_KIND_NAMES = ("encode_partial", "combine", "decode")
+
+STATUS = {0: "FLARE_OK", 1: "FLARE_ERR_INVALID_ARG", 2: "FLARE_ERR_UNSUPPORTED", 3: "FLARE_ERR_NO_MEMORY",
+          4: "FLARE_ERR_HIP"}
+
+
+class FlareError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_ENTRY = ["flare_encode", "flare_decode", "flare_forward", "flare_pp_forward"]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libflare.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m rank_latent_attention_flare_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        base = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
+        for name in _ENTRY:
+            getattr(L, name).argtypes = base
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name + "_ws").argtypes = base + [_vp, ctypes.c_size_t]
+            getattr(L, name + "_ws").restype = ctypes.c_int
+        L.flare_workspace_size.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+        L.flare_workspace_size.restype = ctypes.c_size_t
+        L.flare_status_string.argtypes = [ctypes.c_int]
+        L.flare_status_string.restype = ctypes.c_char_p
+        L.flare_last_error.argtypes = []
+        L.flare_last_error.restype = ctypes.c_char_p
+        L.flare_timing_enable.argtypes = [ctypes.c_int]
+        L.flare_timing_enable.restype = ctypes.c_int
+        L.flare_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]
+        L.flare_timing_read.restype = ctypes.c_int
+        L.flare_copy_kernel.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+        L.flare_copy_kernel.restype = ctypes.c_int
+        L.flare_describe_plan.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                          ctypes.c_char_p, ctypes.c_size_t]
+        L.flare_describe_plan.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _raise(st: int) -> None:
+    if st != 0:
+        raise FlareError(st, lib().flare_last_error().decode())
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return FLARE_F32
+    if dt == torch.bfloat16:
+        return FLARE_BF16
+    raise TypeError(f"libflare handles float32 and bfloat16 tensors, not {dt}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dims(op: int, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor):
+    if Q.dim() != 3 or K.dim() != 4 or V.dim() != 4:
+        raise ValueError("expected Q [H, M, D], K [B, H, N, D] and V [B, H, N, D] (Z [B, H, M, D] for decode)")
+    H, M, D = Q.shape
+    B, H2, N, D2 = K.shape
+    if H2 != H or D2 != D:
+        raise ValueError(f"K shape {tuple(K.shape)} does not match Q shape {tuple(Q.shape)}")
+    want_v = (B, H, M, D) if op == FLARE_OP_DECODE else (B, H, N, D)
+    if tuple(V.shape) != want_v:
+        raise ValueError(f"{'Z' if op == FLARE_OP_DECODE else 'V'} shape {tuple(V.shape)}, expected {want_v}")
+    for t in (Q, K, V):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != Q.dtype:
+            raise ValueError("Q, K and V must be contiguous device tensors of one dtype")
+    return B, H, N, M, D
+
+
+def _out(op, B, H, N, M, D, like: torch.Tensor, out: Optional[torch.Tensor]) -> torch.Tensor:
+    shape = (B, H, M, D) if op == FLARE_OP_ENCODE else (B, H, N, D)
+    if out is None:
+        return torch.empty(shape, dtype=like.dtype, device=like.device)
+    if tuple(out.shape) != shape or out.dtype != like.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError(f"out must be a contiguous {like.dtype} device tensor of shape {shape}")
+    return out
+
+
+def _call(op: int, name: str, Q, K, V, out, stream, workspace):
+    B, H, N, M, D = _dims(op, Q, K, V)
+    Y = _out(op, B, H, N, M, D, Q, out)
+    dt = dtype_code(Q.dtype)
+    args = [Q.data_ptr(), K.data_ptr(), V.data_ptr(), Y.data_ptr(), B, H, N, M, D, dt, _stream(stream)]
+    L = lib()
+    if workspace is None:
+        _raise(getattr(L, name)(*args))
+    else:
+        _raise(getattr(L, name + "_ws")(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size()))
+    return Y
+
+
+def flare_encode(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Z [B, H, M, D] = encode(Q [H, M, D], K, V [B, H, N, D])."""
+    return _call(FLARE_OP_ENCODE, "flare_encode", Q, K, V, out, stream, workspace)
+
+
+def flare_decode(Q, K, Z, out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Y [B, H, N, D] = decode(Q [H, M, D], K [B, H, N, D], Z [B, H, M, D])."""
+    return _call(FLARE_OP_DECODE, "flare_decode", Q, K, Z, out, stream, workspace)
+
+
+def flare_forward(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Y [B, H, N, D] = FLARE(Q, K, V)."""
+    return _call(FLARE_OP_FORWARD, "flare_forward", Q, K, V, out, stream, workspace)
+
+
+def flare_pp_forward(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Y [B, H, N, D] = FLARE++(Q, K, V)."""
+    return _call(FLARE_OP_PP_FORWARD, "flare_pp_forward", Q, K, V, out, stream, workspace)
+
+
+def flare_workspace_size(op: int, B: int, H: int, N: int, M: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().flare_workspace_size(op, B, H, N, M, D, dtype_code(dtype)))
+
+
+def workspace_for(op: int, Q: torch.Tensor, K: torch.Tensor) -> torch.Tensor:
+    """Caller-owned workspace tensor for the *_ws variants (256-byte aligned by torch's allocator)."""
+    H, M, D = Q.shape
+    B, _, N, _ = K.shape
+    n = flare_workspace_size(op, B, H, N, M, D, Q.dtype)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=Q.device)
+
+
+def flare_describe_plan(op: int, B: int, H: int, N: int, M: int, D: int, dtype: torch.dtype) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _raise(lib().flare_describe_plan(op, B, H, N, M, D, dtype_code(dtype), buf, 512))
+    return buf.value.decode()
+
+
+def flare_timing_enable(on: bool) -> None:
+    _raise(lib().flare_timing_enable(1 if on else 0))
+
+
+def flare_timing_read():
+    """{kind name: (total ms, launches)} since the last read or enable."""
+    ms = (ctypes.c_double * FLARE_KERNEL_KINDS)()
+    cnt = (_i64 * FLARE_KERNEL_KINDS)()
+    _raise(lib().flare_timing_read(ms, cnt))
+    return {KERNEL_KIND_NAMES[i]: (ms[i], cnt[i]) for i in range(FLARE_KERNEL_KINDS)}
+
+
+def flare_copy_kernel(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    _raise(lib().flare_copy_kernel(src.data_ptr(), dst.data_ptr(), n, _stream(stream)))

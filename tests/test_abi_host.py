@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library must load, export every function include/flare.h declares, and
+reject bad arguments before touching the device (validation runs before any
+HIP call, so these tests are safe on a machine without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_latent_attention_flare_amd import flare as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flare.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(F.LIB_PATH), reason="libflare.so not built")
+
+OK, INVALID, UNSUPPORTED, NOMEM = 0, 1, 2, 3
+# fake, 256-byte aligned, non-overlapping "device" addresses (never dereferenced)
+PQ, PK, PV, PY, PW = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flare_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 14
+    L = F.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def call(name, *args, ws=None):
+    L = F.lib()
+    fn = getattr(L, name if ws is None else name + "_ws")
+    base = list(args) + [None]
+    if ws is not None:
+        base += list(ws)
+    return fn(*base)
+
+
+def fwd_args(q=PQ, k=PK, v=PV, y=PY, B=1, H=2, N=100, M=64, D=64, dt=F.FLARE_BF16):
+    return (q, k, v, y, B, H, N, M, D, dt)
+
+
+@pytest.mark.parametrize("name", ["flare_encode", "flare_decode", "flare_forward", "flare_pp_forward"])
+def test_null_pointers_rejected(name):
+    for i in range(4):
+        a = list(fwd_args())
+        a[i] = None
+        assert call(name, *a) == INVALID
+        assert "null" in F.lib().flare_last_error().decode()
+
+
+@pytest.mark.parametrize("field", [4, 5, 6, 7, 8])
+def test_sizes_below_one_rejected(field):
+    for bad in (0, -3):
+        a = list(fwd_args())
+        a[field] = bad
+        assert call("flare_forward", *a) == INVALID
+
+
+@pytest.mark.parametrize("dt,D,M", [(F.FLARE_BF16, 16, 64), (F.FLARE_BF16, 48, 64), (F.FLARE_BF16, 64, 257),
+                                    (F.FLARE_F32, 12, 8), (F.FLARE_F32, 256, 8), (F.FLARE_F32, 16, 5000)])
+def test_unsupported_shapes(dt, D, M):
+    assert call("flare_forward", *fwd_args(D=D, M=M, dt=dt)) == UNSUPPORTED
+    assert F.lib().flare_workspace_size(F.FLARE_OP_FORWARD, 1, 2, 100, M, D, dt) == 0
+
+
+def test_bad_dtype_and_grid_limits():
+    assert call("flare_forward", *fwd_args(dt=7)) == INVALID
+    assert call("flare_forward", *fwd_args(B=300, H=300)) == UNSUPPORTED
+
+
+def test_misaligned_pointers_rejected():
+    assert call("flare_forward", *fwd_args(k=PK + 8)) == INVALID
+    assert "aligned" in F.lib().flare_last_error().decode()
+
+
+def test_output_aliasing_rejected():
+    assert call("flare_forward", *fwd_args(y=PK)) == INVALID
+    assert "overlaps" in F.lib().flare_last_error().decode()
+    # partial overlap of Y with V
+    assert call("flare_forward", *fwd_args(y=PV + 4096)) == INVALID
+
+
+def test_workspace_sizes_consistent():
+    L = F.lib()
+    args = (1, 16, 1 << 20, 256, 64, F.FLARE_BF16)
+    enc = L.flare_workspace_size(F.FLARE_OP_ENCODE, *args)
+    dec = L.flare_workspace_size(F.FLARE_OP_DECODE, *args)
+    fwd = L.flare_workspace_size(F.FLARE_OP_FORWARD, *args)
+    pp = L.flare_workspace_size(F.FLARE_OP_PP_FORWARD, *args)
+    assert dec == 0 and 0 < enc < fwd < pp
+    # partials stay small next to the 8 GiB of K/V/Y traffic
+    assert fwd < 0.03 * (1 << 33)
+    assert L.flare_workspace_size(9, *args) == 0
+
+
+def test_workspace_checks():
+    need = F.lib().flare_workspace_size(F.FLARE_OP_FORWARD, 1, 2, 100, 64, 64, F.FLARE_BF16)
+    assert call("flare_forward", *fwd_args(), ws=(PW, need - 1)) == INVALID
+    assert "too small" in F.lib().flare_last_error().decode()
+    assert call("flare_forward", *fwd_args(), ws=(None, need)) == INVALID
+    assert call("flare_forward", *fwd_args(), ws=(PW + 16, need)) == INVALID
+
+
+def test_injected_allocation_failure(monkeypatch):
+    monkeypatch.setenv("FLARE_TEST_FAIL_ALLOC", "1")
+    assert call("flare_forward", *fwd_args()) == NOMEM
+    monkeypatch.delenv("FLARE_TEST_FAIL_ALLOC")
+
+
+def test_status_strings_and_plan():
+    L = F.lib()
+    for code, name in F.STATUS.items():
+        assert L.flare_status_string(code).decode() == name
+    buf = ctypes.create_string_buffer(512)
+    assert L.flare_describe_plan(F.FLARE_OP_FORWARD, 4, 8, 65536, 128, 32, F.FLARE_BF16, buf, 512) == OK
+    txt = buf.value.decode()
+    assert "encode grid" in txt and "decode grid" in txt
+    assert L.flare_describe_plan(F.FLARE_OP_FORWARD, 4, 8, 65536, 128, 33, F.FLARE_BF16, buf, 512) == UNSUPPORTED
+
+
+def test_copy_kernel_argument_checks():
+    L = F.lib()
+    assert L.flare_copy_kernel(PK, PV, 1000, None) == INVALID  # not a multiple of 16
+    assert L.flare_copy_kernel(PK, PK + 256, 4096, None) == INVALID  # overlap
+    assert L.flare_copy_kernel(None, PV, 4096, None) == INVALID
+
+
+def test_timing_read_without_events():
+    import ctypes as C
+    ms = (C.c_double * 3)()
+    cnt = (C.c_int64 * 3)()
+    L = F.lib()
+    assert L.flare_timing_enable(1) == OK
+    assert L.flare_timing_read(ms, cnt) == OK
+    assert list(cnt) == [0, 0, 0]
+    assert L.flare_timing_enable(0) == OK

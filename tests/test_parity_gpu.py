@@ -1,0 +1,216 @@
+"""GPU parity of libflare (through the C ABI) against the fp64 CPU oracle.
+
+* small and ragged shapes: every output element against the oracle, for all
+  four entry points and both storage types (several tiles, tails of tokens
+  and of latents, N = 1, M = 1);
+* the five workloads at full size, in the launch configuration the benchmark
+  times (caller workspace): sampled tokens of two heads against the oracle,
+  computed one by one;
+* properties that hold at any size: constant V, zero queries, scaling and
+  permutation of the tokens, determinism, chunk-count invariance, and the
+  composition identities between the entry points.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flare_inputs import WORKLOADS, f32_to_bf16_bits, make_inputs, workload_inputs
+from rank_latent_attention_flare_amd import flare as F
+from tests.gpu_util import assert_parity, errors, sample_rows, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+OPS = {"encode": F.flare_encode, "decode": F.flare_decode, "forward": F.flare_forward, "pp_forward": F.flare_pp_forward}
+OPCODE = {"encode": F.FLARE_OP_ENCODE, "decode": F.FLARE_OP_DECODE, "forward": F.FLARE_OP_FORWARD,
+          "pp_forward": F.FLARE_OP_PP_FORWARD}
+
+SMALL = [
+    # B, H, N, M, D, dtype
+    (1, 4, 1024, 32, 16, "f32"),
+    (1, 3, 3000, 40, 8, "f32"),
+    (2, 2, 1, 1, 64, "f32"),
+    (1, 1, 2500, 300, 32, "f32"),
+    (2, 3, 1000, 64, 64, "bf16"),
+    (1, 2, 4097, 100, 32, "bf16"),
+    (1, 1, 1, 1, 32, "bf16"),
+    (1, 2, 7, 17, 64, "bf16"),
+    (1, 1, 300, 256, 128, "bf16"),
+    (2, 1, 5000, 200, 64, "bf16"),
+    (1, 2, 777, 33, 128, "bf16"),
+    (3, 1, 2049, 128, 32, "bf16"),
+    (1, 2, 640, 64, 128, "bf16"),
+]
+
+
+def small_id(c):
+    return "B{}H{}N{}M{}D{}-{}".format(*c)
+
+
+def oracle_for(op, Q, K, V):
+    if op == "encode":
+        return oracle.encode(Q, K, V)
+    if op == "decode":
+        return oracle.decode(Q, K, V)
+    if op == "forward":
+        return oracle.forward(Q, K, V)[0]
+    return oracle.pp_forward(Q, K, V)[0]
+
+
+@pytest.mark.parametrize("op", list(OPS))
+@pytest.mark.parametrize("case", SMALL, ids=small_id)
+def test_small_shapes_match_oracle(op, case):
+    B, H, N, M, D, dt = case
+    seed = zlib.crc32(repr((op,) + case).encode()) % 100000
+    Q, K, V = make_inputs(B, H, N, M, D, dt, q_scale=0.5, seed=seed)
+    if op == "decode":
+        Zr = oracle.encode(Q, K, V)
+        V = Zr.astype(np.float32) if dt == "f32" else f32_to_bf16_bits(Zr.astype(np.float32))
+    print(f"[small] op={op} case={small_id(case)} seed={seed}", flush=True)
+    out = OPS[op](to_dev(Q), to_dev(K), to_dev(V))
+    torch.cuda.synchronize()
+    assert_parity(to_host64(out), oracle_for(op, Q, K, V), dt, f"{op} {small_id(case)}")
+
+
+@pytest.mark.parametrize("op", ["forward", "pp_forward"])
+def test_ws_variant_equals_allocating_variant(op):
+    Q, K, V = (to_dev(x) for x in make_inputs(2, 2, 3000, 96, 64, "bf16", 0.5, seed=11))
+    a = OPS[op](Q, K, V)
+    b = OPS[op](Q, K, V, workspace=F.workspace_for(OPCODE[op], Q, K))
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ------------------------------------------------------------ full workloads
+_cache = {}
+
+
+def workload(i):
+    if i not in _cache:
+        _cache.clear()
+        w = WORKLOADS[i]
+        print(f"[workload] generating {w.name}", flush=True)
+        Q, K, V = workload_inputs(w)
+        _cache[i] = (w, Q, K, V, to_dev(Q), to_dev(K), to_dev(V))
+    return _cache[i]
+
+
+def heads_to_check(w):
+    return [(0, 0), (w.B - 1, w.H - 1)] if w.B * w.H > 1 else [(0, 0)]
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_workload_matches_oracle_on_sampled_tokens(i):
+    w, Q, K, V, Qd, Kd, Vd = workload(i)
+    op = w.op
+    print(f"[workload] {w.name} op={op} plan: {F.flare_describe_plan(OPCODE[op], w.B, w.H, w.N, w.M, w.D, Qd.dtype)}",
+          flush=True)
+    ws = F.workspace_for(OPCODE[op], Qd, Kd)
+    Y = OPS[op](Qd, Kd, Vd, workspace=ws)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.N, 2048, seed=i)
+    heads = heads_to_check(w) if i != 1 else None
+    rows_arg = rows if i != 1 else None
+    if op == "forward":
+        Yo, Zo = oracle.forward(Q, K, V, rows=rows_arg, heads=heads)
+    else:
+        Yo, _, Zo = oracle.pp_forward(Q, K, V, rows=rows_arg, heads=heads)
+    Yg = to_host64(Y[:, :, torch.from_numpy(rows).cuda()] if rows_arg is not None else Y)
+    for (b, h) in (heads or [(b, h) for b in range(w.B) for h in range(w.H)]):
+        e = assert_parity(Yg[b, h], Yo[b, h], w.dtype, f"{w.name} Y head ({b},{h})")
+        print(f"[workload] {w.name} Y head ({b},{h}): {e}", flush=True)
+    if op == "forward":
+        Z = F.flare_encode(Qd, Kd, Vd, workspace=F.workspace_for(F.FLARE_OP_ENCODE, Qd, Kd))
+        Zg = to_host64(Z)
+        for (b, h) in (heads or [(b, h) for b in range(w.B) for h in range(w.H)]):
+            assert_parity(Zg[b, h], Zo[b, h], w.dtype, f"{w.name} Z head ({b},{h})")
+
+
+# --------------------------------------------------------------- properties
+@pytest.mark.parametrize("i", [2, 3, 4, 5])
+def test_constant_values_give_exact_constant(i):
+    w, Q, K, V, Qd, Kd, Vd = workload(i)
+    g = torch.Generator(device="cuda").manual_seed(100 + i)
+    c = torch.randn(w.B, w.H, 1, w.D, device="cuda", generator=g).to(Vd.dtype)
+    Vc = c.expand_as(Vd).contiguous()
+    Y = OPS[w.op](Qd, Kd, Vc)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, c.expand_as(Y)), f"max dev {(Y.float() - c.float()).abs().max().item()}"
+
+
+@pytest.mark.parametrize("i", [2, 3, 4])
+def test_values_scale_exactly(i):
+    w, Q, K, V, Qd, Kd, Vd = workload(i)
+    Y1 = F.flare_forward(Qd, Kd, Vd)
+    Y2 = F.flare_forward(Qd, Kd, (Vd.float() * 2).to(Vd.dtype))
+    torch.cuda.synchronize()
+    assert torch.equal((Y1.float() * 2).to(Y1.dtype), Y2)
+
+
+@pytest.mark.parametrize("i", [2, 3, 4])
+def test_zero_queries_give_token_means(i):
+    w, Q, K, V, Qd, Kd, Vd = workload(i)
+    Y = F.flare_forward(torch.zeros_like(Qd), Kd, Vd)
+    mean = Vd.double().mean(dim=2, keepdim=True)
+    torch.cuda.synchronize()
+    e = errors(Y.double().cpu().numpy(), mean.expand(Y.shape).cpu().numpy())
+    assert e["rel_l2"] <= 1e-2 and e["max_abs"] <= 3e-2, e
+
+
+@pytest.mark.parametrize("i", [2, 3, 5])
+def test_token_permutation_permutes_output(i):
+    w, Q, K, V, Qd, Kd, Vd = workload(i)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    perm = torch.randperm(w.N, device="cuda", generator=g)
+    Y = OPS[w.op](Qd, Kd, Vd)
+    Yp = OPS[w.op](Qd, Kd[:, :, perm].contiguous(), Vd[:, :, perm].contiguous())
+    torch.cuda.synchronize()
+    e = errors(Yp.double().cpu().numpy(), Y[:, :, perm].double().cpu().numpy())
+    assert e["rel_l2"] <= 1e-2 and e["max_abs"] <= 3e-2, e
+
+
+@pytest.mark.parametrize("i", [2, 4, 5])
+def test_bitwise_repeatable(i):
+    w, Q, K, V, Qd, Kd, Vd = workload(i)
+    ws = F.workspace_for(OPCODE[w.op], Qd, Kd)
+    a = OPS[w.op](Qd, Kd, Vd, workspace=ws)
+    b = OPS[w.op](Qd, Kd, Vd, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("i", [2, 3])
+def test_chunk_count_invariance(i, monkeypatch):
+    w, Q, K, V, Qd, Kd, Vd = workload(i)
+    a = F.flare_forward(Qd, Kd, Vd)
+    monkeypatch.setenv("FLARE_TEST_CHUNKS", "1")
+    b = F.flare_forward(Qd, Kd, Vd)
+    monkeypatch.setenv("FLARE_TEST_CHUNKS", "5")
+    c = F.flare_forward(Qd, Kd, Vd)
+    torch.cuda.synchronize()
+    for x in (b, c):
+        e = errors(x.double().cpu().numpy(), a.double().cpu().numpy())
+        assert e["rel_l2"] <= 5e-3, e
+
+
+@pytest.mark.parametrize("i", [2, 3, 4])
+def test_forward_is_decode_of_encode_bitwise(i):
+    w, Q, K, V, Qd, Kd, Vd = workload(i)
+    Y = F.flare_forward(Qd, Kd, Vd)
+    Z = F.flare_encode(Qd, Kd, Vd)
+    Y2 = F.flare_decode(Qd, Kd, Z)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
+
+
+def test_pp_forward_is_forward_with_corrected_queries():
+    # B = 1: Q' = Q + encode(Q) is per-head, so the public calls can compose it.
+    Q, K, V = (to_dev(x) for x in make_inputs(1, 4, 20000, 128, 64, "bf16", 0.5, seed=21))
+    Y = F.flare_pp_forward(Q, K, V)
+    Qp = (Q.float() + F.flare_encode(Q, K, V)[0].float()).to(torch.bfloat16)
+    Y2 = F.flare_forward(Qp.contiguous(), K, V)
+    torch.cuda.synchronize()
+    e = errors(Y.double().cpu().numpy(), Y2.double().cpu().numpy())
+    assert e["rel_l2"] <= 1e-2 and e["max_abs"] <= 3e-2, e
