@@ -10,6 +10,8 @@
   permutation of the tokens, determinism, chunk-count invariance, and the
   composition identities between the entry points.
 """
+import json
+import os
 import zlib
 
 import numpy as np
@@ -118,14 +120,21 @@ def test_workload_matches_oracle_on_sampled_tokens(i):
     else:
         Yo, _, Zo = oracle.pp_forward(Q, K, V, rows=rows_arg, heads=heads)
     Yg = to_host64(Y[:, :, torch.from_numpy(rows).cuda()] if rows_arg is not None else Y)
+    report = {"workload": w.name, "op": op, "tokens_checked": int(len(rows) if rows_arg is not None else w.N),
+              "heads": heads or "all", "Y": {}, "Z": {}}
     for (b, h) in (heads or [(b, h) for b in range(w.B) for h in range(w.H)]):
         e = assert_parity(Yg[b, h], Yo[b, h], w.dtype, f"{w.name} Y head ({b},{h})")
-        print(f"[workload] {w.name} Y head ({b},{h}): {e}", flush=True)
+        report["Y"][f"{b},{h}"] = e
     if op == "forward":
         Z = F.flare_encode(Qd, Kd, Vd, workspace=F.workspace_for(F.FLARE_OP_ENCODE, Qd, Kd))
         Zg = to_host64(Z)
         for (b, h) in (heads or [(b, h) for b in range(w.B) for h in range(w.H)]):
-            assert_parity(Zg[b, h], Zo[b, h], w.dtype, f"{w.name} Z head ({b},{h})")
+            report["Z"][f"{b},{h}"] = assert_parity(Zg[b, h], Zo[b, h], w.dtype, f"{w.name} Z head ({b},{h})")
+    out_dir = os.environ.get("FLARE_REPORT_DIR")
+    if out_dir:
+        os.makedirs(out_dir, exist_ok=True)
+        with open(os.path.join(out_dir, f"parity_{w.name}.json"), "w") as f:
+            json.dump(report, f, indent=1)
 
 
 # --------------------------------------------------------------- properties
