@@ -25,6 +25,7 @@ ARCH = "gfx950"
 SOURCES = ["flare.cpp", "kernels_common.hip", "kernels_bf16.hip"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

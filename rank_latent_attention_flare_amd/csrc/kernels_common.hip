@@ -39,16 +39,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (idx >= a.M * a.D) return;
     const int m = idx / a.D, d = idx - m * a.D;
     const int C = a.C, Mp = a.Mp, D = a.D;
-    const int64_t base = (int64_t)bh * C * Mp;
+    const int64_t row0 = (int64_t)bh * C * Mp + m;  // partial row of chunk 0; chunk c adds c*Mp
+    const float* __restrict__ mu = a.in.mu + row0;
+    const float* __restrict__ sg = a.in.sig + row0;
+    const float* __restrict__ ac = a.in.acc + row0 * D + d;
+    const int64_t sacc = (int64_t)Mp * D;
+    // loops unrolled so that many independent loads are in flight at once
     float mx = -INFINITY;
-    for (int c = 0; c < C; ++c) mx = fmaxf(mx, a.in.mu[base + (int64_t)c * Mp + m]);
+#pragma unroll 8
+    for (int c = 0; c < C; ++c) mx = fmaxf(mx, mu[(int64_t)c * Mp]);
     float num = 0.0f, den = 0.0f;
+#pragma unroll 8
     for (int c = 0; c < C; ++c) {
-        const int64_t r = base + (int64_t)c * Mp + m;
-        const float mc = a.in.mu[r];
+        const float mc = mu[(int64_t)c * Mp];
         const float w = (mc == -INFINITY) ? 0.0f : exp2f(mc - mx);
-        num = fmaf(w, a.in.acc[r * D + d], num);
-        den = fmaf(w, a.in.sig[r], den);
+        num = fmaf(w, ac[(int64_t)c * sacc], num);
+        den = fmaf(w, sg[(int64_t)c * Mp], den);
     }
     const float z = num / den;
     const int64_t o = (int64_t)bh * a.M * D + idx;
