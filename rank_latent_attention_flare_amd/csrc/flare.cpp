@@ -53,7 +53,7 @@ struct Plan {
     int C, chunk_len;  // encode split over N
     int G;             // decode workgroups per (b, h)
     size_t esize;
-    size_t off_acc, off_mu, off_sig, off_z, off_qp, total[4];
+    size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[4];
     float c;
 };
 
@@ -126,7 +126,7 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     p->C = int(C);
     p->chunk_len = int(chunk);
     // decode workgroups per (b, h)
-    const int64_t per_wg = 32 * flare::kDecTB * flare::kDecWaves;
+    const int64_t per_wg = 32 * (dt == FLARE_BF16 ? flare::dec_tb_bf16(int(D)) : 2) * flare::kDecWaves;
     int64_t G = std::max<int64_t>(1, (kTargetDecWgs + p->BH - 1) / p->BH);
     G = std::min<int64_t>(G, (N + per_wg - 1) / per_wg);
     p->G = int(G);
@@ -138,6 +138,7 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     p->off_sig = off; off = align256(off + parts * 4);
     const size_t enc_total = off;
     p->off_z = off;   off = align256(off + size_t(p->BH) * size_t(M) * size_t(D) * 4);
+    p->off_zmu = off; off = align256(off + size_t(p->BH) * size_t(M) * 4);
     const size_t fwd_total = off;
     p->off_qp = off;  off = align256(off + size_t(p->BH) * size_t(M) * size_t(D) * p->esize);
     p->total[FLARE_OP_ENCODE] = enc_total;
@@ -232,7 +233,8 @@ hipError_t run_encode_partial(const Plan& p, const void* Q, int64_t q_bstride, c
     });
 }
 
-hipError_t run_combine(const Plan& p, int mode, const void* Q, void* out, char* ws, hipStream_t s) {
+hipError_t run_combine(const Plan& p, int mode, const void* Q, void* out, char* ws, hipStream_t s,
+                       float* zmu = nullptr) {
     CombineArgs a{};
     a.in.acc = (float*)(ws + p.off_acc);
     a.in.mu = (float*)(ws + p.off_mu);
@@ -242,20 +244,46 @@ hipError_t run_combine(const Plan& p, int mode, const void* Q, void* out, char* 
     a.bf16 = p.dt == FLARE_BF16;
     a.Q = Q;
     a.out = out;
+    a.zmu = zmu;
     return timed(1, s, [&] { return flare::launch_combine(a, s); });
 }
 
+// Decode workgroups per (b, h): one resident wave of workgroups over the
+// whole chip (from the kernel's occupancy), each looping over token blocks.
+int decode_groups(const Plan& p, bool z_f32) {
+    if (const char* e = std::getenv("FLARE_TEST_DEC_G")) {
+        const int v = std::atoi(e);
+        if (v > 0) return v;
+    }
+    if (p.dt != FLARE_BF16) return p.G;
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    const int per_cu = flare::dec_wgs_per_cu_bf16(int(p.D), p.Mp, z_f32);
+    const int64_t per_wg = 32 * flare::dec_tb_bf16(int(p.D)) * flare::kDecWaves;
+    int64_t G = (int64_t(cus) * per_cu + p.BH - 1) / p.BH;
+    G = std::max<int64_t>(1, std::min<int64_t>(G, (p.N + per_wg - 1) / per_wg));
+    return int(G);
+}
+
 hipError_t run_decode(const Plan& p, const void* Q, int64_t q_bstride, const void* K, const void* Z, bool z_f32,
-                      void* Y, hipStream_t s) {
+                      void* Y, hipStream_t s, const float* zmu = nullptr) {
     DecodeArgs a{};
     a.Q = Q;
     a.q_bstride = q_bstride;
     a.K = K;
     a.Z = Z;
     a.z_f32 = z_f32;
+    a.zmu = p.dt == FLARE_BF16 ? zmu : nullptr;
     a.Y = Y;
     a.BH = p.BH; a.H = int(p.H); a.N = int(p.N); a.M = int(p.M); a.Mp = p.Mp; a.D = int(p.D);
-    a.G = p.G;
+    a.G = decode_groups(p, z_f32);
     a.c = p.c;
     return timed(2, s, [&] {
         return p.dt == FLARE_BF16 ? flare::launch_decode_bf16(a, s) : flare::launch_decode_f32(a, s);
@@ -297,8 +325,9 @@ flare_status exec(flare_op op, const void* Q, const void* K, const void* V, void
             break;
         case FLARE_OP_FORWARD:
             e = run_encode_partial(p, Q, 0, K, V, ws, s);
-            if (e == hipSuccess) e = run_combine(p, flare::COMBINE_Z_F32, Q, ws + p.off_z, ws, s);
-            if (e == hipSuccess) e = run_decode(p, Q, 0, K, ws + p.off_z, true, Y, s);
+            if (e == hipSuccess)
+                e = run_combine(p, flare::COMBINE_Z_F32, Q, ws + p.off_z, ws, s, (float*)(ws + p.off_zmu));
+            if (e == hipSuccess) e = run_decode(p, Q, 0, K, ws + p.off_z, true, Y, s, (const float*)(ws + p.off_zmu));
             break;
         case FLARE_OP_PP_FORWARD: {
             void* qp = ws + p.off_qp;
@@ -306,8 +335,10 @@ flare_status exec(flare_op op, const void* Q, const void* K, const void* V, void
             e = run_encode_partial(p, Q, 0, K, V, ws, s);
             if (e == hipSuccess) e = run_combine(p, flare::COMBINE_QPRIME, Q, qp, ws, s);
             if (e == hipSuccess) e = run_encode_partial(p, qp, qstride, K, V, ws, s);
-            if (e == hipSuccess) e = run_combine(p, flare::COMBINE_Z_F32, Q, ws + p.off_z, ws, s);
-            if (e == hipSuccess) e = run_decode(p, qp, qstride, K, ws + p.off_z, true, Y, s);
+            if (e == hipSuccess)
+                e = run_combine(p, flare::COMBINE_Z_F32, Q, ws + p.off_z, ws, s, (float*)(ws + p.off_zmu));
+            if (e == hipSuccess)
+                e = run_decode(p, qp, qstride, K, ws + p.off_z, true, Y, s, (const float*)(ws + p.off_zmu));
             break;
         }
     }

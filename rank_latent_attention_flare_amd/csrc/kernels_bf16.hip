@@ -38,9 +38,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Largest per-tile probability sum the encode accepts against its running
 // offset before it re-centres (2^32; keeps every fp32 sum far from overflow).
 constexpr float kSumLimit = 4294967296.0f;
-// Smallest per-token probability sum the decode accepts against its
-// Cauchy-Schwarz offset before it recomputes that block with exact maxima.
-constexpr float kTauFloor = 9.094947017729282e-13f;  // 2^-40
+// Smallest per-token probability sum the decode accepts against its offset
+// before it recomputes that block with exact maxima. Above it the largest
+// term is >= 2^-98 and every term within fp32 precision of it is a normal
+// number, so a loose offset costs no accuracy.
+constexpr float kTauFloor = 8.077935669463161e-28f;  // 2^-90
+// Log2 of kSumLimit: an accepted encode tile has every probability <= 2^32,
+// so c*S <= mu + 32 for every latent offset mu the encode reports.
+constexpr float kSumLimitLog2 = 32.0f;
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -172,7 +177,8 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     constexpr int NS = Sh::NS, IPW = Sh::IPW, SBYTES = Sh::SBYTES;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Sh::SMEM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
     const int wm = wave % WM, wt = wave / WM;
     const int chunk = blockIdx.x, bh = blockIdx.y;
@@ -232,15 +238,9 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     for (int j = 0; j < NS - 1; ++j)
         if (j < ntiles) issue(j, j);
 
-    for (int it = 0; it < ntiles; ++it) {
-        // tile `it` is complete once at most the transfers of the (up to NS-2)
-        // later tiles issued so far are outstanding
-        if (it + NS - 2 < ntiles)
-            wait_vmcnt<(NS - 2) * 2 * IPW>();
-        else
-            wait_vmcnt<0>();
-        raw_barrier();
-        if (it + NS - 1 < ntiles) issue(it + NS - 1, (it + NS - 1) % NS);
+    // Tile `it` (tail: the chunk's last, ragged tile, whose sub-blocks may be
+    // partial or empty; full tiles carry no masking code).
+    auto tile = [&](int it, bool tail) {
         const unsigned char* kt = smem + (it % NS) * SBYTES;
         const unsigned char* vt = kt + T * RB;
         const int valid = n1 - (n0 + it * T);
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
         for (int j = 0; j < SB; ++j) {
             const int sb = wt * SB + j;
             const int nv = valid - 32 * sb;  // valid tokens in this sub-block
-            if (nv <= 0) break;
+            if (tail && nv <= 0) break;
             // S^T for the 32 tokens x (32 * MBW) latents.
             bf16x8 ka[KB];
             const int krow = 32 * sb + enc_row_token(l32);
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) S[mb] = mfma(ka[kb], qop[mb][kb], S[mb]);
             }
-            if (nv < 32) {
+            if (tail) {
 #pragma unroll
                 for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
@@ -322,7 +322,22 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
                 }
             }
         }
+    };
+    const bool ragged = (n1 - n0) % T != 0;
+    const int nfull = ragged ? ntiles - 1 : ntiles;
+    for (int it = 0; it < ntiles; ++it) {
+        // tile `it` is complete once at most the transfers of the (up to NS-2)
+        // later tiles issued so far are outstanding
+        if (it + NS - 2 < ntiles)
+            wait_vmcnt<(NS - 2) * 2 * IPW>();
+        else
+            wait_vmcnt<0>();
+        raw_barrier();
+        if (it + NS - 1 < ntiles) issue(it + NS - 1, (it + NS - 1) % NS);
+        if (it == nfull) break;  // only the ragged tile is left
+        tile(it, false);
     }
+    if (ragged) tile(nfull, true);
 
     // Merge the WT token waves of each latent group (tile buffers are free
     // once every wave is past its last read; all transfers were waited for).
@@ -397,6 +412,252 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
 }
 
 // ---------------------------------------------------------------------------
+// K1, private-stream form (used when one wave's registers hold all latents).
+//
+// Workgroup = NWV waves for one (b, h) and one chunk. Every wave owns ALL
+// latents and its own stream of 32-token sub-blocks (wave w takes sub-blocks
+// w, w + NWV, ...), fed through a private ring of NSW LDS stages by
+// global_load_lds. No workgroup barrier is needed until the final merge; the
+// logit MFMAs of all latent blocks are issued before the softmax VALU work so
+// the matrix core runs under it. Arithmetic is the same as the shared form.
+// ---------------------------------------------------------------------------
+template <int D, int MBW, int NWV>
+struct EncPrivShape {
+    static constexpr int KB = D / 16, DB = D / 32, CH = D / 8, RB = 2 * D;
+    static constexpr int SBYTES = 2 * 32 * RB;  // K then V of one 32-token sub-block
+    static constexpr int BUDGET = 65536;
+    static constexpr int NSW0 = BUDGET / (NWV * SBYTES);
+    static constexpr int NSW = NSW0 < 2 ? 2 : (NSW0 > 8 ? 8 : NSW0);
+    static constexpr int IPS = 32 * CH / 64;  // transfers per tensor per stage
+    static constexpr int MERGE_BYTES = NWV * MBW * (16 * DB + 2) * 65 * 4;
+    static constexpr int RING = NWV * NSW * SBYTES;
+    static constexpr int SMEM = RING > MERGE_BYTES ? RING : MERGE_BYTES;
+    static_assert(IPS * 64 == 32 * CH, "stage transfer split");
+};
+
+template <int D, int MBW, int NWV>
+__global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs a) {
+    using Sh = EncPrivShape<D, MBW, NWV>;
+    constexpr int KB = Sh::KB, DB = Sh::DB, CH = Sh::CH, RB = Sh::RB, NSW = Sh::NSW, IPS = Sh::IPS;
+    constexpr int SBYTES = Sh::SBYTES;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[Sh::SMEM];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5, l32 = lane & 31;
+    const int chunk = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int N = a.N, M = a.M, Mp = a.Mp;
+    const int n0 = chunk * a.chunk_len;
+    const int n1 = min(N, n0 + a.chunk_len);
+    const float c = a.c;
+    const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
+    const uint16_t* __restrict__ Vb = (const uint16_t*)a.V + (int64_t)bh * N * D;
+    const uint16_t* __restrict__ Qb = (const uint16_t*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
+    unsigned char* ring = smem + wave * (NSW * SBYTES);
+
+    bf16x8 qop[MBW][KB];
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) {
+        const int m = 32 * mb + l32;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            qop[mb][kb] = (m < M) ? *(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi) : zero8();
+    }
+    float mu[MBW], ps[MBW];
+    f32x16 acc[MBW][DB];
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) {
+        mu[mb] = -INFINITY;
+        ps[mb] = 0.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mb][db][r] = 0.0f;
+    }
+
+    const int nsb = (n1 - n0 + 31) / 32;                        // sub-blocks in the chunk
+    const int nsub = nsb > wave ? (nsb - wave + NWV - 1) / NWV : 0;  // this wave's share
+    // Byte offset of this lane's IPS 16-byte pieces inside a 32-token block
+    // (row-major source, swizzled destination): the same for every block.
+    uint32_t loff[IPS];
+    int lrow[IPS];
+#pragma unroll
+    for (int i = 0; i < IPS; ++i) {
+        const int p = i * 64 + lane;
+        const int row = p / CH, pos = p % CH;
+        const int ch = pos ^ ((tile_off<D>(row, 0) - row * RB) >> 4);
+        lrow[i] = row;
+        loff[i] = (uint32_t)(row * RB + ch * 16);
+    }
+    auto issue = [&](int k) {
+        const int t0 = n0 + 32 * (wave + k * NWV);
+        unsigned char* st = ring + (k % NSW) * SBYTES;
+        const unsigned char* kb0 = (const unsigned char*)(Kb + (int64_t)t0 * D);
+        const unsigned char* vb0 = (const unsigned char*)(Vb + (int64_t)t0 * D);
+        if (t0 + 32 <= n1) {
+#pragma unroll
+            for (int i = 0; i < IPS; ++i) {
+                dma16(kb0 + loff[i], st + i * 1024);
+                dma16(vb0 + loff[i], st + 32 * RB + i * 1024);
+            }
+        } else {  // ragged tail: rows past the chunk end repeat its last token
+#pragma unroll
+            for (int i = 0; i < IPS; ++i) {
+                const uint32_t o = loff[i] - (uint32_t)(max(0, t0 + lrow[i] - (n1 - 1)) * RB);
+                dma16(kb0 + o, st + i * 1024);
+                dma16(vb0 + o, st + 32 * RB + i * 1024);
+            }
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < NSW - 1; ++k)
+        if (k < nsub) issue(k);
+
+    // One 32-token sub-block k of this wave (tail: the chunk's last, ragged one).
+    auto sub_block = [&](int k, bool tail) {
+        const unsigned char* kt = ring + (k % NSW) * SBYTES;
+        const unsigned char* vt = kt + 32 * RB;
+        const int nv = n1 - (n0 + 32 * (wave + k * NWV));
+        bf16x8 ka[KB];
+        const int krow = enc_row_token(l32);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) ka[kb] = *(const bf16x8*)(kt + tile_off<D>(krow, 2 * kb + hi));
+        // V^T operands of this sub-block (shared by every latent block)
+        bf16x8 va[2][DB];
+        const int g = lane >> 4, gi = lane & 15;
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+            const int row1 = 16 * kp + 8 * (g >> 1) + (gi >> 2);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+                const int off1 = tile_off<D>(row1, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+                const int off2 = tile_off<D>(row1 + 4, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off1));
+                const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off2));
+                const u32x2 w1 = __builtin_bit_cast(u32x2, r1);
+                const u32x2 w2 = __builtin_bit_cast(u32x2, r2);
+                const u32x4 w = {w1[0], w1[1], w2[0], w2[1]};
+                va[kp][db] = __builtin_bit_cast(bf16x8, w);
+            }
+        }
+        // latent blocks in turn; block mb+1's logits are in flight on the
+        // matrix core while block mb's softmax runs on the VALU
+        auto logits = [&](int mb) {
+            f32x16 S;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[r] = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) S = mfma(ka[kb], qop[mb][kb], S);
+            return S;
+        };
+        f32x16 Snext = logits(0);
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+            f32x16 S = Snext;
+            if (mb + 1 < MBW) Snext = logits(mb + 1);
+            if (tail) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int tok = 16 * (i >> 3) + 8 * hi + (i & 7);
+                    if (tok >= nv) S[i] = -INFINITY;
+                }
+            }
+            bf16x8 p0, p1;
+            float ts;
+            enc_probs(S, mu[mb], c, p0, p1, ts);
+            if (wave_any(!(ts <= kSumLimit))) {
+                // re-centre this latent block on its exact running maximum
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+                const float mnew = fmaxf(mu[mb], pair_max(mx) * c);
+                const float alpha = (mu[mb] == -INFINITY) ? 0.0f : exp2_fast(mu[mb] - mnew);
+                ps[mb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[mb][db] *= alpha;
+                mu[mb] = mnew;
+                enc_probs(S, mu[mb], c, p0, p1, ts);
+            }
+            ps[mb] += ts;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                acc[mb][db] = mfma(va[0][db], p0, acc[mb][db]);
+                acc[mb][db] = mfma(va[1][db], p1, acc[mb][db]);
+            }
+        }
+    };
+    // The chunk's last sub-block may be ragged; it is always this wave's last.
+    const bool ragged = nsub > 0 && n1 - (n0 + 32 * (wave + (nsub - 1) * NWV)) < 32;
+    const int nfull = ragged ? nsub - 1 : nsub;
+    for (int k = 0; k < nsub; ++k) {
+        if (k + NSW - 2 < nsub)
+            wait_vmcnt<(NSW - 2) * 2 * IPS>();
+        else
+            wait_vmcnt<0>();
+        if (k + NSW - 1 < nsub) {
+            // the stage refilled here was read in the previous iteration
+            __builtin_amdgcn_s_waitcnt((0x3F & 15) | ((0x3F >> 4) << 14) | (7 << 4) | (0 << 8));
+            issue(k + NSW - 1);
+        }
+        if (k == nfull) break;  // only the ragged sub-block is left (its data has landed)
+        sub_block(k, false);
+    }
+    if (ragged) sub_block(nfull, true);
+
+    // Merge the NWV waves' states (each saw a disjoint set of sub-blocks):
+    // every wave parks its state in LDS in its register layout (rows of 65
+    // floats, one per lane plus a pad against bank conflicts), then all threads
+    // combine disjoint (latent, column) entries and write the chunk's partials.
+    // Entry (m, d) of wave w sits at lane (m % 32) + 32 * ((d / 4) % 2),
+    // register 4 * ((d % 32) / 8) + d % 4 of accumulator (m / 32, d / 32).
+    __syncthreads();
+    float* mf = (float*)smem;
+    constexpr int RL = 65;
+    constexpr int PER_WAVE = MBW * (16 * DB + 2) * RL;
+    {
+        float* dst = mf + wave * PER_WAVE;
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[((mb * DB + db) * 16 + r) * RL + lane] = acc[mb][db][r];
+            dst[(MBW * DB * 16 + 2 * mb) * RL + lane] = mu[mb];
+            dst[(MBW * DB * 16 + 2 * mb + 1) * RL + lane] = ps[mb];
+        }
+    }
+    __syncthreads();
+    const int64_t pbase = ((int64_t)bh * gridDim.x + chunk) * Mp;
+    const int mlim = min(Mp, 32 * MBW);
+    for (int e = tid; e < mlim * D; e += 64 * NWV) {
+        const int m = e / D, d = e - m * D;
+        const int mb = m >> 5, l = m & 31, db = d >> 5, dd = d & 31;
+        const int r = 4 * (dd >> 3) + (dd & 3), ln = l + 32 * ((dd >> 2) & 1);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) mx = fmaxf(mx, mf[w * PER_WAVE + (MBW * DB * 16 + 2 * mb) * RL + l]);
+        float num = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+            const float* src = mf + w * PER_WAVE;
+            const float mw = src[(MBW * DB * 16 + 2 * mb) * RL + l];
+            const float aw = (mw == -INFINITY) ? 0.0f : exp2_fast(mw - mx);
+            num = fmaf(aw, src[((mb * DB + db) * 16 + r) * RL + ln], num);
+            den = fmaf(aw, src[(MBW * DB * 16 + 2 * mb + 1) * RL + l] + src[(MBW * DB * 16 + 2 * mb + 1) * RL + l + 32],
+                       den);
+        }
+        a.out.acc[(pbase + m) * D + d] = num;
+        if (d == 0) {
+            a.out.mu[pbase + m] = mx;
+            a.out.sig[pbase + m] = den;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // K3: decode.
 //
 // Workgroup = kDecWaves waves for one (b, h); Q[h] (or Q'[b,h]) and Z[b,h] are
@@ -424,22 +685,18 @@ __device__ __forceinline__ int dec_zpos(int m) {
     return (m & ~15) + (((r >> 2) & 1) << 3) + ((r >> 3) << 2) + (r & 3);
 }
 
-template <int D>
-__host__ __device__ constexpr int dec_zt_stride(int Mp) {
-    return 2 * Mp + 16;  // bytes per Z^T row (padded)
-}
-
-template <int D, typename ZT>
+template <int D, int TB, typename ZT>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
-    constexpr int KB = D / 16, DB = D / 32, CH = D / 8, TB = kDecTB, NW = kDecWaves;
+    constexpr int KB = D / 16, DB = D / 32, CH = D / 8, NW = kDecWaves;
+    const int Mp = a.Mp, MB = Mp / 32;
+    const int zs = 2 * Mp + 16;  // bytes per Z^T row (padded)
     extern __shared__ __attribute__((aligned(16))) unsigned char dsm[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hi = lane >> 5, l32 = lane & 31;
     const int bh = blockIdx.y;
     const int b = bh / a.H, h = bh - b * a.H;
-    const int N = a.N, M = a.M, Mp = a.Mp, Mb = Mp / 32;
+    const int N = a.N, M = a.M;
     const float c = a.c;
-    const int zs = dec_zt_stride<D>(Mp);
     unsigned char* qs = dsm;                  // [Mp][D] bf16, swizzled
     unsigned char* zt = dsm + Mp * 2 * D;     // [D][zs bytes]
     float* red = (float*)(zt + D * zs);       // [NW] reduction scratch
@@ -467,35 +724,43 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
         *(__bf16*)(zt + d * zs + 2 * dec_zpos(m)) = z;
     }
     __syncthreads();
-    // largest latent norm (for the per-token Cauchy-Schwarz offset)
-    float qn2 = 0.0f;
-    for (int m = tid; m < M; m += 64 * NW) {
-        float s2 = 0.0f;
-        for (int ch = 0; ch < CH; ++ch) {
-            const bf16x8 v = *(const bf16x8*)(qs + tile_off<D>(m, ch));
+    // Offsets. With the encode's merged offsets mu*[m] (log2 units), every
+    // logit of this (b, h) satisfies c*S <= max_m mu*[m] + 32, one offset for
+    // all tokens. Without them, per token: c * max_m |Q[m]| * |K[tok]|
+    // (Cauchy-Schwarz); here only max_m |Q[m]|^2 is prepared.
+    const bool goff = a.zmu != nullptr;
+    float red_in = goff ? -INFINITY : 0.0f;
+    if (goff) {
+        for (int m = tid; m < M; m += 64 * NW) red_in = fmaxf(red_in, a.zmu[(int64_t)bh * M + m]);
+    } else {
+        for (int m = tid; m < M; m += 64 * NW) {
+            float s2 = 0.0f;
+            for (int ch = 0; ch < CH; ++ch) {
+                const bf16x8 v = *(const bf16x8*)(qs + tile_off<D>(m, ch));
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float f = (float)v[j];
-                s2 = fmaf(f, f, s2);
+                for (int j = 0; j < 8; ++j) {
+                    const float f = (float)v[j];
+                    s2 = fmaf(f, f, s2);
+                }
             }
+            red_in = fmaxf(red_in, s2);
         }
-        qn2 = fmaxf(qn2, s2);
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) qn2 = fmaxf(qn2, __shfl_xor(qn2, off, 64));
-    if (lane == 0) red[wave] = qn2;
+    for (int off = 32; off >= 1; off >>= 1) red_in = fmaxf(red_in, __shfl_xor(red_in, off, 64));
+    if (lane == 0) red[wave] = red_in;
     __syncthreads();
-    float qmax2 = red[0];
+    float rmax = red[0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) qmax2 = fmaxf(qmax2, red[w]);
-    const float cq = c * sqrtf(qmax2);
+    for (int w = 1; w < NW; ++w) rmax = fmaxf(rmax, red[w]);
+    const float cq = goff ? 0.0f : c * sqrtf(rmax);
+    const float gnu = goff ? rmax + kSumLimitLog2 : 0.0f;
 
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    const f32x16 zero16 = {};
     const int nblk = (N + 32 * TB - 1) / (32 * TB);
     const int stride = gridDim.x * NW;
-    int blk = blockIdx.x * NW + wave;
 
-    bf16x8 kop[TB][KB], knx[TB][KB];
     auto kload = [&](int bk, bf16x8 (&dst)[TB][KB]) {
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
@@ -505,63 +770,81 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
                 dst[tb][kb] = (bk < nblk && n < N) ? *(const bf16x8*)(Kb + (int64_t)n * D + 16 * kb + 8 * hi) : zero8();
         }
     };
-    if (blk < nblk) kload(blk, kop);
-
-    for (; blk < nblk; blk += stride) {
-        kload(blk + stride, knx);  // next block in flight
-        float nu[TB];
+    auto qread = [&](int mb, bf16x8 (&qa)[KB]) {
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            float s2 = 0.0f;
+        for (int kb = 0; kb < KB; ++kb) qa[kb] = *(const bf16x8*)(qs + tile_off<D>(32 * mb + l32, 2 * kb + hi));
+    };
+    // softmax numerator and denominator of one 32-token block against the
+    // latents of block mb, with per-token offsets off[]
+    auto mask_tail = [&](int mb, f32x16& S) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bf16x2 k2 = {kop[tb][kb][2 * j], kop[tb][kb][2 * j + 1]};
-                    s2 = __builtin_amdgcn_fdot2_f32_bf16(k2, k2, s2, false);
-                }
-            nu[tb] = cq * sqrtf(pair_sum(s2));
+        for (int i = 0; i < 16; ++i) {
+            const int m = 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
+            if (m >= M) S[i] = -INFINITY;
         }
+    };
 
+    // One 64-token block: Y^T[d][tok] = sum_m Z^T[d][m] 2^(c S - nu)  and
+    // tau[tok] = sum_m 2^(c S - nu), latents streamed in blocks of 32.
+    auto process = [&](int bk, const bf16x8 (&kop)[TB][KB]) {
+        float nu[TB];
+        if (goff) {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) nu[tb] = gnu;
+        } else {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                float s2 = 0.0f;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bf16x2 k2 = {kop[tb][kb][2 * j], kop[tb][kb][2 * j + 1]};
+                        s2 = __builtin_amdgcn_fdot2_f32_bf16(k2, k2, s2, false);
+                    }
+                nu[tb] = cq * __builtin_sqrtf(pair_sum(s2));
+            }
+        }
         f32x16 yac[TB][DB];
         float tau[TB];
         auto run = [&](const float (&off)[TB]) {
+            bf16x8 qa[KB];
+            qread(0, qa);
+            f32x16 Snext[TB];
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
+                Snext[tb] = zero16;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) Snext[tb] = mfma(qa[kb], kop[tb][kb], Snext[tb]);
                 tau[tb] = 0.0f;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) yac[tb][db][r] = 0.0f;
             }
-            for (int mb = 0; mb < Mb; ++mb) {
-                bf16x8 qa[KB];
+            // one latent block; the next block's logits go to the matrix core
+            // before this block's softmax runs on the VALU
+            auto mstep = [&](int mb, bool first, bool masked) {
+                f32x16 S[TB];
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    qa[kb] = *(const bf16x8*)(qs + tile_off<D>(32 * mb + l32, 2 * kb + hi));
+                for (int tb = 0; tb < TB; ++tb) S[tb] = Snext[tb];
+                if (mb + 1 < MB) {
+                    qread(mb + 1, qa);
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) {
+                        Snext[tb] = zero16;
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb) Snext[tb] = mfma(qa[kb], kop[tb][kb], Snext[tb]);
+                    }
+                }
                 bf16x8 pb[TB][2];
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
-                    f32x16 S;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) S[r] = 0.0f;
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) S = mfma(qa[kb], kop[tb][kb], S);
-                    if (32 * mb + 32 > M) {
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int m = 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
-                            if (m >= M) S[i] = -INFINITY;
-                        }
-                    }
+                    if (masked) mask_tail(mb, S[tb]);
                     const float nm = -off[tb];
                     float t = tau[tb];
 #pragma unroll
                     for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const float e0 = exp2_fast(fmaf(S[8 * kp + 2 * j], c, nm));
-                            const float e1 = exp2_fast(fmaf(S[8 * kp + 2 * j + 1], c, nm));
+                            const float e0 = exp2_fast(fmaf(S[tb][8 * kp + 2 * j], c, nm));
+                            const float e1 = exp2_fast(fmaf(S[tb][8 * kp + 2 * j + 1], c, nm));
                             const bf16x2 p2 = {(__bf16)e0, (__bf16)e1};
                             t = __builtin_amdgcn_fdot2_f32_bf16(p2, one, t, false);
                             pb[tb][kp][2 * j] = p2[0];
@@ -576,8 +859,25 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
                         const int d = 32 * db + dec_row_d(l32);
                         const bf16x8 za = *(const bf16x8*)(zt + d * zs + 2 * (32 * mb + 16 * kp + 8 * hi));
 #pragma unroll
-                        for (int tb = 0; tb < TB; ++tb) yac[tb][db] = mfma(za, pb[tb][kp], yac[tb][db]);
+                        for (int tb = 0; tb < TB; ++tb)
+                            yac[tb][db] = mfma(za, pb[tb][kp], (first && kp == 0) ? zero16 : yac[tb][db]);
                     }
+            };
+            // only the last latent block can hold padding rows (M % 32 != 0)
+            const bool mtail = (M & 31) != 0;
+            if (MB == 1) {
+                if (mtail)
+                    mstep(0, true, true);
+                else
+                    mstep(0, true, false);
+            } else {
+                mstep(0, true, false);
+#pragma unroll 1
+                for (int mb = 1; mb < MB - 1; ++mb) mstep(mb, false, false);
+                if (mtail)
+                    mstep(MB - 1, false, true);
+                else
+                    mstep(MB - 1, false, false);
             }
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) tau[tb] = pair_sum(tau[tb]);
@@ -591,23 +891,18 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
             float mx[TB];
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) mx[tb] = -INFINITY;
-            for (int mb = 0; mb < Mb; ++mb) {
+#pragma unroll 1
+            for (int mb = 0; mb < MB; ++mb) {
                 bf16x8 qa[KB];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    qa[kb] = *(const bf16x8*)(qs + tile_off<D>(32 * mb + l32, 2 * kb + hi));
+                qread(mb, qa);
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
-                    f32x16 S;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) S[r] = 0.0f;
+                    f32x16 S = zero16;
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) S = mfma(qa[kb], kop[tb][kb], S);
+                    if (32 * mb + 32 > M) mask_tail(mb, S);
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int m = 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
-                        if (m < M) mx[tb] = fmaxf(mx[tb], S[i]);
-                    }
+                    for (int i = 0; i < 16; ++i) mx[tb] = fmaxf(mx[tb], S[i]);
                 }
             }
             float ex[TB];
@@ -618,8 +913,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
         // normalise, round, store
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-            const int n = blk * 32 * TB + 32 * tb + l32;
-            const float inv = 1.0f / tau[tb];
+            const int n = bk * 32 * TB + 32 * tb + l32;
+            const float inv = __builtin_amdgcn_rcpf(tau[tb]);
             if (n < N) {
                 uint16_t* dst = Yb + (int64_t)n * D + 16 * hi;
 #pragma unroll
@@ -635,10 +930,21 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
                 }
             }
         }
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) kop[tb][kb] = knx[tb][kb];
+    };
+
+    // Blocks blk, blk + stride, ... of this wave; two K register sets in
+    // turn so that the next block's rows are always in flight.
+    int blk = blockIdx.x * NW + wave;
+    bf16x8 kA[TB][KB], kB[TB][KB];
+    kload(blk, kA);
+    while (blk < nblk) {
+        kload(blk + stride, kB);
+        process(blk, kA);
+        blk += stride;
+        if (blk >= nblk) break;
+        kload(blk + stride, kA);
+        process(blk, kB);
+        blk += stride;
     }
 }
 
@@ -649,9 +955,30 @@ hipError_t launch_enc(const EncodeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int D, int MBW, int NWV>
+hipError_t launch_enc_priv(const EncodeArgs& a, hipStream_t s) {
+    dim3 grid(a.C, a.BH), block(64 * NWV);
+    hipLaunchKernelGGL((encode_partial_priv_bf16<D, MBW, NWV>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_enc_d(const EncodeArgs& a, hipStream_t s) {
     const EncCfg cfg = enc_cfg_bf16(D, a.Mp / 32);
+    if (cfg.wm == 0) {  // private-stream form: cfg.mbw latent blocks per wave, cfg.wt waves
+#define FLARE_ENCP_CASE(MBW, NWV) \
+    if (cfg.mbw == MBW && cfg.wt == NWV) return launch_enc_priv<D, MBW, NWV>(a, s);
+        FLARE_ENCP_CASE(1, 4)
+        if constexpr (D <= 64) {
+            FLARE_ENCP_CASE(2, 4)
+        }
+        if constexpr (D == 32) {
+            FLARE_ENCP_CASE(3, 4)
+            FLARE_ENCP_CASE(4, 4)
+        }
+#undef FLARE_ENCP_CASE
+        return hipErrorInvalidValue;
+    }
 #define FLARE_ENC_CASE(MBW, WM, WT) \
     if (cfg.mbw == MBW && cfg.wm == WM && cfg.wt == WT) return launch_enc<D, MBW, WM, WT>(a, s);
     FLARE_ENC_CASE(1, 1, 2)
@@ -669,17 +996,22 @@ hipError_t launch_enc_d(const EncodeArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-template <int D, typename ZT>
-hipError_t launch_dec(const DecodeArgs& a, hipStream_t s) {
+template <int D, int TB, typename ZT>
+hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
     const int lds = dec_lds_bytes_bf16(a.Mp, D);
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)decode_bf16<D, ZT>,
+        hipError_t e = hipFuncSetAttribute((const void*)decode_bf16<D, TB, ZT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
     }
     dim3 grid(a.G, a.BH), block(64 * kDecWaves);
-    hipLaunchKernelGGL((decode_bf16<D, ZT>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((decode_bf16<D, TB, ZT>), grid, block, lds, s, a);
     return hipGetLastError();
+}
+
+template <int D, typename ZT>
+hipError_t launch_dec(const DecodeArgs& a, hipStream_t s) {
+    return dec_tb_bf16(D) == 2 ? launch_dec_tb<D, 2, ZT>(a, s) : launch_dec_tb<D, 1, ZT>(a, s);
 }
 
 }  // namespace
@@ -689,17 +1021,49 @@ EncCfg enc_cfg_bf16(int D, int Mb) {
     // instantiated shape that covers Mb latent blocks.
     if (const char* e = std::getenv("FLARE_TEST_ENC_CFG")) {
         int x = 0, y = 0, z = 0;
-        if (std::sscanf(e, "%d,%d,%d", &x, &y, &z) == 3 && x * y >= Mb) return {x, y, z};
+        if (std::sscanf(e, "%d,%d,%d", &x, &y, &z) == 3 && (y == 0 ? x >= Mb : x * y >= Mb)) return {x, y, z};
     }
-    if (Mb <= 1) return {1, 1, 2};
+    // private streams while one wave's registers hold every latent
+    if (D == 32 && Mb <= 4) return {Mb, 0, 4};
+    if (D == 64 && Mb <= 2) return {Mb, 0, 4};
+    if (D == 128 && Mb <= 1) return {1, 0, 4};
     if (Mb <= 2) return {1, 2, 2};
-    if (Mb <= 4) return {1, 4, 1};
+    if (Mb <= 4) return {2, 2, 2};
     if (D == 128) return {1, 8, 1};
     return {2, 4, 1};
 }
 
-int enc_tile_tokens_bf16(EncCfg) { return 64; }
-int enc_threads_bf16(EncCfg cfg) { return 64 * cfg.wm * cfg.wt; }
+int enc_tile_tokens_bf16(EncCfg cfg) { return cfg.wm == 0 ? 32 * cfg.wt : 64; }
+int enc_threads_bf16(EncCfg cfg) { return 64 * (cfg.wm == 0 ? 1 : cfg.wm) * cfg.wt; }
+
+int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32) {
+    const int tb = dec_tb_bf16(D);
+    const int lds = dec_lds_bytes_bf16(Mp, D);
+    const void* fn = nullptr;
+#define FLARE_DEC_FN(DD)                                                                             \
+    if (D == DD)                                                                                     \
+        fn = tb == 2 ? (z_f32 ? (const void*)decode_bf16<DD, 2, float> : (const void*)decode_bf16<DD, 2, uint16_t>) \
+                     : (z_f32 ? (const void*)decode_bf16<DD, 1, float> : (const void*)decode_bf16<DD, 1, uint16_t>);
+    FLARE_DEC_FN(32)
+    FLARE_DEC_FN(64)
+    FLARE_DEC_FN(128)
+#undef FLARE_DEC_FN
+    if (!fn) return 1;
+    if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+        return 1;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * kDecWaves, lds) != hipSuccess || n < 1) return 1;
+    return n;
+}
+
+int dec_tb_bf16(int D) {
+    // Tuning override (tests and sweeps): 32-token blocks per wave and step.
+    if (const char* e = std::getenv("FLARE_TEST_DEC_TB")) {
+        const int v = std::atoi(e);
+        if (v == 1 || v == 2) return v;
+    }
+    return D <= 32 ? 2 : 1;
+}
 
 int dec_lds_bytes_bf16(int Mp, int D) { return Mp * 2 * D + D * (2 * Mp + 16) + 64; }
 

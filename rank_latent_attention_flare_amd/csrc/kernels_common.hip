@@ -44,20 +44,36 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const float* __restrict__ sg = a.in.sig + row0;
     const float* __restrict__ ac = a.in.acc + row0 * D + d;
     const int64_t sacc = (int64_t)Mp * D;
-    // loops unrolled so that many independent loads are in flight at once
+    // chunks in groups of 8: all loads of a group are issued before any use
+    constexpr int G = 8;
     float mx = -INFINITY;
-#pragma unroll 8
-    for (int c = 0; c < C; ++c) mx = fmaxf(mx, mu[(int64_t)c * Mp]);
+    for (int c0 = 0; c0 < C; c0 += G) {
+        float mv[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) mv[j] = (c0 + j < C) ? mu[(int64_t)(c0 + j) * Mp] : -INFINITY;
+#pragma unroll
+        for (int j = 0; j < G; ++j) mx = fmaxf(mx, mv[j]);
+    }
     float num = 0.0f, den = 0.0f;
-#pragma unroll 8
-    for (int c = 0; c < C; ++c) {
-        const float mc = mu[(int64_t)c * Mp];
-        const float w = (mc == -INFINITY) ? 0.0f : exp2f(mc - mx);
-        num = fmaf(w, ac[(int64_t)c * sacc], num);
-        den = fmaf(w, sg[(int64_t)c * Mp], den);
+    for (int c0 = 0; c0 < C; c0 += G) {
+        float mv[G], av[G], sv[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const bool in = c0 + j < C;
+            mv[j] = in ? mu[(int64_t)(c0 + j) * Mp] : -INFINITY;
+            av[j] = in ? ac[(int64_t)(c0 + j) * sacc] : 0.0f;
+            sv[j] = in ? sg[(int64_t)(c0 + j) * Mp] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float w = (mv[j] == -INFINITY) ? 0.0f : exp2f(mv[j] - mx);
+            num = fmaf(w, av[j], num);
+            den = fmaf(w, sv[j], den);
+        }
     }
     const float z = num / den;
     const int64_t o = (int64_t)bh * a.M * D + idx;
+    if (a.zmu && d == 0) a.zmu[(int64_t)bh * a.M + m] = mx;
     if (a.mode == COMBINE_Z_F32) {
         ((float*)a.out)[o] = z;
     } else if (a.mode == COMBINE_Z_DTYPE) {

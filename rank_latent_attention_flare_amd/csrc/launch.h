@@ -39,6 +39,7 @@ struct CombineArgs {
     bool bf16;           // operator dtype (for modes 1 and 2)
     const void* Q;       // mode 2: learned queries [H][M][D]
     void* out;
+    float* zmu;          // optional [BH][M]: merged offsets mu* (log2 units) per latent
 };
 
 struct DecodeArgs {
@@ -47,13 +48,16 @@ struct DecodeArgs {
     const void* K;       // [B][H][N][D]
     const void* Z;       // [BH][M][D], fp32 or operator dtype
     bool z_f32;
+    const float* zmu;    // optional [BH][M] merged encode offsets; null: per-token bound
     void* Y;             // [B][H][N][D]
     int BH, H, N, M, Mp, D;
     int G;               // workgroups per (b, h)
     float c;
 };
 
-// Encode tile configuration for bf16 (waves over latent blocks x waves over tokens).
+// Encode configuration for bf16. wm > 0: shared-tile form with wm waves over
+// latent blocks (mbw blocks each) x wt waves over tokens. wm == 0: private-
+// stream form, wt waves that each own all mbw latent blocks.
 struct EncCfg {
     int mbw, wm, wt;
 };
@@ -62,7 +66,8 @@ int enc_tile_tokens_bf16(EncCfg cfg);
 int enc_threads_bf16(EncCfg cfg);
 
 constexpr int kDecWaves = 4;  // waves per decode workgroup
-constexpr int kDecTB = 2;     // 32-token blocks per wave per step
+int dec_tb_bf16(int D);       // 32-token blocks per wave per step
+int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32);  // resident decode workgroups per CU
 int dec_lds_bytes_bf16(int Mp, int D);
 
 hipError_t launch_encode_bf16(const EncodeArgs& a, hipStream_t s);

@@ -205,13 +205,17 @@ def test_chunk_count_invariance(i, monkeypatch):
 
 
 @pytest.mark.parametrize("i", [2, 3, 4])
-def test_forward_is_decode_of_encode_bitwise(i):
+def test_forward_matches_decode_of_encode(i):
+    # Same Z (rounded once to bf16 in both); the fused forward's decode uses
+    # one offset per (b, h) from the encode, the standalone decode per-token
+    # offsets, so the two agree to rounding, not bit for bit.
     w, Q, K, V, Qd, Kd, Vd = workload(i)
     Y = F.flare_forward(Qd, Kd, Vd)
     Z = F.flare_encode(Qd, Kd, Vd)
     Y2 = F.flare_decode(Qd, Kd, Z)
     torch.cuda.synchronize()
-    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
+    e = errors(Y.double().cpu().numpy(), Y2.double().cpu().numpy())
+    assert e["rel_l2"] <= 2e-3 and e["max_abs"] <= 3e-2, e
 
 
 def test_pp_forward_is_forward_with_corrected_queries():
