@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,10 +35,16 @@ KERNEL_SOURCES = {
 
 
 def source_hash(kind: str) -> str:
+    """Hash of the code (comments and blank space removed) of the sources that
+    define a kernel: recorded with its hardware counters, so that counters taken
+    on an older version of the kernel are not reported against the current one."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -28,8 +28,10 @@
  *             fp32; probabilities, Z and Q' are rounded to nearest-even bf16
  *             where they become MFMA operands, and outputs are rounded to
  *             nearest-even bf16.
- *   Sizes     B, H, N, M, D >= 1. Supported: FLARE_F32 with D <= 128 and
- *             M <= 512; FLARE_BF16 with D in {32, 64, 128} and M <= 256.
+ *   Sizes     B, H, N, M, D >= 1, B*H <= 65535, N <= 2^30. Supported:
+ *             FLARE_F32 with D in {8, 16, 24, 32, 48, 64, 96, 128} and
+ *             M <= 4096; FLARE_BF16 with D in {32, 64, 128} and M <= 256.
+ *             Other sizes return FLARE_ERR_UNSUPPORTED.
  *   Async     Work is enqueued on `stream` (0 = the legacy default stream)
  *             and the call returns; inputs must stay unchanged until the
  *             stream passes the call. Device faults surface at the caller's

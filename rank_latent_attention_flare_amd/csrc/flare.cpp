@@ -108,13 +108,16 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     } else {
         p->Mp = int(M);
         tile = 64;
-        waves_per_wg = 4 * int((M + 255) / 256);
+        const int nth = flare::enc_threads_f32(int(M));
+        waves_per_wg = int((M + nth - 1) / nth) * (nth / 64);
     }
-    // Split over N: enough workgroups to fill the chip, but chunks of at least
-    // 32*Mp tokens so that the partials stay a few percent of the K/V bytes.
+    // Split over N: enough workgroups to fill the chip, but chunks long enough
+    // that the partials stay a few percent of the K/V bytes (bf16: 32*Mp
+    // tokens; fp32, whose lanes each run a whole latent: 4*Mp, at least one tile).
     const int64_t target_wgs = std::max<int64_t>(1, kTargetEncWaves / waves_per_wg);
     int64_t C = std::max<int64_t>(1, (target_wgs + p->BH - 1) / p->BH);
-    const int64_t cmax = std::max<int64_t>(1, N / (32 * int64_t(p->Mp)));
+    const int64_t min_chunk = dt == FLARE_BF16 ? 32 * int64_t(p->Mp) : std::max<int64_t>(tile, 4 * int64_t(p->Mp));
+    const int64_t cmax = std::max<int64_t>(1, N / min_chunk);
     C = std::min(C, cmax);
     if (const char* e = std::getenv("FLARE_TEST_CHUNKS")) {
         const long v = std::strtol(e, nullptr, 10);
@@ -487,8 +490,9 @@ flare_status flare_describe_plan(flare_op op, int64_t B, int64_t H, int64_t N, i
               std::to_string(cfg.wm) + "x" + std::to_string(cfg.wt) + " latent-blocks/wave " + std::to_string(cfg.mbw) +
               " tile " + std::to_string(flare::enc_tile_tokens_bf16(cfg));
     } else {
-        enc = "encode grid (" + std::to_string(p.C) + "," + std::to_string(p.BH) + "," + std::to_string((M + 255) / 256) +
-              ") threads 256";
+        const int nth = flare::enc_threads_f32(int(M));
+        enc = "encode grid (" + std::to_string(p.C) + "," + std::to_string(p.BH) + "," + std::to_string((M + nth - 1) / nth) +
+              ") threads " + std::to_string(nth);
     }
     std::string txt = enc + " chunk " + std::to_string(p.chunk_len) + "; decode grid (" +
                       (dtype == FLARE_BF16 ? std::to_string(p.G) : std::to_string((N + 255) / 256)) + "," +

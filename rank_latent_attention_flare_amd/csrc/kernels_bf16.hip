@@ -668,11 +668,13 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
 //   S^T[m][tok] = Q[m] . K[tok]            (MFMA; A = Q from LDS)
 //   p = 2^(S*c - nu[tok])                  (lane-local: lane holds token l%32)
 //   Y^T[d][tok] += Z^T[d][m] p[m][tok]      (MFMA; A = Z^T from LDS)
-// nu[tok] = c * max_m |Q[m]| * |K[tok]| bounds every logit of the token from
-// above (Cauchy-Schwarz), so no maximum over the latents is needed and the
-// registers do not grow with M. Softmax is invariant to the offset; if a
-// token's probability sum falls below kTauFloor (offset too loose, rare) the
-// block is recomputed with the exact per-token maximum. Y = (P Z) / sum(P),
+// The offset nu bounds every logit of the token from above, so no maximum over
+// the latents is needed and the registers do not grow with M: after the fused
+// encode, one nu per (b, h) = max_m mu*[m] + 32 from the encode's merged
+// offsets; standalone, nu[tok] = c * max_m |Q[m]| * |K[tok]| (Cauchy-Schwarz).
+// Softmax is invariant to the offset; if a token's probability sum falls below
+// kTauFloor (offset too loose, rare) the block is recomputed with the exact
+// per-token maximum. Y = (P Z) / sum(P),
 // rounded to bf16 and stored as 32-byte runs per lane.
 // ---------------------------------------------------------------------------
 // Row d of the Z^T operand read by MFMA row q: makes output register r of

@@ -95,17 +95,18 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 encode partials: grid (C, BH, latent groups of 256); thread = latent.
-// K/V tiles of 64 tokens go through LDS; each thread keeps its latent's exact
-// running maximum, sum and accumulator.
+// fp32 encode partials: grid (C, BH, latent groups of blockDim.x); thread =
+// latent. blockDim.x is M rounded up to 64, at most 256. K/V tiles of 64
+// tokens go through LDS; each thread keeps its latent's exact running maximum,
+// sum and accumulator.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
     constexpr int T = 64;
     __shared__ float kt[T * D], vt[T * D];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, nth = blockDim.x;
     const int chunk = blockIdx.x, bh = blockIdx.y;
-    const int m = blockIdx.z * 256 + tid;
+    const int m = blockIdx.z * nth + tid;
     const int b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M;
     const int n0 = chunk * a.chunk_len, n1 = min(N, n0 + a.chunk_len);
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
     float mu = -INFINITY, sig = 0.0f;
     for (int t0 = n0; t0 < n1; t0 += T) {
         const int nt = min(T, n1 - t0);
-        for (int e = tid; e < nt * D; e += 256) {
+        for (int e = tid; e < nt * D; e += nth) {
             kt[e] = Kb[(int64_t)t0 * D + e];
             vt[e] = Vb[(int64_t)t0 * D + e];
         }
@@ -210,7 +211,8 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
 
 template <int D>
 hipError_t enc_f32(const EncodeArgs& a, hipStream_t s) {
-    dim3 grid(a.C, a.BH, (a.M + 255) / 256), block(256);
+    const int nth = enc_threads_f32(a.M);
+    dim3 grid(a.C, a.BH, (a.M + nth - 1) / nth), block(nth);
     hipLaunchKernelGGL((encode_partial_f32<D>), grid, block, 0, s, a);
     return hipGetLastError();
 }
@@ -237,6 +239,8 @@ hipError_t dec_f32(const DecodeArgs& a, hipStream_t s) {
         case 128: return FN<128>(a, s);  \
         default: return hipErrorInvalidValue; \
     }
+
+int enc_threads_f32(int M) { return M >= 256 ? 256 : (M + 63) / 64 * 64; }
 
 hipError_t launch_encode_f32(const EncodeArgs& a, hipStream_t s) { FLARE_F32_DISPATCH(enc_f32, a, s) }
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { FLARE_F32_DISPATCH(dec_f32, a, s) }

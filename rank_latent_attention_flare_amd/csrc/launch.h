@@ -72,6 +72,7 @@ int dec_lds_bytes_bf16(int Mp, int D);
 
 hipError_t launch_encode_bf16(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+int enc_threads_f32(int M);     // threads per fp32 encode workgroup (latents per group)
 hipError_t launch_encode_f32(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
