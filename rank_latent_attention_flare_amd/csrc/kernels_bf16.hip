@@ -89,12 +89,28 @@ __device__ __forceinline__ bf16x8 zero8() {
     return __builtin_bit_cast(bf16x8, z);
 }
 
-// Probabilities of one 32-token sub-block for one 32-latent block:
-// p = 2^(S*c - mu) rounded to bf16, packed as the two k-halves of the P.V B
-// operand, and the sum of the rounded values.
-__device__ __forceinline__ void enc_probs(const f32x16& S, float mu, float c, bf16x8& p0, bf16x8& p1,
-                                          float& tsum) {
-    const float nm = -mu;
+__device__ __forceinline__ f32x16 splat16(float v) {
+    f32x16 r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = v;
+    return r;
+}
+
+// Query operand with the logit scale folded in: bf16(c * q), rounded to
+// nearest even from the exact fp32 product. The MFMA then yields c*S
+// directly; with the latent's (or token's) offset as its accumulator input it
+// yields the shifted logits c*S - offset that the exponentials take.
+__device__ __forceinline__ bf16x8 scaled_op(bf16x8 q, float c) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (__bf16)((float)q[j] * c);
+    return r;
+}
+
+// Probabilities of one 32-token sub-block for one 32-latent block from its
+// shifted logits X = c*S - mu: p = 2^X rounded to bf16, packed as the two
+// k-halves of the P.V B operand, and the sum of the rounded values.
+__device__ __forceinline__ void enc_probs(const f32x16& X, bf16x8& p0, bf16x8& p1, float& tsum) {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     float t = 0.0f;
     bf16x8 pp[2];
@@ -102,8 +118,8 @@ __device__ __forceinline__ void enc_probs(const f32x16& S, float mu, float c, bf
     for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float e0 = exp2_fast(fmaf(S[8 * kp + 2 * j], c, nm));
-            const float e1 = exp2_fast(fmaf(S[8 * kp + 2 * j + 1], c, nm));
+            const float e0 = exp2_fast(X[8 * kp + 2 * j]);
+            const float e1 = exp2_fast(X[8 * kp + 2 * j + 1]);
             const bf16x2 p2 = {(__bf16)e0, (__bf16)e1};
             t = __builtin_amdgcn_fdot2_f32_bf16(p2, one, t, false);
             pp[kp][2 * j] = p2[0];
@@ -155,6 +171,36 @@ __device__ __forceinline__ void dma16(const void* g, unsigned char* lds_wave_bas
     __builtin_amdgcn_global_load_lds((const void*)g, (void*)lds_wave_base, 16, 0, 0);
 }
 
+// Transposed LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i%4 of the 64-bit words of lanes 4k + i/4 of the group.
+// Two reads form one 8 x bf16 MFMA operand; lds_tr_op2 reads two operands.
+// It is inline asm that waits for its own results before returning: with the
+// compiler builtin, the compiler drains every outstanding global->LDS
+// transfer (vmcnt(0)) before the read, which would empty the prefetch ring on
+// every sub-block. Callers order these reads after the transfers they need
+// (explicit vmcnt wait, then barrier).
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+__device__ __forceinline__ void lds_tr_op2(const unsigned char* p1, const unsigned char* p2,
+                                           const unsigned char* p3, const unsigned char* p4, bf16x8& o1,
+                                           bf16x8& o2) {
+    u32x2 w1, w2, w3, w4;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %6\n\t"
+        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(w4)
+        : "v"(lds_addr(p1)), "v"(lds_addr(p2)), "v"(lds_addr(p3)), "v"(lds_addr(p4))
+        : "memory");
+    const u32x4 a = {w1[0], w1[1], w2[0], w2[1]};
+    const u32x4 b = {w3[0], w3[1], w4[0], w4[1]};
+    o1 = __builtin_bit_cast(bf16x8, a);
+    o2 = __builtin_bit_cast(bf16x8, b);
+}
+
 template <int D, int MBW, int WM, int WT>
 struct EncShape {
     static constexpr int KB = D / 16, DB = D / 32, CH = D / 8, RB = 2 * D;
@@ -198,14 +244,18 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
         const int m = 32 * (wm * MBW + mb) + l32;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-            qop[mb][kb] = (m < M) ? *(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi) : zero8();
+            qop[mb][kb] = (m < M) ? scaled_op(*(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi), c) : zero8();
     }
 
+    // Per latent: offset mu (log2 units; -inf until the first re-centring),
+    // its negation as an MFMA accumulator input, sum of p and accumulator.
     float mu[MBW], ps[MBW];
+    f32x16 nmu[MBW];
     f32x16 acc[MBW][DB];
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
         mu[mb] = -INFINITY;
+        nmu[mb] = splat16(INFINITY);
         ps[mb] = 0.0f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -254,46 +304,53 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             const int krow = 32 * sb + enc_row_token(l32);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) ka[kb] = *(const bf16x8*)(kt + tile_off<D>(krow, 2 * kb + hi));
+            auto mask = [&](f32x16& X) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int tok = 16 * (i >> 3) + 8 * hi + (i & 7);
+                    if (tok >= nv) X[i] = -INFINITY;
+                }
+            };
+            // shifted logits c*S - mu straight from the matrix core
             f32x16 S[MBW];
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
+                S[mb] = mfma(ka[0], qop[mb][0], nmu[mb]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) S[mb][r] = 0.0f;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) S[mb] = mfma(ka[kb], qop[mb][kb], S[mb]);
-            }
-            if (tail) {
-#pragma unroll
-                for (int mb = 0; mb < MBW; ++mb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int tok = 16 * (i >> 3) + 8 * hi + (i & 7);
-                        if (tok >= nv) S[mb][i] = -INFINITY;
-                    }
+                for (int kb = 1; kb < KB; ++kb) S[mb] = mfma(ka[kb], qop[mb][kb], S[mb]);
+                if (tail) mask(S[mb]);
             }
             bf16x8 pb[MBW][2];
             float ts[MBW];
             bool bad = false;
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
-                enc_probs(S[mb], mu[mb], c, pb[mb][0], pb[mb][1], ts[mb]);
+                enc_probs(S[mb], pb[mb][0], pb[mb][1], ts[mb]);
                 bad |= !(ts[mb] <= kSumLimit);
             }
             if (wave_any(bad)) {
                 // Re-centre on the exact running maximum (rare: first tile of a
-                // chunk, or a jump of the maximum by more than ~28 in log2).
+                // chunk, or a jump of the maximum by more than ~28 in log2):
+                // unshifted logits again, then shift by the new offset.
 #pragma unroll
                 for (int mb = 0; mb < MBW; ++mb) {
+                    f32x16 R = mfma(ka[0], qop[mb][0], splat16(0.0f));
+#pragma unroll
+                    for (int kb = 1; kb < KB; ++kb) R = mfma(ka[kb], qop[mb][kb], R);
+                    if (tail) mask(R);
                     float mx = -INFINITY;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[mb][i]);
-                    const float mnew = fmaxf(mu[mb], pair_max(mx) * c);
+                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, R[i]);
+                    const float mnew = fmaxf(mu[mb], pair_max(mx));
                     const float alpha = (mu[mb] == -INFINITY) ? 0.0f : exp2_fast(mu[mb] - mnew);
                     ps[mb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) acc[mb][db] *= alpha;
                     mu[mb] = mnew;
-                    enc_probs(S[mb], mu[mb], c, pb[mb][0], pb[mb][1], ts[mb]);
+                    nmu[mb] = splat16(-mnew);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) S[mb][i] = R[i] - mnew;
+                    enc_probs(S[mb], pb[mb][0], pb[mb][1], ts[mb]);
                 }
             }
 #pragma unroll
@@ -302,24 +359,23 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             // transposed from the row-major tile: lane i of each 16-lane group
             // receives element i%4 of source lanes 4k + i/4.
             const int g = lane >> 4, gi = lane & 15;
+            // operand (kp, db) covers tokens 16*kp.. and rows d = 32*db..
+            auto vaddr = [&](int kp, int db, int second) {
+                const int row = 32 * sb + 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
+                const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+                return vt + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+            };
+            constexpr int NOP = 2 * DB;  // operands of this sub-block
 #pragma unroll
-            for (int kp = 0; kp < 2; ++kp) {
-                const int row1 = 32 * sb + 16 * kp + 8 * (g >> 1) + (gi >> 2);
+            for (int o = 0; o < NOP; o += 2) {
+                const int kp0 = o / DB, db0 = o % DB, kp1 = (o + 1) / DB, db1 = (o + 1) % DB;
+                bf16x8 va0, va1;
+                lds_tr_op2(vaddr(kp0, db0, 0), vaddr(kp0, db0, 1), vaddr(kp1, db1, 0), vaddr(kp1, db1, 1), va0,
+                           va1);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
-                    const int off1 = tile_off<D>(row1, dcol >> 3) + ((dcol >> 2) & 1) * 8;
-                    const int off2 = tile_off<D>(row1 + 4, dcol >> 3) + ((dcol >> 2) & 1) * 8;
-                    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-                    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off1));
-                    const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off2));
-                    const u32x2 w1 = __builtin_bit_cast(u32x2, r1);
-                    const u32x2 w2 = __builtin_bit_cast(u32x2, r2);
-                    const u32x4 w = {w1[0], w1[1], w2[0], w2[1]};
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, w);
+                for (int mb = 0; mb < MBW; ++mb) acc[mb][db0] = mfma(va0, pb[mb][kp0], acc[mb][db0]);
 #pragma unroll
-                    for (int mb = 0; mb < MBW; ++mb) acc[mb][db] = mfma(va, pb[mb][kp], acc[mb][db]);
-                }
+                for (int mb = 0; mb < MBW; ++mb) acc[mb][db1] = mfma(va1, pb[mb][kp1], acc[mb][db1]);
             }
         }
     };
@@ -462,13 +518,15 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
         const int m = 32 * mb + l32;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-            qop[mb][kb] = (m < M) ? *(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi) : zero8();
+            qop[mb][kb] = (m < M) ? scaled_op(*(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi), c) : zero8();
     }
     float mu[MBW], ps[MBW];
+    f32x16 nmu[MBW];  // -mu as the logit MFMA's accumulator input
     f32x16 acc[MBW][DB];
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
         mu[mb] = -INFINITY;
+        nmu[mb] = splat16(INFINITY);
         ps[mb] = 0.0f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -526,38 +584,25 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
         // V^T operands of this sub-block (shared by every latent block)
         bf16x8 va[2][DB];
         const int g = lane >> 4, gi = lane & 15;
+        auto vaddr = [&](int kp, int db, int second) {
+            const int row = 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
+            const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+            return vt + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+        };
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-            const int row1 = 16 * kp + 8 * (g >> 1) + (gi >> 2);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
-                const int off1 = tile_off<D>(row1, dcol >> 3) + ((dcol >> 2) & 1) * 8;
-                const int off2 = tile_off<D>(row1 + 4, dcol >> 3) + ((dcol >> 2) & 1) * 8;
-                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-                const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off1));
-                const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off2));
-                const u32x2 w1 = __builtin_bit_cast(u32x2, r1);
-                const u32x2 w2 = __builtin_bit_cast(u32x2, r2);
-                const u32x4 w = {w1[0], w1[1], w2[0], w2[1]};
-                va[kp][db] = __builtin_bit_cast(bf16x8, w);
-            }
+        for (int o = 0; o < 2 * DB; o += 2) {
+            const int kp0 = o / DB, db0 = o % DB, kp1 = (o + 1) / DB, db1 = (o + 1) % DB;
+            lds_tr_op2(vaddr(kp0, db0, 0), vaddr(kp0, db0, 1), vaddr(kp1, db1, 0), vaddr(kp1, db1, 1),
+                       va[kp0][db0], va[kp1][db1]);
         }
         // latent blocks in turn; block mb+1's logits are in flight on the
         // matrix core while block mb's softmax runs on the VALU
-        auto logits = [&](int mb) {
-            f32x16 S;
+        // logits of latent block mb against this sub-block, shifted by the
+        // accumulator input C0 (-mu: shifted logits; 0: c*S itself)
+        auto logits = [&](int mb, const f32x16& C0) {
+            f32x16 S = mfma(ka[0], qop[mb][0], C0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) S[r] = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) S = mfma(ka[kb], qop[mb][kb], S);
-            return S;
-        };
-        f32x16 Snext = logits(0);
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) {
-            f32x16 S = Snext;
-            if (mb + 1 < MBW) Snext = logits(mb + 1);
+            for (int kb = 1; kb < KB; ++kb) S = mfma(ka[kb], qop[mb][kb], S);
             if (tail) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -565,21 +610,32 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
                     if (tok >= nv) S[i] = -INFINITY;
                 }
             }
+            return S;
+        };
+        f32x16 Snext = logits(0, nmu[0]);
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+            f32x16 S = Snext;
+            if (mb + 1 < MBW) Snext = logits(mb + 1, nmu[mb + 1]);
             bf16x8 p0, p1;
             float ts;
-            enc_probs(S, mu[mb], c, p0, p1, ts);
+            enc_probs(S, p0, p1, ts);
             if (wave_any(!(ts <= kSumLimit))) {
                 // re-centre this latent block on its exact running maximum
+                const f32x16 R = logits(mb, splat16(0.0f));
                 float mx = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
-                const float mnew = fmaxf(mu[mb], pair_max(mx) * c);
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, R[i]);
+                const float mnew = fmaxf(mu[mb], pair_max(mx));
                 const float alpha = (mu[mb] == -INFINITY) ? 0.0f : exp2_fast(mu[mb] - mnew);
                 ps[mb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) acc[mb][db] *= alpha;
                 mu[mb] = mnew;
-                enc_probs(S, mu[mb], c, p0, p1, ts);
+                nmu[mb] = splat16(-mnew);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) S[i] = R[i] - mnew;
+                enc_probs(S, p0, p1, ts);
             }
             ps[mb] += ts;
 #pragma unroll
@@ -707,12 +763,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
     uint16_t* __restrict__ Yb = (uint16_t*)a.Y + (int64_t)bh * N * D;
 
-    // ---- stage Q (bf16, swizzled rows) and Z^T (bf16, permuted latents)
+    // ---- stage c*Q (bf16, swizzled rows) and Z^T (bf16, permuted latents)
     for (int p = tid; p < Mp * CH; p += 64 * NW) {
         const int m = p / CH, ch = p % CH;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (m < M) v = *(const u32x4*)(Qb + (int64_t)m * D + ch * 8);
-        *(u32x4*)(qs + tile_off<D>(m, ch)) = v;
+        bf16x8 v = zero8();
+        if (m < M) v = scaled_op(*(const bf16x8*)(Qb + (int64_t)m * D + ch * 8), c);
+        *(bf16x8*)(qs + tile_off<D>(m, ch)) = v;
     }
     for (int e = tid; e < Mp * D; e += 64 * NW) {
         const int m = e / D, d = e % D;
@@ -728,8 +784,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     __syncthreads();
     // Offsets. With the encode's merged offsets mu*[m] (log2 units), every
     // logit of this (b, h) satisfies c*S <= max_m mu*[m] + 32, one offset for
-    // all tokens. Without them, per token: c * max_m |Q[m]| * |K[tok]|
-    // (Cauchy-Schwarz); here only max_m |Q[m]|^2 is prepared.
+    // all tokens. Without them, per token: max_m |cQ[m]| * |K[tok]|
+    // (Cauchy-Schwarz, on the scaled operand the MFMA uses); here only
+    // max_m |cQ[m]|^2 is prepared.
     const bool goff = a.zmu != nullptr;
     float red_in = goff ? -INFINITY : 0.0f;
     if (goff) {
@@ -755,7 +812,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     float rmax = red[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) rmax = fmaxf(rmax, red[w]);
-    const float cq = goff ? 0.0f : c * sqrtf(rmax);
+    const float cq = goff ? 0.0f : sqrtf(rmax);
     const float gnu = goff ? rmax + kSumLimitLog2 : 0.0f;
 
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -810,14 +867,19 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
         f32x16 yac[TB][DB];
         float tau[TB];
         auto run = [&](const float (&off)[TB]) {
+            // -offset as the logit MFMA's accumulator input: the matrix core
+            // yields c*S - nu, the exponent itself
+            f32x16 noff[TB];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) noff[tb] = splat16(-off[tb]);
             bf16x8 qa[KB];
             qread(0, qa);
             f32x16 Snext[TB];
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
-                Snext[tb] = zero16;
+                Snext[tb] = mfma(qa[0], kop[tb][0], noff[tb]);
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) Snext[tb] = mfma(qa[kb], kop[tb][kb], Snext[tb]);
+                for (int kb = 1; kb < KB; ++kb) Snext[tb] = mfma(qa[kb], kop[tb][kb], Snext[tb]);
                 tau[tb] = 0.0f;
             }
             // one latent block; the next block's logits go to the matrix core
@@ -830,23 +892,22 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
                     qread(mb + 1, qa);
 #pragma unroll
                     for (int tb = 0; tb < TB; ++tb) {
-                        Snext[tb] = zero16;
+                        Snext[tb] = mfma(qa[0], kop[tb][0], noff[tb]);
 #pragma unroll
-                        for (int kb = 0; kb < KB; ++kb) Snext[tb] = mfma(qa[kb], kop[tb][kb], Snext[tb]);
+                        for (int kb = 1; kb < KB; ++kb) Snext[tb] = mfma(qa[kb], kop[tb][kb], Snext[tb]);
                     }
                 }
                 bf16x8 pb[TB][2];
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
                     if (masked) mask_tail(mb, S[tb]);
-                    const float nm = -off[tb];
                     float t = tau[tb];
 #pragma unroll
                     for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const float e0 = exp2_fast(fmaf(S[tb][8 * kp + 2 * j], c, nm));
-                            const float e1 = exp2_fast(fmaf(S[tb][8 * kp + 2 * j + 1], c, nm));
+                            const float e0 = exp2_fast(S[tb][8 * kp + 2 * j]);
+                            const float e1 = exp2_fast(S[tb][8 * kp + 2 * j + 1]);
                             const bf16x2 p2 = {(__bf16)e0, (__bf16)e1};
                             t = __builtin_amdgcn_fdot2_f32_bf16(p2, one, t, false);
                             pb[tb][kp][2 * j] = p2[0];
@@ -909,7 +970,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
             }
             float ex[TB];
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) ex[tb] = pair_max(mx[tb]) * c;
+            for (int tb = 0; tb < TB; ++tb) ex[tb] = pair_max(mx[tb]);
             run(ex);
         }
         // normalise, round, store
@@ -1013,7 +1074,10 @@ hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
 
 template <int D, typename ZT>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t s) {
-    return dec_tb_bf16(D) == 2 ? launch_dec_tb<D, 2, ZT>(a, s) : launch_dec_tb<D, 1, ZT>(a, s);
+    if constexpr (D <= 64) {
+        if (dec_tb_bf16(D) == 2) return launch_dec_tb<D, 2, ZT>(a, s);
+    }
+    return launch_dec_tb<D, 1, ZT>(a, s);
 }
 
 }  // namespace
@@ -1041,13 +1105,14 @@ int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32) {
     const int tb = dec_tb_bf16(D);
     const int lds = dec_lds_bytes_bf16(Mp, D);
     const void* fn = nullptr;
-#define FLARE_DEC_FN(DD)                                                                             \
-    if (D == DD)                                                                                     \
-        fn = tb == 2 ? (z_f32 ? (const void*)decode_bf16<DD, 2, float> : (const void*)decode_bf16<DD, 2, uint16_t>) \
-                     : (z_f32 ? (const void*)decode_bf16<DD, 1, float> : (const void*)decode_bf16<DD, 1, uint16_t>);
-    FLARE_DEC_FN(32)
-    FLARE_DEC_FN(64)
-    FLARE_DEC_FN(128)
+#define FLARE_DEC_FN(DD, TB)                                                                          \
+    if (D == DD && tb == TB)                                                                          \
+        fn = z_f32 ? (const void*)decode_bf16<DD, TB, float> : (const void*)decode_bf16<DD, TB, uint16_t>;
+    FLARE_DEC_FN(32, 1)
+    FLARE_DEC_FN(32, 2)
+    FLARE_DEC_FN(64, 1)
+    FLARE_DEC_FN(64, 2)
+    FLARE_DEC_FN(128, 1)
 #undef FLARE_DEC_FN
     if (!fn) return 1;
     if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
@@ -1058,10 +1123,11 @@ int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32) {
 }
 
 int dec_tb_bf16(int D) {
-    // Tuning override (tests and sweeps): 32-token blocks per wave and step.
+    // Tuning override (tests and sweeps): 32-token blocks per wave and step
+    // (2 is built for D <= 64 only).
     if (const char* e = std::getenv("FLARE_TEST_DEC_TB")) {
         const int v = std::atoi(e);
-        if (v == 1 || v == 2) return v;
+        if (v == 1 || (v == 2 && D <= 64)) return v;
     }
     return D <= 32 ? 2 : 1;
 }
