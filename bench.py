@@ -6,7 +6,9 @@ or the five-launch FLARE++ sequence, through the C ABI's caller-workspace
 entry point. Default workload: the PDE-mesh shape B=4, H=8, N=65536, M=128,
 D=32 in bf16 (the throughput metric is quoted on N=65536, M=128).
 
-Prints one JSON line with throughput (tokens*heads/s), the roofline position
+Before the warmup steps the step runs back to back for --ramp-seconds (untimed)
+so that the GPU reaches its steady clocks; the timed region is always exactly
+--steps full steps. Prints one JSON line with throughput (tokens*heads/s), the roofline position
 of the dominant kernel (its average duration measured with HIP events on the
 launch stream during the timed steps), and the fp64 CPU oracle's throughput
 on a bounded sample of the same workload as a baseline.
@@ -51,8 +53,8 @@ def source_hash(kind: str) -> str:
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", type=int, default=2, help="workload number 1-5 (default 2)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -61,6 +63,9 @@ def parse():
                    help="skip the second pass that times every kernel with HIP events")
     p.add_argument("--calib-copy-mib", type=int, default=512,
                    help="size of the plain copy kernel run once before the timed steps (counter calibration)")
+    p.add_argument("--ramp-seconds", type=float, default=1.0,
+                   help="run the step back to back for this long before the warmup steps, so that the GPU "
+                        "reaches its steady clocks (a cold MI355X needs ~0.1-0.2 s); 0 disables")
     return p.parse_args()
 
 
@@ -107,6 +112,16 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # Clock ramp: the step back to back for a fixed wall time (untimed), then
+    # the W warmup steps, then the timed region.
+    ramp_steps = 0
+    if args.ramp_seconds > 0:
+        t_end = time.perf_counter() + args.ramp_seconds
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                fn(Q, K, V, out=Y, workspace=ws)
+            ramp_steps += 20
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         fn(Q, K, V, out=Y, workspace=ws)
     torch.cuda.synchronize()
@@ -209,7 +224,8 @@ def main():
     line = {
         "metric": "FLARE fwd tokens*heads/s (N=65536, M=128) + roofline fraction",
         "value": round(value, 1), "unit": "tokens*heads/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ramp": {"seconds": args.ramp_seconds, "steps": ramp_steps},
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (" + recipe() + ")",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "op": w.op,
                    "plan": F.flare_describe_plan(op, w.B, w.H, w.N, w.M, w.D, Q.dtype)},

@@ -107,10 +107,10 @@ __device__ __forceinline__ bf16x8 scaled_op(bf16x8 q, float c) {
     return r;
 }
 
-// Probabilities of one 32-token sub-block for one 32-latent block from its
-// shifted logits X = c*S - mu: p = 2^X rounded to bf16, packed as the two
-// k-halves of the P.V B operand, and the sum of the rounded values.
-__device__ __forceinline__ void enc_probs(const f32x16& X, bf16x8& p0, bf16x8& p1, float& tsum) {
+// Probabilities of one lane's 16 entries of a 32x32 block from their shifted
+// logits X (c*S - offset): p = 2^X rounded to bf16, packed as the two k-halves
+// (p0, p1) of an MFMA B operand. Returns the sum of the rounded values.
+__device__ __forceinline__ float exp2_pack_sum(const f32x16& X, bf16x8& p0, bf16x8& p1) {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     float t = 0.0f;
     bf16x8 pp[2];
@@ -128,7 +128,11 @@ __device__ __forceinline__ void enc_probs(const f32x16& X, bf16x8& p0, bf16x8& p
     }
     p0 = pp[0];
     p1 = pp[1];
-    tsum = t;
+    return t;
+}
+
+__device__ __forceinline__ void enc_probs(const f32x16& X, bf16x8& p0, bf16x8& p1, float& tsum) {
+    tsum = exp2_pack_sum(X, p0, p1);
 }
 
 // ---------------------------------------------------------------------------
@@ -208,19 +212,23 @@ struct EncShape {
     static constexpr int T = 64;
     static constexpr int SB = T / (32 * WT);
     static constexpr int SBYTES = 2 * T * RB;  // K tile then V tile
-    static constexpr int NS = (65536 / SBYTES) < 3 ? 3 : ((65536 / SBYTES) > 8 ? 8 : (65536 / SBYTES));
-    static constexpr int IPW = T * CH / (64 * NW);  // transfers per wave per tensor per tile
+    // ring depth: 4 stages of 8 KB tiles (D = 32; measured best on MI355X),
+    // otherwise as many stages as fit in 64 KB, at least 3
+    static constexpr int NS = SBYTES <= 8192 ? 4 : ((65536 / SBYTES) < 3 ? 3 : ((65536 / SBYTES) > 8 ? 8 : (65536 / SBYTES)));
+    static constexpr int PIECES = T * CH / 64;     // 1 KB transfers per tensor per tile
+    static constexpr int IPW = PIECES >= NW ? PIECES / NW : 1;  // per issuing wave
+    static constexpr int NWI = PIECES / IPW;       // issuing waves: the first NWI
     static constexpr int MERGE_BYTES = (WT - 1) * WM * MBW * (16 * DB + 2) * 64 * 4;
     static constexpr int SMEM = NS * SBYTES > MERGE_BYTES ? NS * SBYTES : MERGE_BYTES;
     static_assert(SB >= 1 && SB * 32 * WT == T, "tile split");
-    static_assert(IPW >= 1 && IPW * 64 * NW == T * CH, "tile transfer split");
+    static_assert(IPW * NWI == PIECES && NWI <= NW, "tile transfer split");
 };
 
 template <int D, int MBW, int WM, int WT>
 __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a) {
     using Sh = EncShape<D, MBW, WM, WT>;
     constexpr int KB = Sh::KB, DB = Sh::DB, CH = Sh::CH, RB = Sh::RB, NW = Sh::NW, T = Sh::T, SB = Sh::SB;
-    constexpr int NS = Sh::NS, IPW = Sh::IPW, SBYTES = Sh::SBYTES;
+    constexpr int NS = Sh::NS, IPW = Sh::IPW, NWI = Sh::NWI, SBYTES = Sh::SBYTES;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Sh::SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -263,23 +271,26 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             for (int r = 0; r < 16; ++r) acc[mb][db][r] = 0.0f;
     }
 
-    // Tile j of the chunk -> LDS stage `stage`. Transfer (i, wave) fills LDS
-    // bytes [(i*NW + wave)*1024, +1024) of each tensor's tile, 16 per lane;
-    // the lane fetches the global chunk that the swizzle places there. Rows
-    // past the chunk end fetch the last valid token (finite data; their
-    // logits are masked).
+    // Tile j of the chunk -> LDS stage `stage`. The first NWI waves move the
+    // tile, IPW transfers per tensor each: transfer (i, wave) fills LDS bytes
+    // [(i*NWI + wave)*1024, +1024) of each tensor's tile, 16 per lane; the
+    // lane fetches the global chunk that the swizzle places there. Rows past
+    // the chunk end fetch the last valid token (finite data; their logits are
+    // masked). Waves that move nothing have no transfers to wait for.
     auto issue = [&](int tile, int stage) {
+        if (wave >= NWI) return;
         const int t0 = n0 + tile * T;
         unsigned char* st = smem + stage * SBYTES;
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int p = (i * NW + wave) * 64 + lane;
+            const int pc = i * NWI + wave;
+            const int p = pc * 64 + lane;
             const int row = p / CH, pos = p % CH;
             const int ch = pos ^ ((tile_off<D>(row, 0) - row * RB) >> 4);
             const int n = min(t0 + row, n1 - 1);
             const int64_t g = (int64_t)n * D + ch * 8;
-            dma16(Kb + g, st + (i * NW + wave) * 1024);
-            dma16(Vb + g, st + T * RB + (i * NW + wave) * 1024);
+            dma16(Kb + g, st + pc * 1024);
+            dma16(Vb + g, st + T * RB + pc * 1024);
         }
     };
 
@@ -901,19 +912,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
                     if (masked) mask_tail(mb, S[tb]);
-                    float t = tau[tb];
-#pragma unroll
-                    for (int kp = 0; kp < 2; ++kp)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float e0 = exp2_fast(S[tb][8 * kp + 2 * j]);
-                            const float e1 = exp2_fast(S[tb][8 * kp + 2 * j + 1]);
-                            const bf16x2 p2 = {(__bf16)e0, (__bf16)e1};
-                            t = __builtin_amdgcn_fdot2_f32_bf16(p2, one, t, false);
-                            pb[tb][kp][2 * j] = p2[0];
-                            pb[tb][kp][2 * j + 1] = p2[1];
-                        }
-                    tau[tb] = t;
+                    tau[tb] += exp2_pack_sum(S[tb], pb[tb][0], pb[tb][1]);
                 }
 #pragma unroll
                 for (int kp = 0; kp < 2; ++kp)
@@ -1047,9 +1046,11 @@ hipError_t launch_enc_d(const EncodeArgs& a, hipStream_t s) {
     FLARE_ENC_CASE(1, 1, 2)
     FLARE_ENC_CASE(1, 2, 2)
     FLARE_ENC_CASE(1, 4, 1)
+    FLARE_ENC_CASE(1, 4, 2)
     if constexpr (D == 128) {
         FLARE_ENC_CASE(1, 8, 1)
     } else {
+        FLARE_ENC_CASE(1, 8, 2)
         FLARE_ENC_CASE(2, 4, 1)
         FLARE_ENC_CASE(2, 2, 1)
         FLARE_ENC_CASE(2, 2, 2)
@@ -1129,7 +1130,9 @@ int dec_tb_bf16(int D) {
         const int v = std::atoi(e);
         if (v == 1 || (v == 2 && D <= 64)) return v;
     }
-    return D <= 32 ? 2 : 1;
+    // one block: fewer registers, more resident waves (measured faster on
+    // MI355X than two at D = 32, equal or faster at D = 64)
+    return 1;
 }
 
 int dec_lds_bytes_bf16(int Mp, int D) { return Mp * 2 * D + D * (2 * Mp + 16) + 64; }

@@ -227,3 +227,19 @@ def test_pp_forward_is_forward_with_corrected_queries():
     torch.cuda.synchronize()
     e = errors(Y.double().cpu().numpy(), Y2.double().cpu().numpy())
     assert e["rel_l2"] <= 1e-2 and e["max_abs"] <= 3e-2, e
+
+
+@pytest.mark.parametrize("D", [32, 64])
+def test_two_token_block_decode_matches_oracle(D, monkeypatch):
+    # The decode built for two 32-token blocks per wave and step (a tuning
+    # alternative to the default one) against the oracle, forward and
+    # standalone decode, with ragged tokens and latents.
+    monkeypatch.setenv("FLARE_TEST_DEC_TB", "2")
+    Q, K, V = make_inputs(1, 2, 3001, 100, D, "bf16", 0.5, seed=30 + D)
+    Zb = f32_to_bf16_bits(oracle.encode(Q, K, V).astype(np.float32))
+    print(f"[tb2] D={D}", flush=True)
+    Y = F.flare_forward(to_dev(Q), to_dev(K), to_dev(V))
+    Y2 = F.flare_decode(to_dev(Q), to_dev(K), to_dev(Zb))
+    torch.cuda.synchronize()
+    assert_parity(to_host64(Y), oracle.forward(Q, K, V)[0], "bf16", f"forward D={D}")
+    assert_parity(to_host64(Y2), oracle.decode(Q, K, Zb), "bf16", f"decode D={D}")
