@@ -170,9 +170,11 @@ __device__ __forceinline__ void raw_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// 16 bytes from global memory into LDS at lds_wave_base + 16 * lane.
+// 16 bytes from global memory into LDS at lds_wave_base + 16 * lane. NT: the
+// non-temporal cache policy (K and V are read once per pass).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* g, unsigned char* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((const void*)g, (void*)lds_wave_base, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)g, (void*)lds_wave_base, 16, 0, NT ? 2 : 0);
 }
 
 // Transposed LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane i
@@ -289,8 +291,11 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             const int ch = pos ^ ((tile_off<D>(row, 0) - row * RB) >> 4);
             const int n = min(t0 + row, n1 - 1);
             const int64_t g = (int64_t)n * D + ch * 8;
-            dma16(Kb + g, st + pc * 1024);
-            dma16(Vb + g, st + T * RB + pc * 1024);
+            // non-temporal loads measured faster on MI355X for the D = 64
+            // shapes with two latent blocks per wave, slower for the others
+            constexpr bool NT = D >= 64 && MBW >= 2;
+            dma16<NT>(Kb + g, st + pc * 1024);
+            dma16<NT>(Vb + g, st + T * RB + pc * 1024);
         }
     };
 
