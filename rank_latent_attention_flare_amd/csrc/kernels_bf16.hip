@@ -999,19 +999,40 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
         }
     };
 
-    // Blocks blk, blk + stride, ... of this wave; two K register sets in
-    // turn so that the next block's rows are always in flight.
+    // Blocks blk, blk + stride, ... of this wave. K register sets in turn so
+    // that the rows of the next block (D = 32) or the next two blocks (D >= 64,
+    // measured faster there; at D = 32 the extra registers cost more) are
+    // always in flight.
     int blk = blockIdx.x * NW + wave;
-    bf16x8 kA[TB][KB], kB[TB][KB];
-    kload(blk, kA);
-    while (blk < nblk) {
+    if constexpr (D >= 64) {
+        bf16x8 kA[TB][KB], kB[TB][KB], kC[TB][KB];
+        kload(blk, kA);
         kload(blk + stride, kB);
-        process(blk, kA);
-        blk += stride;
-        if (blk >= nblk) break;
-        kload(blk + stride, kA);
-        process(blk, kB);
-        blk += stride;
+        while (blk < nblk) {
+            kload(blk + 2 * stride, kC);
+            process(blk, kA);
+            blk += stride;
+            if (blk >= nblk) break;
+            kload(blk + 2 * stride, kA);
+            process(blk, kB);
+            blk += stride;
+            if (blk >= nblk) break;
+            kload(blk + 2 * stride, kB);
+            process(blk, kC);
+            blk += stride;
+        }
+    } else {
+        bf16x8 kA[TB][KB], kB[TB][KB];
+        kload(blk, kA);
+        while (blk < nblk) {
+            kload(blk + stride, kB);
+            process(blk, kA);
+            blk += stride;
+            if (blk >= nblk) break;
+            kload(blk + stride, kA);
+            process(blk, kB);
+            blk += stride;
+        }
     }
 }
 

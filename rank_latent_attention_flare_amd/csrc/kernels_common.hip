@@ -24,21 +24,27 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Combine (FLARE++ residual included). One thread per (b, h, m, d):
+// Combine (FLARE++ residual included). One thread per (b, h, m) and four
+// consecutive columns d (D is a multiple of 8):
 //   mu* = max_c mu_c,  w_c = 2^(mu_c - mu*),
 //   Z = sum_c w_c acc_c / sum_c w_c sig_c
-// which is exactly the softmax over all N tokens (log-sum-exp merge).
+// which is exactly the softmax over all N tokens (log-sum-exp merge), summed
+// in chunk order (deterministic).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+typedef float f32x4c __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int bh = blockIdx.y;
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= a.M * a.D) return;
-    const int m = idx / a.D, d = idx - m * a.D;
-    const int C = a.C, Mp = a.Mp, D = a.D;
+    const int D = a.D, D4 = D / 4;
+    const int idx = blockIdx.x * 256 + threadIdx.x;  // (m, d/4)
+    if (idx >= a.M * D4) return;
+    const int m = idx / D4, d = 4 * (idx - m * D4);
+    const int C = a.C, Mp = a.Mp;
     const int64_t row0 = (int64_t)bh * C * Mp + m;  // partial row of chunk 0; chunk c adds c*Mp
     const float* __restrict__ mu = a.in.mu + row0;
     const float* __restrict__ sg = a.in.sig + row0;
@@ -54,42 +60,50 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
         for (int j = 0; j < G; ++j) mx = fmaxf(mx, mv[j]);
     }
-    float num = 0.0f, den = 0.0f;
+    f32x4c num = {0.0f, 0.0f, 0.0f, 0.0f};
+    float den = 0.0f;
     for (int c0 = 0; c0 < C; c0 += G) {
-        float mv[G], av[G], sv[G];
+        float mv[G], sv[G];
+        f32x4c av[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const bool in = c0 + j < C;
             mv[j] = in ? mu[(int64_t)(c0 + j) * Mp] : -INFINITY;
-            av[j] = in ? ac[(int64_t)(c0 + j) * sacc] : 0.0f;
+            av[j] = in ? *(const f32x4c*)(ac + (int64_t)(c0 + j) * sacc) : f32x4c{0.0f, 0.0f, 0.0f, 0.0f};
             sv[j] = in ? sg[(int64_t)(c0 + j) * Mp] : 0.0f;
         }
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const float w = (mv[j] == -INFINITY) ? 0.0f : exp2f(mv[j] - mx);
-            num = fmaf(w, av[j], num);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) num[e] = fmaf(w, av[j][e], num[e]);
             den = fmaf(w, sv[j], den);
         }
     }
-    const float z = num / den;
-    const int64_t o = (int64_t)bh * a.M * D + idx;
+    f32x4c z;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = num[e] / den;
+    const int64_t o = (int64_t)bh * a.M * D + (int64_t)m * D + d;
     if (a.zmu && d == 0) a.zmu[(int64_t)bh * a.M + m] = mx;
-    if (a.mode == COMBINE_Z_F32) {
-        ((float*)a.out)[o] = z;
+    if (a.mode == COMBINE_Z_F32 || (a.mode == COMBINE_Z_DTYPE && !a.bf16)) {
+        *(f32x4c*)((float*)a.out + o) = z;
     } else if (a.mode == COMBINE_Z_DTYPE) {
-        if (a.bf16)
-            ((uint16_t*)a.out)[o] = f32_to_bf16_rne(z);
-        else
-            ((float*)a.out)[o] = z;
+        u16x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = f32_to_bf16_rne(z[e]);
+        *(u16x4*)((uint16_t*)a.out + o) = r;
     } else {
         const int h = bh % a.H;
-        const int64_t qi = (int64_t)h * a.M * D + idx;
+        const int64_t qi = (int64_t)h * a.M * D + (int64_t)m * D + d;
         if (a.bf16) {
-            const uint16_t qb = ((const uint16_t*)a.Q)[qi];
-            const float q = __uint_as_float((uint32_t)qb << 16);
-            ((uint16_t*)a.out)[o] = f32_to_bf16_rne(q + z);
+            const u16x4 qb = *(const u16x4*)((const uint16_t*)a.Q + qi);
+            u16x4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = f32_to_bf16_rne(__uint_as_float((uint32_t)qb[e] << 16) + z[e]);
+            *(u16x4*)((uint16_t*)a.out + o) = r;
         } else {
-            ((float*)a.out)[o] = ((const float*)a.Q)[qi] + z;
+            const f32x4c q = *(const f32x4c*)((const float*)a.Q + qi);
+            *(f32x4c*)((float*)a.out + o) = q + z;
         }
     }
 }
@@ -246,7 +260,8 @@ hipError_t launch_encode_f32(const EncodeArgs& a, hipStream_t s) { FLARE_F32_DIS
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { FLARE_F32_DISPATCH(dec_f32, a, s) }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-    dim3 grid((a.M * a.D + 255) / 256, a.BH), block(256);
+    if (a.D % 4 != 0) return hipErrorInvalidValue;
+    dim3 grid((a.M * (a.D / 4) + 255) / 256, a.BH), block(256);
     hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, a);
     return hipGetLastError();
 }
