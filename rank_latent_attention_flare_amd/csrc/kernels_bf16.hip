@@ -64,6 +64,7 @@ __device__ __forceinline__ float pair_max(float x) {
 }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
+__device__ __forceinline__ bool wave_all(bool p) { return __ballot(!p) == 0; }
 
 // Byte offset of 16-byte chunk `ch` of row `row` in an LDS tile of bf16 rows
 // of width D. Chunks are XOR-swizzled per row so that the row-strided reads
@@ -89,28 +90,12 @@ __device__ __forceinline__ bf16x8 zero8() {
     return __builtin_bit_cast(bf16x8, z);
 }
 
-__device__ __forceinline__ f32x16 splat16(float v) {
-    f32x16 r;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = v;
-    return r;
-}
-
-// Query operand with the logit scale folded in: bf16(c * q), rounded to
-// nearest even from the exact fp32 product. The MFMA then yields c*S
-// directly; with the latent's (or token's) offset as its accumulator input it
-// yields the shifted logits c*S - offset that the exponentials take.
-__device__ __forceinline__ bf16x8 scaled_op(bf16x8 q, float c) {
-    bf16x8 r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = (__bf16)((float)q[j] * c);
-    return r;
-}
-
-// Probabilities of one lane's 16 entries of a 32x32 block from their shifted
-// logits X (c*S - offset): p = 2^X rounded to bf16, packed as the two k-halves
-// (p0, p1) of an MFMA B operand. Returns the sum of the rounded values.
-__device__ __forceinline__ float exp2_pack_sum(const f32x16& X, bf16x8& p0, bf16x8& p1) {
+// Probabilities of one lane's 16 entries of a 32x32 block of logits S:
+// p = 2^(c*S - off) (the scale applied in fp32, one fma per entry), rounded to
+// bf16 and packed as the two k-halves (p0, p1) of an MFMA B operand. Returns
+// the sum of the rounded values.
+__device__ __forceinline__ float exp2_pack_sum(const f32x16& S, float c, float off, bf16x8& p0, bf16x8& p1) {
+    const float nm = -off;
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     float t = 0.0f;
     bf16x8 pp[2];
@@ -118,8 +103,8 @@ __device__ __forceinline__ float exp2_pack_sum(const f32x16& X, bf16x8& p0, bf16
     for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float e0 = exp2_fast(X[8 * kp + 2 * j]);
-            const float e1 = exp2_fast(X[8 * kp + 2 * j + 1]);
+            const float e0 = exp2_fast(fmaf(S[8 * kp + 2 * j], c, nm));
+            const float e1 = exp2_fast(fmaf(S[8 * kp + 2 * j + 1], c, nm));
             const bf16x2 p2 = {(__bf16)e0, (__bf16)e1};
             t = __builtin_amdgcn_fdot2_f32_bf16(p2, one, t, false);
             pp[kp][2 * j] = p2[0];
@@ -131,8 +116,8 @@ __device__ __forceinline__ float exp2_pack_sum(const f32x16& X, bf16x8& p0, bf16
     return t;
 }
 
-__device__ __forceinline__ void enc_probs(const f32x16& X, bf16x8& p0, bf16x8& p1, float& tsum) {
-    tsum = exp2_pack_sum(X, p0, p1);
+__device__ __forceinline__ void enc_probs(const f32x16& S, float c, float mu, bf16x8& p0, bf16x8& p1, float& tsum) {
+    tsum = exp2_pack_sum(S, c, mu, p0, p1);
 }
 
 // ---------------------------------------------------------------------------
@@ -254,18 +239,16 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
         const int m = 32 * (wm * MBW + mb) + l32;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-            qop[mb][kb] = (m < M) ? scaled_op(*(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi), c) : zero8();
+            qop[mb][kb] = (m < M) ? *(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi) : zero8();
     }
 
     // Per latent: offset mu (log2 units; -inf until the first re-centring),
-    // its negation as an MFMA accumulator input, sum of p and accumulator.
+    // sum of p and accumulator.
     float mu[MBW], ps[MBW];
-    f32x16 nmu[MBW];
     f32x16 acc[MBW][DB];
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
         mu[mb] = -INFINITY;
-        nmu[mb] = splat16(INFINITY);
         ps[mb] = 0.0f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -327,11 +310,11 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
                     if (tok >= nv) X[i] = -INFINITY;
                 }
             };
-            // shifted logits c*S - mu straight from the matrix core
+            // logits S (bf16 products, fp32 accumulation)
             f32x16 S[MBW];
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
-                S[mb] = mfma(ka[0], qop[mb][0], nmu[mb]);
+                S[mb] = mfma(ka[0], qop[mb][0], f32x16{});
 #pragma unroll
                 for (int kb = 1; kb < KB; ++kb) S[mb] = mfma(ka[kb], qop[mb][kb], S[mb]);
                 if (tail) mask(S[mb]);
@@ -341,32 +324,24 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             bool bad = false;
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
-                enc_probs(S[mb], pb[mb][0], pb[mb][1], ts[mb]);
+                enc_probs(S[mb], c, mu[mb], pb[mb][0], pb[mb][1], ts[mb]);
                 bad |= !(ts[mb] <= kSumLimit);
             }
             if (wave_any(bad)) {
                 // Re-centre on the exact running maximum (rare: first tile of a
-                // chunk, or a jump of the maximum by more than ~28 in log2):
-                // unshifted logits again, then shift by the new offset.
+                // chunk, or a jump of the maximum by more than ~28 in log2).
 #pragma unroll
                 for (int mb = 0; mb < MBW; ++mb) {
-                    f32x16 R = mfma(ka[0], qop[mb][0], splat16(0.0f));
-#pragma unroll
-                    for (int kb = 1; kb < KB; ++kb) R = mfma(ka[kb], qop[mb][kb], R);
-                    if (tail) mask(R);
                     float mx = -INFINITY;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, R[i]);
-                    const float mnew = fmaxf(mu[mb], pair_max(mx));
+                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[mb][i]);
+                    const float mnew = fmaxf(mu[mb], pair_max(mx) * c);
                     const float alpha = (mu[mb] == -INFINITY) ? 0.0f : exp2_fast(mu[mb] - mnew);
                     ps[mb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) acc[mb][db] *= alpha;
                     mu[mb] = mnew;
-                    nmu[mb] = splat16(-mnew);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) S[mb][i] = R[i] - mnew;
-                    enc_probs(S[mb], pb[mb][0], pb[mb][1], ts[mb]);
+                    enc_probs(S[mb], c, mu[mb], pb[mb][0], pb[mb][1], ts[mb]);
                 }
             }
 #pragma unroll
@@ -534,15 +509,13 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
         const int m = 32 * mb + l32;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-            qop[mb][kb] = (m < M) ? scaled_op(*(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi), c) : zero8();
+            qop[mb][kb] = (m < M) ? *(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi) : zero8();
     }
     float mu[MBW], ps[MBW];
-    f32x16 nmu[MBW];  // -mu as the logit MFMA's accumulator input
     f32x16 acc[MBW][DB];
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
         mu[mb] = -INFINITY;
-        nmu[mb] = splat16(INFINITY);
         ps[mb] = 0.0f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -613,10 +586,10 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
         }
         // latent blocks in turn; block mb+1's logits are in flight on the
         // matrix core while block mb's softmax runs on the VALU
-        // logits of latent block mb against this sub-block, shifted by the
-        // accumulator input C0 (-mu: shifted logits; 0: c*S itself)
-        auto logits = [&](int mb, const f32x16& C0) {
-            f32x16 S = mfma(ka[0], qop[mb][0], C0);
+        // logits of latent block mb against this sub-block (masked on the
+        // ragged tail)
+        auto logits = [&](int mb) {
+            f32x16 S = mfma(ka[0], qop[mb][0], f32x16{});
 #pragma unroll
             for (int kb = 1; kb < KB; ++kb) S = mfma(ka[kb], qop[mb][kb], S);
             if (tail) {
@@ -628,30 +601,26 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
             }
             return S;
         };
-        f32x16 Snext = logits(0, nmu[0]);
+        f32x16 Snext = logits(0);
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) {
             f32x16 S = Snext;
-            if (mb + 1 < MBW) Snext = logits(mb + 1, nmu[mb + 1]);
+            if (mb + 1 < MBW) Snext = logits(mb + 1);
             bf16x8 p0, p1;
             float ts;
-            enc_probs(S, p0, p1, ts);
+            enc_probs(S, c, mu[mb], p0, p1, ts);
             if (wave_any(!(ts <= kSumLimit))) {
                 // re-centre this latent block on its exact running maximum
-                const f32x16 R = logits(mb, splat16(0.0f));
                 float mx = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, R[i]);
-                const float mnew = fmaxf(mu[mb], pair_max(mx));
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+                const float mnew = fmaxf(mu[mb], pair_max(mx) * c);
                 const float alpha = (mu[mb] == -INFINITY) ? 0.0f : exp2_fast(mu[mb] - mnew);
                 ps[mb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) acc[mb][db] *= alpha;
                 mu[mb] = mnew;
-                nmu[mb] = splat16(-mnew);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) S[i] = R[i] - mnew;
-                enc_probs(S, p0, p1, ts);
+                enc_probs(S, c, mu[mb], p0, p1, ts);
             }
             ps[mb] += ts;
 #pragma unroll
@@ -779,12 +748,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
     uint16_t* __restrict__ Yb = (uint16_t*)a.Y + (int64_t)bh * N * D;
 
-    // ---- stage c*Q (bf16, swizzled rows) and Z^T (bf16, permuted latents)
+    // ---- stage Q (bf16, swizzled rows) and Z^T (bf16, permuted latents)
     for (int p = tid; p < Mp * CH; p += 64 * NW) {
         const int m = p / CH, ch = p % CH;
-        bf16x8 v = zero8();
-        if (m < M) v = scaled_op(*(const bf16x8*)(Qb + (int64_t)m * D + ch * 8), c);
-        *(bf16x8*)(qs + tile_off<D>(m, ch)) = v;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (m < M) v = *(const u32x4*)(Qb + (int64_t)m * D + ch * 8);
+        *(u32x4*)(qs + tile_off<D>(m, ch)) = v;
     }
     for (int e = tid; e < Mp * D; e += 64 * NW) {
         const int m = e / D, d = e % D;
@@ -800,9 +769,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     __syncthreads();
     // Offsets. With the encode's merged offsets mu*[m] (log2 units), every
     // logit of this (b, h) satisfies c*S <= max_m mu*[m] + 32, one offset for
-    // all tokens. Without them, per token: max_m |cQ[m]| * |K[tok]|
-    // (Cauchy-Schwarz, on the scaled operand the MFMA uses); here only
-    // max_m |cQ[m]|^2 is prepared.
+    // all tokens. Without them, per token: c * max_m |Q[m]| * |K[tok]|
+    // (Cauchy-Schwarz); here only max_m |Q[m]|^2 is prepared.
     const bool goff = a.zmu != nullptr;
     float red_in = goff ? -INFINITY : 0.0f;
     if (goff) {
@@ -828,7 +796,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     float rmax = red[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) rmax = fmaxf(rmax, red[w]);
-    const float cq = goff ? 0.0f : sqrtf(rmax);
+    const float cq = goff ? 0.0f : c * sqrtf(rmax);
     const float gnu = goff ? rmax + kSumLimitLog2 : 0.0f;
 
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -885,17 +853,18 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
         auto run = [&](const float (&off)[TB]) {
             // -offset as the logit MFMA's accumulator input: the matrix core
             // yields c*S - nu, the exponent itself
-            f32x16 noff[TB];
+            auto logit = [&](const bf16x8 (&qa)[KB], int tb) {
+                f32x16 S = mfma(qa[0], kop[tb][0], f32x16{});
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) noff[tb] = splat16(-off[tb]);
+                for (int kb = 1; kb < KB; ++kb) S = mfma(qa[kb], kop[tb][kb], S);
+                return S;
+            };
             bf16x8 qa[KB];
             qread(0, qa);
             f32x16 Snext[TB];
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
-                Snext[tb] = mfma(qa[0], kop[tb][0], noff[tb]);
-#pragma unroll
-                for (int kb = 1; kb < KB; ++kb) Snext[tb] = mfma(qa[kb], kop[tb][kb], Snext[tb]);
+                Snext[tb] = logit(qa, tb);
                 tau[tb] = 0.0f;
             }
             // one latent block; the next block's logits go to the matrix core
@@ -907,17 +876,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
                 if (mb + 1 < MB) {
                     qread(mb + 1, qa);
 #pragma unroll
-                    for (int tb = 0; tb < TB; ++tb) {
-                        Snext[tb] = mfma(qa[0], kop[tb][0], noff[tb]);
-#pragma unroll
-                        for (int kb = 1; kb < KB; ++kb) Snext[tb] = mfma(qa[kb], kop[tb][kb], Snext[tb]);
-                    }
+                    for (int tb = 0; tb < TB; ++tb) Snext[tb] = logit(qa, tb);
                 }
                 bf16x8 pb[TB][2];
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
                     if (masked) mask_tail(mb, S[tb]);
-                    tau[tb] += exp2_pack_sum(S[tb], pb[tb][0], pb[tb][1]);
+                    tau[tb] += exp2_pack_sum(S[tb], c, off[tb], pb[tb][0], pb[tb][1]);
                 }
 #pragma unroll
                 for (int kp = 0; kp < 2; ++kp)
@@ -974,7 +939,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
             }
             float ex[TB];
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) ex[tb] = pair_max(mx[tb]);
+            for (int tb = 0; tb < TB; ++tb) ex[tb] = pair_max(mx[tb]) * c;
             run(ex);
         }
         // normalise, round, store
