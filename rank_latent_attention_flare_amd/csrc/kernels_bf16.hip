@@ -92,32 +92,38 @@ __device__ __forceinline__ bf16x8 zero8() {
 
 // Probabilities of one lane's 16 entries of a 32x32 block of logits S:
 // p = 2^(c*S - off) (the scale applied in fp32, one fma per entry), rounded to
-// bf16 and packed as the two k-halves (p0, p1) of an MFMA B operand. Returns
-// the sum of the rounded values.
-__device__ __forceinline__ float exp2_pack_sum(const f32x16& S, float c, float off, bf16x8& p0, bf16x8& p1) {
+// bf16 and packed as the two k-halves (p0, p1) of an MFMA B operand.
+__device__ __forceinline__ void exp2_pack(const f32x16& S, float c, float off, bf16x8& p0, bf16x8& p1) {
     const float nm = -off;
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    float t = 0.0f;
     bf16x8 pp[2];
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float e0 = exp2_fast(fmaf(S[8 * kp + 2 * j], c, nm));
-            const float e1 = exp2_fast(fmaf(S[8 * kp + 2 * j + 1], c, nm));
-            const bf16x2 p2 = {(__bf16)e0, (__bf16)e1};
-            t = __builtin_amdgcn_fdot2_f32_bf16(p2, one, t, false);
-            pp[kp][2 * j] = p2[0];
-            pp[kp][2 * j + 1] = p2[1];
-        }
+        for (int j = 0; j < 8; ++j) pp[kp][j] = (__bf16)exp2_fast(fmaf(S[8 * kp + j], c, nm));
     }
     p0 = pp[0];
     p1 = pp[1];
-    return t;
 }
 
-__device__ __forceinline__ void enc_probs(const f32x16& S, float c, float mu, bf16x8& p0, bf16x8& p1, float& tsum) {
-    tsum = exp2_pack_sum(S, c, mu, p0, p1);
+// Column sums of a 32-column B operand pair on the matrix core.
+//
+// Read as the B operand of v_mfma_f32_16x16x32_bf16, the registers of a
+// 32x32x16 B operand (lane l: column l%32, k-half l/32) put column
+// n + 16*((l/16)&1) of the wide product into column n = l%16, k-group l/16, of
+// the narrow one. With A[row][k-group g] = 1 where ((row/4)&1) == (g&1), else
+// 0, output row r of column n sums both k-halves of wide column
+// n + 16*((r/4)&1); the narrow result puts rows 4*(l/16)..+3 in lane l, so
+// every register of lane l holds the sum of wide column l%32. Products with
+// 1 and 0 are exact, so this is the fp32 sum of the bf16 values.
+__device__ __forceinline__ bf16x8 colsum_selector(int lane) {
+    const bool on = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1);
+    const uint32_t w = on ? 0x3f803f80u : 0u;
+    const u32x4 v = {w, w, w, w};
+    return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ f32x4 colsum(const bf16x8& sel, const bf16x8& p0, const bf16x8& p1, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p0, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p1, acc, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -243,9 +249,10 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     }
 
     // Per latent: offset mu (log2 units; -inf until the first re-centring),
-    // sum of p and accumulator.
+    // sum of p (whole sum in both lanes of a latent) and accumulator.
     float mu[MBW], ps[MBW];
     f32x16 acc[MBW][DB];
+    const bf16x8 csel = colsum_selector(lane);
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
         mu[mb] = -INFINITY;
@@ -323,8 +330,10 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             float ts[MBW];
             bool bad = false;
 #pragma unroll
+            for (int mb = 0; mb < MBW; ++mb) exp2_pack(S[mb], c, mu[mb], pb[mb][0], pb[mb][1]);
+#pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
-                enc_probs(S[mb], c, mu[mb], pb[mb][0], pb[mb][1], ts[mb]);
+                ts[mb] = colsum(csel, pb[mb][0], pb[mb][1], f32x4{})[0];
                 bad |= !(ts[mb] <= kSumLimit);
             }
             if (wave_any(bad)) {
@@ -341,7 +350,8 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
 #pragma unroll
                     for (int db = 0; db < DB; ++db) acc[mb][db] *= alpha;
                     mu[mb] = mnew;
-                    enc_probs(S[mb], c, mu[mb], pb[mb][0], pb[mb][1], ts[mb]);
+                    exp2_pack(S[mb], c, mu[mb], pb[mb][0], pb[mb][1]);
+                    ts[mb] = colsum(csel, pb[mb][0], pb[mb][1], f32x4{})[0];
                 }
             }
 #pragma unroll
@@ -438,7 +448,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) {
             const int m = 32 * (wm * MBW + mb) + l32;
-            const float sig = pair_sum(ps[mb]);
+            const float sig = ps[mb];
             if (m < Mp) {
                 if (hi == 0) {
                     a.out.mu[pbase + m] = mu[mb];
@@ -511,8 +521,9 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
         for (int kb = 0; kb < KB; ++kb)
             qop[mb][kb] = (m < M) ? *(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi) : zero8();
     }
-    float mu[MBW], ps[MBW];
+    float mu[MBW], ps[MBW];  // ps: whole sum in both lanes of a latent
     f32x16 acc[MBW][DB];
+    const bf16x8 csel = colsum_selector(lane);
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
         mu[mb] = -INFINITY;
@@ -607,8 +618,8 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
             f32x16 S = Snext;
             if (mb + 1 < MBW) Snext = logits(mb + 1);
             bf16x8 p0, p1;
-            float ts;
-            enc_probs(S, c, mu[mb], p0, p1, ts);
+            exp2_pack(S, c, mu[mb], p0, p1);
+            float ts = colsum(csel, p0, p1, f32x4{})[0];
             if (wave_any(!(ts <= kSumLimit))) {
                 // re-centre this latent block on its exact running maximum
                 float mx = -INFINITY;
@@ -620,7 +631,8 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
 #pragma unroll
                 for (int db = 0; db < DB; ++db) acc[mb][db] *= alpha;
                 mu[mb] = mnew;
-                enc_probs(S, c, mu[mb], p0, p1, ts);
+                exp2_pack(S, c, mu[mb], p0, p1);
+                ts = colsum(csel, p0, p1, f32x4{})[0];
             }
             ps[mb] += ts;
 #pragma unroll
@@ -687,8 +699,7 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
             const float mw = src[(MBW * DB * 16 + 2 * mb) * RL + l];
             const float aw = (mw == -INFINITY) ? 0.0f : exp2_fast(mw - mx);
             num = fmaf(aw, src[((mb * DB + db) * 16 + r) * RL + ln], num);
-            den = fmaf(aw, src[(MBW * DB * 16 + 2 * mb + 1) * RL + l] + src[(MBW * DB * 16 + 2 * mb + 1) * RL + l + 32],
-                       den);
+            den = fmaf(aw, src[(MBW * DB * 16 + 2 * mb + 1) * RL + l], den);
         }
         a.out.acc[(pbase + m) * D + d] = num;
         if (d == 0) {
@@ -728,7 +739,7 @@ __device__ __forceinline__ int dec_zpos(int m) {
     return (m & ~15) + (((r >> 2) & 1) << 3) + ((r >> 3) << 2) + (r & 3);
 }
 
-template <int D, int TB, typename ZT>
+template <int D, int TB, typename ZT, int MBU>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     constexpr int KB = D / 16, DB = D / 32, CH = D / 8, NW = kDecWaves;
     const int Mp = a.Mp, MB = Mp / 32;
@@ -799,7 +810,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     const float cq = goff ? 0.0f : c * sqrtf(rmax);
     const float gnu = goff ? rmax + kSumLimitLog2 : 0.0f;
 
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    const bf16x8 csel = colsum_selector(lane);
     const f32x16 zero16 = {};
     const int nblk = (N + 32 * TB - 1) / (32 * TB);
     const int stride = gridDim.x * NW;
@@ -820,11 +831,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     // softmax numerator and denominator of one 32-token block against the
     // latents of block mb, with per-token offsets off[]
     auto mask_tail = [&](int mb, f32x16& S) {
+        // Rows m >= M. The limit passes through an empty asm statement so the
+        // compares are made here, on the tail block only, instead of being
+        // hoisted out of the token loop for every latent block.
+        int lim = M - 32 * mb - 4 * hi;
+        asm volatile("" : "+v"(lim));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (m >= M) S[i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+            if (8 * (i >> 2) + (i & 3) >= lim) S[i] = -INFINITY;
     };
 
     // One 64-token block: Y^T[d][tok] = sum_m Z^T[d][m] 2^(c S - nu)  and
@@ -849,70 +863,89 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
             }
         }
         f32x16 yac[TB][DB];
-        float tau[TB];
+        float tau[TB];  // whole sum over the latents, both lanes of a token
+        f32x4 tacc[TB];
         auto run = [&](const float (&off)[TB]) {
-            // -offset as the logit MFMA's accumulator input: the matrix core
-            // yields c*S - nu, the exponent itself
+            // logits S = Q K of latent block qa against token block tb
             auto logit = [&](const bf16x8 (&qa)[KB], int tb) {
                 f32x16 S = mfma(qa[0], kop[tb][0], f32x16{});
 #pragma unroll
                 for (int kb = 1; kb < KB; ++kb) S = mfma(qa[kb], kop[tb][kb], S);
                 return S;
             };
+            // Full latent blocks first (logits of block mb in SS[mb % 2]), then
+            // the padded block when M % 32 != 0, with its own logits.
+            const int MBF = M >> 5;
             bf16x8 qa[KB];
-            qread(0, qa);
-            f32x16 Snext[TB];
+            f32x16 SS[2][TB];
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                Snext[tb] = logit(qa, tb);
-                tau[tb] = 0.0f;
+            for (int tb = 0; tb < TB; ++tb) tacc[tb] = f32x4{};
+            if (MBF > 0) {
+                qread(0, qa);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) SS[0][tb] = logit(qa, tb);
             }
-            // one latent block; the next block's logits go to the matrix core
-            // before this block's softmax runs on the VALU
-            auto mstep = [&](int mb, bool first, bool masked) {
-                f32x16 S[TB];
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb) S[tb] = Snext[tb];
-                if (mb + 1 < MB) {
+            // One latent block whose logits are in S: the Z^T operands are
+            // requested from LDS (and, with `next`, the next block's logits go
+            // to the matrix core, into Sn) before the softmax runs on the VALU.
+            auto mstep = [&](int mb, bool first, bool next, f32x16 (&S)[TB], f32x16 (&Sn)[TB]) {
+                if (next) {
                     qread(mb + 1, qa);
 #pragma unroll
-                    for (int tb = 0; tb < TB; ++tb) Snext[tb] = logit(qa, tb);
+                    for (int tb = 0; tb < TB; ++tb) Sn[tb] = logit(qa, tb);
                 }
-                bf16x8 pb[TB][2];
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    if (masked) mask_tail(mb, S[tb]);
-                    tau[tb] += exp2_pack_sum(S[tb], c, off[tb], pb[tb][0], pb[tb][1]);
-                }
+                bf16x8 za[2][DB];
 #pragma unroll
                 for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         const int d = 32 * db + dec_row_d(l32);
-                        const bf16x8 za = *(const bf16x8*)(zt + d * zs + 2 * (32 * mb + 16 * kp + 8 * hi));
+                        za[kp][db] = *(const bf16x8*)(zt + d * zs + 2 * (32 * mb + 16 * kp + 8 * hi));
+                    }
+                bf16x8 pb[TB][2];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    exp2_pack(S[tb], c, off[tb], pb[tb][0], pb[tb][1]);
+                    tacc[tb] = colsum(csel, pb[tb][0], pb[tb][1], tacc[tb]);
+                }
+#pragma unroll
+                for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
 #pragma unroll
                         for (int tb = 0; tb < TB; ++tb)
-                            yac[tb][db] = mfma(za, pb[tb][kp], (first && kp == 0) ? zero16 : yac[tb][db]);
-                    }
+                            yac[tb][db] = mfma(za[kp][db], pb[tb][kp], (first && kp == 0) ? zero16 : yac[tb][db]);
             };
-            // only the last latent block can hold padding rows (M % 32 != 0)
-            const bool mtail = (M & 31) != 0;
-            if (MB == 1) {
-                if (mtail)
-                    mstep(0, true, true);
-                else
-                    mstep(0, true, false);
+            if constexpr (MBU > 0) {
+                // up to MBU latent blocks, unrolled: the two logit buffers
+                // alternate without register copies
+#pragma unroll
+                for (int mb = 0; mb < MBU; ++mb) {
+                    if (mb >= MBF) break;
+                    mstep(mb, mb == 0, mb + 1 < MBF, SS[mb & 1], SS[(mb + 1) & 1]);
+                }
             } else {
-                mstep(0, true, false);
 #pragma unroll 1
-                for (int mb = 1; mb < MB - 1; ++mb) mstep(mb, false, false);
-                if (mtail)
-                    mstep(MB - 1, false, true);
+                for (int mb = 0; mb < MBF; ++mb) {
+                    mstep(mb, mb == 0, mb + 1 < MBF, SS[0], SS[1]);
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) SS[0][tb] = SS[1][tb];
+                }
+            }
+            if (M & 31) {
+                qread(MBF, qa);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    SS[0][tb] = logit(qa, tb);
+                    mask_tail(MBF, SS[0][tb]);
+                }
+                if (MBF == 0)
+                    mstep(0, true, false, SS[0], SS[1]);
                 else
-                    mstep(MB - 1, false, false);
+                    mstep(MBF, false, false, SS[0], SS[1]);
             }
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) tau[tb] = pair_sum(tau[tb]);
+            for (int tb = 0; tb < TB; ++tb) tau[tb] = tacc[tb][0];
         };
         run(nu);
         bool low = false;
@@ -1051,16 +1084,29 @@ hipError_t launch_enc_d(const EncodeArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+// Latent blocks the decode unrolls (M <= 256); larger M runs a rolled loop.
+constexpr int kDecUnroll = 8;
+
+template <int D, int TB, typename ZT>
+const void* dec_kernel(int Mp) {
+    if constexpr (TB == 1) {
+        if (Mp <= 32 * kDecUnroll) return (const void*)decode_bf16<D, TB, ZT, kDecUnroll>;
+    }
+    return (const void*)decode_bf16<D, TB, ZT, 0>;
+}
+
 template <int D, int TB, typename ZT>
 hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
     const int lds = dec_lds_bytes_bf16(a.Mp, D);
+    const void* fn = dec_kernel<D, TB, ZT>(a.Mp);
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)decode_bf16<D, TB, ZT>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
     }
-    dim3 grid(a.G, a.BH), block(64 * kDecWaves);
-    hipLaunchKernelGGL((decode_bf16<D, TB, ZT>), grid, block, lds, s, a);
+    DecodeArgs arg = a;
+    void* args[] = {&arg};
+    hipError_t e = hipLaunchKernel(fn, dim3(a.G, a.BH), dim3(64 * kDecWaves), args, lds, s);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 
@@ -1098,8 +1144,7 @@ int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32) {
     const int lds = dec_lds_bytes_bf16(Mp, D);
     const void* fn = nullptr;
 #define FLARE_DEC_FN(DD, TB)                                                                          \
-    if (D == DD && tb == TB)                                                                          \
-        fn = z_f32 ? (const void*)decode_bf16<DD, TB, float> : (const void*)decode_bf16<DD, TB, uint16_t>;
+    if (D == DD && tb == TB) fn = z_f32 ? dec_kernel<DD, TB, float>(Mp) : dec_kernel<DD, TB, uint16_t>(Mp);
     FLARE_DEC_FN(32, 1)
     FLARE_DEC_FN(32, 2)
     FLARE_DEC_FN(64, 1)
