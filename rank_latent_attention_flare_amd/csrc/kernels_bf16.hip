@@ -281,11 +281,14 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             const int ch = pos ^ ((tile_off<D>(row, 0) - row * RB) >> 4);
             const int n = min(t0 + row, n1 - 1);
             const int64_t g = (int64_t)n * D + ch * 8;
-            // non-temporal loads measured faster on MI355X for the D = 64
-            // shapes with two latent blocks per wave, slower for the others
-            constexpr bool NT = D >= 64 && MBW >= 2;
-            dma16<NT>(Kb + g, st + pc * 1024);
-            dma16<NT>(Vb + g, st + T * RB + pc * 1024);
+            // V is read with the non-temporal policy: K, which the decode
+            // reads again, then stays in the last-level caches when it fits
+            // (measured 7-17% faster decodes on MI355X at 134 MB of K). K is
+            // non-temporal too for the D = 64 shapes with two latent blocks
+            // per wave (faster there; their K does not fit anyway).
+            constexpr bool KNT = D >= 64 && MBW >= 2;
+            dma16<KNT>(Kb + g, st + pc * 1024);
+            dma16<true>(Vb + g, st + T * RB + pc * 1024);
         }
     };
 
@@ -557,14 +560,14 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
 #pragma unroll
             for (int i = 0; i < IPS; ++i) {
                 dma16(kb0 + loff[i], st + i * 1024);
-                dma16(vb0 + loff[i], st + 32 * RB + i * 1024);
+                dma16<true>(vb0 + loff[i], st + 32 * RB + i * 1024);
             }
         } else {  // ragged tail: rows past the chunk end repeat its last token
 #pragma unroll
             for (int i = 0; i < IPS; ++i) {
                 const uint32_t o = loff[i] - (uint32_t)(max(0, t0 + lrow[i] - (n1 - 1)) * RB);
                 dma16(kb0 + o, st + i * 1024);
-                dma16(vb0 + o, st + 32 * RB + i * 1024);
+                dma16<true>(vb0 + o, st + 32 * RB + i * 1024);
             }
         }
     };
