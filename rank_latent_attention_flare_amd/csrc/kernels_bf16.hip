@@ -313,6 +313,31 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             const int krow = 32 * sb + enc_row_token(l32);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) ka[kb] = *(const bf16x8*)(kt + tile_off<D>(krow, 2 * kb + hi));
+            // V^T operands (A of acc^T += V^T P^T; k = 16 tokens), read
+            // transposed from the row-major tile: lane i of each 16-lane group
+            // receives element i%4 of source lanes 4k + i/4. Operand o covers
+            // tokens 16*(o/DB).. and rows d = 32*(o%DB)..
+            const int g = lane >> 4, gi = lane & 15;
+            auto vaddr = [&](int kp, int db, int second) {
+                const int row = 32 * sb + 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
+                const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+                return vt + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+            };
+            constexpr int NOP = 2 * DB;
+            bf16x8 va[NOP];
+            auto read_v = [&]() {
+#pragma unroll
+                for (int o = 0; o < NOP; o += 2) {
+                    const int kp0 = o / DB, db0 = o % DB, kp1 = (o + 1) / DB, db1 = (o + 1) % DB;
+                    lds_tr_op2(vaddr(kp0, db0, 0), vaddr(kp0, db0, 1), vaddr(kp1, db1, 0), vaddr(kp1, db1, 1),
+                               va[o], va[o + 1]);
+                }
+            };
+            // At D >= 64 the reads are issued here, so their latency overlaps
+            // the logits and the softmax (measured 3-4% faster on MI355X); at
+            // D = 32 after the softmax (faster there).
+            constexpr bool kVEarly = D >= 64;
+            if constexpr (kVEarly) read_v();
             auto mask = [&](f32x16& X) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -359,27 +384,13 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             }
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) ps[mb] += ts[mb];
-            // acc^T += V^T P^T. A operand = V^T rows d, k = 16 tokens, read
-            // transposed from the row-major tile: lane i of each 16-lane group
-            // receives element i%4 of source lanes 4k + i/4.
-            const int g = lane >> 4, gi = lane & 15;
-            // operand (kp, db) covers tokens 16*kp.. and rows d = 32*db..
-            auto vaddr = [&](int kp, int db, int second) {
-                const int row = 32 * sb + 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
-                const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
-                return vt + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
-            };
-            constexpr int NOP = 2 * DB;  // operands of this sub-block
+            // acc^T += V^T P^T
+            if constexpr (!kVEarly) read_v();
 #pragma unroll
-            for (int o = 0; o < NOP; o += 2) {
-                const int kp0 = o / DB, db0 = o % DB, kp1 = (o + 1) / DB, db1 = (o + 1) % DB;
-                bf16x8 va0, va1;
-                lds_tr_op2(vaddr(kp0, db0, 0), vaddr(kp0, db0, 1), vaddr(kp1, db1, 0), vaddr(kp1, db1, 1), va0,
-                           va1);
+            for (int o = 0; o < NOP; ++o) {
+                const int kp = o / DB, db = o % DB;
 #pragma unroll
-                for (int mb = 0; mb < MBW; ++mb) acc[mb][db0] = mfma(va0, pb[mb][kp0], acc[mb][db0]);
-#pragma unroll
-                for (int mb = 0; mb < MBW; ++mb) acc[mb][db1] = mfma(va1, pb[mb][kp1], acc[mb][db1]);
+                for (int mb = 0; mb < MBW; ++mb) acc[mb][db] = mfma(va[o], pb[mb][kp], acc[mb][db]);
             }
         }
     };
