@@ -494,8 +494,9 @@ flare_status flare_describe_plan(flare_op op, int64_t B, int64_t H, int64_t N, i
         enc = "encode grid (" + std::to_string(p.C) + "," + std::to_string(p.BH) + "," + std::to_string((M + nth - 1) / nth) +
               ") threads " + std::to_string(nth);
     }
-    std::string txt = enc + " chunk " + std::to_string(p.chunk_len) + "; decode grid (" +
-                      (dtype == FLARE_BF16 ? std::to_string(p.G) : std::to_string((N + 255) / 256)) + "," +
+    // the launched decode grid (bf16: sized from the device's occupancy)
+    const int dec_g = dtype == FLARE_BF16 ? decode_groups(p, op != FLARE_OP_DECODE) : int((N + 255) / 256);
+    std::string txt = enc + " chunk " + std::to_string(p.chunk_len) + "; decode grid (" + std::to_string(dec_g) + "," +
                       std::to_string(p.BH) + "); workspace " + std::to_string(p.total[op]) + " bytes";
     std::snprintf(buf, len, "%s", txt.c_str());
     return FLARE_OK;
