@@ -63,8 +63,8 @@ bool supported(flare_dtype dt, int64_t D, int64_t M, std::string* why) {
             *why = "bf16 supports D in {32, 64, 128}";
             return false;
         }
-        if (M > 256) {
-            *why = "bf16 supports M <= 256";
+        if (M > flare::kBf16MaxM) {
+            *why = "bf16 supports M <= " + std::to_string(flare::kBf16MaxM);
             return false;
         }
         return true;

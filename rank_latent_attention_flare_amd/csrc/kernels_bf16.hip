@@ -38,6 +38,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Largest per-tile probability sum the encode accepts against its running
 // offset before it re-centres (2^32; keeps every fp32 sum far from overflow).
 constexpr float kSumLimit = 4294967296.0f;
+// Latent blocks of 32 the decode unrolls: all of them at the largest M.
+constexpr int kDecMaxBlocks = kBf16MaxM / 32;
 // Smallest per-token probability sum the decode accepts against its offset
 // before it recomputes that block with exact maxima. Above it the largest
 // term is >= 2^-98 and every term within fp32 precision of it is a normal
@@ -753,7 +755,7 @@ __device__ __forceinline__ int dec_zpos(int m) {
     return (m & ~15) + (((r >> 2) & 1) << 3) + ((r >> 3) << 2) + (r & 3);
 }
 
-template <int D, int TB, typename ZT, int MBU>
+template <int D, int TB, typename ZT>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     constexpr int KB = D / 16, DB = D / 32, CH = D / 8, NW = kDecWaves;
     const int Mp = a.Mp, MB = Mp / 32;
@@ -930,21 +932,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
                         for (int tb = 0; tb < TB; ++tb)
                             yac[tb][db] = mfma(za[kp][db], pb[tb][kp], (first && kp == 0) ? zero16 : yac[tb][db]);
             };
-            if constexpr (MBU > 0) {
-                // up to MBU latent blocks, unrolled: the two logit buffers
-                // alternate without register copies
+            // all full latent blocks (M <= 32 * kDecMaxBlocks), unrolled: the
+            // two logit buffers alternate without register copies
 #pragma unroll
-                for (int mb = 0; mb < MBU; ++mb) {
-                    if (mb >= MBF) break;
-                    mstep(mb, mb == 0, mb + 1 < MBF, SS[mb & 1], SS[(mb + 1) & 1]);
-                }
-            } else {
-#pragma unroll 1
-                for (int mb = 0; mb < MBF; ++mb) {
-                    mstep(mb, mb == 0, mb + 1 < MBF, SS[0], SS[1]);
-#pragma unroll
-                    for (int tb = 0; tb < TB; ++tb) SS[0][tb] = SS[1][tb];
-                }
+            for (int mb = 0; mb < kDecMaxBlocks; ++mb) {
+                if (mb >= MBF) break;
+                mstep(mb, mb == 0, mb + 1 < MBF, SS[mb & 1], SS[(mb + 1) & 1]);
             }
             if (M & 31) {
                 qread(MBF, qa);
@@ -1098,21 +1091,15 @@ hipError_t launch_enc_d(const EncodeArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-// Latent blocks the decode unrolls (M <= 256); larger M runs a rolled loop.
-constexpr int kDecUnroll = 8;
-
 template <int D, int TB, typename ZT>
-const void* dec_kernel(int Mp) {
-    if constexpr (TB == 1) {
-        if (Mp <= 32 * kDecUnroll) return (const void*)decode_bf16<D, TB, ZT, kDecUnroll>;
-    }
-    return (const void*)decode_bf16<D, TB, ZT, 0>;
+const void* dec_kernel() {
+    return (const void*)decode_bf16<D, TB, ZT>;
 }
 
 template <int D, int TB, typename ZT>
 hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
     const int lds = dec_lds_bytes_bf16(a.Mp, D);
-    const void* fn = dec_kernel<D, TB, ZT>(a.Mp);
+    const void* fn = dec_kernel<D, TB, ZT>();
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
@@ -1158,7 +1145,7 @@ int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32) {
     const int lds = dec_lds_bytes_bf16(Mp, D);
     const void* fn = nullptr;
 #define FLARE_DEC_FN(DD, TB)                                                                          \
-    if (D == DD && tb == TB) fn = z_f32 ? dec_kernel<DD, TB, float>(Mp) : dec_kernel<DD, TB, uint16_t>(Mp);
+    if (D == DD && tb == TB) fn = z_f32 ? dec_kernel<DD, TB, float>() : dec_kernel<DD, TB, uint16_t>();
     FLARE_DEC_FN(32, 1)
     FLARE_DEC_FN(32, 2)
     FLARE_DEC_FN(64, 1)
