@@ -56,6 +56,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", type=int, default=2, help="workload number 1-5 (default 2)")
+    p.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
+                   help="layout of K, V and Y: [B,H,N,D] (default) or token-major [B,N,H,D]")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true", help="time one replay of a HIP graph holding the K steps")
@@ -91,6 +93,11 @@ def main():
     w = WORKLOADS[args.workload]
     op = F.FLARE_OP_PP_FORWARD if w.op == "pp_forward" else F.FLARE_OP_FORWARD
     fn = F.flare_pp_forward if op == F.FLARE_OP_PP_FORWARD else F.flare_forward
+    if args.layout == "bnhd":
+        fn_ex = F.flare_pp_forward_ex if op == F.FLARE_OP_PP_FORWARD else F.flare_forward_ex
+
+        def fn(Q, K, V, out=None, workspace=None, stream=None):
+            return fn_ex(Q, K, V, F.FLARE_LAYOUT_BNHD, out=out, workspace=workspace, stream=stream)
 
     Qh, Kh, Vh = workload_inputs(w)
 
@@ -99,8 +106,10 @@ def main():
         return t.view(torch.bfloat16) if a.dtype == np.uint16 else t
 
     Q, K, V = dev(Qh), dev(Kh), dev(Vh)
-    Y = torch.empty_like(K)
     ws = F.workspace_for(op, Q, K)
+    if args.layout == "bnhd":  # token-major copies, made before any timing
+        K, V = K.transpose(1, 2).contiguous(), V.transpose(1, 2).contiguous()
+    Y = torch.empty_like(K)
     stream = torch.cuda.current_stream()
 
     # plain copy of known size (scales hardware memory counters to bytes)
@@ -185,7 +194,8 @@ def main():
         dominant = "decode"
         achieved = alg_bytes[dominant] / (ms_step * 1e-3) / 1e9
     traffic = None
-    pmc_path = os.path.join(ROOT, "profiles", f"{dominant}_{w.name}_pmc.json")
+    lay = "" if args.layout == "bhnd" else "_bnhd"
+    pmc_path = os.path.join(ROOT, "profiles", f"{dominant}_{w.name}{lay}_pmc.json")
     if os.path.exists(pmc_path):
         with open(pmc_path) as f:
             pmc = json.load(f)
@@ -228,6 +238,7 @@ def main():
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (" + recipe() + ")",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "op": w.op,
+                   "layout": args.layout,
                    "plan": F.flare_describe_plan(op, w.B, w.H, w.N, w.M, w.D, Q.dtype)},
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kern.items()},
         "roofline": roofline,

@@ -17,7 +17,8 @@
  *
  * Conventions shared by every entry point
  *   Layout    Q is [H][M][D] (one latent set per head, shared over the batch).
- *             K, V and Y are [B][H][N][D]. Z is [B][H][M][D]. All row-major,
+ *             K, V and Y are [B][H][N][D] (the *_ex variants also take them
+ *             token-major, [B][N][H][D]). Z is [B][H][M][D]. All row-major,
  *             contiguous, D innermost.
  *   Memory    All tensor pointers are device pointers on the current HIP
  *             device, 16-byte aligned. The caller owns every tensor; the
@@ -120,6 +121,39 @@ flare_status flare_forward_ws(const void* Q, const void* K, const void* V, void*
 flare_status flare_pp_forward_ws(const void* Q, const void* K, const void* V, void* Y,
                                  int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
                                  flare_dtype dtype, hipStream_t stream, void* workspace, size_t ws_bytes);
+
+/* Layout of the token tensors K, V and Y. Q stays [H][M][D], and Z (the
+ * output of flare_encode, the V argument of flare_decode) stays [B][H][M][D].
+ *   FLARE_LAYOUT_BHND  [B][H][N][D], as everywhere else in this header.
+ *   FLARE_LAYOUT_BNHD  [B][N][H][D]: token-major, i.e. a projection's
+ *                      (B, N, H*D) output read in place, without the head
+ *                      transpose the FLARE skill page applies after its
+ *                      projections and undoes before its output projection
+ *                      ("4. Combine Encode-Decode into Attention Layer"). */
+typedef enum { FLARE_LAYOUT_BHND = 0, FLARE_LAYOUT_BNHD = 1 } flare_layout;
+
+/* The four operations with a layout argument. workspace == NULL with
+ * ws_bytes == 0 allocates scratch memory as the plain entry points do;
+ * otherwise it is caller-owned as for the *_ws variants. Results are those
+ * of the plain entry points on the same values (the layout changes only
+ * where elements live). A layout other than the two above returns
+ * FLARE_ERR_INVALID_ARG. */
+flare_status flare_encode_ex(const void* Q, const void* K, const void* V, void* Y,
+                             int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                             flare_dtype dtype, flare_layout layout, hipStream_t stream,
+                             void* workspace, size_t ws_bytes);
+flare_status flare_decode_ex(const void* Q, const void* K, const void* V, void* Y,
+                             int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                             flare_dtype dtype, flare_layout layout, hipStream_t stream,
+                             void* workspace, size_t ws_bytes);
+flare_status flare_forward_ex(const void* Q, const void* K, const void* V, void* Y,
+                              int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                              flare_dtype dtype, flare_layout layout, hipStream_t stream,
+                              void* workspace, size_t ws_bytes);
+flare_status flare_pp_forward_ex(const void* Q, const void* K, const void* V, void* Y,
+                                 int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                 flare_dtype dtype, flare_layout layout, hipStream_t stream,
+                                 void* workspace, size_t ws_bytes);
 
 /* Static text for a status code. */
 const char* flare_status_string(flare_status s);

@@ -55,7 +55,24 @@ struct Plan {
     size_t esize;
     size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[4];
     float c;
+    int64_t sb, sh, sn;  // element strides of K, V and Y: batch, head, token
 };
+
+// Token strides of K, V and Y for a layout (Q and Z are always [.][H][M][D]).
+flare_status set_layout(Plan* p, flare_layout layout) {
+    if (layout == FLARE_LAYOUT_BHND) {
+        p->sn = p->D;
+        p->sh = p->N * p->D;
+        p->sb = p->H * p->N * p->D;
+    } else if (layout == FLARE_LAYOUT_BNHD) {
+        p->sn = p->H * p->D;
+        p->sh = p->D;
+        p->sb = p->N * p->H * p->D;
+    } else {
+        return fail(FLARE_ERR_INVALID_ARG, "bad layout");
+    }
+    return FLARE_OK;
+}
 
 bool supported(flare_dtype dt, int64_t D, int64_t M, std::string* why) {
     if (dt == FLARE_BF16) {
@@ -224,6 +241,7 @@ hipError_t run_encode_partial(const Plan& p, const void* Q, int64_t q_bstride, c
     a.q_bstride = q_bstride;
     a.K = K;
     a.V = V;
+    a.sb = p.sb; a.sh = p.sh; a.sn = p.sn;
     a.BH = p.BH; a.H = int(p.H); a.N = int(p.N); a.M = int(p.M); a.Mp = p.Mp; a.D = int(p.D);
     a.C = p.C;
     a.chunk_len = p.chunk_len;
@@ -285,6 +303,7 @@ hipError_t run_decode(const Plan& p, const void* Q, int64_t q_bstride, const voi
     a.z_f32 = z_f32;
     a.zmu = p.dt == FLARE_BF16 ? zmu : nullptr;
     a.Y = Y;
+    a.sb = p.sb; a.sh = p.sh; a.sn = p.sn;
     a.BH = p.BH; a.H = int(p.H); a.N = int(p.N); a.M = int(p.M); a.Mp = p.Mp; a.D = int(p.D);
     a.G = decode_groups(p, z_f32);
     a.c = p.c;
@@ -294,9 +313,12 @@ hipError_t run_decode(const Plan& p, const void* Q, int64_t q_bstride, const voi
 }
 
 flare_status prepare(flare_op op, const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H,
-                     int64_t N, int64_t M, int64_t D, flare_dtype dt, void* ws, size_t ws_bytes, Plan* p) {
+                     int64_t N, int64_t M, int64_t D, flare_dtype dt, flare_layout layout, void* ws, size_t ws_bytes,
+                     Plan* p) {
     g_last_error.clear();
     flare_status st = make_plan(B, H, N, M, D, dt, p);
+    if (st != FLARE_OK) return st;
+    st = set_layout(p, layout);
     if (st != FLARE_OK) return st;
     st = check_ptrs(*p, op, Q, K, V, Y);
     if (st != FLARE_OK) return st;
@@ -312,9 +334,10 @@ flare_status prepare(flare_op op, const void* Q, const void* K, const void* V, v
 }
 
 flare_status exec(flare_op op, const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H,
-                  int64_t N, int64_t M, int64_t D, flare_dtype dt, hipStream_t s, void* wsv, size_t ws_bytes) {
+                  int64_t N, int64_t M, int64_t D, flare_dtype dt, flare_layout layout, hipStream_t s, void* wsv,
+                  size_t ws_bytes) {
     Plan p;
-    flare_status st = prepare(op, Q, K, V, Y, B, H, N, M, D, dt, wsv, ws_bytes, &p);
+    flare_status st = prepare(op, Q, K, V, Y, B, H, N, M, D, dt, layout, wsv, ws_bytes, &p);
     if (st != FLARE_OK) return st;
     char* ws = (char*)wsv;
     hipError_t e = hipSuccess;
@@ -350,10 +373,12 @@ flare_status exec(flare_op op, const void* Q, const void* K, const void* V, void
 }
 
 flare_status exec_alloc(flare_op op, const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H,
-                        int64_t N, int64_t M, int64_t D, flare_dtype dt, hipStream_t s) {
+                        int64_t N, int64_t M, int64_t D, flare_dtype dt, flare_layout layout, hipStream_t s) {
     Plan p;
     g_last_error.clear();
     flare_status st = make_plan(B, H, N, M, D, dt, &p);
+    if (st != FLARE_OK) return st;
+    st = set_layout(&p, layout);
     if (st != FLARE_OK) return st;
     st = check_ptrs(p, op, Q, K, V, Y);
     if (st != FLARE_OK) return st;
@@ -365,7 +390,7 @@ flare_status exec_alloc(flare_op op, const void* Q, const void* K, const void* V
         hipError_t e = hipMallocAsync(&ws, need, s);
         if (e != hipSuccess || !ws) return fail(FLARE_ERR_NO_MEMORY, std::string("hipMallocAsync: ") + hipGetErrorString(e));
     }
-    st = exec(op, Q, K, V, Y, B, H, N, M, D, dt, s, ws, need);
+    st = exec(op, Q, K, V, Y, B, H, N, M, D, dt, layout, s, ws, need);
     if (ws) {
         hipError_t e = hipFreeAsync(ws, s);
         if (e != hipSuccess && st == FLARE_OK) return hip_fail(e, "hipFreeAsync");
@@ -379,19 +404,19 @@ extern "C" {
 
 flare_status flare_encode(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
                           int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {
-    return exec_alloc(FLARE_OP_ENCODE, Q, K, V, Y, B, H, N, M, D, dtype, stream);
+    return exec_alloc(FLARE_OP_ENCODE, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream);
 }
 flare_status flare_decode(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
                           int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {
-    return exec_alloc(FLARE_OP_DECODE, Q, K, V, Y, B, H, N, M, D, dtype, stream);
+    return exec_alloc(FLARE_OP_DECODE, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream);
 }
 flare_status flare_forward(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
                            int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {
-    return exec_alloc(FLARE_OP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, stream);
+    return exec_alloc(FLARE_OP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream);
 }
 flare_status flare_pp_forward(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
                               int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {
-    return exec_alloc(FLARE_OP_PP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, stream);
+    return exec_alloc(FLARE_OP_PP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream);
 }
 
 size_t flare_workspace_size(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype) {
@@ -403,21 +428,34 @@ size_t flare_workspace_size(flare_op op, int64_t B, int64_t H, int64_t N, int64_
 
 flare_status flare_encode_ws(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
                              int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws, size_t n) {
-    return exec(FLARE_OP_ENCODE, Q, K, V, Y, B, H, N, M, D, dtype, stream, ws, n);
+    return exec(FLARE_OP_ENCODE, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, ws, n);
 }
 flare_status flare_decode_ws(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
                              int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws, size_t n) {
-    return exec(FLARE_OP_DECODE, Q, K, V, Y, B, H, N, M, D, dtype, stream, ws, n);
+    return exec(FLARE_OP_DECODE, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, ws, n);
 }
 flare_status flare_forward_ws(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
                               int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws, size_t n) {
-    return exec(FLARE_OP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, stream, ws, n);
+    return exec(FLARE_OP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, ws, n);
 }
 flare_status flare_pp_forward_ws(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H,
                                  int64_t N, int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws,
                                  size_t n) {
-    return exec(FLARE_OP_PP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, stream, ws, n);
+    return exec(FLARE_OP_PP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, ws, n);
 }
+
+#define FLARE_EX(NAME, OP)                                                                                     \
+    flare_status NAME(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,     \
+                      int64_t M, int64_t D, flare_dtype dtype, flare_layout layout, hipStream_t stream, void* ws, \
+                      size_t n) {                                                                                 \
+        if (!ws && n == 0) return exec_alloc(OP, Q, K, V, Y, B, H, N, M, D, dtype, layout, stream);              \
+        return exec(OP, Q, K, V, Y, B, H, N, M, D, dtype, layout, stream, ws, n);                                \
+    }
+FLARE_EX(flare_encode_ex, FLARE_OP_ENCODE)
+FLARE_EX(flare_decode_ex, FLARE_OP_DECODE)
+FLARE_EX(flare_forward_ex, FLARE_OP_FORWARD)
+FLARE_EX(flare_pp_forward_ex, FLARE_OP_PP_FORWARD)
+#undef FLARE_EX
 
 const char* flare_status_string(flare_status s) {
     switch (s) {

@@ -236,8 +236,9 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     const int n0 = chunk * a.chunk_len;
     const int n1 = min(N, n0 + a.chunk_len);
     const float c = a.c;
-    const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
-    const uint16_t* __restrict__ Vb = (const uint16_t*)a.V + (int64_t)bh * N * D;
+    const int64_t kvoff = (int64_t)b * a.sb + (int64_t)h * a.sh;
+    const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + kvoff;
+    const uint16_t* __restrict__ Vb = (const uint16_t*)a.V + kvoff;
     const uint16_t* __restrict__ Qb = (const uint16_t*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
 
     // This wave's latent queries as MFMA B operands (column m, k = d).
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             const int row = p / CH, pos = p % CH;
             const int ch = pos ^ ((tile_off<D>(row, 0) - row * RB) >> 4);
             const int n = min(t0 + row, n1 - 1);
-            const int64_t g = (int64_t)n * D + ch * 8;
+            const int64_t g = (int64_t)n * a.sn + ch * 8;
             // V is read with the non-temporal policy: K, which the decode
             // reads again, then stays in the last-level caches when it fits
             // (measured 7-17% faster decodes on MI355X at 134 MB of K). K is
@@ -524,8 +525,9 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
     const int n0 = chunk * a.chunk_len;
     const int n1 = min(N, n0 + a.chunk_len);
     const float c = a.c;
-    const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
-    const uint16_t* __restrict__ Vb = (const uint16_t*)a.V + (int64_t)bh * N * D;
+    const int64_t kvoff = (int64_t)b * a.sb + (int64_t)h * a.sh;
+    const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + kvoff;
+    const uint16_t* __restrict__ Vb = (const uint16_t*)a.V + kvoff;
     const uint16_t* __restrict__ Qb = (const uint16_t*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
     unsigned char* ring = smem + wave * (NSW * SBYTES);
 
@@ -554,6 +556,7 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
     const int nsub = nsb > wave ? (nsb - wave + NWV - 1) / NWV : 0;  // this wave's share
     // Byte offset of this lane's IPS 16-byte pieces inside a 32-token block
     // (row-major source, swizzled destination): the same for every block.
+    const uint32_t rsb = (uint32_t)(2 * a.sn);  // bytes between token rows in HBM
     uint32_t loff[IPS];
     int lrow[IPS];
 #pragma unroll
@@ -562,13 +565,13 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
         const int row = p / CH, pos = p % CH;
         const int ch = pos ^ ((tile_off<D>(row, 0) - row * RB) >> 4);
         lrow[i] = row;
-        loff[i] = (uint32_t)(row * RB + ch * 16);
+        loff[i] = (uint32_t)(row * rsb + ch * 16);
     }
     auto issue = [&](int k) {
         const int t0 = n0 + 32 * (wave + k * NWV);
         unsigned char* st = ring + (k % NSW) * SBYTES;
-        const unsigned char* kb0 = (const unsigned char*)(Kb + (int64_t)t0 * D);
-        const unsigned char* vb0 = (const unsigned char*)(Vb + (int64_t)t0 * D);
+        const unsigned char* kb0 = (const unsigned char*)(Kb + (int64_t)t0 * a.sn);
+        const unsigned char* vb0 = (const unsigned char*)(Vb + (int64_t)t0 * a.sn);
         if (t0 + 32 <= n1) {
 #pragma unroll
             for (int i = 0; i < IPS; ++i) {
@@ -578,7 +581,7 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
         } else {  // ragged tail: rows past the chunk end repeat its last token
 #pragma unroll
             for (int i = 0; i < IPS; ++i) {
-                const uint32_t o = loff[i] - (uint32_t)(max(0, t0 + lrow[i] - (n1 - 1)) * RB);
+                const uint32_t o = loff[i] - (uint32_t)max(0, t0 + lrow[i] - (n1 - 1)) * rsb;
                 dma16(kb0 + o, st + i * 1024);
                 dma16<true>(vb0 + o, st + 32 * RB + i * 1024);
             }
@@ -772,8 +775,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     float* red = (float*)(zt + D * zs);       // [NW] reduction scratch
     const uint16_t* __restrict__ Qb = (const uint16_t*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
     const ZT* __restrict__ Zb = (const ZT*)a.Z + (int64_t)bh * M * D;
-    const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
-    uint16_t* __restrict__ Yb = (uint16_t*)a.Y + (int64_t)bh * N * D;
+    const int64_t sn = a.sn;
+    const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + (int64_t)b * a.sb + (int64_t)h * a.sh;
+    uint16_t* __restrict__ Yb = (uint16_t*)a.Y + (int64_t)b * a.sb + (int64_t)h * a.sh;
 
     // ---- stage Q (bf16, swizzled rows) and Z^T (bf16, permuted latents)
     for (int p = tid; p < Mp * CH; p += 64 * NW) {
@@ -837,7 +841,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
             const int n = bk * 32 * TB + 32 * tb + l32;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                dst[tb][kb] = (bk < nblk && n < N) ? *(const bf16x8*)(Kb + (int64_t)n * D + 16 * kb + 8 * hi) : zero8();
+                dst[tb][kb] = (bk < nblk && n < N) ? *(const bf16x8*)(Kb + (int64_t)n * sn + 16 * kb + 8 * hi) : zero8();
         }
     };
     auto qread = [&](int mb, bf16x8 (&qa)[KB]) {
@@ -988,7 +992,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
             const int n = bk * 32 * TB + 32 * tb + l32;
             const float inv = __builtin_amdgcn_rcpf(tau[tb]);
             if (n < N) {
-                uint16_t* dst = Yb + (int64_t)n * D + 16 * hi;
+                uint16_t* dst = Yb + (int64_t)n * sn + 16 * hi;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     bf16x8 o0, o1;

@@ -125,8 +125,8 @@ __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
     const int N = a.N, M = a.M;
     const int n0 = chunk * a.chunk_len, n1 = min(N, n0 + a.chunk_len);
     const float c = a.c;
-    const float* Kb = (const float*)a.K + (int64_t)bh * N * D;
-    const float* Vb = (const float*)a.V + (int64_t)bh * N * D;
+    const float* Kb = (const float*)a.K + (int64_t)b * a.sb + (int64_t)h * a.sh;
+    const float* Vb = (const float*)a.V + (int64_t)b * a.sb + (int64_t)h * a.sh;
     const float* Qb = (const float*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
     const bool active = m < M;
     float q[D], acc[D];
@@ -139,8 +139,9 @@ __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
     for (int t0 = n0; t0 < n1; t0 += T) {
         const int nt = min(T, n1 - t0);
         for (int e = tid; e < nt * D; e += nth) {
-            kt[e] = Kb[(int64_t)t0 * D + e];
-            vt[e] = Vb[(int64_t)t0 * D + e];
+            const int64_t g = (int64_t)(t0 + e / D) * a.sn + e % D;
+            kt[e] = Kb[g];
+            vt[e] = Vb[g];
         }
         __syncthreads();
         if (active) {
@@ -187,7 +188,8 @@ __global__ __launch_bounds__(256) void decode_f32(DecodeArgs a) {
     const float c = a.c;
     const float* Qb = (const float*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
     const float* Zb = (const float*)a.Z + (int64_t)bh * M * D;
-    const float* kr = (const float*)a.K + ((int64_t)bh * N + n) * D;
+    const int64_t row = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)n * a.sn;
+    const float* kr = (const float*)a.K + row;
     float k[D], y[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(256) void decode_f32(DecodeArgs a) {
 #pragma unroll
         for (int d = 0; d < D; ++d) y[d] = fmaf(p, Zb[(int64_t)m * D + d], y[d]);
     }
-    float* yr = (float*)a.Y + ((int64_t)bh * N + n) * D;
+    float* yr = (float*)a.Y + row;
 #pragma unroll
     for (int d = 0; d < D; ++d) yr[d] = y[d] / tau;
 }

@@ -17,8 +17,9 @@ struct Partials {
 struct EncodeArgs {
     const void* Q;       // [H][M][D] or, with q_bstride > 0, [B][H][M][D]
     int64_t q_bstride;   // elements between batch entries of Q (0: shared)
-    const void* K;       // [B][H][N][D]
-    const void* V;       // [B][H][N][D]
+    const void* K;       // [B][H][N][D] or [B][N][H][D] (strides below)
+    const void* V;       // same layout as K
+    int64_t sb, sh, sn;  // K and V strides in elements: batch, head, token
     int BH, H, N, M, Mp, D;
     int C, chunk_len;    // chunks per (b, h) and tokens per chunk
     float c;             // (1/sqrt(D)) * log2(e)
@@ -45,11 +46,12 @@ struct CombineArgs {
 struct DecodeArgs {
     const void* Q;       // as in EncodeArgs
     int64_t q_bstride;
-    const void* K;       // [B][H][N][D]
+    const void* K;       // [B][H][N][D] or [B][N][H][D] (strides below)
     const void* Z;       // [BH][M][D], fp32 or operator dtype
     bool z_f32;
     const float* zmu;    // optional [BH][M] merged encode offsets; null: per-token bound
-    void* Y;             // [B][H][N][D]
+    void* Y;             // same layout as K
+    int64_t sb, sh, sn;  // K and Y strides in elements: batch, head, token
     int BH, H, N, M, Mp, D;
     int G;               // workgroups per (b, h)
     float c;

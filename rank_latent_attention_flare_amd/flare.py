@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflare.so
 
 FLARE_F32, FLARE_BF16 = 0, 1
 FLARE_OP_ENCODE, FLARE_OP_DECODE, FLARE_OP_FORWARD, FLARE_OP_PP_FORWARD = 0, 1, 2, 3
+FLARE_LAYOUT_BHND, FLARE_LAYOUT_BNHD = 0, 1
 FLARE_KERNEL_KINDS = 3
 KERNEL_KIND_NAMES = ("encode_partial", "combine", "decode")
 
@@ -50,6 +51,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = ctypes.c_int
             getattr(L, name + "_ws").argtypes = base + [_vp, ctypes.c_size_t]
             getattr(L, name + "_ws").restype = ctypes.c_int
+            getattr(L, name + "_ex").argtypes = base[:10] + [ctypes.c_int, _vp, _vp, ctypes.c_size_t]
+            getattr(L, name + "_ex").restype = ctypes.c_int
         L.flare_workspace_size.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
         L.flare_workspace_size.restype = ctypes.c_size_t
         L.flare_status_string.argtypes = [ctypes.c_int]
@@ -144,6 +147,57 @@ def flare_forward(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tenso
 def flare_pp_forward(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tensor:
     """Y [B, H, N, D] = FLARE++(Q, K, V)."""
     return _call(FLARE_OP_PP_FORWARD, "flare_pp_forward", Q, K, V, out, stream, workspace)
+
+
+def _call_ex(op: int, name: str, Q, K, V, layout: int, out, stream, workspace):
+    """K, V and Y token-major ([B, N, H, D]) with FLARE_LAYOUT_BNHD; Z stays [B, H, M, D]."""
+    if layout == FLARE_LAYOUT_BHND:
+        B, H, N, M, D = _dims(op, Q, K, V)
+    else:
+        if Q.dim() != 3 or K.dim() != 4 or V.dim() != 4:
+            raise ValueError("expected Q [H, M, D], K [B, N, H, D] and V [B, N, H, D] (Z [B, H, M, D] for decode)")
+        H, M, D = Q.shape
+        B, N, H2, D2 = K.shape
+        if H2 != H or D2 != D:
+            raise ValueError(f"K shape {tuple(K.shape)} does not match Q shape {tuple(Q.shape)}")
+        want_v = (B, H, M, D) if op == FLARE_OP_DECODE else (B, N, H, D)
+        if tuple(V.shape) != want_v:
+            raise ValueError(f"{'Z' if op == FLARE_OP_DECODE else 'V'} shape {tuple(V.shape)}, expected {want_v}")
+        for t in (Q, K, V):
+            if not t.is_cuda or not t.is_contiguous() or t.dtype != Q.dtype:
+                raise ValueError("Q, K and V must be contiguous device tensors of one dtype")
+    if op == FLARE_OP_ENCODE:
+        shape = (B, H, M, D)
+    else:
+        shape = (B, H, N, D) if layout == FLARE_LAYOUT_BHND else (B, N, H, D)
+    if out is None:
+        out = torch.empty(shape, dtype=Q.dtype, device=Q.device)
+    elif tuple(out.shape) != shape or out.dtype != Q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError(f"out must be a contiguous {Q.dtype} device tensor of shape {shape}")
+    ws, nws = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    _raise(getattr(lib(), name + "_ex")(Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), B, H, N, M, D,
+                                        dtype_code(Q.dtype), layout, _stream(stream), ws, nws))
+    return out
+
+
+def flare_encode_ex(Q, K, V, layout, out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Z [B, H, M, D] = encode(Q, K, V) with K, V in `layout`."""
+    return _call_ex(FLARE_OP_ENCODE, "flare_encode", Q, K, V, layout, out, stream, workspace)
+
+
+def flare_decode_ex(Q, K, Z, layout, out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Y = decode(Q, K, Z) with K and Y in `layout` (Z [B, H, M, D])."""
+    return _call_ex(FLARE_OP_DECODE, "flare_decode", Q, K, Z, layout, out, stream, workspace)
+
+
+def flare_forward_ex(Q, K, V, layout, out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Y = FLARE(Q, K, V) with K, V and Y in `layout`."""
+    return _call_ex(FLARE_OP_FORWARD, "flare_forward", Q, K, V, layout, out, stream, workspace)
+
+
+def flare_pp_forward_ex(Q, K, V, layout, out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Y = FLARE++(Q, K, V) with K, V and Y in `layout`."""
+    return _call_ex(FLARE_OP_PP_FORWARD, "flare_pp_forward", Q, K, V, layout, out, stream, workspace)
 
 
 def flare_workspace_size(op: int, B: int, H: int, N: int, M: int, D: int, dtype: torch.dtype) -> int:

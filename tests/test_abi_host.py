@@ -144,3 +144,19 @@ def test_timing_read_without_events():
     assert L.flare_timing_read(ms, cnt) == OK
     assert list(cnt) == [0, 0, 0]
     assert L.flare_timing_enable(0) == OK
+
+
+@pytest.mark.parametrize("name", ["flare_encode_ex", "flare_decode_ex", "flare_forward_ex", "flare_pp_forward_ex"])
+def test_layout_variants_validate_before_launch(name):
+    fn = getattr(F.lib(), name)
+    # an unknown layout, a null pointer and an unsupported size are all
+    # rejected before any device work (with or without a workspace)
+    for ws in ((None, 0), (PW, 1 << 30)):
+        assert fn(*fwd_args(), 7, None, *ws) == INVALID
+        assert "layout" in F.lib().flare_last_error().decode()
+        assert fn(*fwd_args(k=None), F.FLARE_LAYOUT_BNHD, None, *ws) == INVALID
+        assert fn(*fwd_args(D=48), F.FLARE_LAYOUT_BNHD, None, *ws) == UNSUPPORTED
+    # a too-small caller workspace is rejected too
+    if name != "flare_decode_ex":
+        assert fn(*fwd_args(), F.FLARE_LAYOUT_BNHD, None, PW, 256) == INVALID
+        assert "workspace" in F.lib().flare_last_error().decode()
