@@ -11,7 +11,8 @@ library, widens stored inputs exactly to fp64, and loops over (batch, head).
 Inputs follow the storage convention of ``flare_inputs``: fp32 tensors are
 ``float32`` arrays, bf16 tensors are ``uint16`` arrays of bf16 bit patterns.
 Shapes: Q is [H, M, D] (shared over the batch) or [B, H, M, D]; K and V are
-[B, H, N, D]; the results are fp64 arrays.
+[B, H, N, D]; the token queries q of ``attend`` are [B, H, N, D] and its Z is
+[B, H, M, D]; the results are fp64 arrays.
 """
 from __future__ import annotations
 
@@ -55,7 +56,10 @@ def _load():
                                              _i64p, ctypes.c_int64, _dp, _dp]
         lib.flare_oracle_pp_forward.argtypes = [_dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                 _i64p, ctypes.c_int64, _dp, _dp, _dp]
-        for f in ("flare_oracle_encode", "flare_oracle_decode", "flare_oracle_forward", "flare_oracle_pp_forward"):
+        lib.flare_oracle_attend.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
+                                            ctypes.c_int64, _dp]
+        for f in ("flare_oracle_encode", "flare_oracle_decode", "flare_oracle_forward", "flare_oracle_pp_forward",
+                  "flare_oracle_attend"):
             getattr(lib, f).restype = ctypes.c_int
         lib.flare_oracle_threads.restype = ctypes.c_int
         lib.flare_oracle_set_threads.argtypes = [ctypes.c_int]
@@ -127,6 +131,21 @@ def decode_head(Q, K, Z, rows: Optional[np.ndarray] = None) -> np.ndarray:
     return Y
 
 
+def attend_head(q, Z, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Y[R,D] of one head: token queries q[N,D] attend to Z[M,D] (keys and values)."""
+    q, Z = _c64(q), _c64(Z)
+    N, D = q.shape
+    M = Z.shape[0]
+    if rows is None:
+        R, rp = N, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        R, rp = rows.shape[0], rows.ctypes.data_as(_i64p)
+    Y = np.empty((R, D), np.float64)
+    _check(_load().flare_oracle_attend(_ptr(q), _ptr(Z), N, M, D, rp, R, _ptr(Y)), "attend")
+    return Y
+
+
 def pp_forward_head(Q, K, V, rows: Optional[np.ndarray] = None):
     """(Y, Q', Z) of one head for FLARE++."""
     Q, K, V = _c64(Q), _c64(K), _c64(V)
@@ -163,6 +182,16 @@ def decode(Q, K, Z, rows=None, heads=None) -> np.ndarray:
     Y = np.full((B, H, R, D), np.nan)
     for b, h in (heads or [(b, h) for b in range(B) for h in range(H)]):
         Y[b, h] = decode_head(widen(_q_for(Q, b, h)), widen(K[b, h]), widen(Z[b, h]), rows)
+    return Y
+
+
+def attend(q, Z, rows=None, heads=None) -> np.ndarray:
+    """Y[B,H,R,D] (fp64): token queries q[B,H,N,D] attend to Z[B,H,M,D]."""
+    B, H, N, D = q.shape
+    R = N if rows is None else len(rows)
+    Y = np.full((B, H, R, D), np.nan)
+    for b, h in (heads or [(b, h) for b in range(B) for h in range(H)]):
+        Y[b, h] = attend_head(widen(q[b, h]), widen(Z[b, h]), rows)
     return Y
 
 

@@ -24,8 +24,9 @@
  *        A_dec[n][m] = softmax over m of l[m][n],
  *        Y[n] = sum_m A_dec[n][m] Z[m].
  *    The FLARE skill page's step 3 instead decodes with separately projected
- *    token queries against Z as keys; this oracle follows the transposed-
- *    logit reading (see the readings list of the design notes).
+ *    token queries against Z as keys; the decode follows the transposed-
+ *    logit reading (see the readings list of the design notes), and the
+ *    page's variant is flare_oracle_attend below.
  *  - FLARE++ (FLARE++ skill page, "Core Mechanism"; FLARE++ arXiv abstract:
  *    the encoder's output corrects the learned queries):
  *        Q' = Q + encode(Q, K, V);  Z = encode(Q', K, V);  Y = decode(Q', K, Z).
@@ -123,6 +124,52 @@ int flare_oracle_decode(const double* Q, const double* K, const double* Z,
                 den += e;
                 const double* z = Z + m * D;
                 for (int64_t d = 0; d < D; ++d) y[d] += e * z[d];
+            }
+            for (int64_t d = 0; d < D; ++d) y[d] /= den;
+        }
+        free(logit);
+    }
+    return failed == 1 ? -1 : (failed == 2 ? -2 : 0);
+}
+
+/* Token-query decode of one head ("3. Implement Decode Stage" of the FLARE
+ * skill page, and the decode half of its step 4): every token's own query
+ * q[n] attends to the latent states Z, which serve as keys and values,
+ *     l'[n][m] = s * <q[n], Z[m]>,  A[n][m] = softmax over m of l'[n][m],
+ *     Y[n] = sum_m A[n][m] Z[m].
+ * Y[R][D] from q[N][D] and Z[M][D]; rows as in flare_oracle_decode. */
+int flare_oracle_attend(const double* q, const double* Z, int64_t N, int64_t M, int64_t D,
+                        const int64_t* rows, int64_t R, double* Y) {
+    const double s = 1.0 / sqrt((double)D);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* logit = (double*)malloc((size_t)M * sizeof(double));
+        if (!logit) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < R; ++i) {
+            if (!logit) continue;
+            int64_t n = rows ? rows[i] : i;
+            if (n < 0 || n >= N) {
+#pragma omp atomic write
+                failed = 2;
+                continue;
+            }
+            double mx = -INFINITY;
+            for (int64_t m = 0; m < M; ++m) {
+                logit[m] = s * dot(q + n * D, Z + m * D, D);
+                if (logit[m] > mx) mx = logit[m];
+            }
+            double den = 0.0;
+            double* y = Y + i * D;
+            for (int64_t d = 0; d < D; ++d) y[d] = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                double e = exp(logit[m] - mx);
+                den += e;
+                for (int64_t d = 0; d < D; ++d) y[d] += e * Z[m * D + d];
             }
             for (int64_t d = 0; d < D; ++d) y[d] /= den;
         }

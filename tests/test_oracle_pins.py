@@ -246,3 +246,30 @@ def test_generator_is_deterministic_and_shaped():
     assert a[0].shape == (3, 7, 16) and a[1].shape == (2, 3, 100, 16) and a[0].dtype == np.uint16
     q32 = make_inputs(1, 1, 8, 4, 16, "f32", 2.0, 1.0, seed=3)[0]
     assert q32.dtype == np.float32 and 1.0 < q32.std() < 3.0
+
+
+# ------------------------------------------ token-query decode (skill page)
+@pytest.mark.parametrize("B,H,N,M,D", [(2, 3, 37, 5, 8), (1, 2, 65, 33, 16), (1, 1, 1, 1, 4)])
+def test_attend_is_sdpa_of_token_queries_over_latent_states(B, H, N, M, D):
+    q, Z = rand(B, H, N, D), rand(B, H, M, D)
+    np.testing.assert_allclose(oracle.attend(q, Z), sdpa(q, Z, Z), rtol=1e-12, atol=1e-13)
+
+
+def test_attend_single_latent_and_zero_queries():
+    q, Z1 = rand(1, 2, 9, 8), rand(1, 2, 1, 8)
+    Y = oracle.attend(q, Z1)
+    np.testing.assert_allclose(Y, np.broadcast_to(Z1, Y.shape), rtol=1e-15, atol=0)
+    Z = rand(1, 2, 6, 8)
+    Y0 = oracle.attend(np.zeros((1, 2, 5, 8)), Z)
+    np.testing.assert_allclose(Y0, np.broadcast_to(Z.mean(axis=2, keepdims=True), Y0.shape), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("a,b", [(1.0, -1.0), (0.3, 2.0)])
+def test_attend_two_latent_closed_form(a, b):
+    # D=1 (s=1): token query x has logits a*x and b*x against latent states a
+    # and b, so Y = w*a + (1-w)*b with w = sigmoid((a - b) x).
+    xs = np.array([-2.0, -0.1, 0.0, 1.3])
+    q = xs.reshape(1, 1, 4, 1)
+    Z = np.array([[[[a], [b]]]])
+    w = np.array([sigmoid((a - b) * x) for x in xs])
+    np.testing.assert_allclose(oracle.attend(q, Z)[0, 0, :, 0], w * a + (1 - w) * b, rtol=1e-14, atol=1e-15)
