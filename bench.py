@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", type=int, default=2, help="workload number 1-5 (default 2)")
+    p.add_argument("--variant", choices=["flare", "skill"], default="flare",
+                   help="flare: the workload's forward (default); skill: the FLARE skill page's layer, "
+                        "flare_encode then flare_attend with separate token queries (forward workloads only)")
     p.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
                    help="layout of K, V and Y: [B,H,N,D] (default) or token-major [B,N,H,D]")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
@@ -107,9 +110,23 @@ def main():
 
     Q, K, V = dev(Qh), dev(Kh), dev(Vh)
     ws = F.workspace_for(op, Q, K)
+    if args.variant == "skill":
+        if op != F.FLARE_OP_FORWARD:
+            print("--variant skill needs a FLARE forward workload", file=sys.stderr)
+            sys.exit(2)
+        ws = F.workspace_for(F.FLARE_OP_ENCODE, Q, K)
+        qtok = V.flip(2).contiguous()  # separate token queries: the values in reverse token order
+        Zlat = torch.empty((w.B, w.H, w.M, w.D), dtype=Q.dtype, device=Q.device)
     if args.layout == "bnhd":  # token-major copies, made before any timing
         K, V = K.transpose(1, 2).contiguous(), V.transpose(1, 2).contiguous()
+        if args.variant == "skill":
+            qtok = qtok.transpose(1, 2).contiguous()
     Y = torch.empty_like(K)
+    lay_code = F.FLARE_LAYOUT_BNHD if args.layout == "bnhd" else F.FLARE_LAYOUT_BHND
+    if args.variant == "skill":
+        def fn(Q, K, V, out=None, workspace=None, stream=None):
+            F.flare_encode_ex(Q, K, V, lay_code, out=Zlat, workspace=workspace, stream=stream)
+            return F.flare_attend(qtok, Zlat, lay_code, out=out, stream=stream)
     stream = torch.cuda.current_stream()
 
     # plain copy of known size (scales hardware memory counters to bytes)
@@ -194,7 +211,7 @@ def main():
         dominant = "decode"
         achieved = alg_bytes[dominant] / (ms_step * 1e-3) / 1e9
     traffic = None
-    lay = "" if args.layout == "bhnd" else "_bnhd"
+    lay = ("" if args.layout == "bhnd" else "_bnhd") + ("" if args.variant == "flare" else "_skill")
     pmc_path = os.path.join(ROOT, "profiles", f"{dominant}_{w.name}{lay}_pmc.json")
     if os.path.exists(pmc_path):
         with open(pmc_path) as f:
@@ -219,6 +236,9 @@ def main():
             q = Qh[h]
             if op == F.FLARE_OP_PP_FORWARD:
                 oracle.pp_forward_head(oracle.widen(q), oracle.widen(Kh[b, h]), oracle.widen(Vh[b, h]))
+            elif args.variant == "skill":
+                z = oracle.encode_head(oracle.widen(q), oracle.widen(Kh[b, h]), oracle.widen(Vh[b, h]))
+                oracle.attend_head(oracle.widen(Vh[b, h][::-1]), z)
             else:
                 qq, kk = oracle.widen(q), oracle.widen(Kh[b, h])
                 z = oracle.encode_head(qq, kk, oracle.widen(Vh[b, h]))
@@ -229,7 +249,8 @@ def main():
         el = time.perf_counter() - t0
         cpu = {"value": round(done * w.N / el, 1), "unit": "tokens*heads/s", "cores": oracle.threads(),
                "kind": "oracle", "sample": f"{done} of {len(heads)} heads of {w.name}, full N={w.N}, "
-                                            f"fp64 {w.op}, {el:.1f} s"}
+                                            f"fp64 {w.op if args.variant == 'flare' else 'skill-page layer'}, "
+                                            f"{el:.1f} s"}
 
     line = {
         "metric": "FLARE fwd tokens*heads/s (N=65536, M=128) + roofline fraction",
@@ -238,7 +259,7 @@ def main():
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (" + recipe() + ")",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "op": w.op,
-                   "layout": args.layout,
+                   "layout": args.layout, "variant": args.variant,
                    "plan": F.flare_describe_plan(op, w.B, w.H, w.N, w.M, w.D, Q.dtype)},
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kern.items()},
         "roofline": roofline,

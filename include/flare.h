@@ -155,6 +155,19 @@ flare_status flare_pp_forward_ex(const void* Q, const void* K, const void* V, vo
                                  flare_dtype dtype, flare_layout layout, hipStream_t stream,
                                  void* workspace, size_t ws_bytes);
 
+/* Token-query decode of the FLARE skill page ("3. Implement Decode Stage";
+ * the decode half of "4. Combine Encode-Decode into Attention Layer"): each
+ * token's own query attends to the latent states, which serve as keys and
+ * values,
+ *   Y[b][h][n] = sum_m softmax_m(s * <q[b][h][n], Z[b][h][m]>) * Z[b][h][m].
+ * q and Y are [B][H][N][D] or, with FLARE_LAYOUT_BNHD, [B][N][H][D]; Z is
+ * [B][H][M][D] (e.g. the output of flare_encode). Same types, sizes and
+ * conventions as flare_decode; no workspace is needed. The page's layer is
+ * then flare_encode(latents, k, v) followed by flare_attend(q, Z). */
+flare_status flare_attend(const void* q, const void* Z, void* Y,
+                          int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                          flare_dtype dtype, flare_layout layout, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* flare_status_string(flare_status s);
 

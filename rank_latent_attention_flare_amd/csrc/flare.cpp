@@ -444,6 +444,29 @@ flare_status flare_pp_forward_ws(const void* Q, const void* K, const void* V, vo
     return exec(FLARE_OP_PP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, ws, n);
 }
 
+flare_status flare_attend(const void* q, const void* Z, void* Y, int64_t B, int64_t H, int64_t N, int64_t M,
+                          int64_t D, flare_dtype dtype, flare_layout layout, hipStream_t stream) {
+    Plan p;
+    g_last_error.clear();
+    flare_status st = make_plan(B, H, N, M, D, dtype, &p);
+    if (st != FLARE_OK) return st;
+    st = set_layout(&p, layout);
+    if (st != FLARE_OK) return st;
+    if (!q || !Z || !Y) return fail(FLARE_ERR_INVALID_ARG, "null tensor pointer");
+    for (const void* t : {q, Z, (const void*)Y})
+        if (uintptr_t(t) % 16 != 0) return fail(FLARE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const size_t ntok = size_t(p.BH) * p.N * p.D * p.esize, nz = size_t(p.BH) * p.M * p.D * p.esize;
+    if (overlaps(Y, ntok, q, ntok) || overlaps(Y, ntok, Z, nz))
+        return fail(FLARE_ERR_INVALID_ARG, "output overlaps an input");
+    // The decode kernel with Z in both latent roles: Z[b][h] is the latent
+    // operand of the logits (batch-strided, as FLARE++'s Q') and the values;
+    // the token queries take the place of K. No encode offsets: the
+    // per-token Cauchy-Schwarz bound.
+    hipError_t e = run_decode(p, Z, H * M * D, q, Z, dtype == FLARE_F32, Y, stream);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    return FLARE_OK;
+}
+
 #define FLARE_EX(NAME, OP)                                                                                     \
     flare_status NAME(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,     \
                       int64_t M, int64_t D, flare_dtype dtype, flare_layout layout, hipStream_t stream, void* ws, \

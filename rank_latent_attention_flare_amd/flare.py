@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, name + "_ws").restype = ctypes.c_int
             getattr(L, name + "_ex").argtypes = base[:10] + [ctypes.c_int, _vp, _vp, ctypes.c_size_t]
             getattr(L, name + "_ex").restype = ctypes.c_int
+        L.flare_attend.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
+        L.flare_attend.restype = ctypes.c_int
         L.flare_workspace_size.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
         L.flare_workspace_size.restype = ctypes.c_size_t
         L.flare_status_string.argtypes = [ctypes.c_int]
@@ -198,6 +200,30 @@ def flare_forward_ex(Q, K, V, layout, out=None, stream=None, workspace=None) -> 
 def flare_pp_forward_ex(Q, K, V, layout, out=None, stream=None, workspace=None) -> torch.Tensor:
     """Y = FLARE++(Q, K, V) with K, V and Y in `layout`."""
     return _call_ex(FLARE_OP_PP_FORWARD, "flare_pp_forward", Q, K, V, layout, out, stream, workspace)
+
+
+def flare_attend(q, Z, layout=FLARE_LAYOUT_BHND, out=None, stream=None) -> torch.Tensor:
+    """Y = softmax_M(s q Z^T) Z: token queries q ([B, H, N, D], or [B, N, H, D] token-major) attend to
+    the latent states Z [B, H, M, D]; Y has q's layout."""
+    if q.dim() != 4 or Z.dim() != 4:
+        raise ValueError("expected q [B, H, N, D] (or [B, N, H, D]) and Z [B, H, M, D]")
+    if layout == FLARE_LAYOUT_BHND:
+        B, H, N, D = q.shape
+    else:
+        B, N, H, D = q.shape
+    B2, H2, M, D2 = Z.shape
+    if (B2, H2, D2) != (B, H, D):
+        raise ValueError(f"Z shape {tuple(Z.shape)} does not match q shape {tuple(q.shape)}")
+    for t in (q, Z):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q and Z must be contiguous device tensors of one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError(f"out must be a contiguous {q.dtype} device tensor of shape {tuple(q.shape)}")
+    _raise(lib().flare_attend(q.data_ptr(), Z.data_ptr(), out.data_ptr(), B, H, N, M, D, dtype_code(q.dtype),
+                              layout, _stream(stream)))
+    return out
 
 
 def flare_workspace_size(op: int, B: int, H: int, N: int, M: int, D: int, dtype: torch.dtype) -> int:

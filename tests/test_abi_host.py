@@ -160,3 +160,13 @@ def test_layout_variants_validate_before_launch(name):
     if name != "flare_decode_ex":
         assert fn(*fwd_args(), F.FLARE_LAYOUT_BNHD, None, PW, 256) == INVALID
         assert "workspace" in F.lib().flare_last_error().decode()
+
+
+def test_attend_validates_before_launch():
+    fn = F.lib().flare_attend
+    args = [PQ, PK, PY, 1, 2, 100, 64, 64, F.FLARE_BF16]
+    assert fn(*args, 7, None) == INVALID and "layout" in F.lib().flare_last_error().decode()
+    assert fn(None, *args[1:], 0, None) == INVALID and "null" in F.lib().flare_last_error().decode()
+    assert fn(PQ, PK, PQ + 256, *args[3:], 0, None) == INVALID  # Y overlaps q
+    assert fn(PQ, PK, PY + 8, *args[3:], 0, None) == INVALID    # misaligned
+    assert fn(PQ, PK, PY, 1, 2, 100, 300, 64, F.FLARE_BF16, 0, None) == UNSUPPORTED
