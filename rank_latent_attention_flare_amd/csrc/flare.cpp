@@ -80,8 +80,9 @@ bool supported(flare_dtype dt, int64_t D, int64_t M, std::string* why) {
             *why = "bf16 supports D in {32, 64, 128}";
             return false;
         }
-        if (M > flare::kBf16MaxM) {
-            *why = "bf16 supports M <= " + std::to_string(flare::kBf16MaxM);
+        const int mmax = D == 128 ? flare::kBf16MaxM128 : flare::kBf16MaxM;
+        if (M > mmax) {
+            *why = "bf16 supports M <= " + std::to_string(mmax) + " at D = " + std::to_string(D);
             return false;
         }
         return true;
@@ -133,7 +134,8 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     // tokens; fp32, whose lanes each run a whole latent: 4*Mp, at least one tile).
     const int64_t target_wgs = std::max<int64_t>(1, kTargetEncWaves / waves_per_wg);
     int64_t C = std::max<int64_t>(1, (target_wgs + p->BH - 1) / p->BH);
-    const int64_t min_chunk = dt == FLARE_BF16 ? 32 * int64_t(p->Mp) : std::max<int64_t>(tile, 4 * int64_t(p->Mp));
+    const int64_t min_chunk =
+        dt == FLARE_BF16 ? 32 * int64_t(std::min(p->Mp, 256)) : std::max<int64_t>(tile, 4 * int64_t(p->Mp));
     const int64_t cmax = std::max<int64_t>(1, N / min_chunk);
     C = std::min(C, cmax);
     if (const char* e = std::getenv("FLARE_TEST_CHUNKS")) {
@@ -146,7 +148,7 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     p->C = int(C);
     p->chunk_len = int(chunk);
     // decode workgroups per (b, h)
-    const int64_t per_wg = 32 * (dt == FLARE_BF16 ? flare::dec_tb_bf16(int(D)) : 2) * flare::kDecWaves;
+    const int64_t per_wg = 32 * (dt == FLARE_BF16 ? flare::dec_tb_bf16(int(D), p->Mp) : 2) * flare::kDecWaves;
     int64_t G = std::max<int64_t>(1, (kTargetDecWgs + p->BH - 1) / p->BH);
     G = std::min<int64_t>(G, (N + per_wg - 1) / per_wg);
     p->G = int(G);
@@ -287,7 +289,7 @@ int decode_groups(const Plan& p, bool z_f32) {
             cus = 256;
     }
     const int per_cu = flare::dec_wgs_per_cu_bf16(int(p.D), p.Mp, z_f32);
-    const int64_t per_wg = 32 * flare::dec_tb_bf16(int(p.D)) * flare::kDecWaves;
+    const int64_t per_wg = 32 * flare::dec_tb_bf16(int(p.D), p.Mp) * flare::kDecWaves;
     int64_t G = (int64_t(cus) * per_cu + p.BH - 1) / p.BH;
     G = std::max<int64_t>(1, std::min<int64_t>(G, (p.N + per_wg - 1) / per_wg));
     return int(G);

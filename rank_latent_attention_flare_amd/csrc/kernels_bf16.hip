@@ -38,8 +38,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Largest per-tile probability sum the encode accepts against its running
 // offset before it re-centres (2^32; keeps every fp32 sum far from overflow).
 constexpr float kSumLimit = 4294967296.0f;
-// Latent blocks of 32 the decode unrolls: all of them at the largest M.
-constexpr int kDecMaxBlocks = kBf16MaxM / 32;
 // Smallest per-token probability sum the decode accepts against its offset
 // before it recomputes that block with exact maxima. Above it the largest
 // term is >= 2^-98 and every term within fp32 precision of it is a normal
@@ -758,7 +756,9 @@ __device__ __forceinline__ int dec_zpos(int m) {
     return (m & ~15) + (((r >> 2) & 1) << 3) + ((r >> 3) << 2) + (r & 3);
 }
 
-template <int D, int TB, typename ZT>
+// LONG: M > 256 (more than one group of 8 latent blocks; the group loop costs
+// registers, so the common M <= 256 kernel is built without it).
+template <int D, int TB, typename ZT, bool LONG>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     constexpr int KB = D / 16, DB = D / 32, CH = D / 8, NW = kDecWaves;
     const int Mp = a.Mp, MB = Mp / 32;
@@ -936,12 +936,25 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
                         for (int tb = 0; tb < TB; ++tb)
                             yac[tb][db] = mfma(za[kp][db], pb[tb][kp], (first && kp == 0) ? zero16 : yac[tb][db]);
             };
-            // all full latent blocks (M <= 32 * kDecMaxBlocks), unrolled: the
-            // two logit buffers alternate without register copies
+            // all full latent blocks in groups of 8,
+            // each group unrolled: the two logit buffers alternate without
+            // register copies (8 is even, so block mb's logits are always in
+            // SS[mb % 2]); the first group is separate so that its first
+            // block starts the accumulators from the zero constant
 #pragma unroll
-            for (int mb = 0; mb < kDecMaxBlocks; ++mb) {
-                if (mb >= MBF) break;
-                mstep(mb, mb == 0, mb + 1 < MBF, SS[mb & 1], SS[(mb + 1) & 1]);
+            for (int j = 0; j < 8; ++j) {
+                if (j >= MBF) break;
+                mstep(j, j == 0, j + 1 < MBF, SS[j & 1], SS[(j + 1) & 1]);
+            }
+            if constexpr (LONG) {
+#pragma unroll 1
+                for (int g = 8; g < MBF; g += 8) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        if (g + j >= MBF) break;
+                        mstep(g + j, false, g + j + 1 < MBF, SS[j & 1], SS[(j + 1) & 1]);
+                    }
+                }
             }
             if (M & 31) {
                 qread(MBF, qa);
@@ -1090,20 +1103,24 @@ hipError_t launch_enc_d(const EncodeArgs& a, hipStream_t s) {
         FLARE_ENC_CASE(2, 2, 1)
         FLARE_ENC_CASE(2, 2, 2)
         FLARE_ENC_CASE(2, 1, 2)
+        FLARE_ENC_CASE(2, 8, 1)
     }
 #undef FLARE_ENC_CASE
     return hipErrorInvalidValue;
 }
 
 template <int D, int TB, typename ZT>
-const void* dec_kernel() {
-    return (const void*)decode_bf16<D, TB, ZT>;
+const void* dec_kernel(int Mp) {
+    if constexpr (D <= 64 && TB == 1) {
+        if (Mp > 256) return (const void*)decode_bf16<D, TB, ZT, true>;
+    }
+    return (const void*)decode_bf16<D, TB, ZT, false>;
 }
 
 template <int D, int TB, typename ZT>
 hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
     const int lds = dec_lds_bytes_bf16(a.Mp, D);
-    const void* fn = dec_kernel<D, TB, ZT>();
+    const void* fn = dec_kernel<D, TB, ZT>(a.Mp);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
@@ -1118,7 +1135,7 @@ hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
 template <int D, typename ZT>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t s) {
     if constexpr (D <= 64) {
-        if (dec_tb_bf16(D) == 2) return launch_dec_tb<D, 2, ZT>(a, s);
+        if (dec_tb_bf16(D, a.Mp) == 2) return launch_dec_tb<D, 2, ZT>(a, s);
     }
     return launch_dec_tb<D, 1, ZT>(a, s);
 }
@@ -1138,18 +1155,19 @@ EncCfg enc_cfg_bf16(int D, int Mb) {
     if (Mb <= 2) return {1, 2, 2};
     if (D == 128) return Mb <= 4 ? EncCfg{1, 4, 1} : EncCfg{1, 8, 1};
     if (Mb <= 4) return {2, 2, 2};
-    return {2, 4, 1};
+    if (Mb <= 8) return {2, 4, 1};
+    return {2, 8, 1};
 }
 
 int enc_tile_tokens_bf16(EncCfg cfg) { return cfg.wm == 0 ? 32 * cfg.wt : 64; }
 int enc_threads_bf16(EncCfg cfg) { return 64 * (cfg.wm == 0 ? 1 : cfg.wm) * cfg.wt; }
 
 int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32) {
-    const int tb = dec_tb_bf16(D);
+    const int tb = dec_tb_bf16(D, Mp);
     const int lds = dec_lds_bytes_bf16(Mp, D);
     const void* fn = nullptr;
 #define FLARE_DEC_FN(DD, TB)                                                                          \
-    if (D == DD && tb == TB) fn = z_f32 ? dec_kernel<DD, TB, float>() : dec_kernel<DD, TB, uint16_t>();
+    if (D == DD && tb == TB) fn = z_f32 ? dec_kernel<DD, TB, float>(Mp) : dec_kernel<DD, TB, uint16_t>(Mp);
     FLARE_DEC_FN(32, 1)
     FLARE_DEC_FN(32, 2)
     FLARE_DEC_FN(64, 1)
@@ -1164,12 +1182,12 @@ int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32) {
     return n;
 }
 
-int dec_tb_bf16(int D) {
+int dec_tb_bf16(int D, int Mp) {
     // Tuning override (tests and sweeps): 32-token blocks per wave and step
-    // (2 is built for D <= 64 only).
+    // (2 is built for D <= 64 and M <= 256 only).
     if (const char* e = std::getenv("FLARE_TEST_DEC_TB")) {
         const int v = std::atoi(e);
-        if (v == 1 || (v == 2 && D <= 64)) return v;
+        if (v == 1 || (v == 2 && D <= 64 && Mp <= 256)) return v;
     }
     // one block: fewer registers, more resident waves (measured faster on
     // MI355X than two at D = 32, equal or faster at D = 64)

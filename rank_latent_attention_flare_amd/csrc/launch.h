@@ -68,9 +68,11 @@ int enc_tile_tokens_bf16(EncCfg cfg);
 int enc_threads_bf16(EncCfg cfg);
 
 constexpr int kDecWaves = 4;  // waves per decode workgroup
-// Largest M of the bf16 path: its decode unrolls every latent block.
-constexpr int kBf16MaxM = 256;
-int dec_tb_bf16(int D);       // 32-token blocks per wave per step
+// Largest M of the bf16 path: its decode unrolls every latent block. At
+// D = 128 the decode's LDS (Q and Z^T of the head) caps M at 256.
+constexpr int kBf16MaxM = 512;
+constexpr int kBf16MaxM128 = 256;
+int dec_tb_bf16(int D, int Mp);  // 32-token blocks per wave per step
 int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32);  // resident decode workgroups per CU
 int dec_lds_bytes_bf16(int Mp, int D);
 

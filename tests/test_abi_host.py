@@ -66,7 +66,8 @@ def test_sizes_below_one_rejected(field):
         assert call("flare_forward", *a) == INVALID
 
 
-@pytest.mark.parametrize("dt,D,M", [(F.FLARE_BF16, 16, 64), (F.FLARE_BF16, 48, 64), (F.FLARE_BF16, 64, 257),
+@pytest.mark.parametrize("dt,D,M", [(F.FLARE_BF16, 16, 64), (F.FLARE_BF16, 48, 64), (F.FLARE_BF16, 64, 513),
+                                    (F.FLARE_BF16, 32, 600), (F.FLARE_BF16, 128, 257),
                                     (F.FLARE_F32, 12, 8), (F.FLARE_F32, 256, 8), (F.FLARE_F32, 16, 5000)])
 def test_unsupported_shapes(dt, D, M):
     assert call("flare_forward", *fwd_args(D=D, M=M, dt=dt)) == UNSUPPORTED
@@ -169,4 +170,4 @@ def test_attend_validates_before_launch():
     assert fn(None, *args[1:], 0, None) == INVALID and "null" in F.lib().flare_last_error().decode()
     assert fn(PQ, PK, PQ + 256, *args[3:], 0, None) == INVALID  # Y overlaps q
     assert fn(PQ, PK, PY + 8, *args[3:], 0, None) == INVALID    # misaligned
-    assert fn(PQ, PK, PY, 1, 2, 100, 300, 64, F.FLARE_BF16, 0, None) == UNSUPPORTED
+    assert fn(PQ, PK, PY, 1, 2, 100, 600, 64, F.FLARE_BF16, 0, None) == UNSUPPORTED

@@ -44,6 +44,11 @@ SMALL = [
     (1, 2, 777, 33, 128, "bf16"),
     (3, 1, 2049, 128, 32, "bf16"),
     (1, 2, 640, 64, 128, "bf16"),
+    # more than 8 latent blocks (D <= 64): the decode's grouped latent loop,
+    # with and without a padded last block
+    (1, 2, 1500, 300, 64, "bf16"),
+    (1, 1, 1000, 512, 32, "bf16"),
+    (2, 1, 700, 480, 64, "bf16"),
 ]
 
 
