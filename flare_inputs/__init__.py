@@ -57,7 +57,7 @@ class Workload:
         return (self.H, self.M, self.D), (self.B, self.H, self.N, self.D)
 
 
-# Five workloads. Q scales: 0.02*sqrt(D) for the mesh workload (latent init
+# Five headline workloads and one at the largest M. Q scales: 0.02*sqrt(D) for the mesh workload (latent init
 # N(0, 0.02^2) of the FLARE page, step 1, seen through a sqrt(D) head width),
 # 0.5 for the others; K and V are unit Gaussians everywhere.
 WORKLOADS = {
@@ -66,6 +66,9 @@ WORKLOADS = {
     3: Workload("long-seq-4k", 32, 8, 4096, 64, 64, BF16, 0.5, 1.0, "forward", 3),
     4: Workload("large-mesh-1m", 1, 16, 1048576, 256, 64, BF16, 0.5, 1.0, "forward", 4),
     5: Workload("flarepp-262k", 2, 8, 262144, 128, 64, BF16, 0.5, 1.0, "pp_forward", 5),
+    # the top of the FLARE page's latent range ("Key Hyperparameters": M up
+    # to 512): not one of the five headline configurations
+    6: Workload("latents-512", 1, 8, 262144, 512, 64, BF16, 0.5, 1.0, "forward", 6),
 }
 
 
