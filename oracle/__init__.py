@@ -56,6 +56,9 @@ def _load():
                                              _i64p, ctypes.c_int64, _dp, _dp]
         lib.flare_oracle_pp_forward.argtypes = [_dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                 _i64p, ctypes.c_int64, _dp, _dp, _dp]
+        lib.flare_oracle_backward.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                              _dp, _dp, _dp]
+        lib.flare_oracle_backward.restype = ctypes.c_int
         lib.flare_oracle_attend.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
                                             ctypes.c_int64, _dp]
         for f in ("flare_oracle_encode", "flare_oracle_decode", "flare_oracle_forward", "flare_oracle_pp_forward",
@@ -146,6 +149,17 @@ def attend_head(q, Z, rows: Optional[np.ndarray] = None) -> np.ndarray:
     return Y
 
 
+def backward_head(Q, K, V, dY):
+    """(dQ[M,D], dK[N,D], dV[N,D]) of one head's FLARE forward for the upstream gradient dY[N,D]."""
+    Q, K, V, dY = _c64(Q), _c64(K), _c64(V), _c64(dY)
+    N, D = K.shape
+    M = Q.shape[0]
+    dQ, dK, dV = np.empty((M, D)), np.empty((N, D)), np.empty((N, D))
+    _check(_load().flare_oracle_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dY), N, M, D, _ptr(dQ), _ptr(dK),
+                                         _ptr(dV)), "backward")
+    return dQ, dK, dV
+
+
 def pp_forward_head(Q, K, V, rows: Optional[np.ndarray] = None):
     """(Y, Q', Z) of one head for FLARE++."""
     Q, K, V = _c64(Q), _c64(K), _c64(V)
@@ -193,6 +207,22 @@ def attend(q, Z, rows=None, heads=None) -> np.ndarray:
     for b, h in (heads or [(b, h) for b in range(B) for h in range(H)]):
         Y[b, h] = attend_head(widen(q[b, h]), widen(Z[b, h]), rows)
     return Y
+
+
+def backward(Q, K, V, dY):
+    """(dQ[H,M,D], dK[B,H,N,D], dV[B,H,N,D]) of the FLARE forward, fp64. Q is shared over the
+    batch, so dQ sums the batch entries' gradients."""
+    B, H, N, D = K.shape
+    M = Q.shape[-2]
+    dQ = np.zeros((H, M, D))
+    dK = np.empty((B, H, N, D))
+    dV = np.empty((B, H, N, D))
+    for b in range(B):
+        for h in range(H):
+            q, k, v, g = widen(Q[h]), widen(K[b, h]), widen(V[b, h]), widen(dY[b, h])
+            dq, dK[b, h], dV[b, h] = backward_head(q, k, v, g)
+            dQ[h] += dq
+    return dQ, dK, dV
 
 
 def forward(Q, K, V, rows=None, heads=None):

@@ -201,6 +201,100 @@ int flare_oracle_pp_forward(const double* Q, const double* K, const double* V,
     return flare_oracle_forward(Qp_out, K, V, N, M, D, rows, R, Y, Z_out);
 }
 
+/* Gradients of one head's FLARE forward (Y = decode(Q, K, encode(Q, K, V)))
+ * for an upstream gradient dY[N][D]: dQ[M][D], dK[N][D], dV[N][D]. The
+ * forward is the one defined above; the backward is the chain rule through its
+ * two softmaxes, written out in fp64 (no algorithmic shortcut):
+ *   A[m][n] = softmax_n(l[m][.]),  Z = A V,  Bt[n][m] = softmax_m(l[.][n]),
+ *   Y = Bt Z,  l = s Q K^T;
+ *   dZ = Bt^T dY,  dV = A^T dZ,
+ *   dl[m][n] = A[m][n] (<dZ[m], V[n]> - <dZ[m], Z[m]>)
+ *            + Bt[n][m] (<dY[n], Z[m]> - <dY[n], Y[n]>),
+ *   dQ = s dl K,  dK = s dl^T Q.
+ * (The softmax Jacobian: for p = softmax(x) and an upstream g, dx = p (g -
+ * <p, g>); here g is <dZ[m], V[n]> along n for the encode and <dY[n], Z[m]>
+ * along m for the decode, and <p, g> is <dZ[m], Z[m]> and <dY[n], Y[n]>.)
+ * Returns 0, or -1 when scratch memory cannot be allocated. */
+int flare_oracle_backward(const double* Q, const double* K, const double* V, const double* dY,
+                          int64_t N, int64_t M, int64_t D, double* dQ, double* dK, double* dV) {
+    const double s = 1.0 / sqrt((double)D);
+    double* l = (double*)malloc((size_t)M * N * sizeof(double));
+    double* A = (double*)malloc((size_t)M * N * sizeof(double));
+    double* Bt = (double*)malloc((size_t)M * N * sizeof(double));
+    double* Z = (double*)malloc((size_t)M * D * sizeof(double));
+    double* Y = (double*)malloc((size_t)N * D * sizeof(double));
+    double* dZ = (double*)malloc((size_t)M * D * sizeof(double));
+    double* dl = (double*)malloc((size_t)M * N * sizeof(double));
+    int rc = 0;
+    if (!l || !A || !Bt || !Z || !Y || !dZ || !dl) {
+        rc = -1;
+        goto done;
+    }
+    /* forward, keeping the probabilities */
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) l[m * N + n] = s * dot(Q + m * D, K + n * D, D);
+    for (int64_t m = 0; m < M; ++m) { /* encode softmax over n */
+        double mx = -INFINITY, den = 0.0;
+        for (int64_t n = 0; n < N; ++n) mx = fmax(mx, l[m * N + n]);
+        for (int64_t n = 0; n < N; ++n) den += (A[m * N + n] = exp(l[m * N + n] - mx));
+        for (int64_t n = 0; n < N; ++n) A[m * N + n] /= den;
+    }
+    for (int64_t n = 0; n < N; ++n) { /* decode softmax over m */
+        double mx = -INFINITY, den = 0.0;
+        for (int64_t m = 0; m < M; ++m) mx = fmax(mx, l[m * N + n]);
+        for (int64_t m = 0; m < M; ++m) den += (Bt[n * M + m] = exp(l[m * N + n] - mx));
+        for (int64_t m = 0; m < M; ++m) Bt[n * M + m] /= den;
+    }
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t d = 0; d < D; ++d) {
+            double z = 0.0;
+            for (int64_t n = 0; n < N; ++n) z += A[m * N + n] * V[n * D + d];
+            Z[m * D + d] = z;
+        }
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t d = 0; d < D; ++d) {
+            double y = 0.0;
+            for (int64_t m = 0; m < M; ++m) y += Bt[n * M + m] * Z[m * D + d];
+            Y[n * D + d] = y;
+        }
+    /* backward */
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t d = 0; d < D; ++d) {
+            double g = 0.0;
+            for (int64_t n = 0; n < N; ++n) g += Bt[n * M + m] * dY[n * D + d];
+            dZ[m * D + d] = g;
+        }
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t d = 0; d < D; ++d) {
+            double g = 0.0;
+            for (int64_t m = 0; m < M; ++m) g += A[m * N + n] * dZ[m * D + d];
+            dV[n * D + d] = g;
+        }
+    for (int64_t m = 0; m < M; ++m) {
+        const double gz = dot(dZ + m * D, Z + m * D, D);
+        for (int64_t n = 0; n < N; ++n) {
+            const double gy = dot(dY + n * D, Y + n * D, D);
+            dl[m * N + n] = A[m * N + n] * (dot(dZ + m * D, V + n * D, D) - gz) +
+                            Bt[n * M + m] * (dot(dY + n * D, Z + m * D, D) - gy);
+        }
+    }
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t d = 0; d < D; ++d) {
+            double g = 0.0;
+            for (int64_t n = 0; n < N; ++n) g += dl[m * N + n] * K[n * D + d];
+            dQ[m * D + d] = s * g;
+        }
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t d = 0; d < D; ++d) {
+            double g = 0.0;
+            for (int64_t m = 0; m < M; ++m) g += dl[m * N + n] * Q[m * D + d];
+            dK[n * D + d] = s * g;
+        }
+done:
+    free(l); free(A); free(Bt); free(Z); free(Y); free(dZ); free(dl);
+    return rc;
+}
+
 /* Number of OpenMP threads a parallel region uses (1 without OpenMP). */
 int flare_oracle_threads(void) {
 #ifdef _OPENMP

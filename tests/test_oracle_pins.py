@@ -273,3 +273,48 @@ def test_attend_two_latent_closed_form(a, b):
     Z = np.array([[[[a], [b]]]])
     w = np.array([sigmoid((a - b) * x) for x in xs])
     np.testing.assert_allclose(oracle.attend(q, Z)[0, 0, :, 0], w * a + (1 - w) * b, rtol=1e-14, atol=1e-15)
+
+
+# ------------------------------------------------------------------ backward
+def torch_flare_grads(Q, K, V, dY):
+    """Gradients of sum(Y * dY) for Y = FLARE(Q, K, V), by torch fp64 autograd through two SDPA calls
+    (Q shared over the batch)."""
+    q = torch.tensor(Q, dtype=torch.float64, requires_grad=True)
+    k = torch.tensor(K, dtype=torch.float64, requires_grad=True)
+    v = torch.tensor(V, dtype=torch.float64, requires_grad=True)
+    qb = q.unsqueeze(0).expand(k.shape[0], -1, -1, -1)
+    z = F.scaled_dot_product_attention(qb, k, v)
+    y = F.scaled_dot_product_attention(k, qb, z)
+    (y * torch.tensor(dY, dtype=torch.float64)).sum().backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+@pytest.mark.parametrize("B,H,N,M,D", [(2, 2, 37, 5, 8), (1, 1, 70, 33, 16), (1, 1, 1, 1, 4)])
+def test_backward_is_autograd_of_two_sdpa_calls(B, H, N, M, D):
+    Q, K, V, dY = rand(H, M, D), rand(B, H, N, D), rand(B, H, N, D), rand(B, H, N, D)
+    got = oracle.backward(Q, K, V, dY)
+    want = torch_flare_grads(Q, K, V, dY)
+    for g, w, name in zip(got, want, ("dQ", "dK", "dV")):
+        np.testing.assert_allclose(g, w, rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_backward_matches_central_differences_of_the_forward():
+    B, H, N, M, D = 1, 1, 5, 3, 4
+    Q, K, V, dY = rand(H, M, D), rand(B, H, N, D), rand(B, H, N, D), rand(B, H, N, D)
+    dQ, dK, dV = oracle.backward(Q, K, V, dY)
+
+    def f(q, k, v):
+        return float(np.sum(oracle.forward(q, k, v)[0] * dY))
+
+    h = 1e-6
+    for arr, grad in ((Q, dQ), (K, dK), (V, dV)):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            a0 = arr[idx]
+            arr[idx] = a0 + h
+            fp = f(Q, K, V)
+            arr[idx] = a0 - h
+            fm = f(Q, K, V)
+            arr[idx] = a0
+            fd[idx] = (fp - fm) / (2 * h)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-8)
