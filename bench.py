@@ -56,9 +56,10 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", type=int, default=2, help="workload number 1-5 (default 2)")
-    p.add_argument("--variant", choices=["flare", "skill"], default="flare",
+    p.add_argument("--variant", choices=["flare", "skill", "backward"], default="flare",
                    help="flare: the workload's forward (default); skill: the FLARE skill page's layer, "
-                        "flare_encode then flare_attend with separate token queries (forward workloads only)")
+                        "flare_encode then flare_attend with separate token queries; backward: flare_backward "
+                        "(gradients of Q, K, V); the last two on FLARE forward workloads only")
     p.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
                    help="layout of K, V and Y: [B,H,N,D] (default) or token-major [B,N,H,D]")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
@@ -110,10 +111,22 @@ def main():
 
     Q, K, V = dev(Qh), dev(Kh), dev(Vh)
     ws = F.workspace_for(op, Q, K)
-    if args.variant == "skill":
-        if op != F.FLARE_OP_FORWARD:
-            print("--variant skill needs a FLARE forward workload", file=sys.stderr)
+    if args.variant != "flare" and op != F.FLARE_OP_FORWARD:
+        print(f"--variant {args.variant} needs a FLARE forward workload", file=sys.stderr)
+        sys.exit(2)
+    if args.variant == "backward":
+        if args.layout != "bhnd":
+            print("--variant backward takes the [B,H,N,D] layout", file=sys.stderr)
             sys.exit(2)
+        ws = torch.empty(F.flare_workspace_size(F.FLARE_OP_BACKWARD, w.B, w.H, w.N, w.M, w.D, Q.dtype),
+                         dtype=torch.uint8, device=Q.device)
+        dYt = V.flip(2).contiguous()  # upstream gradient: the values in reverse token order
+        grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+
+        def fn(Q, K, V, out=None, workspace=None, stream=None):
+            F.flare_backward(Q, K, V, dYt, stream=stream, workspace=workspace, out=grads)
+            return grads[1]
+    if args.variant == "skill":
         ws = F.workspace_for(F.FLARE_OP_ENCODE, Q, K)
         qtok = V.flip(2).contiguous()  # separate token queries: the values in reverse token order
         Zlat = torch.empty((w.B, w.H, w.M, w.D), dtype=Q.dtype, device=Q.device)
@@ -185,7 +198,8 @@ def main():
         torch.cuda.synchronize()
         kt = F.flare_timing_read()
         F.flare_timing_enable(False)
-    if not torch.isfinite(Y.float()).all():
+    outs = grads if args.variant == "backward" else (Y,)
+    if not all(torch.isfinite(t.float()).all() for t in outs):
         print("non-finite output", file=sys.stderr)
         sys.exit(1)
 
@@ -203,39 +217,54 @@ def main():
                           "share_of_step": ms / total_ms}
     # algorithmic bytes per launch: encode reads K and V; decode reads K and writes Y
     alg_bytes = {"encode_partial": 2 * kv_bytes, "decode": 2 * kv_bytes}
-    if "encode_partial" in kern and "decode" in kern:
-        dominant = max(("encode_partial", "decode"),
-                       key=lambda k: kern[k]["avg_us"] * kern[k]["launches_per_step"])
-        achieved = alg_bytes[dominant] / (kern[dominant]["avg_us"] * 1e-6) / 1e9
-    else:  # no per-kernel events: attribute the step to one kernel (lower bound)
-        dominant = "decode"
-        achieved = alg_bytes[dominant] / (ms_step * 1e-3) / 1e9
-    traffic = None
-    lay = ("" if args.layout == "bhnd" else "_bnhd") + ("" if args.variant == "flare" else "_skill")
-    pmc_path = os.path.join(ROOT, "profiles", f"{dominant}_{w.name}{lay}_pmc.json")
-    if os.path.exists(pmc_path):
-        with open(pmc_path) as f:
-            pmc = json.load(f)
-        if pmc.get("source_hash") == source_hash(dominant):
-            traffic = pmc.get("hbm_bytes_per_launch")
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "alg_bytes_per_launch": alg_bytes[dominant],
-                "mfma_tflops_step": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
-                "mfma_frac_step": round(flops_step / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-                "hbm_frac_step": round((4 if passes == 1 else 6) * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                       4)}
+    if args.variant == "backward":
+        # fp32 VALU work of the backward kernels per (b, h): logits and the dot products and
+        # accumulations of each kernel (stats 6, dZ 4, dK/dV 10, dQ 8) x M*N*D flops
+        bw_flops = 28 * w.B * w.H * w.N * w.M * w.D
+        bw_ms = kt.get("backward", (0.0, 0))[0] / args.steps if kt else ms_step
+        achieved_tf = bw_flops / (bw_ms * 1e-3) / 1e12
+        roofline = {"bound": "alu", "kernel": "backward", "achieved": round(achieved_tf, 2), "peak": 157.3,
+                    "unit": "TFLOP/s", "frac": round(achieved_tf / 157.3, 4), "traffic": None,
+                    "alg_flops_per_step": bw_flops}
+    else:
+        if "encode_partial" in kern and "decode" in kern:
+            dominant = max(("encode_partial", "decode"),
+                           key=lambda k: kern[k]["avg_us"] * kern[k]["launches_per_step"])
+            achieved = alg_bytes[dominant] / (kern[dominant]["avg_us"] * 1e-6) / 1e9
+        else:  # no per-kernel events: attribute the step to one kernel (lower bound)
+            dominant = "decode"
+            achieved = alg_bytes[dominant] / (ms_step * 1e-3) / 1e9
+        traffic = None
+        lay = ("" if args.layout == "bhnd" else "_bnhd") + ("" if args.variant == "flare" else "_" + args.variant)
+        pmc_path = os.path.join(ROOT, "profiles", f"{dominant}_{w.name}{lay}_pmc.json")
+        if os.path.exists(pmc_path):
+            with open(pmc_path) as f:
+                pmc = json.load(f)
+            if pmc.get("source_hash") == source_hash(dominant):
+                traffic = pmc.get("hbm_bytes_per_launch")
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "alg_bytes_per_launch": alg_bytes[dominant],
+                    "mfma_tflops_step": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
+                    "mfma_frac_step": round(flops_step / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "hbm_frac_step": round((4 if passes == 1 else 6) * kv_bytes / (ms_step * 1e-3) / 1e9
+                                           / HBM_PEAK_GBS, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        bw_n = min(w.N, 16384)
         t0 = time.perf_counter()
         done = 0
         for (b, h) in heads:
             q = Qh[h]
             if op == F.FLARE_OP_PP_FORWARD:
                 oracle.pp_forward_head(oracle.widen(q), oracle.widen(Kh[b, h]), oracle.widen(Vh[b, h]))
+            elif args.variant == "backward":
+                # the first bw_n tokens of the head (the fp64 backward keeps N x M matrices)
+                oracle.backward_head(oracle.widen(q), oracle.widen(Kh[b, h, :bw_n]), oracle.widen(Vh[b, h, :bw_n]),
+                                     oracle.widen(Vh[b, h, :bw_n][::-1]))
             elif args.variant == "skill":
                 z = oracle.encode_head(oracle.widen(q), oracle.widen(Kh[b, h]), oracle.widen(Vh[b, h]))
                 oracle.attend_head(oracle.widen(Vh[b, h][::-1]), z)
@@ -247,9 +276,11 @@ def main():
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
         el = time.perf_counter() - t0
-        cpu = {"value": round(done * w.N / el, 1), "unit": "tokens*heads/s", "cores": oracle.threads(),
-               "kind": "oracle", "sample": f"{done} of {len(heads)} heads of {w.name}, full N={w.N}, "
-                                            f"fp64 {w.op if args.variant == 'flare' else 'skill-page layer'}, "
+        ntok = bw_n if args.variant == "backward" else w.N
+        cores = 1 if args.variant == "backward" else oracle.threads()  # the fp64 backward is one loop nest
+        cpu = {"value": round(done * ntok / el, 1), "unit": "tokens*heads/s", "cores": cores,
+               "kind": "oracle", "sample": f"{done} of {len(heads)} heads of {w.name}, N={ntok} of {w.N}, "
+                                            f"fp64 {w.op if args.variant == 'flare' else args.variant}, "
                                             f"{el:.1f} s"}
 
     line = {

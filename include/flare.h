@@ -70,7 +70,13 @@ typedef enum {
     FLARE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } flare_status;
 
-typedef enum { FLARE_OP_ENCODE = 0, FLARE_OP_DECODE = 1, FLARE_OP_FORWARD = 2, FLARE_OP_PP_FORWARD = 3 } flare_op;
+typedef enum {
+    FLARE_OP_ENCODE = 0,
+    FLARE_OP_DECODE = 1,
+    FLARE_OP_FORWARD = 2,
+    FLARE_OP_PP_FORWARD = 3,
+    FLARE_OP_BACKWARD = 4 /* flare_backward (workspace sizing only) */
+} flare_op;
 
 /* Encode: Y := Z[B][H][M][D] = softmax_n(s Q K^T) V for every (b, h).
  * FLARE skill page, "2. Implement Encode Stage"; encode half of step 4.
@@ -168,6 +174,32 @@ flare_status flare_attend(const void* q, const void* Z, void* Y,
                           int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
                           flare_dtype dtype, flare_layout layout, hipStream_t stream);
 
+/* Backward of flare_forward: the gradients of Q, K and V for an upstream
+ * gradient dY of Y. The FLARE pages train their models end to end (FLARE
+ * skill page, "5. Scale to Million-Point Sequences": gradient checkpointing
+ * for long inputs); this is the chain rule through the encode and decode
+ * softmaxes of the operator above (with l = s Q K^T, A = softmax_n(l),
+ * Bt = softmax_m(l)^T, Z = A V, Y = Bt Z):
+ *   dZ = Bt^T dY,  dV = A^T dZ,
+ *   dl[m][n] = A[m][n] (<dZ[m],V[n]> - <dZ[m],Z[m]>)
+ *            + Bt[n][m] (<dY[n],Z[m]> - <dY[n],Y[n]>),
+ *   dQ = s dl K (summed over the batch, Q being shared),  dK = s dl^T Q.
+ * Inputs Q [H][M][D], K, V, dY [B][H][N][D]; outputs dQ [H][M][D], dK, dV
+ * [B][H][N][D], in the operator dtype (arithmetic in fp32). It recomputes
+ * the forward's encode internally; nothing N x M is stored. Supported for
+ * D in {8, 16, 24, 32, 48, 64} (bf16: 32 and 64) with the forward's M range;
+ * otherwise FLARE_ERR_UNSUPPORTED. Outputs may not overlap inputs or each
+ * other. The _ws variant takes flare_workspace_size(FLARE_OP_BACKWARD, ...)
+ * bytes of caller-owned scratch memory. FLARE++ has no backward here. */
+flare_status flare_backward(const void* Q, const void* K, const void* V, const void* dY,
+                            void* dQ, void* dK, void* dV,
+                            int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                            flare_dtype dtype, hipStream_t stream);
+flare_status flare_backward_ws(const void* Q, const void* K, const void* V, const void* dY,
+                               void* dQ, void* dK, void* dV,
+                               int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                               flare_dtype dtype, hipStream_t stream, void* workspace, size_t ws_bytes);
+
 /* Static text for a status code. */
 const char* flare_status_string(flare_status s);
 
@@ -178,8 +210,8 @@ const char* flare_last_error(void);
 /* ---------------------------------------------------------- measurement
  * Kernel timing with HIP events recorded on the launch stream around every
  * kernel the library enqueues. Kernel kinds: 0 = encode partial (split-N
- * online softmax), 1 = combine, 2 = decode. */
-#define FLARE_KERNEL_KINDS 3
+ * online softmax), 1 = combine, 2 = decode, 3 = backward kernels. */
+#define FLARE_KERNEL_KINDS 4
 
 /* Turn event recording on (1) or off (0) for the calling process, and drop
  * every recorded event. */

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libflare.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["flare.cpp", "kernels_common.hip", "kernels_bf16.hip"]
+SOURCES = ["flare.cpp", "kernels_common.hip", "kernels_bf16.hip", "kernels_backward.hip"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-mfma-vgpr-form",

@@ -53,7 +53,8 @@ struct Plan {
     int C, chunk_len;  // encode split over N
     int G;             // decode workgroups per (b, h)
     size_t esize;
-    size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[4];
+    size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[5];
+    size_t off_zsig, off_nu, off_tau, off_del, off_dz, off_gam;  // backward
     float c;
     int64_t sb, sh, sn;  // element strides of K, V and Y: batch, head, token
 };
@@ -167,6 +168,18 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     p->total[FLARE_OP_DECODE] = 0;
     p->total[FLARE_OP_FORWARD] = fwd_total;
     p->total[FLARE_OP_PP_FORWARD] = off;
+    // backward: the forward's sections (encode partials, reused for the dZ and
+    // dQ partials; Z and mu*), then sig*, the per-token decode statistics, dZ
+    // and gam
+    const size_t tok = size_t(p->BH) * size_t(N) * 4, lat = size_t(p->BH) * size_t(M) * 4;
+    off = fwd_total;
+    p->off_zsig = off; off = align256(off + lat);
+    p->off_nu = off;   off = align256(off + tok);
+    p->off_tau = off;  off = align256(off + tok);
+    p->off_del = off;  off = align256(off + tok);
+    p->off_dz = off;   off = align256(off + lat * size_t(D));
+    p->off_gam = off;  off = align256(off + lat);
+    p->total[FLARE_OP_BACKWARD] = off;
     return FLARE_OK;
 }
 
@@ -257,7 +270,7 @@ hipError_t run_encode_partial(const Plan& p, const void* Q, int64_t q_bstride, c
 }
 
 hipError_t run_combine(const Plan& p, int mode, const void* Q, void* out, char* ws, hipStream_t s,
-                       float* zmu = nullptr) {
+                       float* zmu = nullptr, float* zsig = nullptr) {
     CombineArgs a{};
     a.in.acc = (float*)(ws + p.off_acc);
     a.in.mu = (float*)(ws + p.off_mu);
@@ -268,6 +281,7 @@ hipError_t run_combine(const Plan& p, int mode, const void* Q, void* out, char* 
     a.Q = Q;
     a.out = out;
     a.zmu = zmu;
+    a.zsig = zsig;
     return timed(1, s, [&] { return flare::launch_combine(a, s); });
 }
 
@@ -422,7 +436,7 @@ flare_status flare_pp_forward(const void* Q, const void* K, const void* V, void*
 }
 
 size_t flare_workspace_size(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype) {
-    if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_FORWARD) return 0;
+    if (op < FLARE_OP_ENCODE || op > FLARE_OP_BACKWARD) return 0;
     Plan p;
     if (make_plan(B, H, N, M, D, dtype, &p) != FLARE_OK) return 0;
     return p.total[op];
@@ -444,6 +458,102 @@ flare_status flare_pp_forward_ws(const void* Q, const void* K, const void* V, vo
                                  int64_t N, int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws,
                                  size_t n) {
     return exec(FLARE_OP_PP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, ws, n);
+}
+
+}  // extern "C"
+
+namespace {
+
+flare_status backward(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK, void* dV,
+                      int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dt, hipStream_t s,
+                      void* wsv, size_t ws_bytes, bool alloc) {
+    Plan p;
+    g_last_error.clear();
+    flare_status st = make_plan(B, H, N, M, D, dt, &p);
+    if (st != FLARE_OK) return st;
+    st = set_layout(&p, FLARE_LAYOUT_BHND);
+    if (st != FLARE_OK) return st;
+    if (!flare::backward_supports(int(D)))
+        return fail(FLARE_ERR_UNSUPPORTED, "the backward supports D in {8, 16, 24, 32, 48, 64}");
+    const void* ins[4] = {Q, K, V, dY};
+    void* outs[3] = {dQ, dK, dV};
+    for (const void* t : ins)
+        if (!t) return fail(FLARE_ERR_INVALID_ARG, "null tensor pointer");
+    for (void* t : outs)
+        if (!t) return fail(FLARE_ERR_INVALID_ARG, "null tensor pointer");
+    for (const void* t : {Q, K, V, dY, (const void*)dQ, (const void*)dK, (const void*)dV})
+        if (uintptr_t(t) % 16 != 0) return fail(FLARE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const size_t nq = size_t(p.H) * p.M * p.D * p.esize, nt = size_t(p.BH) * p.N * p.D * p.esize;
+    const size_t nin[4] = {nq, nt, nt, nt}, nout[3] = {nq, nt, nt};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(outs[i], nout[i], ins[j], nin[j])) return fail(FLARE_ERR_INVALID_ARG, "output overlaps an input");
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], nout[i], outs[j], nout[j])) return fail(FLARE_ERR_INVALID_ARG, "outputs overlap");
+    }
+    const size_t need = p.total[FLARE_OP_BACKWARD];
+    if (alloc) {
+        const char* f = std::getenv("FLARE_TEST_FAIL_ALLOC");
+        if (f && std::strcmp(f, "1") == 0) return fail(FLARE_ERR_NO_MEMORY, "allocation failure injected by FLARE_TEST_FAIL_ALLOC");
+        hipError_t e = hipMallocAsync(&wsv, need, s);
+        if (e != hipSuccess || !wsv) return fail(FLARE_ERR_NO_MEMORY, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+    } else {
+        if (!wsv) return fail(FLARE_ERR_INVALID_ARG, "workspace pointer is null");
+        if (uintptr_t(wsv) % 256 != 0) return fail(FLARE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(FLARE_ERR_INVALID_ARG,
+                        "workspace too small: need " + std::to_string(need) + " bytes, got " + std::to_string(ws_bytes));
+    }
+    char* ws = (char*)wsv;
+    // forward encode and combine: Z, mu* and sig*
+    hipError_t e = run_encode_partial(p, Q, 0, K, V, ws, s);
+    if (e == hipSuccess)
+        e = run_combine(p, flare::COMBINE_Z_F32, Q, ws + p.off_z, ws, s, (float*)(ws + p.off_zmu),
+                        (float*)(ws + p.off_zsig));
+    flare::BackwardArgs a{};
+    a.Q = Q; a.K = K; a.V = V; a.dY = dY; a.dQ = dQ; a.dK = dK; a.dV = dV;
+    a.Z = (const float*)(ws + p.off_z);
+    a.zmu = (const float*)(ws + p.off_zmu);
+    a.zsig = (const float*)(ws + p.off_zsig);
+    a.nu = (float*)(ws + p.off_nu);
+    a.tau = (float*)(ws + p.off_tau);
+    a.del = (float*)(ws + p.off_del);
+    a.dZ = (float*)(ws + p.off_dz);
+    a.gam = (float*)(ws + p.off_gam);
+    a.part = (float*)(ws + p.off_acc);
+    a.BH = p.BH; a.H = int(p.H); a.N = int(p.N); a.M = int(p.M); a.D = int(p.D);
+    a.C = p.C; a.chunk_len = p.chunk_len;
+    a.s = float(1.0 / std::sqrt(double(D)));
+    a.c = p.c;
+    a.bf16 = dt == FLARE_BF16;
+    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_stats(a, s); });
+    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz(a, s); });
+    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(a, s); });
+    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dkdv(a, s); });
+    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq(a, s); });
+    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(a, s); });
+    flare_status res = e == hipSuccess ? FLARE_OK : hip_fail(e, "kernel launch");
+    if (alloc) {
+        hipError_t f = hipFreeAsync(wsv, s);
+        if (f != hipSuccess && res == FLARE_OK) return hip_fail(f, "hipFreeAsync");
+    }
+    return res;
+}
+
+}  // namespace
+
+extern "C" {
+
+flare_status flare_backward(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK,
+                            void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
+                            hipStream_t stream) {
+    return backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, stream, nullptr, 0, true);
+}
+
+flare_status flare_backward_ws(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK,
+                               void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
+                               hipStream_t stream, void* workspace, size_t ws_bytes) {
+    return backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, stream, workspace, ws_bytes, false);
 }
 
 flare_status flare_attend(const void* q, const void* Z, void* Y, int64_t B, int64_t H, int64_t N, int64_t M,

@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     for (int e = 0; e < 4; ++e) z[e] = num[e] / den;
     const int64_t o = (int64_t)bh * a.M * D + (int64_t)m * D + d;
     if (a.zmu && d == 0) a.zmu[(int64_t)bh * a.M + m] = mx;
+    if (a.zsig && d == 0) a.zsig[(int64_t)bh * a.M + m] = den;
     if (a.mode == COMBINE_Z_F32 || (a.mode == COMBINE_Z_DTYPE && !a.bf16)) {
         *(f32x4c*)((float*)a.out + o) = z;
     } else if (a.mode == COMBINE_Z_DTYPE) {

@@ -41,6 +41,32 @@ struct CombineArgs {
     const void* Q;       // mode 2: learned queries [H][M][D]
     void* out;
     float* zmu;          // optional [BH][M]: merged offsets mu* (log2 units) per latent
+    float* zsig;         // optional [BH][M]: merged sums sig* against mu*
+};
+
+// Backward of the FLARE forward ([B][H][N][D] layout). Storage of Q, K, V,
+// dY, dQ, dK, dV is the operator dtype; everything else is fp32 workspace.
+struct BackwardArgs {
+    const void* Q;       // [H][M][D]
+    const void* K;       // [B][H][N][D]
+    const void* V;
+    const void* dY;
+    void* dQ;            // [H][M][D]
+    void* dK;            // [B][H][N][D]
+    void* dV;
+    const float* Z;      // [BH][M][D] forward encode output
+    const float* zmu;    // [BH][M] its offsets mu* (log2 units)
+    const float* zsig;   // [BH][M] and sums sig*
+    float* nu;           // [BH][N] decode softmax maximum per token (log2 units)
+    float* tau;          // [BH][N] and sum against it
+    float* del;          // [BH][N] <dY, Y> per token
+    float* dZ;           // [BH][M][D]
+    float* gam;          // [BH][M] <dZ, Z> per latent
+    float* part;         // [BH][C][M][D] per-chunk partial sums (dZ, then dQ)
+    int BH, H, N, M, D;
+    int C, chunk_len;    // token chunks of the latent kernels
+    float s, c;          // 1/sqrt(D) and s * log2(e)
+    bool bf16;
 };
 
 struct DecodeArgs {
@@ -83,5 +109,13 @@ hipError_t launch_encode_f32(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+bool backward_supports(int D);
+hipError_t launch_bw_stats(const BackwardArgs& a, hipStream_t s);
+hipError_t launch_bw_dz(const BackwardArgs& a, hipStream_t s);
+hipError_t launch_bw_dz_combine(const BackwardArgs& a, hipStream_t s);
+hipError_t launch_bw_dkdv(const BackwardArgs& a, hipStream_t s);
+hipError_t launch_bw_dq(const BackwardArgs& a, hipStream_t s);
+hipError_t launch_bw_dq_combine(const BackwardArgs& a, hipStream_t s);
 
 }  // namespace flare

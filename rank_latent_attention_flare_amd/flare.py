@@ -16,10 +16,10 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflare.so")
 
 FLARE_F32, FLARE_BF16 = 0, 1
-FLARE_OP_ENCODE, FLARE_OP_DECODE, FLARE_OP_FORWARD, FLARE_OP_PP_FORWARD = 0, 1, 2, 3
+FLARE_OP_ENCODE, FLARE_OP_DECODE, FLARE_OP_FORWARD, FLARE_OP_PP_FORWARD, FLARE_OP_BACKWARD = 0, 1, 2, 3, 4
 FLARE_LAYOUT_BHND, FLARE_LAYOUT_BNHD = 0, 1
-FLARE_KERNEL_KINDS = 3
-KERNEL_KIND_NAMES = ("encode_partial", "combine", "decode")
+FLARE_KERNEL_KINDS = 4
+KERNEL_KIND_NAMES = ("encode_partial", "combine", "decode", "backward")
 
 STATUS = {0: "FLARE_OK", 1: "FLARE_ERR_INVALID_ARG", 2: "FLARE_ERR_UNSUPPORTED", 3: "FLARE_ERR_NO_MEMORY",
           4: "FLARE_ERR_HIP"}
@@ -53,6 +53,11 @@ def lib() -> ctypes.CDLL:
             getattr(L, name + "_ws").restype = ctypes.c_int
             getattr(L, name + "_ex").argtypes = base[:10] + [ctypes.c_int, _vp, _vp, ctypes.c_size_t]
             getattr(L, name + "_ex").restype = ctypes.c_int
+        bw = [_vp] * 7 + [_i64] * 5 + [ctypes.c_int, _vp]
+        L.flare_backward.argtypes = bw
+        L.flare_backward.restype = ctypes.c_int
+        L.flare_backward_ws.argtypes = bw + [_vp, ctypes.c_size_t]
+        L.flare_backward_ws.restype = ctypes.c_int
         L.flare_attend.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
         L.flare_attend.restype = ctypes.c_int
         L.flare_workspace_size.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
@@ -224,6 +229,23 @@ def flare_attend(q, Z, layout=FLARE_LAYOUT_BHND, out=None, stream=None) -> torch
     _raise(lib().flare_attend(q.data_ptr(), Z.data_ptr(), out.data_ptr(), B, H, N, M, D, dtype_code(q.dtype),
                               layout, _stream(stream)))
     return out
+
+
+def flare_backward(Q, K, V, dY, stream=None, workspace=None, out=None):
+    """(dQ [H, M, D], dK, dV [B, H, N, D]): gradients of the FLARE forward for the upstream gradient dY."""
+    B, H, N, M, D = _dims(FLARE_OP_FORWARD, Q, K, V)
+    if tuple(dY.shape) != (B, H, N, D) or dY.dtype != Q.dtype or not dY.is_contiguous() or not dY.is_cuda:
+        raise ValueError(f"dY must be a contiguous {Q.dtype} device tensor of shape {(B, H, N, D)}")
+    if out is None:
+        out = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    dQ, dK, dV = out
+    args = [Q.data_ptr(), K.data_ptr(), V.data_ptr(), dY.data_ptr(), dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(),
+            B, H, N, M, D, dtype_code(Q.dtype), _stream(stream)]
+    if workspace is None:
+        _raise(lib().flare_backward(*args))
+    else:
+        _raise(lib().flare_backward_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size()))
+    return dQ, dK, dV
 
 
 def flare_workspace_size(op: int, B: int, H: int, N: int, M: int, D: int, dtype: torch.dtype) -> int:

@@ -1,0 +1,100 @@
+"""GPU parity of flare_backward (gradients of the FLARE forward) against the
+fp64 oracle's backward, which is pinned to torch fp64 autograd and to central
+differences of the oracle forward.
+
+Bars. fp32 storage: the kernels work in fp32 and sum in a different order
+than the oracle; the gradients contain differences of nearly equal terms
+(<dZ, V> - <dZ, Z>), so the bar is relative to the largest gradient entry:
+max |gpu - oracle| <= 1e-4 * max |oracle| per tensor. bf16 storage: inputs,
+outputs and the forward's probabilities are bf16, as in the forward's bar:
+rel-L2 <= 1e-2 and max |gpu - oracle| <= 2e-2 * max |oracle| per tensor.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flare_inputs import WORKLOADS, make_inputs, workload_inputs
+from rank_latent_attention_flare_amd import flare as F
+from tests.gpu_util import errors, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, H, N, M, D, dtype
+    (1, 2, 300, 40, 32, "f32"),
+    (2, 2, 500, 17, 16, "f32"),
+    (1, 3, 2049, 64, 8, "f32"),
+    (2, 3, 1000, 64, 64, "bf16"),
+    (1, 2, 777, 33, 32, "bf16"),
+    (1, 2, 4097, 100, 64, "bf16"),
+    (1, 1, 1, 1, 32, "bf16"),
+    (1, 1, 3000, 300, 32, "bf16"),
+]
+
+
+def case_id(c):
+    return "B{}H{}N{}M{}D{}-{}".format(*c)
+
+
+def check_one(g, w, dt, what):
+    e = errors(to_host64(g), w)
+    print(f"[backward] {what} {e}", flush=True)
+    assert e["finite"], f"{what}: non-finite"
+    if dt == "f32":
+        assert e["rel_max"] <= 1e-4, f"{what}: {e}"
+    else:
+        assert e["rel_l2"] <= 1e-2 and e["rel_max"] <= 2e-2, f"{what}: {e}"
+
+
+def check(got, want, dt, what):
+    for g, w, name in zip(got, want, ("dQ", "dK", "dV")):
+        check_one(g, w, dt, f"{what} {name}")
+
+
+@pytest.mark.parametrize("case", CASES, ids=case_id)
+def test_backward_matches_oracle(case):
+    B, H, N, M, D, dt = case
+    seed = zlib.crc32(repr(("backward",) + case).encode()) % 100000
+    Q, K, V = make_inputs(B, H, N, M, D, dt, q_scale=0.5, seed=seed)
+    dY = make_inputs(B, H, N, M, D, dt, seed=seed + 1)[2]
+    print(f"[backward] case={case_id(case)} seed={seed}", flush=True)
+    got = F.flare_backward(to_dev(Q), to_dev(K), to_dev(V), to_dev(dY))
+    torch.cuda.synchronize()
+    check(got, oracle.backward(Q, K, V, dY), dt, case_id(case))
+
+
+def test_backward_workspace_variant_is_identical():
+    B, H, N, M, D, dt = 2, 2, 900, 64, 32, "bf16"
+    Q, K, V = make_inputs(B, H, N, M, D, dt, q_scale=0.5, seed=11)
+    dY = make_inputs(B, H, N, M, D, dt, seed=12)[2]
+    q, k, v, g = to_dev(Q), to_dev(K), to_dev(V), to_dev(dY)
+    a = F.flare_backward(q, k, v, g)
+    ws = torch.empty(F.flare_workspace_size(F.FLARE_OP_BACKWARD, B, H, N, M, D, q.dtype), dtype=torch.uint8,
+                     device="cuda")
+    b = F.flare_backward(q, k, v, g, workspace=ws)
+    c = F.flare_backward(q, k, v, g, workspace=ws)
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, c):
+        assert torch.equal(x, y) and torch.equal(y, z)
+
+
+def test_backward_full_size_one_head_group():
+    # the 65k-mesh workload: every gradient of head 0 (dQ[0] sums its four
+    # batch entries) against the oracle
+    w = WORKLOADS[2]
+    Qh, Kh, Vh = workload_inputs(w)
+    dY = make_inputs(w.B, w.H, w.N, w.M, w.D, w.dtype, seed=99)[2]
+    print(f"[backward] full size {w.name}", flush=True)
+    dQ, dK, dV = F.flare_backward(to_dev(Qh), to_dev(Kh), to_dev(Vh), to_dev(dY))
+    torch.cuda.synchronize()
+    dq_ref = np.zeros((w.M, w.D))
+    for b in range(w.B):
+        dq, dk, dv = oracle.backward_head(oracle.widen(Qh[0]), oracle.widen(Kh[b, 0]), oracle.widen(Vh[b, 0]),
+                                          oracle.widen(dY[b, 0]))
+        dq_ref += dq
+        check_one(dK[b, 0], dk, "bf16", f"{w.name} dK b={b}")
+        check_one(dV[b, 0], dv, "bf16", f"{w.name} dV b={b}")
+    check_one(dQ[0], dq_ref, "bf16", f"{w.name} dQ")
