@@ -117,5 +117,10 @@ hipError_t launch_bw_dz_combine(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_bw_dkdv(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_bw_dq(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_bw_dq_combine(const BackwardArgs& a, hipStream_t s);
+// matrix-core versions of bw_stats and bw_dkdv (bf16, D in {32, 64}, Q, Z and
+// dZ of a head in at most 96 KB of LDS)
+bool bw_bf16_fits(int M, int D);
+hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s);
+hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s);
 
 }  // namespace flare
