@@ -218,13 +218,17 @@ def main():
     # algorithmic bytes per launch: encode reads K and V; decode reads K and writes Y
     alg_bytes = {"encode_partial": 2 * kv_bytes, "decode": 2 * kv_bytes}
     if args.variant == "backward":
-        # fp32 VALU work of the backward kernels per (b, h): logits and the dot products and
-        # accumulations of each kernel (stats 6, dZ 4, dK/dV 10, dQ 8) x M*N*D flops
+        # contraction work of the backward kernels per (b, h): logits and the products and
+        # accumulations of each kernel (stats 6, dZ 4, dK/dV 10, dQ 8) x M*N*D flops; on the
+        # bf16 matrix core for bf16 heads whose Q, Z and dZ fit in LDS (D = 32, or D = 64 with
+        # M <= 256), else fp32 VALU
         bw_flops = 28 * w.B * w.H * w.N * w.M * w.D
         bw_ms = kt.get("backward", (0.0, 0))[0] / args.steps if kt else ms_step
         achieved_tf = bw_flops / (bw_ms * 1e-3) / 1e12
-        roofline = {"bound": "alu", "kernel": "backward", "achieved": round(achieved_tf, 2), "peak": 157.3,
-                    "unit": "TFLOP/s", "frac": round(achieved_tf / 157.3, 4), "traffic": None,
+        on_mfma = w.dtype == "bf16" and (w.D == 32 or (w.D == 64 and w.M <= 256))
+        peak = BF16_MFMA_PEAK_TFLOPS if on_mfma else 157.3
+        roofline = {"bound": "mfma" if on_mfma else "alu", "kernel": "backward", "achieved": round(achieved_tf, 2),
+                    "peak": peak, "unit": "TFLOP/s", "frac": round(achieved_tf / peak, 4), "traffic": None,
                     "alg_flops_per_step": bw_flops}
     else:
         if "encode_partial" in kern and "decode" in kern:

@@ -531,11 +531,13 @@ flare_status backward(const void* Q, const void* K, const void* V, const void* d
     const bool mc = dt == FLARE_BF16 && flare::bw_bf16_fits(int(M), int(D));
     if (e == hipSuccess)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_stats_bf16(a, s) : flare::launch_bw_stats(a, s); });
-    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz(a, s); });
+    if (e == hipSuccess)
+        e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, false, s) : flare::launch_bw_dz(a, s); });
     if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(a, s); });
     if (e == hipSuccess)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_dkdv_bf16(a, s) : flare::launch_bw_dkdv(a, s); });
-    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq(a, s); });
+    if (e == hipSuccess)
+        e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, true, s) : flare::launch_bw_dq(a, s); });
     if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(a, s); });
     flare_status res = e == hipSuccess ? FLARE_OK : hip_fail(e, "kernel launch");
     if (alloc) {

@@ -1296,6 +1296,160 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
     }
 }
 
+// Latent-side backward products, split over token chunks like the encode:
+//   DQ = false: dZ[m]  = sum_n Bt[n][m] dY[n]
+//   DQ = true:  dQ[m]  = s sum_n dl[m][n] K[n]
+// Grid (chunks C, B*H); the 4 waves share the chunk's tokens and split the
+// latent blocks (wave w owns blocks w, w + 4, ...). Per 32-token sub-block a
+// wave loads the token rows straight into MFMA A operands in enc_row_token
+// order (rows = tokens of S^T = K Q^T), so registers 8 kp .. 8 kp + 7 of a lane
+// hold tokens 16 kp + 8 hi + 0..7: the k-slots of the accumulation's B
+// operand. The accumulation's A operand (dY^T or K^T) comes from a transposed
+// read of the same rows, which the wave also writes to its own LDS tile in
+// natural order. Per-chunk partials go to a.part [BH][C][M][D].
+template <int D, bool DQ, int MBW>  // MBW: latent blocks per wave at most
+__global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
+    constexpr int KB = D / 16, DB = D / 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5, l32 = lane & 31;
+    const int chunk = blockIdx.x, bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
+    const int N = a.N, M = a.M, Mp = (M + 31) & ~31, MB = Mp / 32;
+    const int n0 = chunk * a.chunk_len, n1 = min(N, n0 + a.chunk_len);
+    const float c = a.c;
+    unsigned char* qs = bsm;
+    unsigned char* zs = qs + Mp * 2 * D;                 // DQ only
+    unsigned char* dzs = zs + (DQ ? Mp * 2 * D : 0);     // DQ only
+    unsigned char* tt = dzs + (DQ ? Mp * 2 * D : 0) + wave * 32 * 2 * D;  // this wave's token rows
+    stage_rows<D>(qs, (const uint16_t*)a.Q + (int64_t)h * M * D, M, Mp, tid, 256);
+    if constexpr (DQ) {
+        stage_rows<D>(zs, a.Z + (int64_t)bh * M * D, M, Mp, tid, 256);
+        stage_rows<D>(dzs, a.dZ + (int64_t)bh * M * D, M, Mp, tid, 256);
+    }
+    __syncthreads();
+    const int nmb = MB > wave ? (MB - wave + 3) / 4 : 0;  // this wave's latent blocks
+    // per latent (lane column) of each owned block: lambda = mu* + log2 sig*
+    // (+inf for padding) and gam
+    float lam[MBW], gm[MBW];
+    f32x16 acc[MBW][DB];
+#pragma unroll
+    for (int j = 0; j < MBW; ++j) {
+        const int m = 32 * (wave + 4 * j) + l32;
+        const int64_t r = (int64_t)bh * M + min(m, M - 1);
+        lam[j] = (DQ && m < M) ? a.zmu[r] + __log2f(a.zsig[r]) : INFINITY;
+        gm[j] = (DQ && m < M) ? a.gam[r] : 0.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[j][db] = f32x16{};
+    }
+    const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
+    const uint16_t* Vb = (const uint16_t*)a.V + (int64_t)bh * N * D;
+    const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
+    const float* nub = a.nu + (int64_t)bh * N;
+    const float* delb = a.del + (int64_t)bh * N;
+    const int prow = enc_row_token(l32);
+    const int g = lane >> 4, gi = lane & 15;
+    for (int t0 = n0; t0 < n1; t0 += 32) {
+        const int nv = n1 - t0;  // valid tokens in this sub-block (>= 1)
+        const int tn = t0 + min(prow, nv - 1);
+        bf16x8 kA[KB], gA[KB], vA[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int64_t o = (int64_t)tn * D + 16 * kb + 8 * hi;
+            kA[kb] = *(const bf16x8*)(Kb + o);
+            gA[kb] = *(const bf16x8*)(Gb + o);
+            if constexpr (DQ) vA[kb] = *(const bf16x8*)(Vb + o);
+        }
+        // the accumulation's source rows (K for dQ, dY for dZ) in natural
+        // order into this wave's tile; rows past the chunk are zero, so their
+        // (finite) weights add nothing
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            *(bf16x8*)(tt + tile_off<D>(prow, 2 * kb + hi)) = prow < nv ? (DQ ? kA[kb] : gA[kb]) : zero8();
+        // per token (register i: token 16 (i/8) + 8 hi + i%8): nu' and del
+        float nur[16], der[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int tk = 16 * (i >> 3) + 8 * hi + (i & 7);
+            const int tc = t0 + min(tk, nv - 1);
+            nur[i] = tk < nv ? nub[tc] : INFINITY;  // +inf: no weight for tokens past the chunk
+            der[i] = DQ ? delb[tc] : 0.0f;
+        }
+        // the transposed operands of this sub-block (same for every latent block)
+        auto taddr = [&](int kp, int db, int second) {
+            const int row = 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
+            const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+            return tt + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+        };
+        bf16x8 tA[2][DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            lds_tr_op2(taddr(0, db, 0), taddr(0, db, 1), taddr(1, db, 0), taddr(1, db, 1), tA[0][db], tA[1][db]);
+#pragma unroll
+        for (int j = 0; j < MBW; ++j) {
+            if (j >= nmb) break;
+            const int mb = wave + 4 * j;
+            bf16x8 qB[KB], zB[KB], dzB[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int off = tile_off<D>(32 * mb + l32, 2 * kb + hi);
+                qB[kb] = *(const bf16x8*)(qs + off);
+                if constexpr (DQ) {
+                    zB[kb] = *(const bf16x8*)(zs + off);
+                    dzB[kb] = *(const bf16x8*)(dzs + off);
+                }
+            }
+            f32x16 S = mfma(kA[0], qB[0], f32x16{});
+#pragma unroll
+            for (int kb = 1; kb < KB; ++kb) S = mfma(kA[kb], qB[kb], S);
+            f32x16 GY, GV;
+            if constexpr (DQ) {
+                GY = mfma(gA[0], zB[0], f32x16{});
+                GV = mfma(vA[0], dzB[0], f32x16{});
+#pragma unroll
+                for (int kb = 1; kb < KB; ++kb) {
+                    GY = mfma(gA[kb], zB[kb], GY);
+                    GV = mfma(vA[kb], dzB[kb], GV);
+                }
+            }
+            bf16x8 pw[2];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                // decode weight Bt[n][m] (0 past the chunk); clamp: padded
+                // latents (zero rows) stay finite
+                const float p_d = exp2_fast(fminf(fmaf(S[i], c, -nur[i]), 0.0f));
+                float w = p_d;
+                if constexpr (DQ) {
+                    const float p_e = exp2_fast(fmaf(S[i], c, -lam[j]));
+                    w = p_e * (GV[i] - gm[j]) + p_d * (GY[i] - der[i]);
+                }
+                pw[i >> 3][i & 7] = (__bf16)w;
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                acc[j][db] = mfma(tA[0][db], pw[0], acc[j][db]);
+                acc[j][db] = mfma(tA[1][db], pw[1], acc[j][db]);
+            }
+        }
+    }
+    // acc[j][db] register r: d = 32 db + 8 (r/4) + 4 hi + r%4, latent column l32
+    const float scale = DQ ? a.s : 1.0f;
+#pragma unroll
+    for (int j = 0; j < MBW; ++j) {
+        if (j >= nmb) break;
+        const int m = 32 * (wave + 4 * j) + l32;
+        if (m < M) {
+            float* dst = a.part + (((int64_t)bh * gridDim.x + chunk) * M + m) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x4 v = {scale * acc[j][db][4 * g4], scale * acc[j][db][4 * g4 + 1],
+                                     scale * acc[j][db][4 * g4 + 2], scale * acc[j][db][4 * g4 + 3]};
+                    *(f32x4*)(dst + 32 * db + 8 * g4 + 4 * hi) = v;
+                }
+        }
+    }
+}
+
 template <int D, int MBW, int WM, int WT>
 hipError_t launch_enc(const EncodeArgs& a, hipStream_t s) {
     dim3 grid(a.C, a.BH), block(64 * WM * WT);
@@ -1435,8 +1589,10 @@ int dec_tb_bf16(int D, int Mp) {
 int dec_lds_bytes_bf16(int Mp, int D) { return Mp * 2 * D + D * (2 * Mp + 16) + 64; }
 
 bool bw_bf16_fits(int M, int D) {
+    // Q, Z and dZ of the head (and small per-latent or per-wave buffers) in
+    // one CU's LDS; at D = 64 up to M = 256
     const int Mp = (M + 31) / 32 * 32;
-    return (D == 32 || D == 64) && 3 * Mp * 2 * D + 8 * Mp <= 98304;
+    return (D == 32 || (D == 64 && Mp <= 256)) && 3 * Mp * 2 * D + 4 * 32 * 2 * D + 8 * Mp <= 163840;
 }
 
 namespace {
@@ -1458,6 +1614,26 @@ hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s) {
     const int Mp = (a.M + 31) / 32 * 32, lds = 2 * Mp * 2 * a.D;
     if (a.D == 32) return launch_bw_tok(bw_stats_bf16<32>, a, lds, s);
     if (a.D == 64) return launch_bw_tok(bw_stats_bf16<64>, a, lds, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
+    const int Mp = (a.M + 31) / 32 * 32;
+    const int lds = (dq ? 3 : 1) * Mp * 2 * a.D + 4 * 32 * 2 * a.D;
+    auto go = [&](auto fn) -> hipError_t {
+        if (lds > 65536) {
+            hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(fn, dim3(a.C, a.BH), dim3(256), lds, s, a);
+        return hipGetLastError();
+    };
+    const bool wide = Mp > 256;  // more than 2 latent blocks per wave
+    if (a.D == 32) {
+        if (wide) return dq ? go(bw_lat_bf16<32, true, 4>) : go(bw_lat_bf16<32, false, 4>);
+        return dq ? go(bw_lat_bf16<32, true, 2>) : go(bw_lat_bf16<32, false, 2>);
+    }
+    if (a.D == 64 && !wide) return dq ? go(bw_lat_bf16<64, true, 2>) : go(bw_lat_bf16<64, false, 2>);
     return hipErrorInvalidValue;
 }
 

@@ -122,5 +122,6 @@ hipError_t launch_bw_dq_combine(const BackwardArgs& a, hipStream_t s);
 bool bw_bf16_fits(int M, int D);
 hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s);
+hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s);  // dZ (dq false) or dQ partials
 
 }  // namespace flare
