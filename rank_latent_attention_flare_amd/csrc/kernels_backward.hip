@@ -201,20 +201,25 @@ __global__ __launch_bounds__(256) void bw_latent(BackwardArgs a) {
 }
 
 // dZ = sum over chunks of the partials, and gam[m] = <dZ[m], Z[m]>.
-// One thread per (b, h, m).
+// One wave per (b, h, m): lane d sums the chunks of column d (all chunks'
+// loads in flight together), then the wave reduces gam.
 __global__ __launch_bounds__(256) void bw_dz_combine(BackwardArgs a) {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;  // bh * M + m
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // bh * M + m
+    const int d = threadIdx.x & 63;
     if (r >= (int64_t)a.BH * a.M) return;
     const int bh = (int)(r / a.M), m = (int)(r - (int64_t)bh * a.M);
     const int D = a.D, C = a.C;
-    float gam = 0.0f;
-    for (int d = 0; d < D; ++d) {
-        float s = 0.0f;
-        for (int ch = 0; ch < C; ++ch) s += a.part[(((int64_t)bh * C + ch) * a.M + m) * D + d];
+    float s = 0.0f, gz = 0.0f;
+    if (d < D) {
+        const float* p = a.part + ((int64_t)bh * C * a.M + m) * D + d;
+        const int64_t step = (int64_t)a.M * D;
+        for (int ch = 0; ch < C; ++ch) s += p[ch * step];
         a.dZ[r * D + d] = s;
-        gam = fmaf(s, a.Z[r * D + d], gam);
+        gz = s * a.Z[r * D + d];
     }
-    a.gam[r] = gam;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) gz += __shfl_xor(gz, off, 64);
+    if (d == 0) a.gam[r] = gz;
 }
 
 // dQ[h] = sum over the batch and the chunks of the partials (already scaled
@@ -343,8 +348,8 @@ hipError_t launch_bw_dq(const BackwardArgs& a, hipStream_t s) { FLARE_BW_DISPATC
 hipError_t launch_bw_dkdv(const BackwardArgs& a, hipStream_t s) { FLARE_BW_DISPATCH(dkdv_d, a, s) }
 
 hipError_t launch_bw_dz_combine(const BackwardArgs& a, hipStream_t s) {
-    const int64_t n = (int64_t)a.BH * a.M;
-    hipLaunchKernelGGL(bw_dz_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    const int64_t n = (int64_t)a.BH * a.M;  // one wave each, four per workgroup
+    hipLaunchKernelGGL(bw_dz_combine, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
