@@ -30,8 +30,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 KERNEL_SOURCES = {
-    "encode_partial": ["rank_latent_attention_flare_amd/csrc/kernels_bf16.hip"],
-    "decode": ["rank_latent_attention_flare_amd/csrc/kernels_bf16.hip"],
+    "encode_partial": ["rank_latent_attention_flare_amd/csrc/kernels_bf16.hip",
+                       "rank_latent_attention_flare_amd/csrc/gfx950_ops.h"],
+    "decode": ["rank_latent_attention_flare_amd/csrc/kernels_bf16.hip",
+               "rank_latent_attention_flare_amd/csrc/gfx950_ops.h"],
     "combine": ["rank_latent_attention_flare_amd/csrc/kernels_common.hip"],
 }
 

@@ -1,5 +1,6 @@
-// Backward of the FLARE forward (gradients of Q, K and V), fp32 arithmetic on
-// fp32 or bf16 storage.
+// Backward of the FLARE forward (gradients of Q, K and V): fp32 VALU kernels
+// (any supported storage, D <= 64) and, for bf16 heads whose Q, Z and dZ fit in
+// LDS, matrix-core kernels (bw_stats_bf16, bw_dkdv_bf16, bw_lat_bf16).
 //
 // With l[m][n] = s <Q[m], K[n]> (s = 1/sqrt(D)), the encode softmax
 // A[m][n] = softmax_n(l[m][.]), Z = A V, the decode softmax
@@ -16,18 +17,22 @@
 // encode statistics (mu*, sig*) and Z come from the forward's own encode and
 // combine; the decode statistics (nu, tau) and del per token from bw_stats.
 //
-// Layout of work: a pair of lanes (l, l ^ 32) owns one token (token kernels)
-// or one latent (latent kernels), each lane holding half of every D-vector;
-// dot products add the two halves with one cross-lane swap. All exponentials
-// are base 2 on logits scaled by c = s log2(e).
+// Layout of work in the fp32 kernels: a pair of lanes (l, l ^ 32) owns one
+// token (token kernels) or one latent (latent kernels), each lane holding half
+// of every D-vector; dot products add the two halves with one cross-lane swap.
+// All exponentials are base 2 on logits scaled by c = s log2(e).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "launch.h"
 
 namespace flare {
 namespace {
+
+#include "gfx950_ops.h"
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p);
@@ -290,6 +295,397 @@ __global__ __launch_bounds__(256) void bw_dkdv(BackwardArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Backward on the matrix core (bf16 storage; see the backward notes in
+// kernels_backward.hip for the formulas). Token-parallel like the decode: a
+// wave owns 32 tokens and walks the latents in blocks of 32; the head's Q, Z
+// and dZ rows sit in LDS as bf16 (natural latent order, swizzled rows).
+// ---------------------------------------------------------------------------
+// Stage rows [Mp][D] of a matrix (bf16 storage, or fp32 rounded to nearest
+// even) into a swizzled LDS tile; rows >= M are zero.
+template <int D, typename ST>
+__device__ __forceinline__ void stage_rows(unsigned char* dst, const ST* src, int M, int Mp, int tid, int nth) {
+    constexpr int CH = D / 8;
+    for (int p = tid; p < Mp * CH; p += nth) {
+        const int m = p / CH, ch = p % CH;
+        bf16x8 v = zero8();
+        if (m < M) {
+            if constexpr (sizeof(ST) == 4) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = (__bf16)(float)src[(int64_t)m * D + ch * 8 + j];
+            } else {
+                v = *(const bf16x8*)(src + (int64_t)m * D + ch * 8);
+            }
+        }
+        *(bf16x8*)(dst + tile_off<D>(m, ch)) = v;
+    }
+}
+
+// Per token: nu' = log2-sum-exp2 of the logits over the latents (the decode
+// softmax's normaliser, log2 units) and del = <dY, Y> = sum_m Bt[n][m] <dY[n],
+// Z[m]>. Two sweeps over the latents: the exact maximum, then the sums.
+template <int D>
+__global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
+    constexpr int KB = D / 16;
+    extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5, l32 = lane & 31;
+    const int bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
+    const int N = a.N, M = a.M, Mp = (M + 31) & ~31, MB = Mp / 32;
+    const float c = a.c;
+    unsigned char* qs = bsm;
+    unsigned char* zs = bsm + Mp * 2 * D;
+    stage_rows<D>(qs, (const uint16_t*)a.Q + (int64_t)h * M * D, M, Mp, tid, 256);
+    stage_rows<D>(zs, a.Z + (int64_t)bh * M * D, M, Mp, tid, 256);
+    __syncthreads();
+    const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
+    const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
+    const int nblk = (N + 31) / 32;
+    for (int blk = blockIdx.x * 4 + wave; blk < nblk; blk += gridDim.x * 4) {
+        const int n = blk * 32 + l32, nn = min(n, N - 1);
+        bf16x8 kop[KB], gop[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            kop[kb] = *(const bf16x8*)(Kb + (int64_t)nn * D + 16 * kb + 8 * hi);
+            gop[kb] = *(const bf16x8*)(Gb + (int64_t)nn * D + 16 * kb + 8 * hi);
+        }
+        auto rows = [&](const unsigned char* t, int mb, bf16x8 (&op)[KB]) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) op[kb] = *(const bf16x8*)(t + tile_off<D>(32 * mb + l32, 2 * kb + hi));
+        };
+        // register i holds latent 32 mb + 8 (i/4) + 4 hi + i%4 (natural rows)
+        auto valid = [&](int mb, int i) { return 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3) < M; };
+        float mx = -INFINITY;
+        for (int mb = 0; mb < MB; ++mb) {
+            bf16x8 qa[KB];
+            rows(qs, mb, qa);
+            f32x16 S = mfma(qa[0], kop[0], f32x16{});
+#pragma unroll
+            for (int kb = 1; kb < KB; ++kb) S = mfma(qa[kb], kop[kb], S);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (valid(mb, i)) mx = fmaxf(mx, S[i]);
+        }
+        const float nu = pair_max(mx) * c;
+        float tau = 0.0f, pg = 0.0f;
+        for (int mb = 0; mb < MB; ++mb) {
+            bf16x8 qa[KB], za[KB];
+            rows(qs, mb, qa);
+            rows(zs, mb, za);
+            f32x16 S = mfma(qa[0], kop[0], f32x16{});
+            f32x16 G = mfma(za[0], gop[0], f32x16{});
+#pragma unroll
+            for (int kb = 1; kb < KB; ++kb) {
+                S = mfma(qa[kb], kop[kb], S);
+                G = mfma(za[kb], gop[kb], G);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = valid(mb, i) ? exp2_fast(fmaf(S[i], c, -nu)) : 0.0f;
+                tau += p;
+                pg = fmaf(p, G[i], pg);
+            }
+        }
+        tau = pair_sum(tau);
+        pg = pair_sum(pg);
+        if (n < N && hi == 0) {
+            const int64_t o = (int64_t)bh * N + n;
+            a.nu[o] = nu + __log2f(tau);  // with tau = 1: the weights are normalised by nu alone
+            a.tau[o] = 1.0f;
+            a.del[o] = pg / tau;
+        }
+    }
+}
+
+// Per token: dV[n] = sum_m A[m][n] dZ[m] and dK[n] = s sum_m dl[m][n] Q[m].
+// The A operands of the three logit-shaped products (Q K^T, Z dY^T, dZ V^T)
+// take latent rows in the order enc_row_token gives, so that registers
+// 8 kp .. 8 kp + 7 of a lane hold latents 32 mb + 16 kp + 8 hi + 0..7, which
+// are exactly the k-slots of the B operand of the accumulations dK^T += Q^T dl
+// and dV^T += dZ^T A, whose A operands are read transposed from the natural
+// row-major LDS rows.
+template <int D>
+__global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
+    constexpr int KB = D / 16, DB = D / 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5, l32 = lane & 31;
+    const int bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
+    const int N = a.N, M = a.M, Mp = (M + 31) & ~31, MB = Mp / 32;
+    const float c = a.c;
+    unsigned char* qs = bsm;
+    unsigned char* zs = qs + Mp * 2 * D;
+    unsigned char* dzs = zs + Mp * 2 * D;
+    float* lam = (float*)(dzs + Mp * 2 * D);  // [Mp] mu* + log2 sig* (+inf for padding)
+    float* gam = lam + Mp;                     // [Mp]
+    stage_rows<D>(qs, (const uint16_t*)a.Q + (int64_t)h * M * D, M, Mp, tid, 256);
+    stage_rows<D>(zs, a.Z + (int64_t)bh * M * D, M, Mp, tid, 256);
+    stage_rows<D>(dzs, a.dZ + (int64_t)bh * M * D, M, Mp, tid, 256);
+    for (int m = tid; m < Mp; m += 256) {
+        const int64_t r = (int64_t)bh * M + m;
+        lam[m] = m < M ? a.zmu[r] + __log2f(a.zsig[r]) : INFINITY;
+        gam[m] = m < M ? a.gam[r] : 0.0f;
+    }
+    __syncthreads();
+    const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
+    const uint16_t* Vb = (const uint16_t*)a.V + (int64_t)bh * N * D;
+    const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
+    const int g = lane >> 4, gi = lane & 15;
+    const int prow = enc_row_token(l32);
+    const int nblk = (N + 31) / 32;
+    for (int blk = blockIdx.x * 4 + wave; blk < nblk; blk += gridDim.x * 4) {
+        const int n = blk * 32 + l32, nn = min(n, N - 1);
+        bf16x8 kop[KB], vop[KB], gop[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int64_t o = (int64_t)nn * D + 16 * kb + 8 * hi;
+            kop[kb] = *(const bf16x8*)(Kb + o);
+            vop[kb] = *(const bf16x8*)(Vb + o);
+            gop[kb] = *(const bf16x8*)(Gb + o);
+        }
+        const float nu = a.nu[(int64_t)bh * N + nn], del = a.del[(int64_t)bh * N + nn];
+        f32x16 dk[DB], dv[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            dk[db] = f32x16{};
+            dv[db] = f32x16{};
+        }
+        for (int mb = 0; mb < MB; ++mb) {
+            bf16x8 qa[KB], za[KB], dza[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int off = tile_off<D>(32 * mb + prow, 2 * kb + hi);
+                qa[kb] = *(const bf16x8*)(qs + off);
+                za[kb] = *(const bf16x8*)(zs + off);
+                dza[kb] = *(const bf16x8*)(dzs + off);
+            }
+            f32x16 S = mfma(qa[0], kop[0], f32x16{});
+            f32x16 GY = mfma(za[0], gop[0], f32x16{});
+            f32x16 GV = mfma(dza[0], vop[0], f32x16{});
+#pragma unroll
+            for (int kb = 1; kb < KB; ++kb) {
+                S = mfma(qa[kb], kop[kb], S);
+                GY = mfma(za[kb], gop[kb], GY);
+                GV = mfma(dza[kb], vop[kb], GV);
+            }
+            bf16x8 pe[2], pl[2];
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+                const int m0 = 32 * mb + 16 * kp + 8 * hi;
+                const f32x4 l0 = *(const f32x4*)(lam + m0), l1 = *(const f32x4*)(lam + m0 + 4);
+                const f32x4 g0 = *(const f32x4*)(gam + m0), g1 = *(const f32x4*)(gam + m0 + 4);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int i = 8 * kp + j;
+                    const float lj = j < 4 ? l0[j] : l1[j - 4];
+                    const float gj = j < 4 ? g0[j] : g1[j - 4];
+                    const float xe = fmaf(S[i], c, -lj);
+                    // p_dec <= 1 for real latents; the clamp keeps padded
+                    // latents (zero rows) finite
+                    const float xd = fminf(fmaf(S[i], c, -nu), 0.0f);
+                    const float p_e = exp2_fast(xe);
+                    const float p_d = exp2_fast(xd);
+                    const float dl = p_e * (GV[i] - gj) + p_d * (GY[i] - del);
+                    pe[kp][j] = (__bf16)p_e;
+                    pl[kp][j] = (__bf16)dl;
+                }
+            }
+            // Q^T and dZ^T operands (rows d, k = latents of this block),
+            // transposed reads of the natural rows
+            auto taddr = [&](const unsigned char* t, int kp, int db, int second) {
+                const int row = 32 * mb + 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
+                const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+                return t + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+            };
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                bf16x8 qt0, qt1, zt0, zt1;
+                lds_tr_op2(taddr(qs, 0, db, 0), taddr(qs, 0, db, 1), taddr(qs, 1, db, 0), taddr(qs, 1, db, 1), qt0, qt1);
+                lds_tr_op2(taddr(dzs, 0, db, 0), taddr(dzs, 0, db, 1), taddr(dzs, 1, db, 0), taddr(dzs, 1, db, 1), zt0,
+                           zt1);
+                dk[db] = mfma(qt0, pl[0], dk[db]);
+                dk[db] = mfma(qt1, pl[1], dk[db]);
+                dv[db] = mfma(zt0, pe[0], dv[db]);
+                dv[db] = mfma(zt1, pe[1], dv[db]);
+            }
+        }
+        // register r of lane l: d = 32 db + 8 (r/4) + 4 hi + r%4, token l32
+        if (n < N) {
+            uint16_t* dK = (uint16_t*)a.dK + ((int64_t)bh * N + n) * D;
+            uint16_t* dV = (uint16_t*)a.dV + ((int64_t)bh * N + n) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d0 = 32 * db + 8 * g4 + 4 * hi;
+                    u32x2 wk, wv;
+                    const bf16x2 k01 = {(__bf16)(a.s * dk[db][4 * g4]), (__bf16)(a.s * dk[db][4 * g4 + 1])};
+                    const bf16x2 k23 = {(__bf16)(a.s * dk[db][4 * g4 + 2]), (__bf16)(a.s * dk[db][4 * g4 + 3])};
+                    const bf16x2 v01 = {(__bf16)dv[db][4 * g4], (__bf16)dv[db][4 * g4 + 1]};
+                    const bf16x2 v23 = {(__bf16)dv[db][4 * g4 + 2], (__bf16)dv[db][4 * g4 + 3]};
+                    wk[0] = __builtin_bit_cast(uint32_t, k01);
+                    wk[1] = __builtin_bit_cast(uint32_t, k23);
+                    wv[0] = __builtin_bit_cast(uint32_t, v01);
+                    wv[1] = __builtin_bit_cast(uint32_t, v23);
+                    *(u32x2*)(dK + d0) = wk;
+                    *(u32x2*)(dV + d0) = wv;
+                }
+        }
+    }
+}
+
+// Latent-side backward products, split over token chunks like the encode:
+//   DQ = false: dZ[m]  = sum_n Bt[n][m] dY[n]
+//   DQ = true:  dQ[m]  = s sum_n dl[m][n] K[n]
+// Grid (chunks C, B*H); the 4 waves share the chunk's tokens and split the
+// latent blocks (wave w owns blocks w, w + 4, ...). Per 32-token sub-block a
+// wave loads the token rows straight into MFMA A operands in enc_row_token
+// order (rows = tokens of S^T = K Q^T), so registers 8 kp .. 8 kp + 7 of a lane
+// hold tokens 16 kp + 8 hi + 0..7: the k-slots of the accumulation's B
+// operand. The accumulation's A operand (dY^T or K^T) comes from a transposed
+// read of the same rows, which the wave also writes to its own LDS tile in
+// natural order. Per-chunk partials go to a.part [BH][C][M][D].
+template <int D, bool DQ, int MBW>  // MBW: latent blocks per wave at most
+__global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
+    constexpr int KB = D / 16, DB = D / 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5, l32 = lane & 31;
+    const int chunk = blockIdx.x, bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
+    const int N = a.N, M = a.M, Mp = (M + 31) & ~31, MB = Mp / 32;
+    const int n0 = chunk * a.chunk_len, n1 = min(N, n0 + a.chunk_len);
+    const float c = a.c;
+    unsigned char* qs = bsm;
+    unsigned char* zs = qs + Mp * 2 * D;                 // DQ only
+    unsigned char* dzs = zs + (DQ ? Mp * 2 * D : 0);     // DQ only
+    unsigned char* tt = dzs + (DQ ? Mp * 2 * D : 0) + wave * 32 * 2 * D;  // this wave's token rows
+    stage_rows<D>(qs, (const uint16_t*)a.Q + (int64_t)h * M * D, M, Mp, tid, 256);
+    if constexpr (DQ) {
+        stage_rows<D>(zs, a.Z + (int64_t)bh * M * D, M, Mp, tid, 256);
+        stage_rows<D>(dzs, a.dZ + (int64_t)bh * M * D, M, Mp, tid, 256);
+    }
+    __syncthreads();
+    const int nmb = MB > wave ? (MB - wave + 3) / 4 : 0;  // this wave's latent blocks
+    // per latent (lane column) of each owned block: lambda = mu* + log2 sig*
+    // (+inf for padding) and gam
+    float lam[MBW], gm[MBW];
+    f32x16 acc[MBW][DB];
+#pragma unroll
+    for (int j = 0; j < MBW; ++j) {
+        const int m = 32 * (wave + 4 * j) + l32;
+        const int64_t r = (int64_t)bh * M + min(m, M - 1);
+        lam[j] = (DQ && m < M) ? a.zmu[r] + __log2f(a.zsig[r]) : INFINITY;
+        gm[j] = (DQ && m < M) ? a.gam[r] : 0.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[j][db] = f32x16{};
+    }
+    const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
+    const uint16_t* Vb = (const uint16_t*)a.V + (int64_t)bh * N * D;
+    const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
+    const float* nub = a.nu + (int64_t)bh * N;
+    const float* delb = a.del + (int64_t)bh * N;
+    const int prow = enc_row_token(l32);
+    const int g = lane >> 4, gi = lane & 15;
+    for (int t0 = n0; t0 < n1; t0 += 32) {
+        const int nv = n1 - t0;  // valid tokens in this sub-block (>= 1)
+        const int tn = t0 + min(prow, nv - 1);
+        bf16x8 kA[KB], gA[KB], vA[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int64_t o = (int64_t)tn * D + 16 * kb + 8 * hi;
+            kA[kb] = *(const bf16x8*)(Kb + o);
+            gA[kb] = *(const bf16x8*)(Gb + o);
+            if constexpr (DQ) vA[kb] = *(const bf16x8*)(Vb + o);
+        }
+        // the accumulation's source rows (K for dQ, dY for dZ) in natural
+        // order into this wave's tile; rows past the chunk are zero, so their
+        // (finite) weights add nothing
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            *(bf16x8*)(tt + tile_off<D>(prow, 2 * kb + hi)) = prow < nv ? (DQ ? kA[kb] : gA[kb]) : zero8();
+        // per token (register i: token 16 (i/8) + 8 hi + i%8): nu' and del
+        float nur[16], der[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int tk = 16 * (i >> 3) + 8 * hi + (i & 7);
+            const int tc = t0 + min(tk, nv - 1);
+            nur[i] = tk < nv ? nub[tc] : INFINITY;  // +inf: no weight for tokens past the chunk
+            der[i] = DQ ? delb[tc] : 0.0f;
+        }
+        // the transposed operands of this sub-block (same for every latent block)
+        auto taddr = [&](int kp, int db, int second) {
+            const int row = 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
+            const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+            return tt + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+        };
+        bf16x8 tA[2][DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            lds_tr_op2(taddr(0, db, 0), taddr(0, db, 1), taddr(1, db, 0), taddr(1, db, 1), tA[0][db], tA[1][db]);
+#pragma unroll
+        for (int j = 0; j < MBW; ++j) {
+            if (j >= nmb) break;
+            const int mb = wave + 4 * j;
+            bf16x8 qB[KB], zB[KB], dzB[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int off = tile_off<D>(32 * mb + l32, 2 * kb + hi);
+                qB[kb] = *(const bf16x8*)(qs + off);
+                if constexpr (DQ) {
+                    zB[kb] = *(const bf16x8*)(zs + off);
+                    dzB[kb] = *(const bf16x8*)(dzs + off);
+                }
+            }
+            f32x16 S = mfma(kA[0], qB[0], f32x16{});
+#pragma unroll
+            for (int kb = 1; kb < KB; ++kb) S = mfma(kA[kb], qB[kb], S);
+            f32x16 GY, GV;
+            if constexpr (DQ) {
+                GY = mfma(gA[0], zB[0], f32x16{});
+                GV = mfma(vA[0], dzB[0], f32x16{});
+#pragma unroll
+                for (int kb = 1; kb < KB; ++kb) {
+                    GY = mfma(gA[kb], zB[kb], GY);
+                    GV = mfma(vA[kb], dzB[kb], GV);
+                }
+            }
+            bf16x8 pw[2];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                // decode weight Bt[n][m] (0 past the chunk); clamp: padded
+                // latents (zero rows) stay finite
+                const float p_d = exp2_fast(fminf(fmaf(S[i], c, -nur[i]), 0.0f));
+                float w = p_d;
+                if constexpr (DQ) {
+                    const float p_e = exp2_fast(fmaf(S[i], c, -lam[j]));
+                    w = p_e * (GV[i] - gm[j]) + p_d * (GY[i] - der[i]);
+                }
+                pw[i >> 3][i & 7] = (__bf16)w;
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                acc[j][db] = mfma(tA[0][db], pw[0], acc[j][db]);
+                acc[j][db] = mfma(tA[1][db], pw[1], acc[j][db]);
+            }
+        }
+    }
+    // acc[j][db] register r: d = 32 db + 8 (r/4) + 4 hi + r%4, latent column l32
+    const float scale = DQ ? a.s : 1.0f;
+#pragma unroll
+    for (int j = 0; j < MBW; ++j) {
+        if (j >= nmb) break;
+        const int m = 32 * (wave + 4 * j) + l32;
+        if (m < M) {
+            float* dst = a.part + (((int64_t)bh * gridDim.x + chunk) * M + m) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x4 v = {scale * acc[j][db][4 * g4], scale * acc[j][db][4 * g4 + 1],
+                                     scale * acc[j][db][4 * g4 + 2], scale * acc[j][db][4 * g4 + 3]};
+                    *(f32x4*)(dst + 32 * db + 8 * g4 + 4 * hi) = v;
+                }
+        }
+    }
+}
+
 #define FLARE_BW_DISPATCH(FN, a, s)      \
     switch ((a).D) {                     \
         case 8: return FN<8>(a, s);      \
@@ -339,6 +735,62 @@ hipError_t dkdv_d(const BackwardArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+bool bw_bf16_fits(int M, int D) {
+    // Q, Z and dZ of the head (and small per-latent or per-wave buffers) in
+    // one CU's LDS; at D = 64 up to M = 256
+    const int Mp = (M + 31) / 32 * 32;
+    return (D == 32 || (D == 64 && Mp <= 256)) && 3 * Mp * 2 * D + 4 * 32 * 2 * D + 8 * Mp <= 163840;
+}
+
+namespace {
+template <typename F>
+hipError_t launch_bw_tok(F fn, const BackwardArgs& a, int lds, hipStream_t s) {
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+    }
+    const int nblk = (a.N + 31) / 32;
+    int G = (1024 + a.BH - 1) / a.BH;
+    G = std::max(1, std::min(G, (nblk + 3) / 4));
+    hipLaunchKernelGGL(fn, dim3(G, a.BH), dim3(256), lds, s, a);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s) {
+    const int Mp = (a.M + 31) / 32 * 32, lds = 2 * Mp * 2 * a.D;
+    if (a.D == 32) return launch_bw_tok(bw_stats_bf16<32>, a, lds, s);
+    if (a.D == 64) return launch_bw_tok(bw_stats_bf16<64>, a, lds, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
+    const int Mp = (a.M + 31) / 32 * 32;
+    const int lds = (dq ? 3 : 1) * Mp * 2 * a.D + 4 * 32 * 2 * a.D;
+    auto go = [&](auto fn) -> hipError_t {
+        if (lds > 65536) {
+            hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(fn, dim3(a.C, a.BH), dim3(256), lds, s, a);
+        return hipGetLastError();
+    };
+    const bool wide = Mp > 256;  // more than 2 latent blocks per wave
+    if (a.D == 32) {
+        if (wide) return dq ? go(bw_lat_bf16<32, true, 4>) : go(bw_lat_bf16<32, false, 4>);
+        return dq ? go(bw_lat_bf16<32, true, 2>) : go(bw_lat_bf16<32, false, 2>);
+    }
+    if (a.D == 64 && !wide) return dq ? go(bw_lat_bf16<64, true, 2>) : go(bw_lat_bf16<64, false, 2>);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
+    const int Mp = (a.M + 31) / 32 * 32, lds = 3 * Mp * 2 * a.D + 8 * Mp;
+    if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32>, a, lds, s);
+    if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64>, a, lds, s);
+    return hipErrorInvalidValue;
+}
 
 bool backward_supports(int D) { return D == 8 || D == 16 || D == 24 || D == 32 || D == 48 || D == 64; }
 

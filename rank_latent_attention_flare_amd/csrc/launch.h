@@ -1,5 +1,6 @@
 // Internal interface between the host runtime (flare.cpp) and the gfx950
-// kernels (kernels_bf16.hip, kernels_f32.hip). Not part of the public ABI.
+// kernels (kernels_bf16.hip, kernels_common.hip, kernels_backward.hip). Not part
+// of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
