@@ -562,14 +562,18 @@ __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
         stage_rows<D>(dzs, a.dZ + (int64_t)bh * M * D, M, Mp, tid, 256);
     }
     __syncthreads();
-    const int nmb = MB > wave ? (MB - wave + 3) / 4 : 0;  // this wave's latent blocks
+    // NL latent groups x TS token streams: with fewer than 4 latent blocks the
+    // waves of a group split the chunk's sub-blocks and merge at the end
+    const int NL = MB < 4 ? MB : 4, TS = 4 / NL;
+    const int lg = wave % NL, ts = wave / NL;
+    const int nmb = (ts < TS && MB > lg) ? (MB - lg + NL - 1) / NL : 0;  // this wave's latent blocks
     // per latent (lane column) of each owned block: lambda = mu* + log2 sig*
     // (+inf for padding) and gam
     float lam[MBW], gm[MBW];
     f32x16 acc[MBW][DB];
 #pragma unroll
     for (int j = 0; j < MBW; ++j) {
-        const int m = 32 * (wave + 4 * j) + l32;
+        const int m = 32 * (lg + NL * j) + l32;
         const int64_t r = (int64_t)bh * M + min(m, M - 1);
         lam[j] = (DQ && m < M) ? a.zmu[r] + __log2f(a.zsig[r]) : INFINITY;
         gm[j] = (DQ && m < M) ? a.gam[r] : 0.0f;
@@ -583,7 +587,7 @@ __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
     const float* delb = a.del + (int64_t)bh * N;
     const int prow = enc_row_token(l32);
     const int g = lane >> 4, gi = lane & 15;
-    for (int t0 = n0; t0 < n1; t0 += 32) {
+    for (int t0 = n0 + 32 * ts; nmb > 0 && t0 < n1; t0 += 32 * TS) {
         const int nv = n1 - t0;  // valid tokens in this sub-block (>= 1)
         const int tn = t0 + min(prow, nv - 1);
         bf16x8 kA[KB], gA[KB], vA[KB];
@@ -622,7 +626,7 @@ __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
 #pragma unroll
         for (int j = 0; j < MBW; ++j) {
             if (j >= nmb) break;
-            const int mb = wave + 4 * j;
+            const int mb = lg + NL * j;
             bf16x8 qB[KB], zB[KB], dzB[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -666,12 +670,38 @@ __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
             }
         }
     }
+    if (TS > 1) {  // merge the token streams of each latent group (fixed order)
+        __syncthreads();  // staged rows and tiles are no longer read
+        float* mbuf = (float*)bsm;
+        constexpr int PER = MBW * DB * 16 * 64;
+        if (ts > 0) {
+            float* d0 = mbuf + ((ts - 1) * NL + lg) * PER;
+#pragma unroll
+            for (int j = 0; j < MBW; ++j)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) d0[((j * DB + db) * 16 + r) * 64 + lane] = acc[j][db][r];
+        }
+        __syncthreads();
+        if (ts == 0) {
+            for (int t = 1; t < TS; ++t) {
+                const float* s0 = mbuf + ((t - 1) * NL + lg) * PER;
+#pragma unroll
+                for (int j = 0; j < MBW; ++j)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[j][db][r] += s0[((j * DB + db) * 16 + r) * 64 + lane];
+            }
+        }
+    }
     // acc[j][db] register r: d = 32 db + 8 (r/4) + 4 hi + r%4, latent column l32
     const float scale = DQ ? a.s : 1.0f;
 #pragma unroll
     for (int j = 0; j < MBW; ++j) {
-        if (j >= nmb) break;
-        const int m = 32 * (wave + 4 * j) + l32;
+        if (ts != 0 || j >= nmb) break;
+        const int m = 32 * (lg + NL * j) + l32;
         if (m < M) {
             float* dst = a.part + (((int64_t)bh * gridDim.x + chunk) * M + m) * D;
 #pragma unroll
@@ -767,7 +797,9 @@ hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s) {
 
 hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
     const int Mp = (a.M + 31) / 32 * 32;
-    const int lds = (dq ? 3 : 1) * Mp * 2 * a.D + 4 * 32 * 2 * a.D;
+    const int mbw = Mp > 256 ? 4 : 2, nl = std::min(Mp / 32, 4), ts = 4 / nl;
+    const int merge = (ts - 1) * nl * mbw * (a.D / 32) * 16 * 64 * 4;  // token-stream merge
+    const int lds = std::max((dq ? 3 : 1) * Mp * 2 * a.D + 4 * 32 * 2 * a.D, merge);
     auto go = [&](auto fn) -> hipError_t {
         if (lds > 65536) {
             hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);

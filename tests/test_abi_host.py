@@ -171,3 +171,18 @@ def test_attend_validates_before_launch():
     assert fn(PQ, PK, PQ + 256, *args[3:], 0, None) == INVALID  # Y overlaps q
     assert fn(PQ, PK, PY + 8, *args[3:], 0, None) == INVALID    # misaligned
     assert fn(PQ, PK, PY, 1, 2, 100, 600, 64, F.FLARE_BF16, 0, None) == UNSUPPORTED
+
+
+def test_backward_validates_before_launch():
+    fn = F.lib().flare_backward
+    PG, PDQ, PDK, PDV = 0x60000000, 0x70000000, 0x80000000, 0x90000000
+    ok = [PQ, PK, PV, PG, PDQ, PDK, PDV, 1, 2, 100, 64, 32, F.FLARE_BF16, None]
+    a = list(ok); a[3] = None
+    assert fn(*a) == INVALID and "null" in F.lib().flare_last_error().decode()
+    a = list(ok); a[5] = PK  # dK aliases K
+    assert fn(*a) == INVALID and "overlap" in F.lib().flare_last_error().decode()
+    a = list(ok); a[11] = 128  # D = 128: no backward
+    assert fn(*a) == UNSUPPORTED
+    ws = F.lib().flare_workspace_size(F.FLARE_OP_BACKWARD, 1, 2, 100, 64, 32, F.FLARE_BF16)
+    assert ws >= F.lib().flare_workspace_size(F.FLARE_OP_FORWARD, 1, 2, 100, 64, 32, F.FLARE_BF16) > 0
+    assert F.lib().flare_backward_ws(*ok, PW, 256) == INVALID
