@@ -562,9 +562,10 @@ __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
         stage_rows<D>(dzs, a.dZ + (int64_t)bh * M * D, M, Mp, tid, 256);
     }
     __syncthreads();
-    // NL latent groups x TS token streams: with fewer than 4 latent blocks the
-    // waves of a group split the chunk's sub-blocks and merge at the end
-    const int NL = MB < 4 ? MB : 4, TS = 4 / NL;
+    // NL latent groups of up to MBW blocks x TS token streams: the waves of a
+    // group split the chunk's sub-blocks and merge at the end, so each token
+    // row a wave loads serves up to MBW latent blocks
+    const int NL = min(4, (MB + MBW - 1) / MBW), TS = 4 / NL;
     const int lg = wave % NL, ts = wave / NL;
     const int nmb = (ts < TS && MB > lg) ? (MB - lg + NL - 1) / NL : 0;  // this wave's latent blocks
     // per latent (lane column) of each owned block: lambda = mu* + log2 sig*
@@ -797,7 +798,8 @@ hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s) {
 
 hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
     const int Mp = (a.M + 31) / 32 * 32;
-    const int mbw = Mp > 256 ? 4 : 2, nl = std::min(Mp / 32, 4), ts = 4 / nl;
+    // latent blocks per wave: 4 at D = 32 (one wave covers M = 128), else 2
+    const int mbw = a.D == 32 ? 4 : 2, nl = std::min(4, (Mp / 32 + mbw - 1) / mbw), ts = 4 / nl;
     const int merge = (ts - 1) * nl * mbw * (a.D / 32) * 16 * 64 * 4;  // token-stream merge
     const int lds = std::max((dq ? 3 : 1) * Mp * 2 * a.D + 4 * 32 * 2 * a.D, merge);
     auto go = [&](auto fn) -> hipError_t {
@@ -808,12 +810,8 @@ hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
         hipLaunchKernelGGL(fn, dim3(a.C, a.BH), dim3(256), lds, s, a);
         return hipGetLastError();
     };
-    const bool wide = Mp > 256;  // more than 2 latent blocks per wave
-    if (a.D == 32) {
-        if (wide) return dq ? go(bw_lat_bf16<32, true, 4>) : go(bw_lat_bf16<32, false, 4>);
-        return dq ? go(bw_lat_bf16<32, true, 2>) : go(bw_lat_bf16<32, false, 2>);
-    }
-    if (a.D == 64 && !wide) return dq ? go(bw_lat_bf16<64, true, 2>) : go(bw_lat_bf16<64, false, 2>);
+    if (a.D == 32) return dq ? go(bw_lat_bf16<32, true, 4>) : go(bw_lat_bf16<32, false, 4>);
+    if (a.D == 64 && Mp <= 256) return dq ? go(bw_lat_bf16<64, true, 2>) : go(bw_lat_bf16<64, false, 2>);
     return hipErrorInvalidValue;
 }
 
