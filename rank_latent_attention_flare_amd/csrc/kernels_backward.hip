@@ -336,7 +336,19 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
     unsigned char* zs = bsm + Mp * 2 * D;
     stage_rows<D>(qs, (const uint16_t*)a.Q + (int64_t)h * M * D, M, Mp, tid, 256);
     stage_rows<D>(zs, a.Z + (int64_t)bh * M * D, M, Mp, tid, 256);
+    // One offset for the head: every logit satisfies c l <= mu*[m] + 32 (each
+    // tile the forward's encode accepted had probabilities <= 2^32 against
+    // its running offset, and mu* is the largest of those), so 2^(c l - nub)
+    // <= 1 everywhere; a token whose sum falls below 2^-90 is redone against
+    // its exact maximum.
+    float* red = (float*)(zs + Mp * 2 * D);
+    float mz = -INFINITY;
+    for (int m = tid; m < M; m += 256) mz = fmaxf(mz, a.zmu[(int64_t)bh * M + m]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mz = fmaxf(mz, __shfl_xor(mz, off, 64));
+    if (lane == 0) red[wave] = mz;
     __syncthreads();
+    const float nub = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) + 32.0f;
     const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
     const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
     const int nblk = (N + 31) / 32;
@@ -354,39 +366,48 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
         };
         // register i holds latent 32 mb + 8 (i/4) + 4 hi + i%4 (natural rows)
         auto valid = [&](int mb, int i) { return 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3) < M; };
-        float mx = -INFINITY;
-        for (int mb = 0; mb < MB; ++mb) {
-            bf16x8 qa[KB];
-            rows(qs, mb, qa);
-            f32x16 S = mfma(qa[0], kop[0], f32x16{});
+        // sums of 2^(c l - nu) and of those weights times <dY, Z[m]>
+        auto sweep = [&](float nu, float& tau, float& pg) {
+            tau = 0.0f;
+            pg = 0.0f;
+            for (int mb = 0; mb < MB; ++mb) {
+                bf16x8 qa[KB], za[KB];
+                rows(qs, mb, qa);
+                rows(zs, mb, za);
+                f32x16 S = mfma(qa[0], kop[0], f32x16{});
+                f32x16 G = mfma(za[0], gop[0], f32x16{});
 #pragma unroll
-            for (int kb = 1; kb < KB; ++kb) S = mfma(qa[kb], kop[kb], S);
+                for (int kb = 1; kb < KB; ++kb) {
+                    S = mfma(qa[kb], kop[kb], S);
+                    G = mfma(za[kb], gop[kb], G);
+                }
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (valid(mb, i)) mx = fmaxf(mx, S[i]);
-        }
-        const float nu = pair_max(mx) * c;
-        float tau = 0.0f, pg = 0.0f;
-        for (int mb = 0; mb < MB; ++mb) {
-            bf16x8 qa[KB], za[KB];
-            rows(qs, mb, qa);
-            rows(zs, mb, za);
-            f32x16 S = mfma(qa[0], kop[0], f32x16{});
-            f32x16 G = mfma(za[0], gop[0], f32x16{});
-#pragma unroll
-            for (int kb = 1; kb < KB; ++kb) {
-                S = mfma(qa[kb], kop[kb], S);
-                G = mfma(za[kb], gop[kb], G);
+                for (int i = 0; i < 16; ++i) {
+                    const float p = valid(mb, i) ? exp2_fast(fmaf(S[i], c, -nu)) : 0.0f;
+                    tau += p;
+                    pg = fmaf(p, G[i], pg);
+                }
             }
+            tau = pair_sum(tau);
+            pg = pair_sum(pg);
+        };
+        float nu = nub, tau, pg;
+        sweep(nu, tau, pg);
+        if (wave_any(!(tau >= 8.077935669463161e-28f))) {  // 2^-90: redo against the exact maxima
+            float mx = -INFINITY;
+            for (int mb = 0; mb < MB; ++mb) {
+                bf16x8 qa[KB];
+                rows(qs, mb, qa);
+                f32x16 S = mfma(qa[0], kop[0], f32x16{});
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = valid(mb, i) ? exp2_fast(fmaf(S[i], c, -nu)) : 0.0f;
-                tau += p;
-                pg = fmaf(p, G[i], pg);
+                for (int kb = 1; kb < KB; ++kb) S = mfma(qa[kb], kop[kb], S);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (valid(mb, i)) mx = fmaxf(mx, S[i]);
             }
+            nu = pair_max(mx) * c;
+            sweep(nu, tau, pg);
         }
-        tau = pair_sum(tau);
-        pg = pair_sum(pg);
         if (n < N && hi == 0) {
             const int64_t o = (int64_t)bh * N + n;
             a.nu[o] = nu + __log2f(tau);  // with tau = 1: the weights are normalised by nu alone
@@ -790,7 +811,7 @@ hipError_t launch_bw_tok(F fn, const BackwardArgs& a, int lds, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s) {
-    const int Mp = (a.M + 31) / 32 * 32, lds = 2 * Mp * 2 * a.D;
+    const int Mp = (a.M + 31) / 32 * 32, lds = 2 * Mp * 2 * a.D + 16;
     if (a.D == 32) return launch_bw_tok(bw_stats_bf16<32>, a, lds, s);
     if (a.D == 64) return launch_bw_tok(bw_stats_bf16<64>, a, lds, s);
     return hipErrorInvalidValue;
