@@ -681,7 +681,8 @@ __device__ __forceinline__ int dec_zpos(int m) {
 // LONG: M > 256 (more than one group of 8 latent blocks; the group loop costs
 // registers, so the common M <= 256 kernel is built without it).
 template <int D, int TB, typename ZT, bool LONG>
-__global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(D == 32 && TB == 1 && !LONG ? 4 : 1)))
+void decode_bf16(DecodeArgs a) {
     constexpr int KB = D / 16, DB = D / 32, CH = D / 8, NW = kDecWaves;
     const int Mp = a.Mp, MB = Mp / 32;
     const int zs = 2 * Mp + 16;  // bytes per Z^T row (padded)
@@ -757,13 +758,17 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
     const int nblk = (N + 32 * TB - 1) / (32 * TB);
     const int stride = gridDim.x * NW;
 
+    // K rows of one block as MFMA B operands. Rows past the end (the ragged
+    // last block, or a block past the wave's last) load the last token
+    // instead: every column of the logits belongs to one token, so they only
+    // feed outputs that are never stored, and the loads stay unconditional
+    // (a fixed number in flight, which the explicit waits below rely on).
     auto kload = [&](int bk, bf16x8 (&dst)[TB][KB]) {
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-            const int n = bk * 32 * TB + 32 * tb + l32;
+            const int n = min(bk * 32 * TB + 32 * tb + l32, N - 1);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                dst[tb][kb] = (bk < nblk && n < N) ? *(const bf16x8*)(Kb + (int64_t)n * sn + 16 * kb + 8 * hi) : zero8();
+            for (int kb = 0; kb < KB; ++kb) dst[tb][kb] = *(const bf16x8*)(Kb + (int64_t)n * sn + 16 * kb + 8 * hi);
         }
     };
     auto qread = [&](int mb, bf16x8 (&qa)[KB]) {
@@ -785,6 +790,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
 
     // One 64-token block: Y^T[d][tok] = sum_m Z^T[d][m] 2^(c S - nu)  and
     // tau[tok] = sum_m 2^(c S - nu), latents streamed in blocks of 32.
+    // normalised, rounded Y of block ypend (-1: none), not yet stored
+    bf16x8 ypk[TB][2 * DB];
+    int ypend = -1;
     auto process = [&](int bk, const bf16x8 (&kop)[TB][KB]) {
         float nu[TB];
         if (goff) {
@@ -921,63 +929,64 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_bf16(DecodeArgs a) {
             for (int tb = 0; tb < TB; ++tb) ex[tb] = pair_max(mx[tb]) * c;
             run(ex);
         }
-        // normalise, round, store
+        // normalise and round; stored during the next block
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-            const int n = bk * 32 * TB + 32 * tb + l32;
             const float inv = __builtin_amdgcn_rcpf(tau[tb]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    ypk[tb][2 * db][r] = (__bf16)(yac[tb][db][r] * inv);
+                    ypk[tb][2 * db + 1][r] = (__bf16)(yac[tb][db][8 + r] * inv);
+                }
+        }
+        ypend = bk;
+    };
+    // Y rows of block ypend (if any) to memory, 32 bytes per lane and run.
+    auto flush = [&]() {
+        if (ypend < 0) return;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int n = ypend * 32 * TB + 32 * tb + l32;
             if (n < N) {
                 uint16_t* dst = Yb + (int64_t)n * sn + 16 * hi;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    bf16x8 o0, o1;
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        o0[r] = (__bf16)(yac[tb][db][r] * inv);
-                        o1[r] = (__bf16)(yac[tb][db][8 + r] * inv);
-                    }
-                    *(bf16x8*)(dst + 32 * db) = o0;
-                    *(bf16x8*)(dst + 32 * db + 8) = o1;
+                    *(bf16x8*)(dst + 32 * db) = ypk[tb][2 * db];
+                    *(bf16x8*)(dst + 32 * db + 8) = ypk[tb][2 * db + 1];
                 }
             }
         }
     };
 
-    // Blocks blk, blk + stride, ... of this wave. K register sets in turn so
-    // that the rows of the next block (D = 32) or the next two blocks (D >= 64,
-    // measured faster there; at D = 32 the extra registers cost more) are
-    // always in flight.
+    // Blocks blk, blk + stride, ... of this wave, with two K register sets in
+    // turn. Each step first waits for every memory operation in flight: the
+    // K rows of this block and the Y stores of the block before last, both
+    // issued one whole block of work earlier. Only then are the next block's
+    // K rows requested and the previous block's Y stored, so nothing the step
+    // needs is ever behind a transfer issued in the same step. (A wait on a
+    // register set alone would also wait for the later loads and the stores:
+    // the counter is shared and the compiler takes the conservative count.)
     int blk = blockIdx.x * NW + wave;
-    if constexpr (D >= 64) {
-        bf16x8 kA[TB][KB], kB[TB][KB], kC[TB][KB];
-        kload(blk, kA);
+    bf16x8 kA[TB][KB], kB[TB][KB];
+    kload(blk, kA);
+    while (blk < nblk) {
+        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
         kload(blk + stride, kB);
-        while (blk < nblk) {
-            kload(blk + 2 * stride, kC);
-            process(blk, kA);
-            blk += stride;
-            if (blk >= nblk) break;
-            kload(blk + 2 * stride, kA);
-            process(blk, kB);
-            blk += stride;
-            if (blk >= nblk) break;
-            kload(blk + 2 * stride, kB);
-            process(blk, kC);
-            blk += stride;
-        }
-    } else {
-        bf16x8 kA[TB][KB], kB[TB][KB];
-        kload(blk, kA);
-        while (blk < nblk) {
-            kload(blk + stride, kB);
-            process(blk, kA);
-            blk += stride;
-            if (blk >= nblk) break;
-            kload(blk + stride, kA);
-            process(blk, kB);
-            blk += stride;
-        }
+        flush();
+        process(blk, kA);
+        blk += stride;
+        if (blk >= nblk) break;
+        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+        kload(blk + stride, kA);
+        flush();
+        process(blk, kB);
+        blk += stride;
     }
+    flush();
 }
 
 template <int D, int MBW, int WM, int WT>

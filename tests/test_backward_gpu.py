@@ -68,6 +68,28 @@ def test_backward_matches_oracle(case):
     check(got, oracle.backward(Q, K, V, dY), dt, case_id(case))
 
 
+SHARP = [
+    # B, H, N, M, D, q_scale, kv_scale: logits spread over hundreds of log2
+    # units, so most tokens' largest logit lies far below the head's largest
+    # and the statistics take their exact-maximum path for whole waves; at
+    # q_scale 8 waves of both kinds occur
+    (1, 2, 2000, 64, 32, 12.0, 2.0),
+    (1, 1, 3000, 100, 64, 8.0, 2.0),
+]
+
+
+@pytest.mark.parametrize("case", SHARP, ids=lambda c: "B{}H{}N{}M{}D{}-q{}kv{}".format(*c))
+def test_backward_sharp_logits(case):
+    B, H, N, M, D, qs, ks = case
+    seed = zlib.crc32(repr(("sharp",) + case).encode()) % 100000
+    Q, K, V = make_inputs(B, H, N, M, D, "bf16", q_scale=qs, kv_scale=ks, seed=seed)
+    dY = make_inputs(B, H, N, M, D, "bf16", seed=seed + 1)[2]
+    print(f"[backward] sharp case={case} seed={seed}", flush=True)
+    got = F.flare_backward(to_dev(Q), to_dev(K), to_dev(V), to_dev(dY))
+    torch.cuda.synchronize()
+    check(got, oracle.backward(Q, K, V, dY), "bf16", f"sharp {case}")
+
+
 def test_backward_workspace_variant_is_identical():
     B, H, N, M, D, dt = 2, 2, 900, 64, 32, "bf16"
     Q, K, V = make_inputs(B, H, N, M, D, dt, q_scale=0.5, seed=11)
