@@ -22,6 +22,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <algorithm>
+#include <type_traits>
 
 #include "launch.h"
 
@@ -120,6 +121,79 @@ __device__ __forceinline__ void dma16(const void* g, unsigned char* lds_wave_bas
     __builtin_amdgcn_global_load_lds((const void*)g, (void*)lds_wave_base, 16, 0, NT ? 2 : 0);
 }
 
+// Calls f(std::integral_constant<int, I>{}) for I = B .. E-1, so that the
+// index is a constant expression inside f.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// lds_tr_op2 with constant instruction offsets: operand 1 from a1 + O1 and
+// a2 + O1, operand 2 from a3 + O2 and a4 + O2 (LDS byte addresses). Waits for
+// its own results, as lds_tr_op2 does.
+template <int O1, int O2>
+__device__ __forceinline__ void lds_tr_op2_imm(uint32_t a1, uint32_t a2, uint32_t a3, uint32_t a4, bf16x8& o1,
+                                               bf16x8& o2) {
+    static_assert(O1 >= 0 && O1 < 65536 && O2 >= 0 && O2 < 65536, "LDS instruction offset range");
+    u32x2 w1, w2, w3, w4;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:%9\n\t"
+        "ds_read_b64_tr_b16 %3, %7 offset:%9\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(w4)
+        : "v"(a1), "v"(a2), "v"(a3), "v"(a4), "i"(O1), "i"(O2)
+        : "memory");
+    const u32x4 x = {w1[0], w1[1], w2[0], w2[1]};
+    const u32x4 y = {w3[0], w3[1], w4[0], w4[1]};
+    o1 = __builtin_bit_cast(bf16x8, x);
+    o2 = __builtin_bit_cast(bf16x8, y);
+}
+
+// 16-byte LDS reads from kofs[i] + O (LDS byte addresses), N at a time, in
+// inline asm that waits for its own results. Reads the compiler can see
+// after a global->LDS transfer make it wait for every transfer in flight
+// (it cannot tell which LDS bytes they write), which would drain the ring.
+template <int N, int O>
+__device__ __forceinline__ void lds_b128(const uint32_t* addr, bf16x8* r) {
+    static_assert(O >= 0 && O < 65536, "LDS instruction offset range");
+    if constexpr (N == 2) {
+        u32x4 x, y;
+        asm volatile(
+            "ds_read_b128 %0, %2 offset:%4\n\t"
+            "ds_read_b128 %1, %3 offset:%4\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(x), "=&v"(y)
+            : "v"(addr[0]), "v"(addr[1]), "i"(O)
+            : "memory");
+        r[0] = __builtin_bit_cast(bf16x8, x);
+        r[1] = __builtin_bit_cast(bf16x8, y);
+    } else {
+        static_assert(N % 4 == 0, "reads come in fours");
+#pragma unroll
+        for (int q = 0; q < N; q += 4) {
+            u32x4 x, y, z, w;
+            asm volatile(
+                "ds_read_b128 %0, %4 offset:%8\n\t"
+                "ds_read_b128 %1, %5 offset:%8\n\t"
+                "ds_read_b128 %2, %6 offset:%8\n\t"
+                "ds_read_b128 %3, %7 offset:%8\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(x), "=&v"(y), "=&v"(z), "=&v"(w)
+                : "v"(addr[q]), "v"(addr[q + 1]), "v"(addr[q + 2]), "v"(addr[q + 3]), "i"(O)
+                : "memory");
+            r[q] = __builtin_bit_cast(bf16x8, x);
+            r[q + 1] = __builtin_bit_cast(bf16x8, y);
+            r[q + 2] = __builtin_bit_cast(bf16x8, z);
+            r[q + 3] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+}
+
 template <int D, int MBW, int WM, int WT>
 struct EncShape {
     static constexpr int KB = D / 16, DB = D / 32, CH = D / 8, RB = 2 * D;
@@ -189,29 +263,62 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     // Tile j of the chunk -> LDS stage `stage`. The first NWI waves move the
     // tile, IPW transfers per tensor each: transfer (i, wave) fills LDS bytes
     // [(i*NWI + wave)*1024, +1024) of each tensor's tile, 16 per lane; the
-    // lane fetches the global chunk that the swizzle places there. Rows past
-    // the chunk end fetch the last valid token (finite data; their logits are
+    // lane fetches the global chunk that the swizzle places there. Its byte
+    // offset from the tile's first token is the same for every full tile, so
+    // those need only a wave-uniform base; the ragged last tile clamps rows
+    // past the chunk end to its last token (finite data; their logits are
     // masked). Waves that move nothing have no transfers to wait for.
-    auto issue = [&](int tile, int stage) {
+    constexpr bool KNT = D >= 64 && MBW >= 2;
+    const bool fixed_off = a.sn < (int64_t(1) << 24);  // T * sn * 2 bytes fit in 32 bits
+    uint32_t poff[IPW];
+    auto piece = [&](int i, int& row, int& ch) __attribute__((always_inline)) {
+        const int p = (i * NWI + wave) * 64 + lane;
+        row = p / CH;
+        ch = (p % CH) ^ ((tile_off<D>(row, 0) - row * RB) >> 4);
+    };
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        int row, ch;
+        piece(i, row, ch);
+        poff[i] = fixed_off ? (uint32_t)(row * (int)a.sn + ch * 8) * 2u : 0u;
+    }
+    auto issue = [&](int tile, int stage) __attribute__((always_inline)) {
         if (wave >= NWI) return;
         const int t0 = n0 + tile * T;
         unsigned char* st = smem + stage * SBYTES;
+        if (fixed_off && t0 + T <= n1) {
+            const unsigned char* kg = (const unsigned char*)(Kb + (int64_t)t0 * a.sn);
+            const unsigned char* vg = (const unsigned char*)(Vb + (int64_t)t0 * a.sn);
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int pc = i * NWI + wave;
-            const int p = pc * 64 + lane;
-            const int row = p / CH, pos = p % CH;
-            const int ch = pos ^ ((tile_off<D>(row, 0) - row * RB) >> 4);
-            const int n = min(t0 + row, n1 - 1);
-            const int64_t g = (int64_t)n * a.sn + ch * 8;
-            // V is read with the non-temporal policy: K, which the decode
-            // reads again, then stays in the last-level caches when it fits
-            // (measured 7-17% faster decodes on MI355X at 134 MB of K). K is
-            // non-temporal too for the D = 64 shapes with two latent blocks
-            // per wave (faster there; their K does not fit anyway).
-            constexpr bool KNT = D >= 64 && MBW >= 2;
-            dma16<KNT>(Kb + g, st + pc * 1024);
-            dma16<true>(Vb + g, st + T * RB + pc * 1024);
+            for (int i = 0; i < IPW; ++i) {
+                const int pc = i * NWI + wave;
+                // V is read with the non-temporal policy: K, which the decode
+                // reads again, then stays in the last-level caches when it
+                // fits (measured 7-17% faster decodes on MI355X at 134 MB of
+                // K). K is non-temporal too for the D = 64 shapes with two
+                // latent blocks per wave (faster there; their K does not fit
+                // anyway).
+                // (the offset is re-materialised here so that its zero
+                // extension stays next to the loads, which then take the
+                // uniform base in scalar registers; V goes first so that the
+                // compiler does not merge these loads with the clamped ones)
+                uint32_t po = poff[i];
+                asm volatile("" : "+v"(po));
+                dma16<true>(vg + po, st + T * RB + pc * 1024);
+                dma16<KNT>(kg + po, st + pc * 1024);
+            }
+            asm volatile("" ::: "memory");
+        } else {
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int pc = i * NWI + wave;
+                int row, ch;
+                piece(i, row, ch);
+                const int n = min(t0 + row, n1 - 1);
+                const int64_t g = (int64_t)n * a.sn + ch * 8;
+                dma16<KNT>(Kb + g, st + pc * 1024);
+                dma16<true>(Vb + g, st + T * RB + pc * 1024);
+            }
         }
     };
 
@@ -219,49 +326,71 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j)
         if (j < ntiles) issue(j, j);
+    // Everything in flight so far (the latent queries and the first tiles,
+    // issued back to back) lands together. Waiting for it here, once, leaves
+    // the loop with nothing but its own transfers outstanding; otherwise the
+    // compiler guards the loop's first use of the queries with a full wait
+    // on every pass.
+    wait_vmcnt<0>();
 
-    // Tile `it` (tail: the chunk's last, ragged tile, whose sub-blocks may be
-    // partial or empty; full tiles carry no masking code).
-    auto tile = [&](int it, bool tail) {
-        const unsigned char* kt = smem + (it % NS) * SBYTES;
-        const unsigned char* vt = kt + T * RB;
-        const int valid = n1 - (n0 + it * T);
+    // LDS byte offsets of this lane's operands in stage 0, sub-block 0 of its
+    // token group. Stage s, sub-block j and (for V) k-half kp add
+    // s*SBYTES + 32*j*RB + 16*kp*RB: the row swizzle repeats every 16 rows,
+    // so those are constants (instruction offsets in the unrolled loop).
+    // K rows as A operands of S^T = K Q^T; V^T operands (A of acc^T += V^T
+    // P^T; k = 16 tokens) read transposed from the row-major V tile: lane i of
+    // each 16-lane group receives element i%4 of source lanes 4k + i/4.
+    const int r0 = 32 * wt * SB;
+    uint32_t kofs[KB];
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-            const int sb = wt * SB + j;
-            const int nv = valid - 32 * sb;  // valid tokens in this sub-block
-            if (tail && nv <= 0) break;
+    for (int kb = 0; kb < KB; ++kb) kofs[kb] = lds_addr(smem) + tile_off<D>(r0 + enc_row_token(l32), 2 * kb + hi);
+    uint32_t vofs[DB][2];
+    {
+        const int g = lane >> 4, gi = lane & 15;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int second = 0; second < 2; ++second) {
+                const int row = r0 + 8 * (g >> 1) + (gi >> 2) + 4 * second;
+                const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+                vofs[db][second] = lds_addr(smem) + T * RB + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+            }
+    }
+
+    // Tile `it` in LDS stage S (a constant) plus sro bytes (0 in the unrolled
+    // loop; the stage offset otherwise). tail: the chunk's last, ragged tile,
+    // whose sub-blocks may be partial or empty.
+    auto tile = [&](int it, bool tail, auto stage_c, int sro) __attribute__((always_inline)) {
+        constexpr int S = decltype(stage_c)::value;
+        const int valid = n1 - (n0 + it * T);
+        static_for<0, SB>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int SOFF = S * SBYTES + 32 * j * RB;  // stage and sub-block
+            const int nv = valid - 32 * (wt * SB + j);     // valid tokens in this sub-block
+            if (tail && nv <= 0) return;
             // S^T for the 32 tokens x (32 * MBW) latents.
             bf16x8 ka[KB];
-            const int krow = 32 * sb + enc_row_token(l32);
+            uint32_t kad[KB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) ka[kb] = *(const bf16x8*)(kt + tile_off<D>(krow, 2 * kb + hi));
-            // V^T operands (A of acc^T += V^T P^T; k = 16 tokens), read
-            // transposed from the row-major tile: lane i of each 16-lane group
-            // receives element i%4 of source lanes 4k + i/4. Operand o covers
-            // tokens 16*(o/DB).. and rows d = 32*(o%DB)..
-            const int g = lane >> 4, gi = lane & 15;
-            auto vaddr = [&](int kp, int db, int second) {
-                const int row = 32 * sb + 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
-                const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
-                return vt + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
-            };
+            for (int kb = 0; kb < KB; ++kb) kad[kb] = kofs[kb] + sro;
+            lds_b128<KB, SOFF>(kad, ka);
             constexpr int NOP = 2 * DB;
             bf16x8 va[NOP];
-            auto read_v = [&]() {
-#pragma unroll
-                for (int o = 0; o < NOP; o += 2) {
-                    const int kp0 = o / DB, db0 = o % DB, kp1 = (o + 1) / DB, db1 = (o + 1) % DB;
-                    lds_tr_op2(vaddr(kp0, db0, 0), vaddr(kp0, db0, 1), vaddr(kp1, db1, 0), vaddr(kp1, db1, 1),
-                               va[o], va[o + 1]);
-                }
+            auto read_v = [&]() __attribute__((always_inline)) {
+                static_for<0, NOP / 2>([&](auto oc) __attribute__((always_inline)) {
+                    constexpr int o = 2 * decltype(oc)::value;
+                    constexpr int kp0 = o / DB, db0 = o % DB, kp1 = (o + 1) / DB, db1 = (o + 1) % DB;
+                    lds_tr_op2_imm<SOFF + 16 * kp0 * RB, SOFF + 16 * kp1 * RB>(
+                        vofs[db0][0] + sro, vofs[db0][1] + sro, vofs[db1][0] + sro, vofs[db1][1] + sro, va[o],
+                        va[o + 1]);
+                });
             };
             // At D >= 64 the reads are issued here, so their latency overlaps
             // the logits and the softmax (measured 3-4% faster on MI355X); at
             // D = 32 after the softmax (faster there).
             constexpr bool kVEarly = D >= 64;
             if constexpr (kVEarly) read_v();
-            auto mask = [&](f32x16& X) {
+            auto mask = [&](f32x16& X) __attribute__((always_inline)) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int tok = 16 * (i >> 3) + 8 * hi + (i & 7);
@@ -269,19 +398,19 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
                 }
             };
             // logits S (bf16 products, fp32 accumulation)
-            f32x16 S[MBW];
+            f32x16 Sx[MBW];
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
-                S[mb] = mfma(ka[0], qop[mb][0], f32x16{});
+                Sx[mb] = mfma(ka[0], qop[mb][0], f32x16{});
 #pragma unroll
-                for (int kb = 1; kb < KB; ++kb) S[mb] = mfma(ka[kb], qop[mb][kb], S[mb]);
-                if (tail) mask(S[mb]);
+                for (int kb = 1; kb < KB; ++kb) Sx[mb] = mfma(ka[kb], qop[mb][kb], Sx[mb]);
+                if (tail) mask(Sx[mb]);
             }
             bf16x8 pb[MBW][2];
             float ts[MBW];
             bool bad = false;
 #pragma unroll
-            for (int mb = 0; mb < MBW; ++mb) exp2_pack(S[mb], c, mu[mb], pb[mb][0], pb[mb][1]);
+            for (int mb = 0; mb < MBW; ++mb) exp2_pack(Sx[mb], c, mu[mb], pb[mb][0], pb[mb][1]);
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
                 ts[mb] = colsum(csel, pb[mb][0], pb[mb][1], f32x4{})[0];
@@ -294,14 +423,14 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
                 for (int mb = 0; mb < MBW; ++mb) {
                     float mx = -INFINITY;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[mb][i]);
+                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, Sx[mb][i]);
                     const float mnew = fmaxf(mu[mb], pair_max(mx) * c);
                     const float alpha = (mu[mb] == -INFINITY) ? 0.0f : exp2_fast(mu[mb] - mnew);
                     ps[mb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) acc[mb][db] *= alpha;
                     mu[mb] = mnew;
-                    exp2_pack(S[mb], c, mu[mb], pb[mb][0], pb[mb][1]);
+                    exp2_pack(Sx[mb], c, mu[mb], pb[mb][0], pb[mb][1]);
                     ts[mb] = colsum(csel, pb[mb][0], pb[mb][1], f32x4{})[0];
                 }
             }
@@ -315,23 +444,36 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
 #pragma unroll
                 for (int mb = 0; mb < MBW; ++mb) acc[mb][db] = mfma(va[o], pb[mb][kp], acc[mb][db]);
             }
-        }
+        });
     };
     const bool ragged = (n1 - n0) % T != 0;
     const int nfull = ragged ? ntiles - 1 : ntiles;
-    for (int it = 0; it < ntiles; ++it) {
-        // tile `it` is complete once at most the transfers of the (up to NS-2)
-        // later tiles issued so far are outstanding
+    // Tile `it` is complete once at most the transfers of the (up to NS-2)
+    // later tiles issued so far are outstanding; then the stage that tile
+    // it-1 used is free for tile it+NS-1.
+    auto sync_issue = [&](int it) __attribute__((always_inline)) {
         if (it + NS - 2 < ntiles)
             wait_vmcnt<(NS - 2) * 2 * IPW>();
         else
             wait_vmcnt<0>();
         raw_barrier();
         if (it + NS - 1 < ntiles) issue(it + NS - 1, (it + NS - 1) % NS);
-        if (it == nfull) break;  // only the ragged tile is left
-        tile(it, false);
+    };
+    int it = 0;
+    // Full tiles NS at a time, each stage's offsets constant (they fit the
+    // 16-bit instruction offset for D <= 64); then the rest one at a time.
+    constexpr bool kImm = (NS - 1) * SBYTES + (SB - 1) * 32 * RB + 16 * RB < 65536;
+    if constexpr (kImm) {
+        for (; it + NS <= nfull; it += NS)
+            static_for<0, NS>([&](auto sc) __attribute__((always_inline)) {
+                sync_issue(it + decltype(sc)::value);
+                tile(it + decltype(sc)::value, false, sc, 0);
+            });
     }
-    if (ragged) tile(nfull, true);
+    for (; it < ntiles; ++it) {
+        sync_issue(it);
+        tile(it, it == nfull, std::integral_constant<int, 0>{}, (it % NS) * SBYTES);
+    }
 
     // Merge the WT token waves of each latent group (tile buffers are free
     // once every wave is past its last read; all transfers were waited for).
