@@ -829,7 +829,8 @@ void decode_bf16(DecodeArgs a) {
     const int Mp = a.Mp, MB = Mp / 32;
     const int zs = 2 * Mp + 16;  // bytes per Z^T row (padded)
     extern __shared__ __attribute__((aligned(16))) unsigned char dsm[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block indices live in scalar registers
     const int hi = lane >> 5, l32 = lane & 31;
     const int bh = blockIdx.y;
     const int b = bh / a.H, h = bh - b * a.H;
@@ -905,12 +906,33 @@ void decode_bf16(DecodeArgs a) {
     // instead: every column of the logits belongs to one token, so they only
     // feed outputs that are never stored, and the loads stay unconditional
     // (a fixed number in flight, which the explicit waits below rely on).
+    // A lane's byte offset from its block's first token row is the same for
+    // every block (when T * sn * 2 bytes fit in 32 bits), so whole blocks are
+    // addressed from a uniform base in scalar registers.
+    const bool fixed_off = sn < (int64_t(1) << 24);
+    uint32_t roff[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) roff[tb] = fixed_off ? (uint32_t)((32 * tb + l32) * (int)sn + 8 * hi) * 2u : 0u;
     auto kload = [&](int bk, bf16x8 (&dst)[TB][KB]) {
+        const int nb = bk * 32 * TB;
+        if (fixed_off && nb + 32 * TB <= N) {
+            const unsigned char* kg = (const unsigned char*)(Kb + (int64_t)nb * sn);
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            const int n = min(bk * 32 * TB + 32 * tb + l32, N - 1);
+            for (int tb = 0; tb < TB; ++tb) {
+                uint32_t o = roff[tb];
+                asm volatile("" : "+v"(o));  // keeps the zero extension next to the loads
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) dst[tb][kb] = *(const bf16x8*)(Kb + (int64_t)n * sn + 16 * kb + 8 * hi);
+                for (int kb = 0; kb < KB; ++kb) dst[tb][kb] = *(const bf16x8*)(kg + o + 32 * kb);
+            }
+            asm volatile("" ::: "memory");
+        } else {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int n = min(nb + 32 * tb + l32, N - 1);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    dst[tb][kb] = *(const bf16x8*)(Kb + (int64_t)n * sn + 16 * kb + 8 * hi);
+            }
         }
     };
     auto qread = [&](int mb, bf16x8 (&qa)[KB]) {
@@ -1088,15 +1110,31 @@ void decode_bf16(DecodeArgs a) {
     // Y rows of block ypend (if any) to memory, 32 bytes per lane and run.
     auto flush = [&]() {
         if (ypend < 0) return;
+        const int nb = ypend * 32 * TB;
+        if (fixed_off && nb + 32 * TB <= N) {
+            unsigned char* yg = (unsigned char*)(Yb + (int64_t)nb * sn);
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            const int n = ypend * 32 * TB + 32 * tb + l32;
-            if (n < N) {
-                uint16_t* dst = Yb + (int64_t)n * sn + 16 * hi;
+            for (int tb = 0; tb < TB; ++tb) {
+                uint32_t o = roff[tb] + 16 * hi;  // the row's d = 16*hi.. run (roff holds 8*hi)
+                asm volatile("" : "+v"(o));
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    *(bf16x8*)(dst + 32 * db) = ypk[tb][2 * db];
-                    *(bf16x8*)(dst + 32 * db + 8) = ypk[tb][2 * db + 1];
+                    *(bf16x8*)(yg + o + 64 * db) = ypk[tb][2 * db];
+                    *(bf16x8*)(yg + o + 64 * db + 16) = ypk[tb][2 * db + 1];
+                }
+            }
+            asm volatile("" ::: "memory");
+        } else {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int n = nb + 32 * tb + l32;
+                if (n < N) {
+                    uint16_t* dst = Yb + (int64_t)n * sn + 16 * hi;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        *(bf16x8*)(dst + 32 * db) = ypk[tb][2 * db];
+                        *(bf16x8*)(dst + 32 * db + 8) = ypk[tb][2 * db + 1];
+                    }
                 }
             }
         }
