@@ -38,6 +38,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 typedef float f32x4c __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
+template <int G>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int bh = blockIdx.y;
     const int D = a.D, D4 = D / 4;
@@ -50,18 +51,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const float* __restrict__ sg = a.in.sig + row0;
     const float* __restrict__ ac = a.in.acc + row0 * D + d;
     const int64_t sacc = (int64_t)Mp * D;
-    // chunks in groups of 8: all loads of a group are issued before any use
-    constexpr int G = 8;
-    float mx = -INFINITY;
-    for (int c0 = 0; c0 < C; c0 += G) {
-        float mv[G];
-#pragma unroll
-        for (int j = 0; j < G; ++j) mv[j] = (c0 + j < C) ? mu[(int64_t)(c0 + j) * Mp] : -INFINITY;
-#pragma unroll
-        for (int j = 0; j < G; ++j) mx = fmaxf(mx, mv[j]);
-    }
+    // One pass over the chunks in groups of G: every load of a group is
+    // issued before any use (one memory round trip per group), and a group
+    // whose largest offset exceeds the running one rescales the sums first
+    // (exact algebra: both are scaled by the same power of two).
+    float mx = -INFINITY, den = 0.0f;
     f32x4c num = {0.0f, 0.0f, 0.0f, 0.0f};
-    float den = 0.0f;
     for (int c0 = 0; c0 < C; c0 += G) {
         float mv[G], sv[G];
         f32x4c av[G];
@@ -71,6 +66,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
             mv[j] = in ? mu[(int64_t)(c0 + j) * Mp] : -INFINITY;
             av[j] = in ? *(const f32x4c*)(ac + (int64_t)(c0 + j) * sacc) : f32x4c{0.0f, 0.0f, 0.0f, 0.0f};
             sv[j] = in ? sg[(int64_t)(c0 + j) * Mp] : 0.0f;
+        }
+        float gm = mx;
+#pragma unroll
+        for (int j = 0; j < G; ++j) gm = fmaxf(gm, mv[j]);
+        if (gm > mx) {
+            const float r = (mx == -INFINITY) ? 0.0f : exp2f(mx - gm);
+            num *= r;
+            den *= r;
+            mx = gm;
         }
 #pragma unroll
         for (int j = 0; j < G; ++j) {
@@ -265,7 +269,11 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { FLARE_F32_DIS
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     if (a.D % 4 != 0) return hipErrorInvalidValue;
     dim3 grid((a.M * (a.D / 4) + 255) / 256, a.BH), block(256);
-    hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, a);
+    // groups of 8 chunks when that covers them all (fewer registers), else 16
+    if (a.C <= 8)
+        hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, s, a);
     return hipGetLastError();
 }
 
