@@ -328,7 +328,8 @@ template <int D>
 __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
     constexpr int KB = D / 16;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M, Mp = (M + 31) & ~31, MB = Mp / 32;
     const float c = a.c;
@@ -428,7 +429,8 @@ template <int D>
 __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
     constexpr int KB = D / 16, DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M, Mp = (M + 31) & ~31, MB = Mp / 32;
     const float c = a.c;
@@ -568,7 +570,8 @@ template <int D, bool DQ, int MBW>  // MBW: latent blocks per wave at most
 __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
     constexpr int KB = D / 16, DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int chunk = blockIdx.x, bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M, Mp = (M + 31) & ~31, MB = Mp / 32;
     const int n0 = chunk * a.chunk_len, n1 = min(N, n0 + a.chunk_len);
