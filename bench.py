@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=2, help="workload number 1-5 (default 2)")
+    p.add_argument("--workload", type=int, default=2, help="workload number 1-6 (default 2)")
     p.add_argument("--variant", choices=["flare", "skill", "backward"], default="flare",
                    help="flare: the workload's forward (default); skill: the FLARE skill page's layer, "
                         "flare_encode then flare_attend with separate token queries; backward: flare_backward "
