@@ -59,6 +59,10 @@ def _load():
         lib.flare_oracle_backward.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                               _dp, _dp, _dp]
         lib.flare_oracle_backward.restype = ctypes.c_int
+        for f in ("flare_oracle_encode_backward", "flare_oracle_pp_backward"):
+            getattr(lib, f).argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _dp,
+                                        _dp, _dp]
+            getattr(lib, f).restype = ctypes.c_int
         lib.flare_oracle_attend.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
                                             ctypes.c_int64, _dp]
         for f in ("flare_oracle_encode", "flare_oracle_decode", "flare_oracle_forward", "flare_oracle_pp_forward",
@@ -160,6 +164,28 @@ def backward_head(Q, K, V, dY):
     return dQ, dK, dV
 
 
+def encode_backward_head(Q, K, V, dZ):
+    """(dQ[M,D], dK[N,D], dV[N,D]) of one head's encode for the upstream gradient dZ[M,D]."""
+    Q, K, V, dZ = _c64(Q), _c64(K), _c64(V), _c64(dZ)
+    N, D = K.shape
+    M = Q.shape[0]
+    dQ, dK, dV = np.empty((M, D)), np.empty((N, D)), np.empty((N, D))
+    _check(_load().flare_oracle_encode_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dZ), N, M, D, _ptr(dQ), _ptr(dK),
+                                                _ptr(dV)), "encode_backward")
+    return dQ, dK, dV
+
+
+def pp_backward_head(Q, K, V, dY):
+    """(dQ[M,D], dK[N,D], dV[N,D]) of one head's FLARE++ forward for the upstream gradient dY[N,D]."""
+    Q, K, V, dY = _c64(Q), _c64(K), _c64(V), _c64(dY)
+    N, D = K.shape
+    M = Q.shape[0]
+    dQ, dK, dV = np.empty((M, D)), np.empty((N, D)), np.empty((N, D))
+    _check(_load().flare_oracle_pp_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dY), N, M, D, _ptr(dQ), _ptr(dK),
+                                            _ptr(dV)), "pp_backward")
+    return dQ, dK, dV
+
+
 def pp_forward_head(Q, K, V, rows: Optional[np.ndarray] = None):
     """(Y, Q', Z) of one head for FLARE++."""
     Q, K, V = _c64(Q), _c64(K), _c64(V)
@@ -221,6 +247,22 @@ def backward(Q, K, V, dY):
         for h in range(H):
             q, k, v, g = widen(Q[h]), widen(K[b, h]), widen(V[b, h]), widen(dY[b, h])
             dq, dK[b, h], dV[b, h] = backward_head(q, k, v, g)
+            dQ[h] += dq
+    return dQ, dK, dV
+
+
+def pp_backward(Q, K, V, dY):
+    """(dQ[H,M,D], dK[B,H,N,D], dV[B,H,N,D]) of the FLARE++ forward, fp64. Q is shared over the
+    batch, so dQ sums the batch entries' gradients."""
+    B, H, N, D = K.shape
+    M = Q.shape[-2]
+    dQ = np.zeros((H, M, D))
+    dK = np.empty((B, H, N, D))
+    dV = np.empty((B, H, N, D))
+    for b in range(B):
+        for h in range(H):
+            q, k, v, g = widen(Q[h]), widen(K[b, h]), widen(V[b, h]), widen(dY[b, h])
+            dq, dK[b, h], dV[b, h] = pp_backward_head(q, k, v, g)
             dQ[h] += dq
     return dQ, dK, dV
 

@@ -295,6 +295,97 @@ done:
     return rc;
 }
 
+/* Gradients of one head's encode alone, Z = encode(Q, K, V) (defined above),
+ * for an upstream gradient dZ[M][D]: dQ[M][D], dK[N][D], dV[N][D]. The chain
+ * rule through the one softmax, in fp64:
+ *   A[m][n] = softmax_n(l[m][.]),  l = s Q K^T,  Z = A V;
+ *   dV = A^T dZ,  dl[m][n] = A[m][n] (<dZ[m], V[n]> - <dZ[m], Z[m]>),
+ *   dQ = s dl K,  dK = s dl^T Q.
+ * Returns 0, or -1 when scratch memory cannot be allocated. */
+int flare_oracle_encode_backward(const double* Q, const double* K, const double* V, const double* dZ,
+                                 int64_t N, int64_t M, int64_t D, double* dQ, double* dK, double* dV) {
+    const double s = 1.0 / sqrt((double)D);
+    double* A = (double*)malloc((size_t)M * N * sizeof(double));
+    double* Z = (double*)malloc((size_t)M * D * sizeof(double));
+    double* dl = (double*)malloc((size_t)M * N * sizeof(double));
+    int rc = 0;
+    if (!A || !Z || !dl) {
+        rc = -1;
+        goto done;
+    }
+    for (int64_t m = 0; m < M; ++m) { /* softmax over n of the logits */
+        double mx = -INFINITY, den = 0.0;
+        for (int64_t n = 0; n < N; ++n) mx = fmax(mx, s * dot(Q + m * D, K + n * D, D));
+        for (int64_t n = 0; n < N; ++n) den += (A[m * N + n] = exp(s * dot(Q + m * D, K + n * D, D) - mx));
+        for (int64_t n = 0; n < N; ++n) A[m * N + n] /= den;
+    }
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t d = 0; d < D; ++d) {
+            double z = 0.0;
+            for (int64_t n = 0; n < N; ++n) z += A[m * N + n] * V[n * D + d];
+            Z[m * D + d] = z;
+        }
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t d = 0; d < D; ++d) {
+            double g = 0.0;
+            for (int64_t m = 0; m < M; ++m) g += A[m * N + n] * dZ[m * D + d];
+            dV[n * D + d] = g;
+        }
+    for (int64_t m = 0; m < M; ++m) {
+        const double gz = dot(dZ + m * D, Z + m * D, D);
+        for (int64_t n = 0; n < N; ++n) dl[m * N + n] = A[m * N + n] * (dot(dZ + m * D, V + n * D, D) - gz);
+    }
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t d = 0; d < D; ++d) {
+            double g = 0.0;
+            for (int64_t n = 0; n < N; ++n) g += dl[m * N + n] * K[n * D + d];
+            dQ[m * D + d] = s * g;
+        }
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t d = 0; d < D; ++d) {
+            double g = 0.0;
+            for (int64_t m = 0; m < M; ++m) g += dl[m * N + n] * Q[m * D + d];
+            dK[n * D + d] = s * g;
+        }
+done:
+    free(A); free(Z); free(dl);
+    return rc;
+}
+
+/* Gradients of one head's FLARE++ forward (defined above: Q' = Q +
+ * encode(Q, K, V), then Y = FLARE(Q', K, V)) for an upstream gradient dY[N][D].
+ * The chain rule through the two stages: the FLARE backward with queries Q'
+ * gives dQ' and the second stage's dK, dV; the encode backward with dZ = dQ'
+ * gives the first stage's; dQ = dQ' + dQ(encode), dK and dV are the sums.
+ * Returns 0, or -1 when scratch memory cannot be allocated. */
+int flare_oracle_pp_backward(const double* Q, const double* K, const double* V, const double* dY,
+                             int64_t N, int64_t M, int64_t D, double* dQ, double* dK, double* dV) {
+    double* Qp = (double*)malloc((size_t)M * D * sizeof(double));
+    double* dQp = (double*)malloc((size_t)M * D * sizeof(double));
+    double* dK1 = (double*)malloc((size_t)N * D * sizeof(double));
+    double* dV1 = (double*)malloc((size_t)N * D * sizeof(double));
+    int rc = 0;
+    if (!Qp || !dQp || !dK1 || !dV1) {
+        rc = -1;
+        goto done;
+    }
+    rc = flare_oracle_encode(Q, K, V, N, M, D, Qp);
+    if (rc) goto done;
+    for (int64_t i = 0; i < M * D; ++i) Qp[i] += Q[i];
+    rc = flare_oracle_backward(Qp, K, V, dY, N, M, D, dQp, dK, dV);
+    if (rc) goto done;
+    rc = flare_oracle_encode_backward(Q, K, V, dQp, N, M, D, dQ, dK1, dV1);
+    if (rc) goto done;
+    for (int64_t i = 0; i < M * D; ++i) dQ[i] += dQp[i];
+    for (int64_t i = 0; i < N * D; ++i) {
+        dK[i] += dK1[i];
+        dV[i] += dV1[i];
+    }
+done:
+    free(Qp); free(dQp); free(dK1); free(dV1);
+    return rc;
+}
+
 /* Number of OpenMP threads a parallel region uses (1 without OpenMP). */
 int flare_oracle_threads(void) {
 #ifdef _OPENMP

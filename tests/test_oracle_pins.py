@@ -318,3 +318,70 @@ def test_backward_matches_central_differences_of_the_forward():
             arr[idx] = a0
             fd[idx] = (fp - fm) / (2 * h)
         np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-8)
+
+
+# ------------------------------------------------------------ FLARE++ backward
+def torch_pp_grads(Q, K, V, dY):
+    """Gradients of sum(Y * dY) for Y = FLARE++(Q, K, V), by torch fp64 autograd through three SDPA
+    calls: Z0 = SDPA(Q, K, V), Q' = Q + Z0, Y = SDPA(K, Q', SDPA(Q', K, V)) (Q shared over the batch)."""
+    q = torch.tensor(Q, dtype=torch.float64, requires_grad=True)
+    k = torch.tensor(K, dtype=torch.float64, requires_grad=True)
+    v = torch.tensor(V, dtype=torch.float64, requires_grad=True)
+    qb = q.unsqueeze(0).expand(k.shape[0], -1, -1, -1)
+    qp = qb + F.scaled_dot_product_attention(qb, k, v)
+    z = F.scaled_dot_product_attention(qp, k, v)
+    y = F.scaled_dot_product_attention(k, qp, z)
+    (y * torch.tensor(dY, dtype=torch.float64)).sum().backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+@pytest.mark.parametrize("N,M,D", [(37, 5, 8), (70, 33, 16), (1, 1, 4)])
+def test_encode_backward_is_autograd_of_one_sdpa_call(N, M, D):
+    Q, K, V, dZ = rand(M, D), rand(N, D), rand(N, D), rand(M, D)
+    got = oracle.encode_backward_head(Q, K, V, dZ)
+    q, k, v = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Q, K, V))
+    (F.scaled_dot_product_attention(q, k, v) * torch.tensor(dZ, dtype=torch.float64)).sum().backward()
+    for g, w, name in zip(got, (q.grad.numpy(), k.grad.numpy(), v.grad.numpy()), ("dQ", "dK", "dV")):
+        np.testing.assert_allclose(g, w, rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+@pytest.mark.parametrize("B,H,N,M,D", [(2, 2, 37, 5, 8), (1, 1, 70, 33, 16), (1, 1, 1, 1, 4)])
+def test_pp_backward_is_autograd_of_three_sdpa_calls(B, H, N, M, D):
+    Q, K, V, dY = rand(H, M, D), rand(B, H, N, D), rand(B, H, N, D), rand(B, H, N, D)
+    got = oracle.pp_backward(Q, K, V, dY)
+    want = torch_pp_grads(Q, K, V, dY)
+    for g, w, name in zip(got, want, ("dQ", "dK", "dV")):
+        np.testing.assert_allclose(g, w, rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_pp_backward_matches_central_differences_of_the_forward():
+    B, H, N, M, D = 2, 1, 5, 3, 4
+    Q, K, V, dY = rand(H, M, D), rand(B, H, N, D), rand(B, H, N, D), rand(B, H, N, D)
+    dQ, dK, dV = oracle.pp_backward(Q, K, V, dY)
+
+    def f(q, k, v):
+        return float(np.sum(oracle.pp_forward(q, k, v)[0] * dY))
+
+    h = 1e-6
+    for arr, grad in ((Q, dQ), (K, dK), (V, dV)):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            a0 = arr[idx]
+            arr[idx] = a0 + h
+            fp = f(Q, K, V)
+            arr[idx] = a0 - h
+            fm = f(Q, K, V)
+            arr[idx] = a0
+            fd[idx] = (fp - fm) / (2 * h)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_pp_backward_differs_from_the_flare_backward():
+    # the first stage contributes: dropping it (the FLARE backward at Q' alone) changes every gradient
+    B, H, N, M, D = 1, 1, 20, 4, 8
+    Q, K, V, dY = rand(H, M, D), rand(B, H, N, D), rand(B, H, N, D), rand(B, H, N, D)
+    pp = oracle.pp_backward(Q, K, V, dY)
+    Qp = oracle.pp_forward(Q, K, V)[1][:, :, :, :].reshape(B, H, M, D)[0]
+    second = oracle.backward(Qp, K, V, dY)
+    for a, b in zip(pp, second):
+        assert np.max(np.abs(a - b)) > 1e-3
