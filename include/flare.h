@@ -75,7 +75,8 @@ typedef enum {
     FLARE_OP_DECODE = 1,
     FLARE_OP_FORWARD = 2,
     FLARE_OP_PP_FORWARD = 3,
-    FLARE_OP_BACKWARD = 4 /* flare_backward (workspace sizing only) */
+    FLARE_OP_BACKWARD = 4,   /* flare_backward (workspace sizing only) */
+    FLARE_OP_PP_BACKWARD = 5 /* flare_pp_backward (workspace sizing only) */
 } flare_op;
 
 /* Encode: Y := Z[B][H][M][D] = softmax_n(s Q K^T) V for every (b, h).
@@ -190,7 +191,7 @@ flare_status flare_attend(const void* q, const void* Z, void* Y,
  * D in {8, 16, 24, 32, 48, 64} (bf16: 32 and 64) with the forward's M range;
  * otherwise FLARE_ERR_UNSUPPORTED. Outputs may not overlap inputs or each
  * other. The _ws variant takes flare_workspace_size(FLARE_OP_BACKWARD, ...)
- * bytes of caller-owned scratch memory. FLARE++ has no backward here. */
+ * bytes of caller-owned scratch memory. */
 flare_status flare_backward(const void* Q, const void* K, const void* V, const void* dY,
                             void* dQ, void* dK, void* dV,
                             int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
@@ -199,6 +200,28 @@ flare_status flare_backward_ws(const void* Q, const void* K, const void* V, cons
                                void* dQ, void* dK, void* dV,
                                int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
                                flare_dtype dtype, hipStream_t stream, void* workspace, size_t ws_bytes);
+
+/* Backward of flare_pp_forward (FLARE++ skill page, "Core Mechanism"; FLARE++
+ * abstract: Q' = Q + encode(Q, K, V), then the FLARE forward with Q'). The
+ * chain rule through the two stages: the FLARE backward at Q' (one batch
+ * entry at a time, Q' being per entry) gives dQ' and the second stage's dK,
+ * dV; the encode's backward for dZ = dQ' (dV += A^T dQ', dl = A (dQ' V^T -
+ * <dQ', Z>), dQ += s dl K, dK += s dl^T Q, with A, Z of the first encode)
+ * gives the first stage's; dQ = sum over the batch of dQ' plus the first
+ * stage's. Same arguments, layouts, dtypes, support range and error
+ * behaviour as flare_backward; each stage's gradients are summed in fp32 and
+ * rounded once (dQ' is rounded to the operator dtype before it feeds the
+ * first stage). The _ws variant takes flare_workspace_size(
+ * FLARE_OP_PP_BACKWARD, ...) bytes. */
+flare_status flare_pp_backward(const void* Q, const void* K, const void* V, const void* dY,
+                               void* dQ, void* dK, void* dV,
+                               int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                               flare_dtype dtype, hipStream_t stream);
+flare_status flare_pp_backward_ws(const void* Q, const void* K, const void* V, const void* dY,
+                                  void* dQ, void* dK, void* dV,
+                                  int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                  flare_dtype dtype, hipStream_t stream,
+                                  void* workspace, size_t workspace_bytes);
 
 /* Static text for a status code. */
 const char* flare_status_string(flare_status s);

@@ -414,6 +414,27 @@ flare_status exec_alloc(flare_op op, const void* Q, const void* K, const void* V
     return st;
 }
 
+// FLARE++ backward workspace: one FLARE backward's (sized for the whole batch
+// and for one batch entry, whichever is larger), then Q' and dQ' [B][H][M][D],
+// a zero dY, the first stage's dK and dV [B][H][N][D] and its dQ [H][M][D].
+struct PPLayout {
+    size_t bw, qp, dqp, dy0, dk1, dv1, dq1, total;
+};
+PPLayout pp_layout(const Plan& pf, const Plan& p1) {
+    PPLayout L{};
+    const size_t qm = size_t(pf.BH) * pf.M * pf.D * pf.esize, tok = size_t(pf.BH) * pf.N * pf.D * pf.esize;
+    size_t off = align256(std::max(pf.total[FLARE_OP_BACKWARD], p1.total[FLARE_OP_BACKWARD]));
+    L.bw = 0;
+    L.qp = off;  off = align256(off + qm);
+    L.dqp = off; off = align256(off + qm);
+    L.dy0 = off; off = align256(off + tok);
+    L.dk1 = off; off = align256(off + tok);
+    L.dv1 = off; off = align256(off + tok);
+    L.dq1 = off; off = align256(off + size_t(pf.H) * pf.M * pf.D * pf.esize);
+    L.total = off;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -436,9 +457,14 @@ flare_status flare_pp_forward(const void* Q, const void* K, const void* V, void*
 }
 
 size_t flare_workspace_size(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype) {
-    if (op < FLARE_OP_ENCODE || op > FLARE_OP_BACKWARD) return 0;
+    if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_BACKWARD) return 0;
     Plan p;
     if (make_plan(B, H, N, M, D, dtype, &p) != FLARE_OK) return 0;
+    if (op == FLARE_OP_PP_BACKWARD) {
+        Plan p1;
+        if (make_plan(1, H, N, M, D, dtype, &p1) != FLARE_OK) return 0;
+        return pp_layout(p, p1).total;
+    }
     return p.total[op];
 }
 
@@ -464,47 +490,12 @@ flare_status flare_pp_forward_ws(const void* Q, const void* K, const void* V, vo
 
 namespace {
 
-flare_status backward(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK, void* dV,
-                      int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dt, hipStream_t s,
-                      void* wsv, size_t ws_bytes, bool alloc) {
-    Plan p;
-    g_last_error.clear();
-    flare_status st = make_plan(B, H, N, M, D, dt, &p);
-    if (st != FLARE_OK) return st;
-    st = set_layout(&p, FLARE_LAYOUT_BHND);
-    if (st != FLARE_OK) return st;
-    if (!flare::backward_supports(int(D)))
-        return fail(FLARE_ERR_UNSUPPORTED, "the backward supports D in {8, 16, 24, 32, 48, 64}");
-    const void* ins[4] = {Q, K, V, dY};
-    void* outs[3] = {dQ, dK, dV};
-    for (const void* t : ins)
-        if (!t) return fail(FLARE_ERR_INVALID_ARG, "null tensor pointer");
-    for (void* t : outs)
-        if (!t) return fail(FLARE_ERR_INVALID_ARG, "null tensor pointer");
-    for (const void* t : {Q, K, V, dY, (const void*)dQ, (const void*)dK, (const void*)dV})
-        if (uintptr_t(t) % 16 != 0) return fail(FLARE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    const size_t nq = size_t(p.H) * p.M * p.D * p.esize, nt = size_t(p.BH) * p.N * p.D * p.esize;
-    const size_t nin[4] = {nq, nt, nt, nt}, nout[3] = {nq, nt, nt};
-    for (int i = 0; i < 3; ++i) {
-        for (int j = 0; j < 4; ++j)
-            if (overlaps(outs[i], nout[i], ins[j], nin[j])) return fail(FLARE_ERR_INVALID_ARG, "output overlaps an input");
-        for (int j = 0; j < i; ++j)
-            if (overlaps(outs[i], nout[i], outs[j], nout[j])) return fail(FLARE_ERR_INVALID_ARG, "outputs overlap");
-    }
-    const size_t need = p.total[FLARE_OP_BACKWARD];
-    if (alloc) {
-        const char* f = std::getenv("FLARE_TEST_FAIL_ALLOC");
-        if (f && std::strcmp(f, "1") == 0) return fail(FLARE_ERR_NO_MEMORY, "allocation failure injected by FLARE_TEST_FAIL_ALLOC");
-        hipError_t e = hipMallocAsync(&wsv, need, s);
-        if (e != hipSuccess || !wsv) return fail(FLARE_ERR_NO_MEMORY, std::string("hipMallocAsync: ") + hipGetErrorString(e));
-    } else {
-        if (!wsv) return fail(FLARE_ERR_INVALID_ARG, "workspace pointer is null");
-        if (uintptr_t(wsv) % 256 != 0) return fail(FLARE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-        if (ws_bytes < need)
-            return fail(FLARE_ERR_INVALID_ARG,
-                        "workspace too small: need " + std::to_string(need) + " bytes, got " + std::to_string(ws_bytes));
-    }
-    char* ws = (char*)wsv;
+// Launches of one FLARE backward over a plan's (b, h) problems, in the
+// workspace ws (laid out by the plan). With dz_given (the operator dtype,
+// [B][H][M][D]) the gradient of Z is that tensor instead of Btᵀ dY: the
+// FLARE++ backward uses it, with dY zero, for its first stage (the encode).
+hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void* V, const void* dY, void* dQ,
+                         void* dK, void* dV, char* ws, hipStream_t s, const void* dz_given) {
     // forward encode and combine: Z, mu* and sig*
     hipError_t e = run_encode_partial(p, Q, 0, K, V, ws, s);
     if (e == hipSuccess)
@@ -523,28 +514,143 @@ flare_status backward(const void* Q, const void* K, const void* V, const void* d
     a.part = (float*)(ws + p.off_acc);
     a.BH = p.BH; a.H = int(p.H); a.N = int(p.N); a.M = int(p.M); a.D = int(p.D);
     a.C = p.C; a.chunk_len = p.chunk_len;
-    a.s = float(1.0 / std::sqrt(double(D)));
+    a.s = float(1.0 / std::sqrt(double(p.D)));
     a.c = p.c;
-    a.bf16 = dt == FLARE_BF16;
+    a.bf16 = p.dt == FLARE_BF16;
     // bf16 heads whose Q, Z and dZ fit in LDS: the per-token kernels on the
     // matrix core; otherwise (and for fp32) the fp32 VALU kernels
-    const bool mc = dt == FLARE_BF16 && flare::bw_bf16_fits(int(M), int(D));
+    const bool mc = a.bf16 && flare::bw_bf16_fits(int(p.M), int(p.D));
     if (e == hipSuccess)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_stats_bf16(a, s) : flare::launch_bw_stats(a, s); });
-    if (e == hipSuccess)
-        e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, false, s) : flare::launch_bw_dz(a, s); });
-    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(a, s); });
+    if (dz_given) {
+        // dZ given: one "chunk" of partials holding it, merged as usual
+        // (which also forms gam = <dZ, Z>)
+        if (e == hipSuccess)
+            e = timed(3, s, [&] { return flare::launch_widen(dz_given, a.part, int64_t(p.BH) * p.M * p.D, a.bf16, s); });
+        flare::BackwardArgs one = a;
+        one.C = 1;
+        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(one, s); });
+    } else {
+        if (e == hipSuccess)
+            e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, false, s) : flare::launch_bw_dz(a, s); });
+        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(a, s); });
+    }
     if (e == hipSuccess)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_dkdv_bf16(a, s) : flare::launch_bw_dkdv(a, s); });
     if (e == hipSuccess)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, true, s) : flare::launch_bw_dq(a, s); });
     if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(a, s); });
-    flare_status res = e == hipSuccess ? FLARE_OK : hip_fail(e, "kernel launch");
+    return e;
+}
+
+// Shared argument checks of the backward entry points: null and alignment,
+// outputs overlapping inputs or each other.
+flare_status check_backward_ptrs(const Plan& p, const void* Q, const void* K, const void* V, const void* dY,
+                                 void* dQ, void* dK, void* dV) {
+    const void* ins[4] = {Q, K, V, dY};
+    void* outs[3] = {dQ, dK, dV};
+    for (const void* t : ins)
+        if (!t) return fail(FLARE_ERR_INVALID_ARG, "null tensor pointer");
+    for (void* t : outs)
+        if (!t) return fail(FLARE_ERR_INVALID_ARG, "null tensor pointer");
+    for (const void* t : {Q, K, V, dY, (const void*)dQ, (const void*)dK, (const void*)dV})
+        if (uintptr_t(t) % 16 != 0) return fail(FLARE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const size_t nq = size_t(p.H) * p.M * p.D * p.esize, nt = size_t(p.BH) * p.N * p.D * p.esize;
+    const size_t nin[4] = {nq, nt, nt, nt}, nout[3] = {nq, nt, nt};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(outs[i], nout[i], ins[j], nin[j])) return fail(FLARE_ERR_INVALID_ARG, "output overlaps an input");
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], nout[i], outs[j], nout[j])) return fail(FLARE_ERR_INVALID_ARG, "outputs overlap");
+    }
+    return FLARE_OK;
+}
+
+// Workspace: caller's (checked against need) or stream-ordered allocation.
+flare_status get_workspace(size_t need, hipStream_t s, void*& wsv, size_t ws_bytes, bool alloc) {
+    if (alloc) {
+        const char* f = std::getenv("FLARE_TEST_FAIL_ALLOC");
+        if (f && std::strcmp(f, "1") == 0) return fail(FLARE_ERR_NO_MEMORY, "allocation failure injected by FLARE_TEST_FAIL_ALLOC");
+        hipError_t e = hipMallocAsync(&wsv, need, s);
+        if (e != hipSuccess || !wsv) return fail(FLARE_ERR_NO_MEMORY, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+        return FLARE_OK;
+    }
+    if (!wsv) return fail(FLARE_ERR_INVALID_ARG, "workspace pointer is null");
+    if (uintptr_t(wsv) % 256 != 0) return fail(FLARE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(FLARE_ERR_INVALID_ARG,
+                    "workspace too small: need " + std::to_string(need) + " bytes, got " + std::to_string(ws_bytes));
+    return FLARE_OK;
+}
+
+flare_status finish(flare_status res, hipError_t e, bool alloc, void* wsv, hipStream_t s) {
+    if (res == FLARE_OK && e != hipSuccess) res = hip_fail(e, "kernel launch");
     if (alloc) {
         hipError_t f = hipFreeAsync(wsv, s);
         if (f != hipSuccess && res == FLARE_OK) return hip_fail(f, "hipFreeAsync");
     }
     return res;
+}
+
+flare_status backward(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK, void* dV,
+                      int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dt, hipStream_t s,
+                      void* wsv, size_t ws_bytes, bool alloc) {
+    Plan p;
+    g_last_error.clear();
+    flare_status st = make_plan(B, H, N, M, D, dt, &p);
+    if (st != FLARE_OK) return st;
+    st = set_layout(&p, FLARE_LAYOUT_BHND);
+    if (st != FLARE_OK) return st;
+    if (!flare::backward_supports(int(D)))
+        return fail(FLARE_ERR_UNSUPPORTED, "the backward supports D in {8, 16, 24, 32, 48, 64}");
+    st = check_backward_ptrs(p, Q, K, V, dY, dQ, dK, dV);
+    if (st != FLARE_OK) return st;
+    st = get_workspace(p.total[FLARE_OP_BACKWARD], s, wsv, ws_bytes, alloc);
+    if (st != FLARE_OK) return st;
+    const hipError_t e = backward_core(p, Q, K, V, dY, dQ, dK, dV, (char*)wsv, s, nullptr);
+    return finish(FLARE_OK, e, alloc, wsv, s);
+}
+
+flare_status pp_backward(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK, void* dV,
+                         int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dt, hipStream_t s,
+                         void* wsv, size_t ws_bytes, bool alloc) {
+    Plan pf, p1;
+    g_last_error.clear();
+    flare_status st = make_plan(B, H, N, M, D, dt, &pf);
+    if (st != FLARE_OK) return st;
+    st = make_plan(1, H, N, M, D, dt, &p1);
+    if (st != FLARE_OK) return st;
+    if ((st = set_layout(&pf, FLARE_LAYOUT_BHND)) != FLARE_OK || (st = set_layout(&p1, FLARE_LAYOUT_BHND)) != FLARE_OK)
+        return st;
+    if (!flare::backward_supports(int(D)))
+        return fail(FLARE_ERR_UNSUPPORTED, "the backward supports D in {8, 16, 24, 32, 48, 64}");
+    st = check_backward_ptrs(pf, Q, K, V, dY, dQ, dK, dV);
+    if (st != FLARE_OK) return st;
+    const PPLayout L = pp_layout(pf, p1);
+    st = get_workspace(L.total, s, wsv, ws_bytes, alloc);
+    if (st != FLARE_OK) return st;
+    char* ws = (char*)wsv;
+    const bool bf = dt == FLARE_BF16;
+    const size_t e = pf.esize, qm = size_t(H) * M * D, tok = size_t(H) * N * D;  // per batch entry
+    // Q' = Q + encode(Q, K, V) for every batch entry
+    hipError_t err = run_encode_partial(pf, Q, 0, K, V, ws, s);
+    if (err == hipSuccess) err = run_combine(pf, flare::COMBINE_QPRIME, Q, ws + L.qp, ws, s);
+    // second stage: the FLARE backward at Q' (one batch entry at a time, its
+    // queries being its own), giving dQ' and the second stage's dK, dV
+    for (int64_t b = 0; b < B && err == hipSuccess; ++b)
+        err = backward_core(p1, ws + L.qp + b * qm * e, (const char*)K + b * tok * e, (const char*)V + b * tok * e,
+                            (const char*)dY + b * tok * e, ws + L.dqp + b * qm * e, (char*)dK + b * tok * e,
+                            (char*)dV + b * tok * e, ws + L.bw, s, nullptr);
+    // first stage: the encode's backward for dZ = dQ' (the FLARE backward with
+    // dY = 0 and dZ given), into the stage-one buffers
+    if (err == hipSuccess) err = flare::launch_fill_zero(ws + L.dy0, size_t(B) * tok * e, s);
+    if (err == hipSuccess)
+        err = backward_core(pf, Q, K, V, ws + L.dy0, ws + L.dq1, ws + L.dk1, ws + L.dv1, ws + L.bw, s, ws + L.dqp);
+    // sums of the two stages (fp32, rounded once)
+    if (err == hipSuccess) err = flare::launch_add_into(dK, ws + L.dk1, int64_t(B) * tok, bf, s);
+    if (err == hipSuccess) err = flare::launch_add_into(dV, ws + L.dv1, int64_t(B) * tok, bf, s);
+    if (err == hipSuccess) err = flare::launch_batch_sum(dQ, ws + L.dq1, ws + L.dqp, int(B), int64_t(qm), bf, s);
+    return finish(FLARE_OK, err, alloc, wsv, s);
 }
 
 }  // namespace
@@ -561,6 +667,18 @@ flare_status flare_backward_ws(const void* Q, const void* K, const void* V, cons
                                void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
                                hipStream_t stream, void* workspace, size_t ws_bytes) {
     return backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, stream, workspace, ws_bytes, false);
+}
+
+flare_status flare_pp_backward(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK,
+                               void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
+                               hipStream_t stream) {
+    return pp_backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, stream, nullptr, 0, true);
+}
+
+flare_status flare_pp_backward_ws(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK,
+                                  void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
+                                  hipStream_t stream, void* workspace, size_t ws_bytes) {
+    return pp_backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, stream, workspace, ws_bytes, false);
 }
 
 flare_status flare_attend(const void* q, const void* Z, void* Y, int64_t B, int64_t H, int64_t N, int64_t M,

@@ -8,6 +8,9 @@
 //                    one lane per token in the decode, each with an exact
 //                    online softmax (running maximum, rescaled sums).
 //  copy_kernel       plain 16-byte-per-lane copy of known traffic.
+//  fill_zero, widen, add_into, batch_sum
+//                    elementwise helpers of the FLARE++ backward (sums of
+//                    its two stages' gradients, in fp32 then rounded).
 //
 // Operator (FLARE skill page, steps 2 and 4; FLARE arXiv abstract):
 // Z[m] = softmax_n(s <Q[m], K[n]>) V, Y[n] = softmax_m(s <Q[m], K[n]>) Z, with
@@ -15,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "launch.h"
 
@@ -230,6 +235,48 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
         dst[i] = src[i];
 }
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* __restrict__ dst, size_t n16) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) dst[i] = z;
+}
+
+template <typename T>
+__device__ __forceinline__ float ld_f(const T* p) {
+    if constexpr (sizeof(T) == 2) return __uint_as_float((uint32_t)(*(const uint16_t*)p) << 16);
+    else return *(const float*)p;
+}
+template <typename T>
+__device__ __forceinline__ void st_f(T* p, float v) {
+    if constexpr (sizeof(T) == 2) *(uint16_t*)p = f32_to_bf16_rne(v);
+    else *(float*)p = v;
+}
+
+// dst[i] = (float) src[i]
+template <typename T>
+__global__ __launch_bounds__(256) void widen_kernel(const T* __restrict__ src, float* __restrict__ dst, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = ld_f(src + i);
+}
+
+// dst[i] = dst[i] + src[i], summed in fp32 and rounded once to T
+template <typename T>
+__global__ __launch_bounds__(256) void add_into_kernel(T* __restrict__ dst, const T* __restrict__ src, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        st_f(dst + i, ld_f(dst + i) + ld_f(src + i));
+}
+
+// dst[i] = base[i] + sum_b add[b * n + i], in fp32 over b in order, rounded once
+template <typename T>
+__global__ __launch_bounds__(256) void batch_sum_kernel(T* __restrict__ dst, const T* __restrict__ base,
+                                                        const T* __restrict__ add, int B, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        float v = ld_f(base + i);
+        for (int b = 0; b < B; ++b) v += ld_f(add + (int64_t)b * n + i);
+        st_f(dst + i, v);
+    }
+}
+
+unsigned elementwise_blocks(int64_t n) { return (unsigned)std::min<int64_t>(8192, std::max<int64_t>(1, (n + 255) / 256)); }
+
 template <int D>
 hipError_t enc_f32(const EncodeArgs& a, hipStream_t s) {
     const int nth = enc_threads_f32(a.M);
@@ -274,6 +321,45 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, a);
     else
         hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s) {
+    if (bytes % 16 != 0) return hipErrorInvalidValue;
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(elementwise_blocks((int64_t)n16)), dim3(256), 0, s, (u32x4*)dst, n16);
+    return hipGetLastError();
+}
+
+hipError_t launch_widen(const void* src, float* dst, int64_t n, bool bf16, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (bf16)
+        hipLaunchKernelGGL(widen_kernel<uint16_t>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (const uint16_t*)src, dst, n);
+    else
+        hipLaunchKernelGGL(widen_kernel<float>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (const float*)src, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_into(void* dst, const void* src, int64_t n, bool bf16, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (bf16)
+        hipLaunchKernelGGL(add_into_kernel<uint16_t>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (uint16_t*)dst,
+                           (const uint16_t*)src, n);
+    else
+        hipLaunchKernelGGL(add_into_kernel<float>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (float*)dst,
+                           (const float*)src, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_batch_sum(void* dst, const void* base, const void* add, int B, int64_t n, bool bf16, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (bf16)
+        hipLaunchKernelGGL(batch_sum_kernel<uint16_t>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (uint16_t*)dst,
+                           (const uint16_t*)base, (const uint16_t*)add, B, n);
+    else
+        hipLaunchKernelGGL(batch_sum_kernel<float>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (float*)dst,
+                           (const float*)base, (const float*)add, B, n);
     return hipGetLastError();
 }
 

@@ -110,6 +110,11 @@ hipError_t launch_encode_f32(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+// elementwise helpers (bf16 or fp32 storage; sums in fp32, rounded once)
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s);  // bytes % 16 == 0
+hipError_t launch_widen(const void* src, float* dst, int64_t n, bool bf16, hipStream_t s);
+hipError_t launch_add_into(void* dst, const void* src, int64_t n, bool bf16, hipStream_t s);
+hipError_t launch_batch_sum(void* dst, const void* base, const void* add, int B, int64_t n, bool bf16, hipStream_t s);
 
 bool backward_supports(int D);
 hipError_t launch_bw_stats(const BackwardArgs& a, hipStream_t s);

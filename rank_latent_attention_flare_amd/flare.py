@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflare.so
 
 FLARE_F32, FLARE_BF16 = 0, 1
 FLARE_OP_ENCODE, FLARE_OP_DECODE, FLARE_OP_FORWARD, FLARE_OP_PP_FORWARD, FLARE_OP_BACKWARD = 0, 1, 2, 3, 4
+FLARE_OP_PP_BACKWARD = 5
 FLARE_LAYOUT_BHND, FLARE_LAYOUT_BNHD = 0, 1
 FLARE_KERNEL_KINDS = 4
 KERNEL_KIND_NAMES = ("encode_partial", "combine", "decode", "backward")
@@ -58,6 +59,10 @@ def lib() -> ctypes.CDLL:
         L.flare_backward.restype = ctypes.c_int
         L.flare_backward_ws.argtypes = bw + [_vp, ctypes.c_size_t]
         L.flare_backward_ws.restype = ctypes.c_int
+        L.flare_pp_backward.argtypes = bw
+        L.flare_pp_backward.restype = ctypes.c_int
+        L.flare_pp_backward_ws.argtypes = bw + [_vp, ctypes.c_size_t]
+        L.flare_pp_backward_ws.restype = ctypes.c_int
         L.flare_attend.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
         L.flare_attend.restype = ctypes.c_int
         L.flare_workspace_size.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
@@ -245,6 +250,23 @@ def flare_backward(Q, K, V, dY, stream=None, workspace=None, out=None):
         _raise(lib().flare_backward(*args))
     else:
         _raise(lib().flare_backward_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size()))
+    return dQ, dK, dV
+
+
+def flare_pp_backward(Q, K, V, dY, stream=None, workspace=None, out=None):
+    """(dQ [H, M, D], dK, dV [B, H, N, D]): gradients of the FLARE++ forward for the upstream gradient dY."""
+    B, H, N, M, D = _dims(FLARE_OP_PP_FORWARD, Q, K, V)
+    if tuple(dY.shape) != (B, H, N, D) or dY.dtype != Q.dtype or not dY.is_contiguous() or not dY.is_cuda:
+        raise ValueError(f"dY must be a contiguous {Q.dtype} device tensor of shape {(B, H, N, D)}")
+    if out is None:
+        out = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    dQ, dK, dV = out
+    args = [Q.data_ptr(), K.data_ptr(), V.data_ptr(), dY.data_ptr(), dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(),
+            B, H, N, M, D, dtype_code(Q.dtype), _stream(stream)]
+    if workspace is None:
+        _raise(lib().flare_pp_backward(*args))
+    else:
+        _raise(lib().flare_pp_backward_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size()))
     return dQ, dK, dV
 
 

@@ -186,3 +186,22 @@ def test_backward_validates_before_launch():
     ws = F.lib().flare_workspace_size(F.FLARE_OP_BACKWARD, 1, 2, 100, 64, 32, F.FLARE_BF16)
     assert ws >= F.lib().flare_workspace_size(F.FLARE_OP_FORWARD, 1, 2, 100, 64, 32, F.FLARE_BF16) > 0
     assert F.lib().flare_backward_ws(*ok, PW, 256) == INVALID
+
+
+def test_pp_backward_validates_before_launch():
+    fn = F.lib().flare_pp_backward
+    PG, PDQ, PDK, PDV = 0x60000000, 0x70000000, 0x80000000, 0x90000000
+    ok = [PQ, PK, PV, PG, PDQ, PDK, PDV, 1, 2, 100, 64, 32, F.FLARE_BF16, None]
+    a = list(ok); a[6] = None
+    assert fn(*a) == INVALID and "null" in F.lib().flare_last_error().decode()
+    a = list(ok); a[4] = PQ + 64  # dQ overlaps Q
+    assert fn(*a) == INVALID and "overlap" in F.lib().flare_last_error().decode()
+    a = list(ok); a[11] = 128  # D = 128: no backward
+    assert fn(*a) == UNSUPPORTED
+    # its workspace holds a FLARE backward's plus Q', dQ', a zero dY and the first stage's gradients
+    args = (2, 2, 100, 64, 32, F.FLARE_BF16)
+    ws = F.lib().flare_workspace_size(F.FLARE_OP_PP_BACKWARD, *args)
+    tok = 2 * 2 * 100 * 32 * 2
+    assert ws >= F.lib().flare_workspace_size(F.FLARE_OP_BACKWARD, *args) + 3 * tok > 0
+    assert F.lib().flare_pp_backward_ws(*ok, PW, 256) == INVALID
+    assert "workspace" in F.lib().flare_last_error().decode()
