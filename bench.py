@@ -60,8 +60,9 @@ def parse():
     p.add_argument("--workload", type=int, default=2, help="workload number 1-6 (default 2)")
     p.add_argument("--variant", choices=["flare", "skill", "backward"], default="flare",
                    help="flare: the workload's forward (default); skill: the FLARE skill page's layer, "
-                        "flare_encode then flare_attend with separate token queries; backward: flare_backward "
-                        "(gradients of Q, K, V); the last two on FLARE forward workloads only")
+                        "flare_encode then flare_attend with separate token queries (FLARE forward workloads only); "
+                        "backward: the gradients of Q, K, V (flare_backward, or flare_pp_backward on the "
+                        "FLARE++ workload)")
     p.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
                    help="layout of K, V and Y: [B,H,N,D] (default) or token-major [B,N,H,D]")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
@@ -113,20 +114,25 @@ def main():
 
     Q, K, V = dev(Qh), dev(Kh), dev(Vh)
     ws = F.workspace_for(op, Q, K)
-    if args.variant != "flare" and op != F.FLARE_OP_FORWARD:
+    if args.variant == "skill" and op != F.FLARE_OP_FORWARD:
         print(f"--variant {args.variant} needs a FLARE forward workload", file=sys.stderr)
         sys.exit(2)
     if args.variant == "backward":
+        # the backward of the workload's operator: flare_backward, or
+        # flare_pp_backward on the FLARE++ workload
         if args.layout != "bhnd":
             print("--variant backward takes the [B,H,N,D] layout", file=sys.stderr)
             sys.exit(2)
-        ws = torch.empty(F.flare_workspace_size(F.FLARE_OP_BACKWARD, w.B, w.H, w.N, w.M, w.D, Q.dtype),
+        pp = op == F.FLARE_OP_PP_FORWARD
+        bw_op = F.FLARE_OP_PP_BACKWARD if pp else F.FLARE_OP_BACKWARD
+        bw_fn = F.flare_pp_backward if pp else F.flare_backward
+        ws = torch.empty(F.flare_workspace_size(bw_op, w.B, w.H, w.N, w.M, w.D, Q.dtype),
                          dtype=torch.uint8, device=Q.device)
         dYt = V.flip(2).contiguous()  # upstream gradient: the values in reverse token order
         grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
 
         def fn(Q, K, V, out=None, workspace=None, stream=None):
-            F.flare_backward(Q, K, V, dYt, stream=stream, workspace=workspace, out=grads)
+            bw_fn(Q, K, V, dYt, stream=stream, workspace=workspace, out=grads)
             return grads[1]
     if args.variant == "skill":
         ws = F.workspace_for(F.FLARE_OP_ENCODE, Q, K)
@@ -224,7 +230,9 @@ def main():
         # accumulations of each kernel (stats 6, dZ 4, dK/dV 10, dQ 8) x M*N*D flops; on the
         # bf16 matrix core for bf16 heads whose Q, Z and dZ fit in LDS (D = 32, or D = 64 with
         # M <= 256), else fp32 VALU
-        bw_flops = 28 * w.B * w.H * w.N * w.M * w.D
+        # FLARE++: the second stage's 28, plus the first stage's statistics, dK/dV and dQ
+        # kernels (6 + 10 + 8), which run with dY = 0 and the given dZ
+        bw_flops = (52 if op == F.FLARE_OP_PP_FORWARD else 28) * w.B * w.H * w.N * w.M * w.D
         bw_ms = kt.get("backward", (0.0, 0))[0] / args.steps if kt else ms_step
         achieved_tf = bw_flops / (bw_ms * 1e-3) / 1e12
         on_mfma = w.dtype == "bf16" and (w.D == 32 or (w.D == 64 and w.M <= 256))
@@ -265,7 +273,10 @@ def main():
         done = 0
         for (b, h) in heads:
             q = Qh[h]
-            if op == F.FLARE_OP_PP_FORWARD:
+            if args.variant == "backward" and op == F.FLARE_OP_PP_FORWARD:
+                oracle.pp_backward_head(oracle.widen(q), oracle.widen(Kh[b, h, :bw_n]),
+                                        oracle.widen(Vh[b, h, :bw_n]), oracle.widen(Vh[b, h, :bw_n][::-1]))
+            elif op == F.FLARE_OP_PP_FORWARD:
                 oracle.pp_forward_head(oracle.widen(q), oracle.widen(Kh[b, h]), oracle.widen(Vh[b, h]))
             elif args.variant == "backward":
                 # the first bw_n tokens of the head (the fp64 backward keeps N x M matrices)

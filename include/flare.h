@@ -209,9 +209,9 @@ flare_status flare_backward_ws(const void* Q, const void* K, const void* V, cons
  * <dQ', Z>), dQ += s dl K, dK += s dl^T Q, with A, Z of the first encode)
  * gives the first stage's; dQ = sum over the batch of dQ' plus the first
  * stage's. Same arguments, layouts, dtypes, support range and error
- * behaviour as flare_backward; each stage's gradients are summed in fp32 and
- * rounded once (dQ' is rounded to the operator dtype before it feeds the
- * first stage). The _ws variant takes flare_workspace_size(
+ * behaviour as flare_backward; the stages' gradients are summed in fp32 and
+ * rounded once (dQ' and the second stage's dK, dV are rounded to the
+ * operator dtype first). The _ws variant takes flare_workspace_size(
  * FLARE_OP_PP_BACKWARD, ...) bytes. */
 flare_status flare_pp_backward(const void* Q, const void* K, const void* V, const void* dY,
                                void* dQ, void* dK, void* dV,

@@ -416,9 +416,9 @@ flare_status exec_alloc(flare_op op, const void* Q, const void* K, const void* V
 
 // FLARE++ backward workspace: one FLARE backward's (sized for the whole batch
 // and for one batch entry, whichever is larger), then Q' and dQ' [B][H][M][D],
-// a zero dY, the first stage's dK and dV [B][H][N][D] and its dQ [H][M][D].
+// a zero dY [B][H][N][D] and the first stage's dQ [H][M][D].
 struct PPLayout {
-    size_t bw, qp, dqp, dy0, dk1, dv1, dq1, total;
+    size_t bw, qp, dqp, dy0, dq1, total;
 };
 PPLayout pp_layout(const Plan& pf, const Plan& p1) {
     PPLayout L{};
@@ -428,8 +428,6 @@ PPLayout pp_layout(const Plan& pf, const Plan& p1) {
     L.qp = off;  off = align256(off + qm);
     L.dqp = off; off = align256(off + qm);
     L.dy0 = off; off = align256(off + tok);
-    L.dk1 = off; off = align256(off + tok);
-    L.dv1 = off; off = align256(off + tok);
     L.dq1 = off; off = align256(off + size_t(pf.H) * pf.M * pf.D * pf.esize);
     L.total = off;
     return L;
@@ -495,7 +493,7 @@ namespace {
 // [B][H][M][D]) the gradient of Z is that tensor instead of Btᵀ dY: the
 // FLARE++ backward uses it, with dY zero, for its first stage (the encode).
 hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void* V, const void* dY, void* dQ,
-                         void* dK, void* dV, char* ws, hipStream_t s, const void* dz_given) {
+                         void* dK, void* dV, char* ws, hipStream_t s, const void* dz_given, bool accum_kv = false) {
     // forward encode and combine: Z, mu* and sig*
     hipError_t e = run_encode_partial(p, Q, 0, K, V, ws, s);
     if (e == hipSuccess)
@@ -517,6 +515,7 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     a.s = float(1.0 / std::sqrt(double(p.D)));
     a.c = p.c;
     a.bf16 = p.dt == FLARE_BF16;
+    a.accum = accum_kv;
     // bf16 heads whose Q, Z and dZ fit in LDS: the per-token kernels on the
     // matrix core; otherwise (and for fp32) the fp32 VALU kernels
     const bool mc = a.bf16 && flare::bw_bf16_fits(int(p.M), int(p.D));
@@ -642,13 +641,12 @@ flare_status pp_backward(const void* Q, const void* K, const void* V, const void
                             (const char*)dY + b * tok * e, ws + L.dqp + b * qm * e, (char*)dK + b * tok * e,
                             (char*)dV + b * tok * e, ws + L.bw, s, nullptr);
     // first stage: the encode's backward for dZ = dQ' (the FLARE backward with
-    // dY = 0 and dZ given), into the stage-one buffers
+    // dY = 0 and dZ given); its dK, dV are added to the second stage's in the
+    // kernel (fp32 sum, rounded once), its dQ goes to a buffer
     if (err == hipSuccess) err = flare::launch_fill_zero(ws + L.dy0, size_t(B) * tok * e, s);
     if (err == hipSuccess)
-        err = backward_core(pf, Q, K, V, ws + L.dy0, ws + L.dq1, ws + L.dk1, ws + L.dv1, ws + L.bw, s, ws + L.dqp);
-    // sums of the two stages (fp32, rounded once)
-    if (err == hipSuccess) err = flare::launch_add_into(dK, ws + L.dk1, int64_t(B) * tok, bf, s);
-    if (err == hipSuccess) err = flare::launch_add_into(dV, ws + L.dv1, int64_t(B) * tok, bf, s);
+        err = backward_core(pf, Q, K, V, ws + L.dy0, ws + L.dq1, dK, dV, ws + L.bw, s, ws + L.dqp, true);
+    // dQ = the first stage's + the sum over the batch of dQ' (fp32, rounded once)
     if (err == hipSuccess) err = flare::launch_batch_sum(dQ, ws + L.dq1, ws + L.dqp, int(B), int64_t(qm), bf, s);
     return finish(FLARE_OK, err, alloc, wsv, s);
 }

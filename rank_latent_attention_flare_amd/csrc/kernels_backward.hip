@@ -289,8 +289,11 @@ __global__ __launch_bounds__(256) void bw_dkdv(BackwardArgs a) {
     if (n < N) {
 #pragma unroll
         for (int i = 0; i < H2; ++i) {
-            st<T>((T*)a.dK + row + i, a.s * dk[i]);
-            st<T>((T*)a.dV + row + i, dv[i]);
+            // accum: added to what dK, dV hold (fp32 sum, rounded once)
+            const float k0 = a.accum ? ld<T>((const T*)a.dK + row + i) : 0.0f;
+            const float v0 = a.accum ? ld<T>((const T*)a.dV + row + i) : 0.0f;
+            st<T>((T*)a.dK + row + i, k0 + a.s * dk[i]);
+            st<T>((T*)a.dV + row + i, v0 + dv[i]);
         }
     }
 }
@@ -540,10 +543,25 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int d0 = 32 * db + 8 * g4 + 4 * hi;
                     u32x2 wk, wv;
-                    const bf16x2 k01 = {(__bf16)(a.s * dk[db][4 * g4]), (__bf16)(a.s * dk[db][4 * g4 + 1])};
-                    const bf16x2 k23 = {(__bf16)(a.s * dk[db][4 * g4 + 2]), (__bf16)(a.s * dk[db][4 * g4 + 3])};
-                    const bf16x2 v01 = {(__bf16)dv[db][4 * g4], (__bf16)dv[db][4 * g4 + 1]};
-                    const bf16x2 v23 = {(__bf16)dv[db][4 * g4 + 2], (__bf16)dv[db][4 * g4 + 3]};
+                    float k[4], v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        k[j] = a.s * dk[db][4 * g4 + j];
+                        v[j] = dv[db][4 * g4 + j];
+                    }
+                    if (a.accum) {  // added to what dK, dV hold (fp32 sum, rounded once)
+                        const u32x2 ok = *(const u32x2*)(dK + d0), ov = *(const u32x2*)(dV + d0);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t wk0 = ok[j >> 1], wv0 = ov[j >> 1];
+                            k[j] += __uint_as_float((j & 1) ? (wk0 & 0xffff0000u) : (wk0 << 16));
+                            v[j] += __uint_as_float((j & 1) ? (wv0 & 0xffff0000u) : (wv0 << 16));
+                        }
+                    }
+                    const bf16x2 k01 = {(__bf16)k[0], (__bf16)k[1]};
+                    const bf16x2 k23 = {(__bf16)k[2], (__bf16)k[3]};
+                    const bf16x2 v01 = {(__bf16)v[0], (__bf16)v[1]};
+                    const bf16x2 v23 = {(__bf16)v[2], (__bf16)v[3]};
                     wk[0] = __builtin_bit_cast(uint32_t, k01);
                     wk[1] = __builtin_bit_cast(uint32_t, k23);
                     wv[0] = __builtin_bit_cast(uint32_t, v01);

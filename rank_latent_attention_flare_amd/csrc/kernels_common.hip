@@ -8,9 +8,10 @@
 //                    one lane per token in the decode, each with an exact
 //                    online softmax (running maximum, rescaled sums).
 //  copy_kernel       plain 16-byte-per-lane copy of known traffic.
-//  fill_zero, widen, add_into, batch_sum
-//                    elementwise helpers of the FLARE++ backward (sums of
-//                    its two stages' gradients, in fp32 then rounded).
+//  fill_zero, widen, batch_sum
+//                    elementwise helpers of the FLARE++ backward (a zero
+//                    upstream gradient, dQ' widened to fp32, and the sum of
+//                    its two stages' dQ in fp32, rounded once).
 //
 // Operator (FLARE skill page, steps 2 and 4; FLARE arXiv abstract):
 // Z[m] = softmax_n(s <Q[m], K[n]>) V, Y[n] = softmax_m(s <Q[m], K[n]>) Z, with
@@ -257,13 +258,6 @@ __global__ __launch_bounds__(256) void widen_kernel(const T* __restrict__ src, f
     for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = ld_f(src + i);
 }
 
-// dst[i] = dst[i] + src[i], summed in fp32 and rounded once to T
-template <typename T>
-__global__ __launch_bounds__(256) void add_into_kernel(T* __restrict__ dst, const T* __restrict__ src, int64_t n) {
-    for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        st_f(dst + i, ld_f(dst + i) + ld_f(src + i));
-}
-
 // dst[i] = base[i] + sum_b add[b * n + i], in fp32 over b in order, rounded once
 template <typename T>
 __global__ __launch_bounds__(256) void batch_sum_kernel(T* __restrict__ dst, const T* __restrict__ base,
@@ -338,17 +332,6 @@ hipError_t launch_widen(const void* src, float* dst, int64_t n, bool bf16, hipSt
         hipLaunchKernelGGL(widen_kernel<uint16_t>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (const uint16_t*)src, dst, n);
     else
         hipLaunchKernelGGL(widen_kernel<float>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (const float*)src, dst, n);
-    return hipGetLastError();
-}
-
-hipError_t launch_add_into(void* dst, const void* src, int64_t n, bool bf16, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    if (bf16)
-        hipLaunchKernelGGL(add_into_kernel<uint16_t>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (uint16_t*)dst,
-                           (const uint16_t*)src, n);
-    else
-        hipLaunchKernelGGL(add_into_kernel<float>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (float*)dst,
-                           (const float*)src, n);
     return hipGetLastError();
 }
 

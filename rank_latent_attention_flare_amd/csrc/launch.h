@@ -68,6 +68,7 @@ struct BackwardArgs {
     int C, chunk_len;    // token chunks of the latent kernels
     float s, c;          // 1/sqrt(D) and s * log2(e)
     bool bf16;
+    bool accum;          // dK, dV are added to what the outputs hold
 };
 
 struct DecodeArgs {
@@ -113,7 +114,6 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // elementwise helpers (bf16 or fp32 storage; sums in fp32, rounded once)
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s);  // bytes % 16 == 0
 hipError_t launch_widen(const void* src, float* dst, int64_t n, bool bf16, hipStream_t s);
-hipError_t launch_add_into(void* dst, const void* src, int64_t n, bool bf16, hipStream_t s);
 hipError_t launch_batch_sum(void* dst, const void* base, const void* add, int B, int64_t n, bool bf16, hipStream_t s);
 
 bool backward_supports(int D);
