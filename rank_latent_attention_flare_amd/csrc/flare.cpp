@@ -519,7 +519,11 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     // bf16 heads whose Q, Z and dZ fit in LDS: the per-token kernels on the
     // matrix core; otherwise (and for fp32) the fp32 VALU kernels
     const bool mc = a.bf16 && flare::bw_bf16_fits(int(p.M), int(p.D));
-    if (e == hipSuccess)
+    // With dZ given (the encode's backward alone), the matrix-core kernels
+    // skip the decode term and need no per-token statistics; the fp32
+    // kernels compute the full formula with the caller's dY = 0.
+    a.enc_only = mc && dz_given;
+    if (e == hipSuccess && !a.enc_only)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_stats_bf16(a, s) : flare::launch_bw_stats(a, s); });
     if (dz_given) {
         // dZ given: one "chunk" of partials holding it, merged as usual
@@ -643,7 +647,9 @@ flare_status pp_backward(const void* Q, const void* K, const void* V, const void
     // first stage: the encode's backward for dZ = dQ' (the FLARE backward with
     // dY = 0 and dZ given); its dK, dV are added to the second stage's in the
     // kernel (fp32 sum, rounded once), its dQ goes to a buffer
-    if (err == hipSuccess) err = flare::launch_fill_zero(ws + L.dy0, size_t(B) * tok * e, s);
+    // (the zero dY is read by the fp32 kernels only)
+    if (err == hipSuccess && !(bf && flare::bw_bf16_fits(int(M), int(D))))
+        err = flare::launch_fill_zero(ws + L.dy0, size_t(B) * tok * e, s);
     if (err == hipSuccess)
         err = backward_core(pf, Q, K, V, ws + L.dy0, ws + L.dq1, dK, dV, ws + L.bw, s, ws + L.dqp, true);
     // dQ = the first stage's + the sum over the batch of dQ' (fp32, rounded once)

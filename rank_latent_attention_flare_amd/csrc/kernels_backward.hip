@@ -428,7 +428,9 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
 // are exactly the k-slots of the B operand of the accumulations dK^T += Q^T dl
 // and dV^T += dZ^T A, whose A operands are read transposed from the natural
 // row-major LDS rows.
-template <int D>
+// ENC: the encode's backward alone (first stage of the FLARE++ backward):
+// dl = A (dZ V^T - gam), no decode weights, no dY.
+template <int D, bool ENC = false>
 __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
     constexpr int KB = D / 16, DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
@@ -465,9 +467,9 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
             const int64_t o = (int64_t)nn * D + 16 * kb + 8 * hi;
             kop[kb] = *(const bf16x8*)(Kb + o);
             vop[kb] = *(const bf16x8*)(Vb + o);
-            gop[kb] = *(const bf16x8*)(Gb + o);
+            if constexpr (!ENC) gop[kb] = *(const bf16x8*)(Gb + o);
         }
-        const float nu = a.nu[(int64_t)bh * N + nn], del = a.del[(int64_t)bh * N + nn];
+        const float nu = ENC ? 0.0f : a.nu[(int64_t)bh * N + nn], del = ENC ? 0.0f : a.del[(int64_t)bh * N + nn];
         f32x16 dk[DB], dv[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -480,16 +482,17 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
             for (int kb = 0; kb < KB; ++kb) {
                 const int off = tile_off<D>(32 * mb + prow, 2 * kb + hi);
                 qa[kb] = *(const bf16x8*)(qs + off);
-                za[kb] = *(const bf16x8*)(zs + off);
+                if constexpr (!ENC) za[kb] = *(const bf16x8*)(zs + off);
                 dza[kb] = *(const bf16x8*)(dzs + off);
             }
             f32x16 S = mfma(qa[0], kop[0], f32x16{});
-            f32x16 GY = mfma(za[0], gop[0], f32x16{});
             f32x16 GV = mfma(dza[0], vop[0], f32x16{});
+            f32x16 GY;
+            if constexpr (!ENC) GY = mfma(za[0], gop[0], f32x16{});
 #pragma unroll
             for (int kb = 1; kb < KB; ++kb) {
                 S = mfma(qa[kb], kop[kb], S);
-                GY = mfma(za[kb], gop[kb], GY);
+                if constexpr (!ENC) GY = mfma(za[kb], gop[kb], GY);
                 GV = mfma(dza[kb], vop[kb], GV);
             }
             bf16x8 pe[2], pl[2];
@@ -504,12 +507,14 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
                     const float lj = j < 4 ? l0[j] : l1[j - 4];
                     const float gj = j < 4 ? g0[j] : g1[j - 4];
                     const float xe = fmaf(S[i], c, -lj);
-                    // p_dec <= 1 for real latents; the clamp keeps padded
-                    // latents (zero rows) finite
-                    const float xd = fminf(fmaf(S[i], c, -nu), 0.0f);
                     const float p_e = exp2_fast(xe);
-                    const float p_d = exp2_fast(xd);
-                    const float dl = p_e * (GV[i] - gj) + p_d * (GY[i] - del);
+                    float dl = p_e * (GV[i] - gj);
+                    if constexpr (!ENC) {
+                        // p_dec <= 1 for real latents; the clamp keeps padded
+                        // latents (zero rows) finite
+                        const float xd = fminf(fmaf(S[i], c, -nu), 0.0f);
+                        dl = fmaf(exp2_fast(xd), GY[i] - del, dl);
+                    }
                     pe[kp][j] = (__bf16)p_e;
                     pl[kp][j] = (__bf16)dl;
                 }
@@ -584,7 +589,9 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
 // operand. The accumulation's A operand (dY^T or K^T) comes from a transposed
 // read of the same rows, which the wave also writes to its own LDS tile in
 // natural order. Per-chunk partials go to a.part [BH][C][M][D].
-template <int D, bool DQ, int MBW>  // MBW: latent blocks per wave at most
+// ENC (with DQ): the encode's backward alone, dl = A (dZ V^T - gam), for the
+// first stage of the FLARE++ backward: no decode weights, no dY.
+template <int D, bool DQ, int MBW, bool ENC = false>  // MBW: latent blocks per wave at most
 __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
     constexpr int KB = D / 16, DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
@@ -638,7 +645,7 @@ __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
         for (int kb = 0; kb < KB; ++kb) {
             const int64_t o = (int64_t)tn * D + 16 * kb + 8 * hi;
             kA[kb] = *(const bf16x8*)(Kb + o);
-            gA[kb] = *(const bf16x8*)(Gb + o);
+            if constexpr (!ENC) gA[kb] = *(const bf16x8*)(Gb + o);
             if constexpr (DQ) vA[kb] = *(const bf16x8*)(Vb + o);
         }
         // the accumulation's source rows (K for dQ, dY for dZ) in natural
@@ -649,12 +656,14 @@ __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
             *(bf16x8*)(tt + tile_off<D>(prow, 2 * kb + hi)) = prow < nv ? (DQ ? kA[kb] : gA[kb]) : zero8();
         // per token (register i: token 16 (i/8) + 8 hi + i%8): nu' and del
         float nur[16], der[16];
+        if constexpr (!ENC) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int tk = 16 * (i >> 3) + 8 * hi + (i & 7);
-            const int tc = t0 + min(tk, nv - 1);
-            nur[i] = tk < nv ? nub[tc] : INFINITY;  // +inf: no weight for tokens past the chunk
-            der[i] = DQ ? delb[tc] : 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                const int tk = 16 * (i >> 3) + 8 * hi + (i & 7);
+                const int tc = t0 + min(tk, nv - 1);
+                nur[i] = tk < nv ? nub[tc] : INFINITY;  // +inf: no weight for tokens past the chunk
+                der[i] = DQ ? delb[tc] : 0.0f;
+            }
         }
         // the transposed operands of this sub-block (same for every latent block)
         auto taddr = [&](int kp, int db, int second) {
@@ -685,24 +694,30 @@ __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
             for (int kb = 1; kb < KB; ++kb) S = mfma(kA[kb], qB[kb], S);
             f32x16 GY, GV;
             if constexpr (DQ) {
-                GY = mfma(gA[0], zB[0], f32x16{});
                 GV = mfma(vA[0], dzB[0], f32x16{});
 #pragma unroll
-                for (int kb = 1; kb < KB; ++kb) {
-                    GY = mfma(gA[kb], zB[kb], GY);
-                    GV = mfma(vA[kb], dzB[kb], GV);
+                for (int kb = 1; kb < KB; ++kb) GV = mfma(vA[kb], dzB[kb], GV);
+                if constexpr (!ENC) {
+                    GY = mfma(gA[0], zB[0], f32x16{});
+#pragma unroll
+                    for (int kb = 1; kb < KB; ++kb) GY = mfma(gA[kb], zB[kb], GY);
                 }
             }
             bf16x8 pw[2];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                // decode weight Bt[n][m] (0 past the chunk); clamp: padded
-                // latents (zero rows) stay finite
-                const float p_d = exp2_fast(fminf(fmaf(S[i], c, -nur[i]), 0.0f));
-                float w = p_d;
-                if constexpr (DQ) {
-                    const float p_e = exp2_fast(fmaf(S[i], c, -lam[j]));
-                    w = p_e * (GV[i] - gm[j]) + p_d * (GY[i] - der[i]);
+                float w;
+                if constexpr (ENC) {
+                    w = exp2_fast(fmaf(S[i], c, -lam[j])) * (GV[i] - gm[j]);
+                } else {
+                    // decode weight Bt[n][m] (0 past the chunk); clamp: padded
+                    // latents (zero rows) stay finite
+                    const float p_d = exp2_fast(fminf(fmaf(S[i], c, -nur[i]), 0.0f));
+                    w = p_d;
+                    if constexpr (DQ) {
+                        const float p_e = exp2_fast(fmaf(S[i], c, -lam[j]));
+                        w = p_e * (GV[i] - gm[j]) + p_d * (GY[i] - der[i]);
+                    }
                 }
                 pw[i >> 3][i & 7] = (__bf16)w;
             }
@@ -852,6 +867,11 @@ hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
         hipLaunchKernelGGL(fn, dim3(a.C, a.BH), dim3(256), lds, s, a);
         return hipGetLastError();
     };
+    if (dq && a.enc_only) {
+        if (a.D == 32) return go(bw_lat_bf16<32, true, 4, true>);
+        if (a.D == 64 && Mp <= 256) return go(bw_lat_bf16<64, true, 2, true>);
+        return hipErrorInvalidValue;
+    }
     if (a.D == 32) return dq ? go(bw_lat_bf16<32, true, 4>) : go(bw_lat_bf16<32, false, 4>);
     if (a.D == 64 && Mp <= 256) return dq ? go(bw_lat_bf16<64, true, 2>) : go(bw_lat_bf16<64, false, 2>);
     return hipErrorInvalidValue;
@@ -859,6 +879,11 @@ hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
 
 hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
     const int Mp = (a.M + 31) / 32 * 32, lds = 3 * Mp * 2 * a.D + 8 * Mp;
+    if (a.enc_only) {
+        if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32, true>, a, lds, s);
+        if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64, true>, a, lds, s);
+        return hipErrorInvalidValue;
+    }
     if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32>, a, lds, s);
     if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64>, a, lds, s);
     return hipErrorInvalidValue;

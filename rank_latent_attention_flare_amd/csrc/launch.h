@@ -69,6 +69,7 @@ struct BackwardArgs {
     float s, c;          // 1/sqrt(D) and s * log2(e)
     bool bf16;
     bool accum;          // dK, dV are added to what the outputs hold
+    bool enc_only;       // matrix-core kernels: the encode's backward alone (dY unused)
 };
 
 struct DecodeArgs {
