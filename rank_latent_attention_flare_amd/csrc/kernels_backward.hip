@@ -428,6 +428,14 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
 // are exactly the k-slots of the B operand of the accumulations dK^T += Q^T dl
 // and dV^T += dZ^T A, whose A operands are read transposed from the natural
 // row-major LDS rows.
+// 8 bytes from LDS in inline asm that waits for its own result (the data
+// came by a global->LDS transfer the compiler cannot track).
+__device__ __forceinline__ u32x2 lds_u32x2(const unsigned char* p) {
+    u32x2 r;
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(lds_addr(p)) : "memory");
+    return r;
+}
+
 // ENC: the encode's backward alone (first stage of the FLARE++ backward):
 // dl = A (dZ V^T - gam), no decode weights, no dY.
 template <int D, bool ENC = false>
@@ -440,12 +448,16 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
     const int N = a.N, M = a.M, Mp = (M + 31) & ~31, MB = Mp / 32;
     const float c = a.c;
     unsigned char* qs = bsm;
-    unsigned char* zs = qs + Mp * 2 * D;
-    unsigned char* dzs = zs + Mp * 2 * D;
+    unsigned char* zs = qs + Mp * 2 * D;               // Z rows (not with ENC)
+    unsigned char* dzs = zs + (ENC ? 0 : Mp * 2 * D);
     float* lam = (float*)(dzs + Mp * 2 * D);  // [Mp] mu* + log2 sig* (+inf for padding)
     float* gam = lam + Mp;                     // [Mp]
+    // ENC with accum: this wave's 32 rows of the old dK and dV, brought in at
+    // the start of each token block (global->LDS transfers, no registers)
+    unsigned char* oldk = (unsigned char*)(gam + Mp) + wave * 2 * (32 * 2 * D);
+    unsigned char* oldv = oldk + 32 * 2 * D;
     stage_rows<D>(qs, (const uint16_t*)a.Q + (int64_t)h * M * D, M, Mp, tid, 256);
-    stage_rows<D>(zs, a.Z + (int64_t)bh * M * D, M, Mp, tid, 256);
+    if constexpr (!ENC) stage_rows<D>(zs, a.Z + (int64_t)bh * M * D, M, Mp, tid, 256);
     stage_rows<D>(dzs, a.dZ + (int64_t)bh * M * D, M, Mp, tid, 256);
     for (int m = tid; m < Mp; m += 256) {
         const int64_t r = (int64_t)bh * M + m;
@@ -470,6 +482,23 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
             if constexpr (!ENC) gop[kb] = *(const bf16x8*)(Gb + o);
         }
         const float nu = ENC ? 0.0f : a.nu[(int64_t)bh * N + nn], del = ENC ? 0.0f : a.del[(int64_t)bh * N + nn];
+        if constexpr (ENC) {
+            if (a.accum) {
+                // 1 KB per transfer: lane l of transfer i fills bytes
+                // i*1024 + 16*l of the row-major [32][D] tile (rows past N
+                // repeat the last token; only rows < N are stored)
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i) {
+                    const int byte = i * 1024 + 16 * lane;
+                    const int row = byte / (2 * D), col = byte % (2 * D);
+                    const int64_t go = ((int64_t)bh * N + min(blk * 32 + row, N - 1)) * 2 * D + col;
+                    __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.dK + go),
+                                                     (void*)(oldk + i * 1024), 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.dV + go),
+                                                     (void*)(oldv + i * 1024), 16, 0, 0);
+                }
+            }
+        }
         f32x16 dk[DB], dv[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -539,6 +568,9 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
             }
         }
         // register r of lane l: d = 32 db + 8 (r/4) + 4 hi + r%4, token l32
+        if constexpr (ENC) {
+            if (a.accum) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this block's transfers landed
+        }
         if (n < N) {
             uint16_t* dK = (uint16_t*)a.dK + ((int64_t)bh * N + n) * D;
             uint16_t* dV = (uint16_t*)a.dV + ((int64_t)bh * N + n) * D;
@@ -555,7 +587,15 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
                         v[j] = dv[db][4 * g4 + j];
                     }
                     if (a.accum) {  // added to what dK, dV hold (fp32 sum, rounded once)
-                        const u32x2 ok = *(const u32x2*)(dK + d0), ov = *(const u32x2*)(dV + d0);
+                        u32x2 ok, ov;
+                        if constexpr (ENC) {
+                            // from this wave's LDS copy (transfers waited for above)
+                            ok = lds_u32x2(oldk + l32 * 2 * D + 2 * d0);
+                            ov = lds_u32x2(oldv + l32 * 2 * D + 2 * d0);
+                        } else {
+                            ok = *(const u32x2*)(dK + d0);
+                            ov = *(const u32x2*)(dV + d0);
+                        }
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const uint32_t wk0 = ok[j >> 1], wv0 = ov[j >> 1];
@@ -878,7 +918,8 @@ hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
 }
 
 hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
-    const int Mp = (a.M + 31) / 32 * 32, lds = 3 * Mp * 2 * a.D + 8 * Mp;
+    const int Mp = (a.M + 31) / 32 * 32;
+    const int lds = (a.enc_only ? 2 : 3) * Mp * 2 * a.D + 8 * Mp + (a.enc_only && a.accum ? 4 * 2 * 32 * 2 * a.D : 0);
     if (a.enc_only) {
         if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32, true>, a, lds, s);
         if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64, true>, a, lds, s);
