@@ -166,3 +166,22 @@ def test_pp_backward_workspace_variant_is_identical():
     torch.cuda.synchronize()
     for x, y, z in zip(a, b, c):
         assert torch.equal(x, y) and torch.equal(y, z)
+
+
+def test_pp_backward_full_size_one_head_group():
+    # FLARE++ at the 65k-mesh size: every gradient of head 0 (dQ[0] sums its
+    # four batch entries) against the oracle
+    w = WORKLOADS[2]
+    Qh, Kh, Vh = workload_inputs(w)
+    dY = make_inputs(w.B, w.H, w.N, w.M, w.D, w.dtype, seed=98)[2]
+    print(f"[pp_backward] full size {w.name}", flush=True)
+    dQ, dK, dV = F.flare_pp_backward(to_dev(Qh), to_dev(Kh), to_dev(Vh), to_dev(dY))
+    torch.cuda.synchronize()
+    dq_ref = np.zeros((w.M, w.D))
+    for b in range(w.B):
+        dq, dk, dv = oracle.pp_backward_head(oracle.widen(Qh[0]), oracle.widen(Kh[b, 0]), oracle.widen(Vh[b, 0]),
+                                             oracle.widen(dY[b, 0]))
+        dq_ref += dq
+        check_one(dK[b, 0], dk, "bf16", f"pp {w.name} dK b={b}")
+        check_one(dV[b, 0], dv, "bf16", f"pp {w.name} dV b={b}")
+    check_one(dQ[0], dq_ref, "bf16", f"pp {w.name} dQ")
