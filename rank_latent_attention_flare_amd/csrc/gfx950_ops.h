@@ -27,6 +27,14 @@ __device__ __forceinline__ float pair_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Wait until at most N vector memory operations of this wave are outstanding
+// (they complete in issue order); LDS and scalar counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
 __device__ __forceinline__ bool wave_all(bool p) { return __ballot(!p) == 0; }
 

@@ -326,7 +326,9 @@ __device__ __forceinline__ void stage_rows(unsigned char* dst, const ST* src, in
 
 // Per token: nu' = log2-sum-exp2 of the logits over the latents (the decode
 // softmax's normaliser, log2 units) and del = <dY, Y> = sum_m Bt[n][m] <dY[n],
-// Z[m]>. Two sweeps over the latents: the exact maximum, then the sums.
+// Z[m]>. One sweep over the latents against a bound on every logit of the
+// head, with a second against the token's exact maximum where the first
+// underflows.
 template <int D>
 __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
     constexpr int KB = D / 16;
@@ -355,21 +357,37 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
     const float nub = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) + 32.0f;
     const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
     const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
-    const int nblk = (N + 31) / 32;
-    for (int blk = blockIdx.x * 4 + wave; blk < nblk; blk += gridDim.x * 4) {
-        const int n = blk * 32 + l32, nn = min(n, N - 1);
-        bf16x8 kop[KB], gop[KB];
+    const int nblk = (N + 31) / 32, bstep = gridDim.x * 4;
+    int blk = blockIdx.x * 4 + wave;
+    if (blk >= nblk) return;  // no barrier follows
+    // this block's K and dY rows; the next block's are loaded while this one
+    // is processed (clamped to the last block, so the loads are unconditional
+    // and the compiler's wait before the first use covers exactly them)
+    bf16x8 kop[KB], gop[KB], kpf[KB], gpf[KB];
+    auto load = [&](int bk, bf16x8(&ko)[KB], bf16x8(&go)[KB]) {
+        const int nn = min(bk * 32 + l32, N - 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            kop[kb] = *(const bf16x8*)(Kb + (int64_t)nn * D + 16 * kb + 8 * hi);
-            gop[kb] = *(const bf16x8*)(Gb + (int64_t)nn * D + 16 * kb + 8 * hi);
+            ko[kb] = *(const bf16x8*)(Kb + (int64_t)nn * D + 16 * kb + 8 * hi);
+            go[kb] = *(const bf16x8*)(Gb + (int64_t)nn * D + 16 * kb + 8 * hi);
         }
-        auto rows = [&](const unsigned char* t, int mb, bf16x8 (&op)[KB]) {
+    };
+    load(blk, kpf, gpf);
+    auto rows = [&](const unsigned char* t, int mb, bf16x8 (&op)[KB]) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) op[kb] = *(const bf16x8*)(t + tile_off<D>(32 * mb + l32, 2 * kb + hi));
-        };
-        // register i holds latent 32 mb + 8 (i/4) + 4 hi + i%4 (natural rows)
-        auto valid = [&](int mb, int i) { return 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3) < M; };
+        for (int kb = 0; kb < KB; ++kb) op[kb] = *(const bf16x8*)(t + tile_off<D>(32 * mb + l32, 2 * kb + hi));
+    };
+    // register i holds latent 32 mb + 8 (i/4) + 4 hi + i%4 (natural rows);
+    // only the last block can hold padding rows
+    auto valid = [&](int mb, int i) { return 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3) < M; };
+    const bool padded = M != Mp;
+    for (; blk < nblk; blk += bstep) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            kop[kb] = kpf[kb];
+            gop[kb] = gpf[kb];
+        }
+        load(min(blk + bstep, nblk - 1), kpf, gpf);
         // sums of 2^(c l - nu) and of those weights times <dY, Z[m]>
         auto sweep = [&](float nu, float& tau, float& pg) {
             tau = 0.0f;
@@ -385,11 +403,20 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
                     S = mfma(qa[kb], kop[kb], S);
                     G = mfma(za[kb], gop[kb], G);
                 }
+                if (padded && mb == MB - 1) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = valid(mb, i) ? exp2_fast(fmaf(S[i], c, -nu)) : 0.0f;
-                    tau += p;
-                    pg = fmaf(p, G[i], pg);
+                    for (int i = 0; i < 16; ++i) {
+                        const float p = valid(mb, i) ? exp2_fast(fmaf(S[i], c, -nu)) : 0.0f;
+                        tau += p;
+                        pg = fmaf(p, G[i], pg);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float p = exp2_fast(fmaf(S[i], c, -nu));
+                        tau += p;
+                        pg = fmaf(p, G[i], pg);
+                    }
                 }
             }
             tau = pair_sum(tau);
@@ -412,12 +439,13 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
             nu = pair_max(mx) * c;
             sweep(nu, tau, pg);
         }
-        if (n < N && hi == 0) {
-            const int64_t o = (int64_t)bh * N + n;
-            a.nu[o] = nu + __log2f(tau);  // with tau = 1: the weights are normalised by nu alone
-            a.tau[o] = 1.0f;
-            a.del[o] = pg / tau;
-        }
+        // every lane stores (both lanes of a token hold the same sums, and
+        // lanes past N repeat token N - 1's values), so the stores are
+        // unconditional and the next wait stays exact
+        const int64_t o = (int64_t)bh * N + min(blk * 32 + l32, N - 1);
+        a.nu[o] = nu + __log2f(tau);  // with tau = 1: the weights are normalised by nu alone
+        a.tau[o] = 1.0f;
+        a.del[o] = pg / tau;
     }
 }
 
@@ -470,23 +498,52 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
     const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
     const int g = lane >> 4, gi = lane & 15;
     const int prow = enc_row_token(l32);
-    const int nblk = (N + 31) / 32;
-    for (int blk = blockIdx.x * 4 + wave; blk < nblk; blk += gridDim.x * 4) {
-        const int n = blk * 32 + l32, nn = min(n, N - 1);
-        bf16x8 kop[KB], vop[KB], gop[KB];
+    const int nblk = (N + 31) / 32, bstep = gridDim.x * 4;
+    int blk = blockIdx.x * 4 + wave;
+    if (blk >= nblk) return;  // no barrier follows
+    // this block's K, V (and dY) rows and per-token statistics; the next
+    // block's are loaded while this one is processed (clamped to the last
+    // block, so the loads are unconditional and the compiler's wait before
+    // the first use covers exactly them)
+    // (at D = 64 the second set of rows would cost occupancy, and with ENC
+    // the LDS reads after the global->LDS transfers make the compiler wait
+    // for every load in flight: there each block's rows are loaded at its
+    // start)
+    constexpr bool PF = D <= 32 && !ENC;
+    bf16x8 kop[KB], vop[KB], gop[KB], kpf[KB], vpf[KB], gpf[KB];
+    float nu, del, nupf = 0.0f, delpf = 0.0f;
+    auto load = [&](int bk) {
+        const int nn = min(bk * 32 + l32, N - 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int64_t o = (int64_t)nn * D + 16 * kb + 8 * hi;
-            kop[kb] = *(const bf16x8*)(Kb + o);
-            vop[kb] = *(const bf16x8*)(Vb + o);
-            if constexpr (!ENC) gop[kb] = *(const bf16x8*)(Gb + o);
+            kpf[kb] = *(const bf16x8*)(Kb + o);
+            vpf[kb] = *(const bf16x8*)(Vb + o);
+            if constexpr (!ENC) gpf[kb] = *(const bf16x8*)(Gb + o);
         }
-        const float nu = ENC ? 0.0f : a.nu[(int64_t)bh * N + nn], del = ENC ? 0.0f : a.del[(int64_t)bh * N + nn];
+        if constexpr (!ENC) {
+            nupf = a.nu[(int64_t)bh * N + nn];
+            delpf = a.del[(int64_t)bh * N + nn];
+        }
+    };
+    if constexpr (PF) load(blk);
+    const bool padded = M != Mp;
+    for (; blk < nblk; blk += bstep) {
+        const int n = blk * 32 + l32, nn = min(n, N - 1);
+        if constexpr (!PF) load(blk);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            kop[kb] = kpf[kb];
+            vop[kb] = vpf[kb];
+            if constexpr (!ENC) gop[kb] = gpf[kb];
+        }
+        nu = nupf;
+        del = delpf;
         if constexpr (ENC) {
             if (a.accum) {
                 // 1 KB per transfer: lane l of transfer i fills bytes
                 // i*1024 + 16*l of the row-major [32][D] tile (rows past N
-                // repeat the last token; only rows < N are stored)
+                // repeat the last token)
 #pragma unroll
                 for (int i = 0; i < D / 16; ++i) {
                     const int byte = i * 1024 + 16 * lane;
@@ -497,8 +554,10 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
                     __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.dV + go),
                                                      (void*)(oldv + i * 1024), 16, 0, 0);
                 }
+                asm volatile("" ::: "memory");  // the transfers stay ahead of the next block's loads
             }
         }
+        if constexpr (PF) load(min(blk + bstep, nblk - 1));
         f32x16 dk[DB], dv[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -540,8 +599,9 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
                     float dl = p_e * (GV[i] - gj);
                     if constexpr (!ENC) {
                         // p_dec <= 1 for real latents; the clamp keeps padded
-                        // latents (zero rows) finite
-                        const float xd = fminf(fmaf(S[i], c, -nu), 0.0f);
+                        // latents (zero rows, last block only) finite
+                        float xd = fmaf(S[i], c, -nu);
+                        if (padded && mb == MB - 1) xd = fminf(xd, 0.0f);
                         dl = fmaf(exp2_fast(xd), GY[i] - del, dl);
                     }
                     pe[kp][j] = (__bf16)p_e;
@@ -569,11 +629,16 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
         }
         // register r of lane l: d = 32 db + 8 (r/4) + 4 hi + r%4, token l32
         if constexpr (ENC) {
-            if (a.accum) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this block's transfers landed
+            // this block's transfers landed (only the next block's 2 KB
+            // loads, if any, were issued after them)
+            if (a.accum) wait_vmcnt<PF ? 2 * KB : 0>();
         }
-        if (n < N) {
-            uint16_t* dK = (uint16_t*)a.dK + ((int64_t)bh * N + n) * D;
-            uint16_t* dV = (uint16_t*)a.dV + ((int64_t)bh * N + n) * D;
+        // every lane stores: lanes past N repeat token N - 1's rows and
+        // values, so the stores are unconditional and the next wait stays
+        // exact
+        {
+            uint16_t* dK = (uint16_t*)a.dK + ((int64_t)bh * N + nn) * D;
+            uint16_t* dV = (uint16_t*)a.dV + ((int64_t)bh * N + nn) * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -632,7 +697,8 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
 // ENC (with DQ): the encode's backward alone, dl = A (dZ V^T - gam), for the
 // first stage of the FLARE++ backward: no decode weights, no dY.
 template <int D, bool DQ, int MBW, bool ENC = false>  // MBW: latent blocks per wave at most
-__global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && !DQ ? 3 : 1))) void bw_lat_bf16(
+    BackwardArgs a) {
     constexpr int KB = D / 16, DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
     const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
@@ -677,17 +743,44 @@ __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
     const float* delb = a.del + (int64_t)bh * N;
     const int prow = enc_row_token(l32);
     const int g = lane >> 4, gi = lane & 15;
-    for (int t0 = n0 + 32 * ts; nmb > 0 && t0 < n1; t0 += 32 * TS) {
-        const int nv = n1 - t0;  // valid tokens in this sub-block (>= 1)
-        const int tn = t0 + min(prow, nv - 1);
-        bf16x8 kA[KB], gA[KB], vA[KB];
+    // This sub-block's token rows and per-token statistics (one token per
+    // lane, spread to the register layout by lane permutes); the next
+    // sub-block's are loaded while this one is processed (clamped to this
+    // one at the chunk's end, so the loads are unconditional and the
+    // compiler's wait before the first use covers exactly them). At D = 64
+    // the second set of rows would cost occupancy: there each sub-block's
+    // rows are loaded at its start and the statistics where they are used.
+    constexpr bool PF = D <= 32;
+    bf16x8 kA[KB], gA[KB], vA[KB], kP[KB], gP[KB], vP[KB];
+    float nuP = 0.0f, deP = 0.0f;
+    auto load = [&](int t) {
+        const int nv = n1 - t, tn = t + min(prow, nv - 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int64_t o = (int64_t)tn * D + 16 * kb + 8 * hi;
-            kA[kb] = *(const bf16x8*)(Kb + o);
-            if constexpr (!ENC) gA[kb] = *(const bf16x8*)(Gb + o);
-            if constexpr (DQ) vA[kb] = *(const bf16x8*)(Vb + o);
+            kP[kb] = *(const bf16x8*)(Kb + o);
+            if constexpr (!ENC) gP[kb] = *(const bf16x8*)(Gb + o);
+            if constexpr (DQ) vP[kb] = *(const bf16x8*)(Vb + o);
         }
+        if constexpr (!ENC && PF) {
+            const int tc = t + min(l32, nv - 1);
+            nuP = nub[tc];
+            if constexpr (DQ) deP = delb[tc];
+        }
+    };
+    int t0 = n0 + 32 * ts;
+    if (PF && nmb > 0 && t0 < n1) load(t0);
+    for (; nmb > 0 && t0 < n1; t0 += 32 * TS) {
+        const int nv = n1 - t0;  // valid tokens in this sub-block (>= 1)
+        if constexpr (!PF) load(t0);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            kA[kb] = kP[kb];
+            gA[kb] = gP[kb];
+            vA[kb] = vP[kb];
+        }
+        const float nuc = nuP, dec = deP;
+        if constexpr (PF) load(t0 + 32 * TS < n1 ? t0 + 32 * TS : t0);
         // the accumulation's source rows (K for dQ, dY for dZ) in natural
         // order into this wave's tile; rows past the chunk are zero, so their
         // (finite) weights add nothing
@@ -695,14 +788,20 @@ __global__ __launch_bounds__(256) void bw_lat_bf16(BackwardArgs a) {
         for (int kb = 0; kb < KB; ++kb)
             *(bf16x8*)(tt + tile_off<D>(prow, 2 * kb + hi)) = prow < nv ? (DQ ? kA[kb] : gA[kb]) : zero8();
         // per token (register i: token 16 (i/8) + 8 hi + i%8): nu' and del
+        // (past the chunk: the last token's, with zero rows above)
         float nur[16], der[16];
         if constexpr (!ENC) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int tk = 16 * (i >> 3) + 8 * hi + (i & 7);
-                const int tc = t0 + min(tk, nv - 1);
-                nur[i] = tk < nv ? nub[tc] : INFINITY;  // +inf: no weight for tokens past the chunk
-                der[i] = DQ ? delb[tc] : 0.0f;
+                if constexpr (PF) {
+                    nur[i] = __shfl(nuc, tk, 64);
+                    der[i] = DQ ? __shfl(dec, tk, 64) : 0.0f;
+                } else {
+                    const int tc = t0 + min(tk, nv - 1);
+                    nur[i] = nub[tc];
+                    der[i] = DQ ? delb[tc] : 0.0f;
+                }
             }
         }
         // the transposed operands of this sub-block (same for every latent block)

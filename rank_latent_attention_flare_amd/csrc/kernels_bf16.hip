@@ -99,12 +99,6 @@ __device__ __forceinline__ f32x4 colsum(const bf16x8& sel, const bf16x8& p0, con
 // unchanged. At the end the WT token waves of a latent group merge their
 // states through LDS and one writes (mu, sum, acc) for the chunk.
 // ---------------------------------------------------------------------------
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // wait for every outstanding global load, including the prefetched tiles).
 // LDS ordering is explicit: each wave waits for its own transfers first.
