@@ -32,6 +32,9 @@ CASES = [
     (1, 2, 4097, 100, 64, "bf16"),
     (1, 1, 1, 1, 32, "bf16"),
     (1, 1, 3000, 300, 32, "bf16"),
+    # many heads: two token blocks per wave in the token-side kernels, the
+    # second one ragged (next-block loads clamped to the last block)
+    (2, 128, 777, 33, 32, "bf16"),
     # bf16 heads whose Q, Z and dZ do not fit in LDS take the fp32 VALU kernels
     (1, 1, 600, 300, 64, "bf16"),
 ]
