@@ -538,11 +538,16 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
             e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, false, s) : flare::launch_bw_dz(a, s); });
         if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(a, s); });
     }
+    // bf16 at D = 32 (M <= 128): the dK/dV kernel also forms the dQ
+    // partials, one per workgroup, in fg chunk slots
+    const int fg = mc ? flare::bw_fused_dq_groups(a) : 0;
     if (e == hipSuccess)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_dkdv_bf16(a, s) : flare::launch_bw_dkdv(a, s); });
-    if (e == hipSuccess)
+    if (e == hipSuccess && fg == 0)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, true, s) : flare::launch_bw_dq(a, s); });
-    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(a, s); });
+    flare::BackwardArgs dqa = a;
+    if (fg > 0) dqa.C = fg;
+    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(dqa, s); });
     return e;
 }
 

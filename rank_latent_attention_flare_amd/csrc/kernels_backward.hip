@@ -466,8 +466,9 @@ __device__ __forceinline__ u32x2 lds_u32x2(const unsigned char* p) {
 
 // ENC: the encode's backward alone (first stage of the FLARE++ backward):
 // dl = A (dZ V^T - gam), no decode weights, no dY.
-template <int D, bool ENC = false>
-__global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
+template <int D, bool ENC = false, bool FDQ = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1))) void bw_dkdv_bf16(BackwardArgs a) {
+    static_assert(!(FDQ && (ENC || D != 32)), "dQ fused at D = 32 with the full formula only");
     constexpr int KB = D / 16, DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
     const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
@@ -484,6 +485,18 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
     // the start of each token block (global->LDS transfers, no registers)
     unsigned char* oldk = (unsigned char*)(gam + Mp) + wave * 2 * (32 * 2 * D);
     unsigned char* oldv = oldk + 32 * 2 * D;
+    // FDQ (dQ fused in): this wave's K rows of the block (zero past N) and
+    // its dl tile [token][latent] of the current latent block, bf16 rows
+    // (swizzled); the head's dQ^T sums over this wave's tokens stay in
+    // registers, for up to MBX latent blocks
+    unsigned char* ktile = (unsigned char*)(gam + Mp) + wave * (32 * 2 * D + 32 * 64);
+    unsigned char* ptile = ktile + 32 * 2 * D;
+    constexpr int MBX = 4, MBU = FDQ ? MBX : 1;
+    f32x16 dq[FDQ ? MBX : 1][DB];
+#pragma unroll
+    for (int j = 0; j < (FDQ ? MBX : 1); ++j)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dq[j][db] = f32x16{};
     stage_rows<D>(qs, (const uint16_t*)a.Q + (int64_t)h * M * D, M, Mp, tid, 256);
     if constexpr (!ENC) stage_rows<D>(zs, a.Z + (int64_t)bh * M * D, M, Mp, tid, 256);
     stage_rows<D>(dzs, a.dZ + (int64_t)bh * M * D, M, Mp, tid, 256);
@@ -500,7 +513,7 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
     const int prow = enc_row_token(l32);
     const int nblk = (N + 31) / 32, bstep = gridDim.x * 4;
     int blk = blockIdx.x * 4 + wave;
-    if (blk >= nblk) return;  // no barrier follows
+    if (!FDQ && blk >= nblk) return;  // no barrier follows (FDQ: the waves merge at the end)
     // this block's K, V (and dY) rows and per-token statistics; the next
     // block's are loaded while this one is processed (clamped to the last
     // block, so the loads are unconditional and the compiler's wait before
@@ -509,7 +522,7 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
     // the LDS reads after the global->LDS transfers make the compiler wait
     // for every load in flight: there each block's rows are loaded at its
     // start)
-    constexpr bool PF = D <= 32 && !ENC;
+    constexpr bool PF = D <= 32 && !ENC && !FDQ;
     bf16x8 kop[KB], vop[KB], gop[KB], kpf[KB], vpf[KB], gpf[KB];
     float nu, del, nupf = 0.0f, delpf = 0.0f;
     auto load = [&](int bk) {
@@ -564,7 +577,28 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
             dk[db] = f32x16{};
             dv[db] = f32x16{};
         }
-        for (int mb = 0; mb < MB; ++mb) {
+        // FDQ: K^T operands of this block (rows d, k = tokens), transposed
+        // reads of the K tile; rows past N are zero, so their dl adds nothing
+        auto tr_addr = [&](const unsigned char* t, int row0, int kp, int db, int second) {
+            const int row = row0 + 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
+            const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+            return t + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+        };
+        bf16x8 kt[2][DB];
+        if constexpr (FDQ) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                *(bf16x8*)(ktile + tile_off<D>(l32, 2 * kb + hi)) = n < N ? kop[kb] : zero8();
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                lds_tr_op2(tr_addr(ktile, 0, 0, db, 0), tr_addr(ktile, 0, 0, db, 1), tr_addr(ktile, 0, 1, db, 0),
+                           tr_addr(ktile, 0, 1, db, 1), kt[0][db], kt[1][db]);
+        }
+        // (FDQ: unrolled, so that each latent block's dQ sums stay in registers)
+#pragma unroll MBU
+        for (int mb = 0; mb < (FDQ ? MBX : MB); ++mb) {
+            if (FDQ && mb >= MB) continue;
+            f32x16(&dqb)[DB] = dq[FDQ ? mb : 0];
             bf16x8 qa[KB], za[KB], dza[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -626,6 +660,22 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
                 dv[db] = mfma(zt0, pe[0], dv[db]);
                 dv[db] = mfma(zt1, pe[1], dv[db]);
             }
+            if constexpr (FDQ) {
+                // dQ^T[d][m] += sum over tokens K^T[d][n] dl[m][n]: dl goes
+                // through the wave's tile [token][latent] (pl[kp] holds
+                // latents 16 kp + 8 hi + 0..7 of token l32), and transposed
+                // reads give the B operands (k = tokens, columns = latents)
+                *(bf16x8*)(ptile + tile_off<32>(l32, hi)) = pl[0];
+                *(bf16x8*)(ptile + tile_off<32>(l32, 2 + hi)) = pl[1];
+                bf16x8 pt0, pt1;
+                lds_tr_op2(tr_addr(ptile, 0, 0, 0, 0), tr_addr(ptile, 0, 0, 0, 1), tr_addr(ptile, 0, 1, 0, 0),
+                           tr_addr(ptile, 0, 1, 0, 1), pt0, pt1);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dqb[db] = mfma(kt[0][db], pt0, dqb[db]);
+                    dqb[db] = mfma(kt[1][db], pt1, dqb[db]);
+                }
+            }
         }
         // register r of lane l: d = 32 db + 8 (r/4) + 4 hi + r%4, token l32
         if constexpr (ENC) {
@@ -679,6 +729,51 @@ __global__ __launch_bounds__(256) void bw_dkdv_bf16(BackwardArgs a) {
                     *(u32x2*)(dK + d0) = wk;
                     *(u32x2*)(dV + d0) = wv;
                 }
+        }
+    }
+    if constexpr (FDQ) {
+        // merge the four waves' dQ^T sums (fixed order) and write this
+        // workgroup's partial: slot blockIdx.x of [BH][gridDim.x][M][D],
+        // scaled by s. Register r of accumulator (j, db): d = 32 db +
+        // 8 (r/4) + 4 hi + r%4, latent 32 j + l32.
+        __syncthreads();  // staged rows and tiles are no longer read
+        float* mbuf = (float*)bsm;
+        constexpr int PER = MBX * DB * 16 * 64;
+        if (wave > 0) {
+            float* d0 = mbuf + (wave - 1) * PER;
+#pragma unroll
+            for (int j = 0; j < MBX; ++j)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) d0[((j * DB + db) * 16 + r) * 64 + lane] = dq[j][db][r];
+        }
+        __syncthreads();
+        if (wave == 0) {
+            for (int t = 0; t < 3; ++t) {
+                const float* s0 = mbuf + t * PER;
+#pragma unroll
+                for (int j = 0; j < MBX; ++j)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) dq[j][db][r] += s0[((j * DB + db) * 16 + r) * 64 + lane];
+            }
+#pragma unroll
+            for (int j = 0; j < MBX; ++j) {
+                const int m = 32 * j + l32;
+                if (j < MB && m < M) {
+                    float* dst = a.part + (((int64_t)bh * gridDim.x + blockIdx.x) * M + m) * D;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const f32x4 v = {a.s * dq[j][db][4 * g4], a.s * dq[j][db][4 * g4 + 1],
+                                             a.s * dq[j][db][4 * g4 + 2], a.s * dq[j][db][4 * g4 + 3]};
+                            *(f32x4*)(dst + 32 * db + 8 * g4 + 4 * hi) = v;
+                        }
+                }
+            }
         }
     }
 }
@@ -971,19 +1066,28 @@ bool bw_bf16_fits(int M, int D) {
 }
 
 namespace {
+// Workgroups per (b, h) of the token-side kernels: about 1024 in all, at most
+// one per four 32-token blocks.
+int tok_groups(const BackwardArgs& a) {
+    const int nblk = (a.N + 31) / 32;
+    return std::max(1, std::min((1024 + a.BH - 1) / a.BH, (nblk + 3) / 4));
+}
 template <typename F>
-hipError_t launch_bw_tok(F fn, const BackwardArgs& a, int lds, hipStream_t s) {
+hipError_t launch_bw_tok(F fn, const BackwardArgs& a, int lds, hipStream_t s, int G = 0) {
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
     }
-    const int nblk = (a.N + 31) / 32;
-    int G = (1024 + a.BH - 1) / a.BH;
-    G = std::max(1, std::min(G, (nblk + 3) / 4));
-    hipLaunchKernelGGL(fn, dim3(G, a.BH), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(fn, dim3(G > 0 ? G : tok_groups(a), a.BH), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 }  // namespace
+
+int bw_fused_dq_groups(const BackwardArgs& a) {
+    const int Mp = (a.M + 31) / 32 * 32;
+    if (!a.bf16 || a.enc_only || a.D != 32 || Mp > 128 || a.C < 1) return 0;
+    return std::min(tok_groups(a), a.C);
+}
 
 hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s) {
     const int Mp = (a.M + 31) / 32 * 32, lds = 2 * Mp * 2 * a.D + 16;
@@ -1023,6 +1127,12 @@ hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
         if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32, true>, a, lds, s);
         if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64, true>, a, lds, s);
         return hipErrorInvalidValue;
+    }
+    if (const int fg = bw_fused_dq_groups(a)) {
+        // dQ fused in: per-wave K and dl tiles, and the four waves' sums
+        // merged through LDS at the end
+        const int lds_f = std::max(lds + 4 * (32 * 2 * a.D + 32 * 64), 3 * 4 * (a.D / 32) * 16 * 64 * 4);
+        return launch_bw_tok(bw_dkdv_bf16<32, false, true>, a, lds_f, s, fg);
     }
     if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32>, a, lds, s);
     if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64>, a, lds, s);
