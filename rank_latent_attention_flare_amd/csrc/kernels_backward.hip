@@ -16,6 +16,8 @@
 // Nothing N x M is stored: every kernel recomputes the logits it needs. The
 // encode statistics (mu*, sig*) and Z come from the forward's own encode and
 // combine; the decode statistics (nu, tau) and del per token from bw_stats.
+// dQ's partial sums come from the latent kernels, or (bf16, D = 32, M <= 128)
+// from the dK/dV kernel itself.
 //
 // Layout of work in the fp32 kernels: a pair of lanes (l, l ^ 32) owns one
 // token (token kernels) or one latent (latent kernels), each lane holding half
@@ -456,6 +458,9 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
 // are exactly the k-slots of the B operand of the accumulations dK^T += Q^T dl
 // and dV^T += dZ^T A, whose A operands are read transposed from the natural
 // row-major LDS rows.
+// FDQ (bf16, D = 32, M <= 128): the same kernel also forms dQ's partial sums,
+// dQ^T[d][m] += K^T[d][n] dl[m][n] over the workgroup's tokens, so that no
+// separate latent-side pass over K, V and dY is needed for dQ.
 // 8 bytes from LDS in inline asm that waits for its own result (the data
 // came by a global->LDS transfer the compiler cannot track).
 __device__ __forceinline__ u32x2 lds_u32x2(const unsigned char* p) {
