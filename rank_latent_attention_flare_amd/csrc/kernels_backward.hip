@@ -331,8 +331,9 @@ __device__ __forceinline__ void stage_rows(unsigned char* dst, const ST* src, in
 // Z[m]>. One sweep over the latents against a bound on every logit of the
 // head, with a second against the token's exact maximum where the first
 // underflows.
-template <int D>
+template <int D, bool FDZ = false>
 __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
+    static_assert(!FDZ || D == 32, "dZ fused at D = 32 only");
     constexpr int KB = D / 16;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
     const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
@@ -350,6 +351,19 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
     // <= 1 everywhere; a token whose sum falls below 2^-90 is redone against
     // its exact maximum.
     float* red = (float*)(zs + Mp * 2 * D);
+    // FDZ (dZ fused in): this wave's dY rows of the block (zero past N) and
+    // its Bt tile [token][latent] of the current latent block, bf16 rows
+    // (swizzled); the head's dZ^T sums over this wave's tokens stay in
+    // registers, for up to MBX latent blocks
+    unsigned char* gtile = (unsigned char*)(red + 4) + wave * (32 * 2 * D + 32 * 64);
+    unsigned char* btile = gtile + 32 * 2 * D;
+    constexpr int DB = D / 32, MBX = 4, MBU = FDZ ? MBX : 1;
+    f32x16 dz[FDZ ? MBX : 1][DB];
+#pragma unroll
+    for (int j = 0; j < (FDZ ? MBX : 1); ++j)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dz[j][db] = f32x16{};
+    const int g = lane >> 4, gi = lane & 15;
     float mz = -INFINITY;
     for (int m = tid; m < M; m += 256) mz = fmaxf(mz, a.zmu[(int64_t)bh * M + m]);
 #pragma unroll
@@ -361,7 +375,7 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
     const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
     const int nblk = (N + 31) / 32, bstep = gridDim.x * 4;
     int blk = blockIdx.x * 4 + wave;
-    if (blk >= nblk) return;  // no barrier follows
+    if (!FDZ && blk >= nblk) return;  // no barrier follows (FDZ: the waves merge at the end)
     // this block's K and dY rows; the next block's are loaded while this one
     // is processed (clamped to the last block, so the loads are unconditional
     // and the compiler's wait before the first use covers exactly them)
@@ -374,7 +388,7 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
             go[kb] = *(const bf16x8*)(Gb + (int64_t)nn * D + 16 * kb + 8 * hi);
         }
     };
-    load(blk, kpf, gpf);
+    load(min(blk, nblk - 1), kpf, gpf);
     auto rows = [&](const unsigned char* t, int mb, bf16x8 (&op)[KB]) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) op[kb] = *(const bf16x8*)(t + tile_off<D>(32 * mb + l32, 2 * kb + hi));
@@ -445,9 +459,101 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
         // lanes past N repeat token N - 1's values), so the stores are
         // unconditional and the next wait stays exact
         const int64_t o = (int64_t)bh * N + min(blk * 32 + l32, N - 1);
-        a.nu[o] = nu + __log2f(tau);  // with tau = 1: the weights are normalised by nu alone
+        const float nup = nu + __log2f(tau);
+        a.nu[o] = nup;  // with tau = 1: the weights are normalised by nu alone
         a.tau[o] = 1.0f;
         a.del[o] = pg / tau;
+        if constexpr (FDZ) {
+            // dZ^T[d][m] += sum over tokens dY^T[d][n] Bt[n][m], Bt = 2^(c l - nu'):
+            // the dY rows and, per latent block, Bt go through the wave's
+            // tiles (rows = tokens), and transposed reads give dY^T (rows d,
+            // k = tokens) and Bt (k = tokens, columns = latents). Padding
+            // latents only touch their own (unwritten) columns.
+            auto tr_addr = [&](const unsigned char* t, int kp, int db, int second) {
+                const int row = 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
+                const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+                return t + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+            };
+            const int n = blk * 32 + l32;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                *(bf16x8*)(gtile + tile_off<D>(l32, 2 * kb + hi)) = n < N ? gop[kb] : zero8();
+            bf16x8 gt[2][DB];
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                lds_tr_op2(tr_addr(gtile, 0, db, 0), tr_addr(gtile, 0, db, 1), tr_addr(gtile, 1, db, 0),
+                           tr_addr(gtile, 1, db, 1), gt[0][db], gt[1][db]);
+#pragma unroll MBU
+            for (int mb = 0; mb < MBX; ++mb) {
+                if (mb >= MB) continue;
+                bf16x8 qa[KB];
+                rows(qs, mb, qa);
+                f32x16 S = mfma(qa[0], kop[0], f32x16{});
+#pragma unroll
+                for (int kb = 1; kb < KB; ++kb) S = mfma(qa[kb], kop[kb], S);
+                // register i: latent 32 mb + 8 (i/4) + 4 hi + i%4 -> 8 bytes per 4
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    bf16x2 w01 = {(__bf16)exp2_fast(fmaf(S[4 * q], c, -nup)), (__bf16)exp2_fast(fmaf(S[4 * q + 1], c, -nup))};
+                    bf16x2 w23 = {(__bf16)exp2_fast(fmaf(S[4 * q + 2], c, -nup)), (__bf16)exp2_fast(fmaf(S[4 * q + 3], c, -nup))};
+                    const u32x2 w = {__builtin_bit_cast(uint32_t, w01), __builtin_bit_cast(uint32_t, w23)};
+                    *(u32x2*)(btile + tile_off<32>(l32, q) + 8 * hi) = w;
+                }
+                bf16x8 bt0, bt1;
+                lds_tr_op2(tr_addr(btile, 0, 0, 0), tr_addr(btile, 0, 0, 1), tr_addr(btile, 1, 0, 0),
+                           tr_addr(btile, 1, 0, 1), bt0, bt1);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dz[mb][db] = mfma(gt[0][db], bt0, dz[mb][db]);
+                    dz[mb][db] = mfma(gt[1][db], bt1, dz[mb][db]);
+                }
+            }
+        }
+    }
+    if constexpr (FDZ) {
+        // merge the four waves' dZ^T sums (fixed order) and write this
+        // workgroup's partial: slot blockIdx.x of [BH][gridDim.x][M][D].
+        // Register r of accumulator (j, db): d = 32 db + 8 (r/4) + 4 hi + r%4,
+        // latent 32 j + l32.
+        __syncthreads();  // staged rows and tiles are no longer read
+        float* mbuf = (float*)bsm;
+        constexpr int PER = MBX * DB * 16 * 64;
+        if (wave > 0) {
+            float* d0 = mbuf + (wave - 1) * PER;
+#pragma unroll
+            for (int j = 0; j < MBX; ++j)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) d0[((j * DB + db) * 16 + r) * 64 + lane] = dz[j][db][r];
+        }
+        __syncthreads();
+        if (wave == 0) {
+            for (int t = 0; t < 3; ++t) {
+                const float* s0 = mbuf + t * PER;
+#pragma unroll
+                for (int j = 0; j < MBX; ++j)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) dz[j][db][r] += s0[((j * DB + db) * 16 + r) * 64 + lane];
+            }
+#pragma unroll
+            for (int j = 0; j < MBX; ++j) {
+                const int m = 32 * j + l32;
+                if (j < MB && m < M) {
+                    float* dst = a.part + (((int64_t)bh * gridDim.x + blockIdx.x) * M + m) * D;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const f32x4 v = {dz[j][db][4 * g4], dz[j][db][4 * g4 + 1], dz[j][db][4 * g4 + 2],
+                                             dz[j][db][4 * g4 + 3]};
+                            *(f32x4*)(dst + 32 * db + 8 * g4 + 4 * hi) = v;
+                        }
+                }
+            }
+        }
     }
 }
 
@@ -1088,7 +1194,7 @@ hipError_t launch_bw_tok(F fn, const BackwardArgs& a, int lds, hipStream_t s, in
 }
 }  // namespace
 
-int bw_fused_dq_groups(const BackwardArgs& a) {
+int bw_fused_groups(const BackwardArgs& a) {
     const int Mp = (a.M + 31) / 32 * 32;
     if (!a.bf16 || a.enc_only || a.D != 32 || Mp > 128 || a.C < 1) return 0;
     return std::min(tok_groups(a), a.C);
@@ -1096,6 +1202,12 @@ int bw_fused_dq_groups(const BackwardArgs& a) {
 
 hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s) {
     const int Mp = (a.M + 31) / 32 * 32, lds = 2 * Mp * 2 * a.D + 16;
+    if (const int fg = bw_fused_groups(a)) {
+        // dZ fused in: per-wave dY and Bt tiles, and the four waves' sums
+        // merged through LDS at the end
+        const int lds_f = std::max(lds + 4 * (32 * 2 * a.D + 32 * 64), 3 * 4 * (a.D / 32) * 16 * 64 * 4);
+        return launch_bw_tok(bw_stats_bf16<32, true>, a, lds_f, s, fg);
+    }
     if (a.D == 32) return launch_bw_tok(bw_stats_bf16<32>, a, lds, s);
     if (a.D == 64) return launch_bw_tok(bw_stats_bf16<64>, a, lds, s);
     return hipErrorInvalidValue;
@@ -1133,7 +1245,7 @@ hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
         if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64, true>, a, lds, s);
         return hipErrorInvalidValue;
     }
-    if (const int fg = bw_fused_dq_groups(a)) {
+    if (const int fg = bw_fused_groups(a)) {
         // dQ fused in: per-wave K and dl tiles, and the four waves' sums
         // merged through LDS at the end
         const int lds_f = std::max(lds + 4 * (32 * 2 * a.D + 32 * 64), 3 * 4 * (a.D / 32) * 16 * 64 * 4);
