@@ -16,8 +16,9 @@
 // Nothing N x M is stored: every kernel recomputes the logits it needs. The
 // encode statistics (mu*, sig*) and Z come from the forward's own encode and
 // combine; the decode statistics (nu, tau) and del per token from bw_stats.
-// dQ's partial sums come from the latent kernels, or (bf16, D = 32, M <= 128)
-// from the dK/dV kernel itself.
+// The dZ and dQ partial sums come from the latent kernels, or (bf16, D = 32,
+// M <= 128) from the token-side kernels themselves: dZ from bw_stats_bf16,
+// dQ from bw_dkdv_bf16.
 //
 // Layout of work in the fp32 kernels: a pair of lanes (l, l ^ 32) owns one
 // token (token kernels) or one latent (latent kernels), each lane holding half
@@ -330,7 +331,8 @@ __device__ __forceinline__ void stage_rows(unsigned char* dst, const ST* src, in
 // softmax's normaliser, log2 units) and del = <dY, Y> = sum_m Bt[n][m] <dY[n],
 // Z[m]>. One sweep over the latents against a bound on every logit of the
 // head, with a second against the token's exact maximum where the first
-// underflows.
+// underflows. FDZ (D = 32, M <= 128): a further sweep forms Bt and the dZ
+// partial sums, dZ^T[d][m] += dY^T[d][n] Bt[n][m] over the workgroup's tokens.
 template <int D, bool FDZ = false>
 __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
     static_assert(!FDZ || D == 32, "dZ fused at D = 32 only");
