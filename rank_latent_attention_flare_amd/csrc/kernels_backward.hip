@@ -231,19 +231,29 @@ __global__ __launch_bounds__(256) void bw_dz_combine(BackwardArgs a) {
 }
 
 // dQ[h] = sum over the batch and the chunks of the partials (already scaled
-// by s), stored in the operator dtype. One thread per (h, m, d).
+// by s), stored in the operator dtype. A workgroup covers 64 consecutive
+// entries (h, m, d); its four waves sum interleaved quarters of the B * C
+// partials, which are then added in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void bw_dq_combine(BackwardArgs a) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (h * M + m) * D + d
+    __shared__ float red[3][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t e = (int64_t)blockIdx.x * 64 + lane;  // (h * M + m) * D + d
     const int64_t MD = (int64_t)a.M * a.D;
-    if (e >= (int64_t)a.H * MD) return;
-    const int h = (int)(e / MD);
-    const int64_t md = e - (int64_t)h * MD;
-    const int B = a.BH / a.H, C = a.C;
+    const bool in = e < (int64_t)a.H * MD;
     float s = 0.0f;
-    for (int b = 0; b < B; ++b)
-        for (int ch = 0; ch < C; ++ch) s += a.part[((int64_t)(b * a.H + h) * C + ch) * MD + md];
-    st<T>((T*)a.dQ + e, s);
+    if (in) {
+        const int h = (int)(e / MD);
+        const int64_t md = e - (int64_t)h * MD;
+        const int B = a.BH / a.H, C = a.C;
+        for (int q = w; q < B * C; q += 4) {
+            const int b = q / C, ch = q - b * C;
+            s += a.part[((int64_t)(b * a.H + h) * C + ch) * MD + md];
+        }
+    }
+    if (w > 0) red[w - 1][lane] = s;
+    __syncthreads();
+    if (w == 0 && in) st<T>((T*)a.dQ + e, s + red[0][lane] + red[1][lane] + red[2][lane]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1272,11 +1282,11 @@ hipError_t launch_bw_dz_combine(const BackwardArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bw_dq_combine(const BackwardArgs& a, hipStream_t s) {
-    const int64_t n = (int64_t)a.H * a.M * a.D;
+    const int64_t n = (int64_t)a.H * a.M * a.D;  // 64 entries per workgroup
     if (a.bf16)
-        hipLaunchKernelGGL(bw_dq_combine<uint16_t>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bw_dq_combine<uint16_t>, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(bw_dq_combine<float>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bw_dq_combine<float>, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
