@@ -506,8 +506,11 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
                 // register i: latent 32 mb + 8 (i/4) + 4 hi + i%4 -> 8 bytes per 4
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    bf16x2 w01 = {(__bf16)exp2_fast(fmaf(S[4 * q], c, -nup)), (__bf16)exp2_fast(fmaf(S[4 * q + 1], c, -nup))};
-                    bf16x2 w23 = {(__bf16)exp2_fast(fmaf(S[4 * q + 2], c, -nup)), (__bf16)exp2_fast(fmaf(S[4 * q + 3], c, -nup))};
+                    float bt[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bt[j] = exp2_fast(fmaf(S[4 * q + j], c, -nup));
+                    const bf16x2 w01 = {(__bf16)bt[0], (__bf16)bt[1]};
+                    const bf16x2 w23 = {(__bf16)bt[2], (__bf16)bt[3]};
                     const u32x2 w = {__builtin_bit_cast(uint32_t, w01), __builtin_bit_cast(uint32_t, w23)};
                     *(u32x2*)(btile + tile_off<32>(l32, q) + 8 * hi) = w;
                 }
