@@ -523,10 +523,12 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     // skip the decode term and need no per-token statistics; the fp32
     // kernels compute the full formula with the caller's dY = 0.
     a.enc_only = mc && dz_given;
-    // bf16 at D = 32 (M <= 128): the token-side kernels also form the
-    // latent-side partials (dZ in the statistics kernel, dQ in the dK/dV
-    // kernel), one per workgroup, in fg chunk slots
-    const int fg = mc ? flare::bw_fused_groups(a) : 0;
+    // bf16 at D = 32 (M <= 128), and for dZ also at D = 64 (M <= 64): the
+    // token-side kernels also form the latent-side partials (dZ in the
+    // statistics kernel, dQ in the dK/dV kernel), one per workgroup, in fz
+    // and fq chunk slots
+    const int fz = mc ? flare::bw_fused_dz_groups(a) : 0;
+    const int fq = mc ? flare::bw_fused_dq_groups(a) : 0;
     if (e == hipSuccess && !a.enc_only)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_stats_bf16(a, s) : flare::launch_bw_stats(a, s); });
     if (dz_given) {
@@ -538,18 +540,18 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
         one.C = 1;
         if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(one, s); });
     } else {
-        if (e == hipSuccess && fg == 0)
+        if (e == hipSuccess && fz == 0)
             e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, false, s) : flare::launch_bw_dz(a, s); });
         flare::BackwardArgs dza = a;
-        if (fg > 0) dza.C = fg;
+        if (fz > 0) dza.C = fz;
         if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(dza, s); });
     }
     if (e == hipSuccess)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_dkdv_bf16(a, s) : flare::launch_bw_dkdv(a, s); });
-    if (e == hipSuccess && fg == 0)
+    if (e == hipSuccess && fq == 0)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, true, s) : flare::launch_bw_dq(a, s); });
     flare::BackwardArgs dqa = a;
-    if (fg > 0) dqa.C = fg;
+    if (fq > 0) dqa.C = fq;
     if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(dqa, s); });
     return e;
 }

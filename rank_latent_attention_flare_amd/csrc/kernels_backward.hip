@@ -341,11 +341,12 @@ __device__ __forceinline__ void stage_rows(unsigned char* dst, const ST* src, in
 // softmax's normaliser, log2 units) and del = <dY, Y> = sum_m Bt[n][m] <dY[n],
 // Z[m]>. One sweep over the latents against a bound on every logit of the
 // head, with a second against the token's exact maximum where the first
-// underflows. FDZ (D = 32, M <= 128): a further sweep forms Bt and the dZ
-// partial sums, dZ^T[d][m] += dY^T[d][n] Bt[n][m] over the workgroup's tokens.
+// underflows. FDZ (D = 32 with M <= 128, or D = 64 with M <= 64): a further
+// sweep forms Bt and the dZ partial sums, dZ^T[d][m] += dY^T[d][n] Bt[n][m]
+// over the workgroup's tokens.
 template <int D, bool FDZ = false>
 __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
-    static_assert(!FDZ || D == 32, "dZ fused at D = 32 only");
+    static_assert(!FDZ || D == 32 || D == 64, "dZ fused at D = 32 or 64 only");
     constexpr int KB = D / 16;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
     const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
     // registers, for up to MBX latent blocks
     unsigned char* gtile = (unsigned char*)(red + 4) + wave * (32 * 2 * D + 32 * 64);
     unsigned char* btile = gtile + 32 * 2 * D;
-    constexpr int DB = D / 32, MBX = 4, MBU = FDZ ? MBX : 1;
+    constexpr int DB = D / 32, MBX = 4 / DB, MBU = FDZ ? MBX : 1;  // 64 accumulator registers
     f32x16 dz[FDZ ? MBX : 1][DB];
 #pragma unroll
     for (int j = 0; j < (FDZ ? MBX : 1); ++j)
@@ -481,11 +482,14 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
             // tiles (rows = tokens), and transposed reads give dY^T (rows d,
             // k = tokens) and Bt (k = tokens, columns = latents). Padding
             // latents only touch their own (unwritten) columns.
-            auto tr_addr = [&](const unsigned char* t, int kp, int db, int second) {
+            // W: the tile's row width in bf16 (D for dY, 32 latents for Bt)
+            auto tr_addr = [&](auto W, const unsigned char* t, int kp, int db, int second) {
                 const int row = 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
                 const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
-                return t + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+                return t + tile_off<decltype(W)::value>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
             };
+            const std::integral_constant<int, D> wd;
+            const std::integral_constant<int, 32> wb;
             const int n = blk * 32 + l32;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -493,8 +497,8 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
             bf16x8 gt[2][DB];
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                lds_tr_op2(tr_addr(gtile, 0, db, 0), tr_addr(gtile, 0, db, 1), tr_addr(gtile, 1, db, 0),
-                           tr_addr(gtile, 1, db, 1), gt[0][db], gt[1][db]);
+                lds_tr_op2(tr_addr(wd, gtile, 0, db, 0), tr_addr(wd, gtile, 0, db, 1), tr_addr(wd, gtile, 1, db, 0),
+                           tr_addr(wd, gtile, 1, db, 1), gt[0][db], gt[1][db]);
 #pragma unroll MBU
             for (int mb = 0; mb < MBX; ++mb) {
                 if (mb >= MB) continue;
@@ -515,8 +519,8 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
                     *(u32x2*)(btile + tile_off<32>(l32, q) + 8 * hi) = w;
                 }
                 bf16x8 bt0, bt1;
-                lds_tr_op2(tr_addr(btile, 0, 0, 0), tr_addr(btile, 0, 0, 1), tr_addr(btile, 1, 0, 0),
-                           tr_addr(btile, 1, 0, 1), bt0, bt1);
+                lds_tr_op2(tr_addr(wb, btile, 0, 0, 0), tr_addr(wb, btile, 0, 0, 1), tr_addr(wb, btile, 1, 0, 0),
+                           tr_addr(wb, btile, 1, 0, 1), bt0, bt1);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     dz[mb][db] = mfma(gt[0][db], bt0, dz[mb][db]);
@@ -1209,19 +1213,26 @@ hipError_t launch_bw_tok(F fn, const BackwardArgs& a, int lds, hipStream_t s, in
 }
 }  // namespace
 
-int bw_fused_groups(const BackwardArgs& a) {
+int bw_fused_dq_groups(const BackwardArgs& a) {
     const int Mp = (a.M + 31) / 32 * 32;
     if (!a.bf16 || a.enc_only || a.D != 32 || Mp > 128 || a.C < 1) return 0;
     return std::min(tok_groups(a), a.C);
 }
 
+int bw_fused_dz_groups(const BackwardArgs& a) {
+    const int Mp = (a.M + 31) / 32 * 32;
+    if (!a.bf16 || a.enc_only || !((a.D == 32 && Mp <= 128) || (a.D == 64 && Mp <= 64)) || a.C < 1) return 0;
+    return std::min(tok_groups(a), a.C);
+}
+
 hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s) {
     const int Mp = (a.M + 31) / 32 * 32, lds = 2 * Mp * 2 * a.D + 16;
-    if (const int fg = bw_fused_groups(a)) {
+    if (const int fg = bw_fused_dz_groups(a)) {
         // dZ fused in: per-wave dY and Bt tiles, and the four waves' sums
-        // merged through LDS at the end
-        const int lds_f = std::max(lds + 4 * (32 * 2 * a.D + 32 * 64), 3 * 4 * (a.D / 32) * 16 * 64 * 4);
-        return launch_bw_tok(bw_stats_bf16<32, true>, a, lds_f, s, fg);
+        // (64 registers each) merged through LDS at the end
+        const int lds_f = std::max(lds + 4 * (32 * 2 * a.D + 32 * 64), 3 * 16 * 64 * 64 * 4 / 16);
+        if (a.D == 32) return launch_bw_tok(bw_stats_bf16<32, true>, a, lds_f, s, fg);
+        return launch_bw_tok(bw_stats_bf16<64, true>, a, lds_f, s, fg);
     }
     if (a.D == 32) return launch_bw_tok(bw_stats_bf16<32>, a, lds, s);
     if (a.D == 64) return launch_bw_tok(bw_stats_bf16<64>, a, lds, s);
@@ -1260,7 +1271,7 @@ hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
         if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64, true>, a, lds, s);
         return hipErrorInvalidValue;
     }
-    if (const int fg = bw_fused_groups(a)) {
+    if (const int fg = bw_fused_dq_groups(a)) {
         // dQ fused in: per-wave K and dl tiles, and the four waves' sums
         // merged through LDS at the end
         const int lds_f = std::max(lds + 4 * (32 * 2 * a.D + 32 * 64), 3 * 4 * (a.D / 32) * 16 * 64 * 4);

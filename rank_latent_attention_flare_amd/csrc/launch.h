@@ -130,11 +130,13 @@ bool bw_bf16_fits(int M, int D);
 hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s);
 // Workgroups per (b, h) of the token-side kernels when they also form the
-// latent-side partials (bf16, D = 32, the full formula, M <= 128), else 0: the
-// statistics kernel then writes the dZ partials and the dK/dV kernel the dQ
-// partials, each into that many chunk slots of a.part, and no separate
-// latent-side launch runs.
-int bw_fused_groups(const BackwardArgs& a);
+// latent-side partials, else 0: the statistics kernel the dZ partials (bf16,
+// the full formula, D = 32 with M <= 128 or D = 64 with M <= 64) and the dK/dV
+// kernel the dQ partials (bf16, the full formula, D = 32, M <= 128), each into
+// that many chunk slots of a.part; the separate latent-side launch is then
+// skipped.
+int bw_fused_dz_groups(const BackwardArgs& a);
+int bw_fused_dq_groups(const BackwardArgs& a);
 hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s);  // dZ (dq false) or dQ partials
 
 }  // namespace flare
