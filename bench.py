@@ -8,10 +8,16 @@ D=32 in bf16 (the throughput metric is quoted on N=65536, M=128).
 
 Before the warmup steps the step runs back to back for --ramp-seconds (untimed)
 so that the GPU reaches its steady clocks; the timed region is always exactly
---steps full steps. Prints one JSON line with throughput (tokens*heads/s), the roofline position
-of the dominant kernel (its average duration measured with HIP events on the
-launch stream during the timed steps), and the fp64 CPU oracle's throughput
-on a bounded sample of the same workload as a baseline.
+--steps full steps, back to back (hot: whatever the last-level caches still
+hold of the previous step). Prints one JSON line with
+  * throughput (tokens*heads/s) of the timed region;
+  * the roofline position of the dominant kernel: its average duration over a
+    second pass of the same steps, from HIP events that the library binds to
+    each kernel's dispatch on the launch stream (hipExtLaunchKernel), i.e. the
+    kernel's own execution time as a rocprofv3 kernel trace reports it;
+  * a cold-cache pass (--cold-mib): each step timed on its own after a write
+    that evicts the L2s and the Infinity Cache, with its own kernel durations;
+  * the fp64 CPU oracle's throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -52,6 +58,51 @@ def source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def trace_summary(path: str, steps: int, cold: bool) -> str:
+    """Markdown summary of a rocprofv3 kernel trace (kernel_trace.csv) of one
+    default bench.py run: per kernel, the average duration over all launches
+    and over each pass of the run, told apart by launch order. The passes, in
+    order: the clock ramp and warmup, the timed region (back to back; each
+    kernel's duration there includes the wait for the previous kernel's tail),
+    the kernel pass (the durations bench.py reports: isolated kernels) and, if
+    run, the cold pass. Each of the last three holds `steps` steps."""
+    import csv
+    import statistics
+    rows = sorted(csv.DictReader(open(path, newline="")), key=lambda r: int(r["Start_Timestamp"]))
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    passes = ["timed", "kernel pass"] + (["cold"] if cold else [])
+    out = ["| kernel | launches | avg us (all) | " + " | ".join(f"avg us ({p})" for p in passes) + " |",
+           "|---|---|---|" + "---|" * len(passes)]
+    # kernels that run every step (copies, fills and the flush run far fewer
+    # times); the least frequent of them runs once per step
+    step_kernels = {k: d for k, d in by.items() if len(d) >= steps * len(passes)}
+    once = min(len(d) for d in step_kernels.values())
+    for name, d in sorted(step_kernels.items(), key=lambda kv: -sum(kv[1])):
+        n = len(d)
+        k = steps * round(n / once)
+        cols = []
+        for i in range(len(passes)):
+            lo = n - (len(passes) - i) * k
+            cols.append(f"{statistics.mean(d[lo:lo + k]):.2f}")
+        short = name.replace("void ", "").replace("flare::(anonymous namespace)::", "").split("(")[0]
+        out.append(f"| {short} | {n} | {statistics.mean(d):.2f} | " + " | ".join(cols) + " |")
+    return "\n".join(out)
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -70,8 +121,17 @@ def parse():
     p.add_argument("--graph", action="store_true", help="time one replay of a HIP graph holding the K steps")
     p.add_argument("--no-events", action="store_true",
                    help="skip the second pass that times every kernel with HIP events")
+    p.add_argument("--cold-mib", type=int, default=1024,
+                   help="cold-cache pass: write this many MiB between individually timed steps, which evicts the "
+                        "L2s and the 256 MB Infinity Cache, and report it beside the back-to-back (hot) figures; "
+                        "0 skips the pass")
+    p.add_argument("--cold-flush", choices=["read", "write"], default="read",
+                   help="how the cold pass evicts the caches: read the flush buffer (default) or write it")
     p.add_argument("--calib-copy-mib", type=int, default=512,
                    help="size of the plain copy kernel run once before the timed steps (counter calibration)")
+    p.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                   help="print the per-pass kernel summary of a rocprofv3 kernel trace of a default run of this "
+                        "script with the same --steps and --cold-mib, and exit")
     p.add_argument("--ramp-seconds", type=float, default=1.0,
                    help="run the step back to back for this long before the warmup steps, so that the GPU "
                         "reaches its steady clocks (a cold MI355X needs ~0.1-0.2 s); 0 disables")
@@ -80,6 +140,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.steps, args.cold_mib > 0))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this "
               "build: the kernels shard by (batch, head) or by tokens, see the design notes.", file=sys.stderr)
@@ -196,16 +259,54 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    # Per-kernel durations: the same K steps again with a HIP event pair
-    # recorded on the launch stream around every kernel.
+    # Per-kernel durations: the same K steps again, each kernel launched with
+    # a HIP event pair bound to its dispatch (its own start and end).
+    # The pass is itself timed like the timed region: dispatch-bound events add
+    # no packets to the stream, so its step time should match (reported).
     kt = {}
+    ev_ms_step = None
     if not args.no_events:
         F.flare_timing_enable(True)
+        start.record(stream)
         for _ in range(args.steps):
             fn(Q, K, V, out=Y, workspace=ws)
+        end.record(stream)
         torch.cuda.synchronize()
+        ev_ms_step = start.elapsed_time(end) / args.steps
         kt = F.flare_timing_read()
         F.flare_timing_enable(False)
+    # Cold-cache pass: every step timed on its own, after a pass over
+    # --cold-mib MiB that leaves none of the step's inputs in the L2s or the
+    # Infinity Cache; kernel durations again from dispatch-bound events. The
+    # default flush reads (a sum): a written flush leaves the caches full of
+    # dirty lines whose write-back then runs during the timed step.
+    cold = None
+    if args.cold_mib > 0:
+        flush = torch.ones(args.cold_mib << 20, dtype=torch.uint8, device="cuda")
+        flush_sink = torch.empty((), dtype=torch.int32, device="cuda")
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        F.flare_timing_enable(True)
+        for a_ev, b_ev in pairs:
+            if args.cold_flush == "write":
+                flush.fill_(1)
+            else:
+                flush_sink.copy_(flush.sum(dtype=torch.int32))
+            a_ev.record(stream)
+            fn(Q, K, V, out=Y, workspace=ws)
+            b_ev.record(stream)
+        torch.cuda.synchronize()
+        kt_cold = F.flare_timing_read()
+        F.flare_timing_enable(False)
+        del flush
+        step_ms = sorted(a_ev.elapsed_time(b_ev) for a_ev, b_ev in pairs)
+        med = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1]
+                                                                          + step_ms[len(step_ms) // 2])
+        cold = {"flush_mib": args.cold_mib, "flush": args.cold_flush, "steps": args.steps, "ms_per_step_median": round(med, 5),
+                "ms_per_step_min": round(step_ms[0], 5),
+                "value_median": round(w.B * w.H * w.N / (med * 1e-3), 1),
+                "kernels": {k: {"avg_us": round(1e3 * ms / cnt, 3), "launches_per_step": cnt / args.steps}
+                            for k, (ms, cnt) in kt_cold.items() if cnt}}
     outs = grads if args.variant == "backward" else (Y,)
     if not all(torch.isfinite(t.float()).all() for t in outs):
         print("non-finite output", file=sys.stderr)
@@ -230,12 +331,15 @@ def main():
         # accumulations of each kernel (stats 6, dZ 4, dK/dV 10, dQ 8) x M*N*D flops; on the
         # bf16 matrix core for bf16 heads whose Q, Z and dZ fit in LDS (D = 32, or D = 64 with
         # M <= 256), else fp32 VALU
-        # FLARE++: the second stage's 28, plus the first stage's statistics, dK/dV and dQ
-        # kernels (6 + 10 + 8), which run with dY = 0 and the given dZ
-        bw_flops = (52 if op == F.FLARE_OP_PP_FORWARD else 28) * w.B * w.H * w.N * w.M * w.D
+        # FLARE++: the second stage's 28, plus the first stage's: on the matrix core its
+        # encode-only dK/dV (8: logits, dl from dZ V^T, and the dK and dV products) and dQ
+        # (6: logits, dZ V^T, dl K) kernels, with no statistics kernel; the fp32 kernels
+        # compute the full formula with dY = 0 (statistics 6, dK/dV 10, dQ 8)
+        on_mfma = w.dtype == "bf16" and (w.D == 32 or (w.D == 64 and w.M <= 256))
+        pp_first = 14 if on_mfma else 24
+        bw_flops = ((28 + pp_first) if op == F.FLARE_OP_PP_FORWARD else 28) * w.B * w.H * w.N * w.M * w.D
         bw_ms = kt.get("backward", (0.0, 0))[0] / args.steps if kt else ms_step
         achieved_tf = bw_flops / (bw_ms * 1e-3) / 1e12
-        on_mfma = w.dtype == "bf16" and (w.D == 32 or (w.D == 64 and w.M <= 256))
         peak = BF16_MFMA_PEAK_TFLOPS if on_mfma else 157.3
         roofline = {"bound": "mfma" if on_mfma else "alu", "kernel": "backward", "achieved": round(achieved_tf, 2),
                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved_tf / peak, 4), "traffic": None,
@@ -256,6 +360,13 @@ def main():
                 pmc = json.load(f)
             if pmc.get("source_hash") == source_hash(dominant):
                 traffic = pmc.get("hbm_bytes_per_launch")
+        if cold and dominant in cold["kernels"]:
+            cold_gbs = alg_bytes[dominant] / (cold["kernels"][dominant]["avg_us"] * 1e-6) / 1e9
+            cold["roofline"] = {"kernel": dominant, "achieved": round(cold_gbs, 1),
+                                "frac": round(cold_gbs / HBM_PEAK_GBS, 4),
+                                "hbm_frac_step": round((4 if passes == 1 else 6) * kv_bytes
+                                                       / (cold["ms_per_step_median"] * 1e-3) / 1e9
+                                                       / HBM_PEAK_GBS, 4)}
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "alg_bytes_per_launch": alg_bytes[dominant],
@@ -296,7 +407,7 @@ def main():
         ntok = bw_n if args.variant == "backward" else w.N
         cores = 1 if args.variant == "backward" else oracle.threads()  # the fp64 backward is one loop nest
         cpu = {"value": round(done * ntok / el, 1), "unit": "tokens*heads/s", "cores": cores,
-               "kind": "oracle", "sample": f"{done} of {len(heads)} heads of {w.name}, N={ntok} of {w.N}, "
+               "cpu_model": cpu_model(), "kind": "oracle", "sample": f"{done} of {len(heads)} heads of {w.name}, N={ntok} of {w.N}, "
                                             f"fp64 {w.op if args.variant == 'flare' else args.variant}, "
                                             f"{el:.1f} s"}
 
@@ -304,13 +415,16 @@ def main():
         "metric": "FLARE fwd tokens*heads/s (N=65536, M=128) + roofline fraction",
         "value": round(value, 1), "unit": "tokens*heads/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ramp": {"seconds": args.ramp_seconds, "steps": ramp_steps},
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": round(ms_step, 5),
+        "ms_per_step_kernel_pass": None if ev_ms_step is None else round(ev_ms_step, 5),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (" + recipe() + ")",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "op": w.op,
                    "layout": args.layout, "variant": args.variant,
                    "plan": F.flare_describe_plan(op, w.B, w.H, w.N, w.M, w.D, Q.dtype)},
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kern.items()},
         "roofline": roofline,
+        "cold": cold,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

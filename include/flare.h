@@ -31,8 +31,9 @@
  *             nearest-even bf16.
  *   Sizes     B, H, N, M, D >= 1, B*H <= 65535, N <= 2^30. Supported:
  *             FLARE_F32 with D in {8, 16, 24, 32, 48, 64, 96, 128} and
- *             M <= 4096; FLARE_BF16 with D in {32, 64, 128} and M <= 256.
- *             Other sizes return FLARE_ERR_UNSUPPORTED.
+ *             M <= 4096; FLARE_BF16 with D in {32, 64} and M <= 512, or
+ *             D = 128 and M <= 256. Other sizes return
+ *             FLARE_ERR_UNSUPPORTED.
  *   Async     Work is enqueued on `stream` (0 = the legacy default stream)
  *             and the call returns; inputs must stay unchanged until the
  *             stream passes the call. Device faults surface at the caller's
@@ -76,7 +77,8 @@ typedef enum {
     FLARE_OP_FORWARD = 2,
     FLARE_OP_PP_FORWARD = 3,
     FLARE_OP_BACKWARD = 4,   /* flare_backward (workspace sizing only) */
-    FLARE_OP_PP_BACKWARD = 5 /* flare_pp_backward (workspace sizing only) */
+    FLARE_OP_PP_BACKWARD = 5, /* flare_pp_backward (workspace sizing only) */
+    FLARE_OP_PP_QUERIES = 6   /* flare_pp_queries */
 } flare_op;
 
 /* Encode: Y := Z[B][H][M][D] = softmax_n(s Q K^T) V for every (b, h).
@@ -107,6 +109,24 @@ flare_status flare_forward(const void* Q, const void* K, const void* V, void* Y,
 flare_status flare_pp_forward(const void* Q, const void* K, const void* V, void* Y,
                               int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
                               flare_dtype dtype, hipStream_t stream);
+
+/* FLARE++ corrected queries alone: Qp[b][h] = Q[h] + encode(Q, K, V)[b][h],
+ * rounded to nearest-even in dtype, as [B][H][M][D]. These are the dynamic,
+ * input-conditioned latent queries of the FLARE++ skill page ("Core
+ * Mechanism", "Mathematical Formulation"), with the residual of the FLARE++
+ * arXiv abstract (the encoder's output corrects the learned queries). The
+ * values are bit for bit the Q' that flare_pp_forward computes for the same
+ * inputs and then uses in its second encode and its decode (same kernels,
+ * same split of the tokens), so flare_pp_forward at B = 1 equals
+ * flare_forward with Q = Qp[0]. Inputs Q [H][M][D], K and V [B][H][N][D];
+ * output Qp [B][H][M][D] (may not overlap an input). The _ws variant takes
+ * flare_workspace_size(FLARE_OP_PP_QUERIES, ...) bytes of scratch memory. */
+flare_status flare_pp_queries(const void* Q, const void* K, const void* V, void* Qp,
+                              int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                              flare_dtype dtype, hipStream_t stream);
+flare_status flare_pp_queries_ws(const void* Q, const void* K, const void* V, void* Qp,
+                                 int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                 flare_dtype dtype, hipStream_t stream, void* workspace, size_t ws_bytes);
 
 /* Scratch bytes the *_ws variant of `op` needs for these sizes (0 when the
  * sizes or type are invalid or unsupported). */
@@ -186,10 +206,15 @@ flare_status flare_attend(const void* q, const void* Z, void* Y,
  *            + Bt[n][m] (<dY[n],Z[m]> - <dY[n],Y[n]>),
  *   dQ = s dl K (summed over the batch, Q being shared),  dK = s dl^T Q.
  * Inputs Q [H][M][D], K, V, dY [B][H][N][D]; outputs dQ [H][M][D], dK, dV
- * [B][H][N][D], in the operator dtype (arithmetic in fp32). It recomputes
- * the forward's encode internally; nothing N x M is stored. Supported for
- * D in {8, 16, 24, 32, 48, 64} (bf16: 32 and 64) with the forward's M range;
- * otherwise FLARE_ERR_UNSUPPORTED. Outputs may not overlap inputs or each
+ * [B][H][N][D], in the operator dtype. Precision follows the forward's:
+ * FLARE_F32 computes in fp32 throughout; FLARE_BF16 heads whose Q, Z and
+ * dZ fit in one compute unit's LDS (D = 32, or D = 64 with M <= 256) run on
+ * bf16 MFMA with fp32 accumulation, the probabilities, dl and the staged
+ * Q, Z and dZ being rounded to nearest-even bf16 where they become MFMA
+ * operands; other bf16 heads run fp32 arithmetic on the widened inputs.
+ * It recomputes the forward's encode internally; nothing N x M is stored.
+ * Supported for D in {8, 16, 24, 32, 48, 64} (bf16: 32 and 64) with the
+ * forward's M range; otherwise FLARE_ERR_UNSUPPORTED. Outputs may not overlap inputs or each
  * other. The _ws variant takes flare_workspace_size(FLARE_OP_BACKWARD, ...)
  * bytes of caller-owned scratch memory. */
 flare_status flare_backward(const void* Q, const void* K, const void* V, const void* dY,
@@ -230,6 +255,29 @@ const char* flare_status_string(flare_status s);
  * pointer stays valid until the thread's next libflare call. */
 const char* flare_last_error(void);
 
+/* --------------------------------------------------------------- tuning
+ * Process-wide overrides of the launch plan, for tests and measurement
+ * sweeps. They change how the work is split across workgroups, never what is
+ * computed: results differ at most by rounding. A value of 0 restores the
+ * library's own choice; negative values and unknown keys return
+ * FLARE_ERR_INVALID_ARG. Overrides apply to calls that start after the set. */
+typedef enum {
+    FLARE_TUNE_CHUNKS = 0,      /* encode: token chunks per (b, h) (capped at N) */
+    FLARE_TUNE_ENC_MBW = 1,     /* bf16 encode shape: latent blocks of 32 per wave, */
+    FLARE_TUNE_ENC_WM = 2,      /*   waves over latent blocks (0: one wave owns them all), */
+    FLARE_TUNE_ENC_WT = 3,      /*   waves over tokens. Used together when MBW > 0 and they
+                                 *   cover M; a shape that is not built fails the launch
+                                 *   with FLARE_ERR_HIP. */
+    FLARE_TUNE_DEC_TB = 4,      /* bf16 decode: 32-token blocks per wave and step (1; 2 at
+                                 *   D <= 64 and M <= 256) */
+    FLARE_TUNE_DEC_GROUPS = 5,  /* decode: workgroups per (b, h) */
+    FLARE_TUNE_FAIL_ALLOC = 6,  /* 1: the allocating entry points fail with
+                                 *   FLARE_ERR_NO_MEMORY (error-path tests) */
+    FLARE_TUNE_KEYS = 7
+} flare_tune;
+
+flare_status flare_set_tuning(flare_tune key, int64_t value);
+
 /* ---------------------------------------------------------- measurement
  * Kernel timing with HIP events recorded on the launch stream around every
  * kernel the library enqueues. Kernel kinds: 0 = encode partial (split-N
@@ -237,7 +285,10 @@ const char* flare_last_error(void);
 #define FLARE_KERNEL_KINDS 4
 
 /* Turn event recording on (1) or off (0) for the calling process, and drop
- * every recorded event. */
+ * every recorded event. While it is on, each kernel is launched with
+ * hipExtLaunchKernel and an event pair bound to its dispatch, so the elapsed
+ * time of a pair is the kernel's own execution time (as a kernel trace
+ * reports it), without the launch gaps. */
 flare_status flare_timing_enable(int on);
 
 /* Wait for the recorded events, add the elapsed milliseconds of each kernel

@@ -6,13 +6,16 @@
 //   decode      K3 decode (Z given)
 //   forward     K1 -> K2 (fp32 Z) -> K3
 //   pp_forward  K1(Q) -> K2 (Q' = Q + Z0) -> K1(Q') -> K2 (fp32 Z) -> K3(Q')
+//   pp_queries  K1(Q) -> K2 (Q' = Q + Z0, the output)
 // FLARE skill page steps 2-4 and FLARE arXiv abstract (encode/decode);
 // FLARE++ skill page "Core Mechanism" and FLARE++ arXiv abstract (Q').
 #include "flare.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -40,6 +43,10 @@ flare_status hip_fail(hipError_t e, const char* what) {
     return fail(FLARE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// Tuning overrides (flare_set_tuning); 0 = the library's own choice.
+std::atomic<int64_t> g_tune[FLARE_TUNE_KEYS];
+int64_t tune(flare_tune k) { return g_tune[k].load(std::memory_order_relaxed); }
+
 constexpr int kTargetEncWaves = 2048;  // waves over all encode workgroups
 constexpr int kTargetDecWgs = 1024;    // decode workgroups
 constexpr int64_t kMaxGridY = 65535;
@@ -51,9 +58,11 @@ struct Plan {
     int64_t B, H, N, M, D;
     int BH, Mp;
     int C, chunk_len;  // encode split over N
-    int G;             // decode workgroups per (b, h)
+    int G;             // decode workgroups per (b, h) (fp32; bf16: decode_groups)
+    int tb;            // bf16 decode: 32-token blocks per wave and step
+    flare::EncCfg cfg; // bf16 encode workgroup shape
     size_t esize;
-    size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[5];
+    size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[7];
     size_t off_zsig, off_nu, off_tau, off_del, off_dz, off_gam;  // backward
     float c;
     int64_t sb, sh, sn;  // element strides of K, V and Y: batch, head, token
@@ -121,10 +130,20 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     int tile, waves_per_wg;
     if (dt == FLARE_BF16) {
         p->Mp = int((M + 31) / 32 * 32);
-        const flare::EncCfg cfg = flare::enc_cfg_bf16(int(D), p->Mp / 32);
-        tile = flare::enc_tile_tokens_bf16(cfg);
-        waves_per_wg = flare::enc_threads_bf16(cfg) / 64;
+        p->cfg = flare::enc_cfg_bf16(int(D), p->Mp / 32);
+        // an override must cover the latent blocks (and name a built shape,
+        // else the launch fails)
+        const flare::EncCfg o{int(tune(FLARE_TUNE_ENC_MBW)), int(tune(FLARE_TUNE_ENC_WM)),
+                              int(tune(FLARE_TUNE_ENC_WT))};
+        if (o.mbw > 0 && o.wt > 0 && o.wm >= 0 && (o.wm == 0 ? o.mbw : o.mbw * o.wm) >= p->Mp / 32) p->cfg = o;
+        tile = flare::enc_tile_tokens_bf16(p->cfg);
+        waves_per_wg = flare::enc_threads_bf16(p->cfg) / 64;
+        p->tb = flare::dec_tb_bf16(int(D), p->Mp);
+        const int64_t otb = tune(FLARE_TUNE_DEC_TB);
+        if (otb > 0 && flare::dec_tb_built_bf16(int(D), p->Mp, int(otb))) p->tb = int(otb);
     } else {
+        p->tb = 2;
+        p->cfg = flare::EncCfg{0, 0, 0};
         p->Mp = int(M);
         tile = 64;
         const int nth = flare::enc_threads_f32(int(M));
@@ -139,17 +158,14 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
         dt == FLARE_BF16 ? 32 * int64_t(std::min(p->Mp, 256)) : std::max<int64_t>(tile, 4 * int64_t(p->Mp));
     const int64_t cmax = std::max<int64_t>(1, N / min_chunk);
     C = std::min(C, cmax);
-    if (const char* e = std::getenv("FLARE_TEST_CHUNKS")) {
-        const long v = std::strtol(e, nullptr, 10);
-        if (v > 0) C = v;
-    }
+    if (tune(FLARE_TUNE_CHUNKS) > 0) C = std::min<int64_t>(tune(FLARE_TUNE_CHUNKS), N);
     int64_t chunk = (N + C - 1) / C;
     chunk = (chunk + tile - 1) / tile * tile;
     C = (N + chunk - 1) / chunk;
     p->C = int(C);
     p->chunk_len = int(chunk);
     // decode workgroups per (b, h)
-    const int64_t per_wg = 32 * (dt == FLARE_BF16 ? flare::dec_tb_bf16(int(D), p->Mp) : 2) * flare::kDecWaves;
+    const int64_t per_wg = 32 * p->tb * flare::kDecWaves;
     int64_t G = std::max<int64_t>(1, (kTargetDecWgs + p->BH - 1) / p->BH);
     G = std::min<int64_t>(G, (N + per_wg - 1) / per_wg);
     p->G = int(G);
@@ -168,6 +184,7 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     p->total[FLARE_OP_DECODE] = 0;
     p->total[FLARE_OP_FORWARD] = fwd_total;
     p->total[FLARE_OP_PP_FORWARD] = off;
+    p->total[FLARE_OP_PP_QUERIES] = enc_total;
     // backward: the forward's sections (encode partials, reused for the dZ and
     // dQ partials; Z and mu*), then sig*, the per-token decode statistics, dZ
     // and gam
@@ -180,6 +197,7 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     p->off_dz = off;   off = align256(off + lat * size_t(D));
     p->off_gam = off;  off = align256(off + lat);
     p->total[FLARE_OP_BACKWARD] = off;
+    p->total[FLARE_OP_PP_BACKWARD] = 0;  // sized by pp_layout
     return FLARE_OK;
 }
 
@@ -199,16 +217,21 @@ flare_status check_ptrs(const Plan& p, flare_op op, const void* Q, const void* K
     const size_t nkv = size_t(p.BH) * p.N * p.D * e;
     const size_t nz = size_t(p.BH) * p.M * p.D * e;
     const size_t nv = op == FLARE_OP_DECODE ? nz : nkv;
-    const size_t ny = op == FLARE_OP_ENCODE ? nz : nkv;
+    const size_t ny = (op == FLARE_OP_ENCODE || op == FLARE_OP_PP_QUERIES) ? nz : nkv;
     if (overlaps(Y, ny, Q, nq) || overlaps(Y, ny, K, nkv) || overlaps(Y, ny, V, nv))
         return fail(FLARE_ERR_INVALID_ARG, "output overlaps an input");
     return FLARE_OK;
 }
 
 // ------------------------------------------------------------------ timing
+// While timing is on, every kernel is launched with hipExtLaunchKernel and a
+// pair of events bound to its dispatch (the events then hold the kernel's own
+// start and end, as a kernel trace shows them), tagged with the kind the
+// calling launcher set in t_kind. With timing off the launch path reads one
+// atomic flag and takes no lock.
 struct Timing {
     std::mutex mu;
-    bool on = false;
+    std::atomic<bool> on{false};
     struct Rec {
         int kind;
         hipEvent_t a, b;
@@ -217,6 +240,7 @@ struct Timing {
     std::vector<hipEvent_t> pool;
 };
 Timing g_timing;
+thread_local int t_kind = -1;
 
 hipEvent_t take_event() {
     if (!g_timing.pool.empty()) {
@@ -230,22 +254,11 @@ hipEvent_t take_event() {
 }
 
 template <class F>
-hipError_t timed(int kind, hipStream_t s, F&& launch) {
-    std::unique_lock<std::mutex> lk(g_timing.mu);
-    if (!g_timing.on) {
-        lk.unlock();
-        return launch();
-    }
-    hipEvent_t a = take_event(), b = take_event();
-    if (!a || !b) return hipErrorOutOfMemory;
-    hipError_t e = hipEventRecord(a, s);
-    if (e != hipSuccess) return e;
-    e = launch();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(b, s);
-    if (e != hipSuccess) return e;
-    g_timing.recs.push_back({kind, a, b});
-    return hipSuccess;
+hipError_t timed(int kind, hipStream_t, F&& launch) {
+    t_kind = kind;
+    const hipError_t e = launch();
+    t_kind = -1;
+    return e;
 }
 
 // --------------------------------------------------------------- launchers
@@ -261,6 +274,7 @@ hipError_t run_encode_partial(const Plan& p, const void* Q, int64_t q_bstride, c
     a.C = p.C;
     a.chunk_len = p.chunk_len;
     a.c = p.c;
+    a.cfg = p.cfg;
     a.out.acc = (float*)(ws + p.off_acc);
     a.out.mu = (float*)(ws + p.off_mu);
     a.out.sig = (float*)(ws + p.off_sig);
@@ -288,12 +302,10 @@ hipError_t run_combine(const Plan& p, int mode, const void* Q, void* out, char* 
 // Decode workgroups per (b, h): one resident wave of workgroups over the
 // whole chip (from the kernel's occupancy), each looping over token blocks.
 int decode_groups(const Plan& p, bool z_f32) {
-    if (const char* e = std::getenv("FLARE_TEST_DEC_G")) {
-        const int v = std::atoi(e);
-        if (v > 0) return v;
-    }
+    if (tune(FLARE_TUNE_DEC_GROUPS) > 0) return int(std::min<int64_t>(tune(FLARE_TUNE_DEC_GROUPS), 1 << 20));
     if (p.dt != FLARE_BF16) return p.G;
-    static int cus = 0;
+    static std::atomic<int> cus_cache{0};
+    int cus = cus_cache.load(std::memory_order_relaxed);
     if (cus == 0) {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
@@ -301,9 +313,10 @@ int decode_groups(const Plan& p, bool z_f32) {
             cus = n;
         else
             cus = 256;
+        cus_cache.store(cus, std::memory_order_relaxed);
     }
-    const int per_cu = flare::dec_wgs_per_cu_bf16(int(p.D), p.Mp, z_f32);
-    const int64_t per_wg = 32 * flare::dec_tb_bf16(int(p.D), p.Mp) * flare::kDecWaves;
+    const int per_cu = flare::dec_wgs_per_cu_bf16(int(p.D), p.Mp, p.tb, z_f32);
+    const int64_t per_wg = 32 * p.tb * flare::kDecWaves;
     int64_t G = (int64_t(cus) * per_cu + p.BH - 1) / p.BH;
     G = std::max<int64_t>(1, std::min<int64_t>(G, (p.N + per_wg - 1) / per_wg));
     return int(G);
@@ -322,6 +335,7 @@ hipError_t run_decode(const Plan& p, const void* Q, int64_t q_bstride, const voi
     a.sb = p.sb; a.sh = p.sh; a.sn = p.sn;
     a.BH = p.BH; a.H = int(p.H); a.N = int(p.N); a.M = int(p.M); a.Mp = p.Mp; a.D = int(p.D);
     a.G = decode_groups(p, z_f32);
+    a.tb = p.tb;
     a.c = p.c;
     return timed(2, s, [&] {
         return p.dt == FLARE_BF16 ? flare::launch_decode_bf16(a, s) : flare::launch_decode_f32(a, s);
@@ -365,6 +379,11 @@ flare_status exec(flare_op op, const void* Q, const void* K, const void* V, void
         case FLARE_OP_DECODE:
             e = run_decode(p, Q, 0, K, V, dt == FLARE_F32, Y, s);
             break;
+        case FLARE_OP_PP_QUERIES:
+            // the first two launches of pp_forward, with Q' written to the output
+            e = run_encode_partial(p, Q, 0, K, V, ws, s);
+            if (e == hipSuccess) e = run_combine(p, flare::COMBINE_QPRIME, Q, Y, ws, s);
+            break;
         case FLARE_OP_FORWARD:
             e = run_encode_partial(p, Q, 0, K, V, ws, s);
             if (e == hipSuccess)
@@ -401,8 +420,7 @@ flare_status exec_alloc(flare_op op, const void* Q, const void* K, const void* V
     const size_t need = p.total[op];
     void* ws = nullptr;
     if (need > 0) {
-        const char* f = std::getenv("FLARE_TEST_FAIL_ALLOC");
-        if (f && std::strcmp(f, "1") == 0) return fail(FLARE_ERR_NO_MEMORY, "allocation failure injected by FLARE_TEST_FAIL_ALLOC");
+        if (tune(FLARE_TUNE_FAIL_ALLOC) == 1) return fail(FLARE_ERR_NO_MEMORY, "allocation failure injected (FLARE_TUNE_FAIL_ALLOC)");
         hipError_t e = hipMallocAsync(&ws, need, s);
         if (e != hipSuccess || !ws) return fail(FLARE_ERR_NO_MEMORY, std::string("hipMallocAsync: ") + hipGetErrorString(e));
     }
@@ -435,6 +453,23 @@ PPLayout pp_layout(const Plan& pf, const Plan& p1) {
 
 }  // namespace
 
+namespace flare {
+hipError_t launch_raw(const void* fn, dim3 grid, dim3 block, void** args, size_t shm, hipStream_t s) {
+    if (!g_timing.on.load(std::memory_order_relaxed)) return hipLaunchKernel(fn, grid, block, args, shm, s);
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    hipEvent_t a = take_event(), b = take_event();
+    if (!a || !b) return hipErrorOutOfMemory;
+    const hipError_t e = hipExtLaunchKernel(fn, grid, block, args, shm, s, a, b, 0);
+    if (e != hipSuccess) {
+        g_timing.pool.push_back(a);
+        g_timing.pool.push_back(b);
+        return e;
+    }
+    g_timing.recs.push_back({t_kind, a, b});
+    return hipSuccess;
+}
+}  // namespace flare
+
 extern "C" {
 
 flare_status flare_encode(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H, int64_t N,
@@ -455,7 +490,7 @@ flare_status flare_pp_forward(const void* Q, const void* K, const void* V, void*
 }
 
 size_t flare_workspace_size(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype) {
-    if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_BACKWARD) return 0;
+    if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_QUERIES) return 0;
     Plan p;
     if (make_plan(B, H, N, M, D, dtype, &p) != FLARE_OK) return 0;
     if (op == FLARE_OP_PP_BACKWARD) {
@@ -482,6 +517,15 @@ flare_status flare_pp_forward_ws(const void* Q, const void* K, const void* V, vo
                                  int64_t N, int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws,
                                  size_t n) {
     return exec(FLARE_OP_PP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, ws, n);
+}
+flare_status flare_pp_queries(const void* Q, const void* K, const void* V, void* Qp, int64_t B, int64_t H,
+                              int64_t N, int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {
+    return exec_alloc(FLARE_OP_PP_QUERIES, Q, K, V, Qp, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream);
+}
+flare_status flare_pp_queries_ws(const void* Q, const void* K, const void* V, void* Qp, int64_t B, int64_t H,
+                                 int64_t N, int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws,
+                                 size_t n) {
+    return exec(FLARE_OP_PP_QUERIES, Q, K, V, Qp, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, ws, n);
 }
 
 }  // extern "C"
@@ -582,8 +626,7 @@ flare_status check_backward_ptrs(const Plan& p, const void* Q, const void* K, co
 // Workspace: caller's (checked against need) or stream-ordered allocation.
 flare_status get_workspace(size_t need, hipStream_t s, void*& wsv, size_t ws_bytes, bool alloc) {
     if (alloc) {
-        const char* f = std::getenv("FLARE_TEST_FAIL_ALLOC");
-        if (f && std::strcmp(f, "1") == 0) return fail(FLARE_ERR_NO_MEMORY, "allocation failure injected by FLARE_TEST_FAIL_ALLOC");
+        if (tune(FLARE_TUNE_FAIL_ALLOC) == 1) return fail(FLARE_ERR_NO_MEMORY, "allocation failure injected (FLARE_TUNE_FAIL_ALLOC)");
         hipError_t e = hipMallocAsync(&wsv, need, s);
         if (e != hipSuccess || !wsv) return fail(FLARE_ERR_NO_MEMORY, std::string("hipMallocAsync: ") + hipGetErrorString(e));
         return FLARE_OK;
@@ -744,6 +787,14 @@ const char* flare_status_string(flare_status s) {
 
 const char* flare_last_error(void) { return g_last_error.c_str(); }
 
+flare_status flare_set_tuning(flare_tune key, int64_t value) {
+    g_last_error.clear();
+    if (key < 0 || key >= FLARE_TUNE_KEYS) return fail(FLARE_ERR_INVALID_ARG, "unknown tuning key");
+    if (value < 0) return fail(FLARE_ERR_INVALID_ARG, "tuning values are >= 0 (0 = the library's choice)");
+    g_tune[key].store(value, std::memory_order_relaxed);
+    return FLARE_OK;
+}
+
 flare_status flare_timing_enable(int on) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     for (auto& r : g_timing.recs) {
@@ -751,7 +802,7 @@ flare_status flare_timing_enable(int on) {
         g_timing.pool.push_back(r.b);
     }
     g_timing.recs.clear();
-    g_timing.on = on != 0;
+    g_timing.on.store(on != 0);
     return FLARE_OK;
 }
 
@@ -797,7 +848,7 @@ flare_status flare_describe_plan(flare_op op, int64_t B, int64_t H, int64_t N, i
     if (st != FLARE_OK) return st;
     std::string enc;
     if (dtype == FLARE_BF16) {
-        const flare::EncCfg cfg = flare::enc_cfg_bf16(int(D), p.Mp / 32);
+        const flare::EncCfg cfg = p.cfg;
         enc = "encode grid (" + std::to_string(p.C) + "," + std::to_string(p.BH) + ") waves " +
               std::to_string(cfg.wm) + "x" + std::to_string(cfg.wt) + " latent-blocks/wave " + std::to_string(cfg.mbw) +
               " tile " + std::to_string(flare::enc_tile_tokens_bf16(cfg));

@@ -1153,36 +1153,36 @@ template <int D>
 hipError_t stats_d(const BackwardArgs& a, hipStream_t s) {
     dim3 grid((a.N + kTokPerBlock - 1) / kTokPerBlock, a.BH);
     if (a.bf16)
-        hipLaunchKernelGGL((bw_stats<D, uint16_t>), grid, dim3(256), 0, s, a);
+        FLARE_LAUNCH((bw_stats<D, uint16_t>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((bw_stats<D, float>), grid, dim3(256), 0, s, a);
+        FLARE_LAUNCH((bw_stats<D, float>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 template <int D>
 hipError_t dz_d(const BackwardArgs& a, hipStream_t s) {
     dim3 grid(a.C, a.BH, (a.M + 127) / 128);
     if (a.bf16)
-        hipLaunchKernelGGL((bw_latent<D, uint16_t, false>), grid, dim3(256), 0, s, a);
+        FLARE_LAUNCH((bw_latent<D, uint16_t, false>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((bw_latent<D, float, false>), grid, dim3(256), 0, s, a);
+        FLARE_LAUNCH((bw_latent<D, float, false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 template <int D>
 hipError_t dq_d(const BackwardArgs& a, hipStream_t s) {
     dim3 grid(a.C, a.BH, (a.M + 127) / 128);
     if (a.bf16)
-        hipLaunchKernelGGL((bw_latent<D, uint16_t, true>), grid, dim3(256), 0, s, a);
+        FLARE_LAUNCH((bw_latent<D, uint16_t, true>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((bw_latent<D, float, true>), grid, dim3(256), 0, s, a);
+        FLARE_LAUNCH((bw_latent<D, float, true>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 template <int D>
 hipError_t dkdv_d(const BackwardArgs& a, hipStream_t s) {
     dim3 grid((a.N + kTokPerBlock - 1) / kTokPerBlock, a.BH);
     if (a.bf16)
-        hipLaunchKernelGGL((bw_dkdv<D, uint16_t>), grid, dim3(256), 0, s, a);
+        FLARE_LAUNCH((bw_dkdv<D, uint16_t>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((bw_dkdv<D, float>), grid, dim3(256), 0, s, a);
+        FLARE_LAUNCH((bw_dkdv<D, float>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1208,7 +1208,7 @@ hipError_t launch_bw_tok(F fn, const BackwardArgs& a, int lds, hipStream_t s, in
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fn, dim3(G > 0 ? G : tok_groups(a), a.BH), dim3(256), lds, s, a);
+    FLARE_LAUNCH(fn, dim3(G > 0 ? G : tok_groups(a), a.BH), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 }  // namespace
@@ -1250,7 +1250,7 @@ hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
             hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(fn, dim3(a.C, a.BH), dim3(256), lds, s, a);
+        FLARE_LAUNCH(fn, dim3(a.C, a.BH), dim3(256), lds, s, a);
         return hipGetLastError();
     };
     if (dq && a.enc_only) {
@@ -1291,16 +1291,16 @@ hipError_t launch_bw_dkdv(const BackwardArgs& a, hipStream_t s) { FLARE_BW_DISPA
 
 hipError_t launch_bw_dz_combine(const BackwardArgs& a, hipStream_t s) {
     const int64_t n = (int64_t)a.BH * a.M;  // one wave each, four per workgroup
-    hipLaunchKernelGGL(bw_dz_combine, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, a);
+    FLARE_LAUNCH(bw_dz_combine, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_bw_dq_combine(const BackwardArgs& a, hipStream_t s) {
     const int64_t n = (int64_t)a.H * a.M * a.D;  // 64 entries per workgroup
     if (a.bf16)
-        hipLaunchKernelGGL(bw_dq_combine<uint16_t>, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, a);
+        FLARE_LAUNCH(bw_dq_combine<uint16_t>, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(bw_dq_combine<float>, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, a);
+        FLARE_LAUNCH(bw_dq_combine<float>, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

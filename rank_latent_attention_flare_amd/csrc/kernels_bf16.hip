@@ -22,6 +22,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <algorithm>
+#include <atomic>
+#include <mutex>
+#include <vector>
 #include <type_traits>
 
 #include "launch.h"
@@ -1166,20 +1169,20 @@ void decode_bf16(DecodeArgs a) {
 template <int D, int MBW, int WM, int WT>
 hipError_t launch_enc(const EncodeArgs& a, hipStream_t s) {
     dim3 grid(a.C, a.BH), block(64 * WM * WT);
-    hipLaunchKernelGGL((encode_partial_bf16<D, MBW, WM, WT>), grid, block, 0, s, a);
+    FLARE_LAUNCH((encode_partial_bf16<D, MBW, WM, WT>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
 template <int D, int MBW, int NWV>
 hipError_t launch_enc_priv(const EncodeArgs& a, hipStream_t s) {
     dim3 grid(a.C, a.BH), block(64 * NWV);
-    hipLaunchKernelGGL((encode_partial_priv_bf16<D, MBW, NWV>), grid, block, 0, s, a);
+    FLARE_LAUNCH((encode_partial_priv_bf16<D, MBW, NWV>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_enc_d(const EncodeArgs& a, hipStream_t s) {
-    const EncCfg cfg = enc_cfg_bf16(D, a.Mp / 32);
+    const EncCfg cfg = a.cfg;
     if (cfg.wm == 0) {  // private-stream form: cfg.mbw latent blocks per wave, cfg.wt waves
 #define FLARE_ENCP_CASE(MBW, NWV) \
     if (cfg.mbw == MBW && cfg.wt == NWV) return launch_enc_priv<D, MBW, NWV>(a, s);
@@ -1222,25 +1225,45 @@ const void* dec_kernel(int Mp) {
     return (const void*)decode_bf16<D, TB, ZT, false>;
 }
 
+// Dynamic LDS above 64 KB must be allowed per kernel (and device) before a
+// launch or an occupancy query; done once, for the largest size any plan
+// gives a decode kernel.
+constexpr int kDecMaxLds = 160 * 1024;
+hipError_t allow_dec_lds(const void* fn) {
+    struct Done {
+        const void* fn;
+        int dev;
+    };
+    static std::mutex mu;
+    static std::vector<Done> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(mu);
+    for (const Done& d : done)
+        if (d.fn == fn && d.dev == dev) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDecMaxLds);
+    if (e == hipSuccess) done.push_back({fn, dev});
+    return e;
+}
+
 template <int D, int TB, typename ZT>
 hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
     const int lds = dec_lds_bytes_bf16(a.Mp, D);
     const void* fn = dec_kernel<D, TB, ZT>(a.Mp);
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        hipError_t e = allow_dec_lds(fn);
         if (e != hipSuccess) return e;
     }
     DecodeArgs arg = a;
     void* args[] = {&arg};
-    hipError_t e = hipLaunchKernel(fn, dim3(a.G, a.BH), dim3(64 * kDecWaves), args, lds, s);
-    if (e != hipSuccess) return e;
-    return hipGetLastError();
+    return launch_raw(fn, dim3(a.G, a.BH), dim3(64 * kDecWaves), args, lds, s);
 }
 
 template <int D, typename ZT>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t s) {
     if constexpr (D <= 64) {
-        if (dec_tb_bf16(D, a.Mp) == 2) return launch_dec_tb<D, 2, ZT>(a, s);
+        if (a.tb == 2) return launch_dec_tb<D, 2, ZT>(a, s);
     }
     return launch_dec_tb<D, 1, ZT>(a, s);
 }
@@ -1248,12 +1271,6 @@ hipError_t launch_dec(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 EncCfg enc_cfg_bf16(int D, int Mb) {
-    // Tuning override (tests and sweeps): "mbw,wm,wt"; must name an
-    // instantiated shape that covers Mb latent blocks.
-    if (const char* e = std::getenv("FLARE_TEST_ENC_CFG")) {
-        int x = 0, y = 0, z = 0;
-        if (std::sscanf(e, "%d,%d,%d", &x, &y, &z) == 3 && (y == 0 ? x >= Mb : x * y >= Mb)) return {x, y, z};
-    }
     // one latent block: private streams; more: shared tiles (measured equal
     // or faster on MI355X for 2-8 blocks)
     if (Mb <= 1) return {1, 0, 4};
@@ -1267,8 +1284,16 @@ EncCfg enc_cfg_bf16(int D, int Mb) {
 int enc_tile_tokens_bf16(EncCfg cfg) { return cfg.wm == 0 ? 32 * cfg.wt : 64; }
 int enc_threads_bf16(EncCfg cfg) { return 64 * (cfg.wm == 0 ? 1 : cfg.wm) * cfg.wt; }
 
-int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32) {
-    const int tb = dec_tb_bf16(D, Mp);
+// Resident decode workgroups per CU, from the kernel's occupancy at its LDS
+// size. Computed once per (D, tb, Z type, Mp) and cached: the query and the
+// attribute call cost more than a launch.
+int dec_wgs_per_cu_bf16(int D, int Mp, int tb, bool z_f32) {
+    const int di = D == 32 ? 0 : D == 64 ? 1 : D == 128 ? 2 : -1;
+    if (di < 0 || tb < 1 || tb > 2 || Mp < 32 || Mp > kBf16MaxM || Mp % 32) return 1;
+    static std::atomic<int> cache[3][2][2][kBf16MaxM / 32];
+    std::atomic<int>& slot = cache[di][tb - 1][z_f32 ? 1 : 0][Mp / 32 - 1];
+    const int known = slot.load(std::memory_order_relaxed);
+    if (known > 0) return known;
     const int lds = dec_lds_bytes_bf16(Mp, D);
     const void* fn = nullptr;
 #define FLARE_DEC_FN(DD, TB)                                                                          \
@@ -1280,24 +1305,17 @@ int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32) {
     FLARE_DEC_FN(128, 1)
 #undef FLARE_DEC_FN
     if (!fn) return 1;
-    if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-        return 1;
+    if (lds > 65536 && allow_dec_lds(fn) != hipSuccess) return 1;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * kDecWaves, lds) != hipSuccess || n < 1) return 1;
+    slot.store(n, std::memory_order_relaxed);
     return n;
 }
 
-int dec_tb_bf16(int D, int Mp) {
-    // Tuning override (tests and sweeps): 32-token blocks per wave and step
-    // (2 is built for D <= 64 and M <= 256 only).
-    if (const char* e = std::getenv("FLARE_TEST_DEC_TB")) {
-        const int v = std::atoi(e);
-        if (v == 1 || (v == 2 && D <= 64 && Mp <= 256)) return v;
-    }
-    // one block: fewer registers, more resident waves (measured faster on
-    // MI355X than two at D = 32, equal or faster at D = 64)
-    return 1;
-}
+// One block: fewer registers, more resident waves (measured faster on MI355X
+// than two at D = 32, equal or faster at D = 64).
+int dec_tb_bf16(int, int) { return 1; }
+bool dec_tb_built_bf16(int D, int Mp, int tb) { return tb == 1 || (tb == 2 && D <= 64 && Mp <= 256); }
 
 int dec_lds_bytes_bf16(int Mp, int D) { return Mp * 2 * D + D * (2 * Mp + 16) + 64; }
 

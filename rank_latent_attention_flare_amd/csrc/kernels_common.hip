@@ -275,14 +275,14 @@ template <int D>
 hipError_t enc_f32(const EncodeArgs& a, hipStream_t s) {
     const int nth = enc_threads_f32(a.M);
     dim3 grid(a.C, a.BH, (a.M + nth - 1) / nth), block(nth);
-    hipLaunchKernelGGL((encode_partial_f32<D>), grid, block, 0, s, a);
+    FLARE_LAUNCH((encode_partial_f32<D>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t dec_f32(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((a.N + 255) / 256, a.BH), block(256);
-    hipLaunchKernelGGL((decode_f32<D>), grid, block, 0, s, a);
+    FLARE_LAUNCH((decode_f32<D>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -312,9 +312,9 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     dim3 grid((a.M * (a.D / 4) + 255) / 256, a.BH), block(256);
     // groups of 8 chunks when that covers them all (fewer registers), else 16
     if (a.C <= 8)
-        hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, a);
+        FLARE_LAUNCH(combine_kernel<8>, grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, s, a);
+        FLARE_LAUNCH(combine_kernel<16>, grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -322,26 +322,26 @@ hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s) {
     if (bytes % 16 != 0) return hipErrorInvalidValue;
     const size_t n16 = bytes / 16;
     if (n16 == 0) return hipSuccess;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(elementwise_blocks((int64_t)n16)), dim3(256), 0, s, (u32x4*)dst, n16);
+    FLARE_LAUNCH(fill_zero_kernel, dim3(elementwise_blocks((int64_t)n16)), dim3(256), 0, s, (u32x4*)dst, n16);
     return hipGetLastError();
 }
 
 hipError_t launch_widen(const void* src, float* dst, int64_t n, bool bf16, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     if (bf16)
-        hipLaunchKernelGGL(widen_kernel<uint16_t>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (const uint16_t*)src, dst, n);
+        FLARE_LAUNCH(widen_kernel<uint16_t>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (const uint16_t*)src, dst, n);
     else
-        hipLaunchKernelGGL(widen_kernel<float>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (const float*)src, dst, n);
+        FLARE_LAUNCH(widen_kernel<float>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (const float*)src, dst, n);
     return hipGetLastError();
 }
 
 hipError_t launch_batch_sum(void* dst, const void* base, const void* add, int B, int64_t n, bool bf16, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     if (bf16)
-        hipLaunchKernelGGL(batch_sum_kernel<uint16_t>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (uint16_t*)dst,
+        FLARE_LAUNCH(batch_sum_kernel<uint16_t>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (uint16_t*)dst,
                            (const uint16_t*)base, (const uint16_t*)add, B, n);
     else
-        hipLaunchKernelGGL(batch_sum_kernel<float>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (float*)dst,
+        FLARE_LAUNCH(batch_sum_kernel<float>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (float*)dst,
                            (const float*)base, (const float*)add, B, n);
     return hipGetLastError();
 }
@@ -351,7 +351,7 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) 
     if (n16 == 0) return hipSuccess;
     size_t blocks = (n16 + 255) / 256;
     if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4*)src, (u32x4*)dst, n16);
+    FLARE_LAUNCH(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4*)src, (u32x4*)dst, n16);
     return hipGetLastError();
 }
 

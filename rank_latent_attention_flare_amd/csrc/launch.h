@@ -8,6 +8,38 @@
 
 namespace flare {
 
+// Every kernel launch of the library goes through launch_raw (flare.cpp):
+// hipLaunchKernel, or, while kernel timing is on (flare_timing_enable),
+// hipExtLaunchKernel with a HIP event pair bound to the dispatch itself, so
+// that the events carry the kernel's own start and end times.
+hipError_t launch_raw(const void* fn, dim3 grid, dim3 block, void** args, size_t shm, hipStream_t s);
+
+template <class T>
+struct ident {
+    using type = T;
+};
+// Typed front end: the arguments are converted to the kernel's parameter
+// types before their addresses are handed to the runtime.
+template <typename... P>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t shm, hipStream_t s,
+                  typename ident<P>::type... args) {
+    void* ptrs[] = {(void*)&args..., nullptr};
+    return launch_raw((const void*)kernel, grid, block, ptrs, shm, s);
+}
+// In a function returning hipError_t: launch, and return the error if any.
+#define FLARE_LAUNCH(...)                                  \
+    do {                                                   \
+        const hipError_t flare_e_ = ::flare::launch(__VA_ARGS__); \
+        if (flare_e_ != hipSuccess) return flare_e_;       \
+    } while (0)
+
+// Encode configuration for bf16. wm > 0: shared-tile form with wm waves over
+// latent blocks (mbw blocks each) x wt waves over tokens. wm == 0: private-
+// stream form, wt waves that each own all mbw latent blocks.
+struct EncCfg {
+    int mbw, wm, wt;
+};
+
 // Where the split-N encode writes its per-chunk online-softmax state.
 struct Partials {
     float* acc;  // [BH][C][Mp][D] unnormalised sums of p * V
@@ -25,6 +57,7 @@ struct EncodeArgs {
     int C, chunk_len;    // chunks per (b, h) and tokens per chunk
     float c;             // (1/sqrt(D)) * log2(e)
     Partials out;
+    EncCfg cfg;          // bf16: the workgroup shape (from the plan)
 };
 
 // What the combine writes.
@@ -83,16 +116,11 @@ struct DecodeArgs {
     int64_t sb, sh, sn;  // K and Y strides in elements: batch, head, token
     int BH, H, N, M, Mp, D;
     int G;               // workgroups per (b, h)
+    int tb;              // bf16: 32-token blocks per wave and step (1 or 2)
     float c;
 };
 
-// Encode configuration for bf16. wm > 0: shared-tile form with wm waves over
-// latent blocks (mbw blocks each) x wt waves over tokens. wm == 0: private-
-// stream form, wt waves that each own all mbw latent blocks.
-struct EncCfg {
-    int mbw, wm, wt;
-};
-EncCfg enc_cfg_bf16(int D, int Mb);
+EncCfg enc_cfg_bf16(int D, int Mb);  // the library's choice for Mb latent blocks
 int enc_tile_tokens_bf16(EncCfg cfg);
 int enc_threads_bf16(EncCfg cfg);
 
@@ -101,8 +129,9 @@ constexpr int kDecWaves = 4;  // waves per decode workgroup
 // D = 128 the decode's LDS (Q and Z^T of the head) caps M at 256.
 constexpr int kBf16MaxM = 512;
 constexpr int kBf16MaxM128 = 256;
-int dec_tb_bf16(int D, int Mp);  // 32-token blocks per wave per step
-int dec_wgs_per_cu_bf16(int D, int Mp, bool z_f32);  // resident decode workgroups per CU
+int dec_tb_bf16(int D, int Mp);  // 32-token blocks per wave per step (the library's choice)
+bool dec_tb_built_bf16(int D, int Mp, int tb);  // whether a decode with tb blocks is built for (D, Mp)
+int dec_wgs_per_cu_bf16(int D, int Mp, int tb, bool z_f32);  // resident decode workgroups per CU (cached)
 int dec_lds_bytes_bf16(int Mp, int D);
 
 hipError_t launch_encode_bf16(const EncodeArgs& a, hipStream_t s);

@@ -18,7 +18,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflare.so
 FLARE_F32, FLARE_BF16 = 0, 1
 FLARE_OP_ENCODE, FLARE_OP_DECODE, FLARE_OP_FORWARD, FLARE_OP_PP_FORWARD, FLARE_OP_BACKWARD = 0, 1, 2, 3, 4
 FLARE_OP_PP_BACKWARD = 5
+FLARE_OP_PP_QUERIES = 6
 FLARE_LAYOUT_BHND, FLARE_LAYOUT_BNHD = 0, 1
+FLARE_TUNE_CHUNKS, FLARE_TUNE_ENC_MBW, FLARE_TUNE_ENC_WM, FLARE_TUNE_ENC_WT = 0, 1, 2, 3
+FLARE_TUNE_DEC_TB, FLARE_TUNE_DEC_GROUPS, FLARE_TUNE_FAIL_ALLOC = 4, 5, 6
 FLARE_KERNEL_KINDS = 4
 KERNEL_KIND_NAMES = ("encode_partial", "combine", "decode", "backward")
 
@@ -37,6 +40,7 @@ _lib = None
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
 _ENTRY = ["flare_encode", "flare_decode", "flare_forward", "flare_pp_forward"]
+_ENTRY_WS = _ENTRY + ["flare_pp_queries"]  # entry points with a *_ws variant
 
 
 def lib() -> ctypes.CDLL:
@@ -47,11 +51,12 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"{LIB_PATH} is not built; run `python -m rank_latent_attention_flare_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         base = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
-        for name in _ENTRY:
+        for name in _ENTRY_WS:
             getattr(L, name).argtypes = base
             getattr(L, name).restype = ctypes.c_int
             getattr(L, name + "_ws").argtypes = base + [_vp, ctypes.c_size_t]
             getattr(L, name + "_ws").restype = ctypes.c_int
+        for name in _ENTRY:
             getattr(L, name + "_ex").argtypes = base[:10] + [ctypes.c_int, _vp, _vp, ctypes.c_size_t]
             getattr(L, name + "_ex").restype = ctypes.c_int
         bw = [_vp] * 7 + [_i64] * 5 + [ctypes.c_int, _vp]
@@ -71,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.flare_status_string.restype = ctypes.c_char_p
         L.flare_last_error.argtypes = []
         L.flare_last_error.restype = ctypes.c_char_p
+        L.flare_set_tuning.argtypes = [ctypes.c_int, _i64]
+        L.flare_set_tuning.restype = ctypes.c_int
         L.flare_timing_enable.argtypes = [ctypes.c_int]
         L.flare_timing_enable.restype = ctypes.c_int
         L.flare_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]
@@ -120,7 +127,7 @@ def _dims(op: int, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor):
 
 
 def _out(op, B, H, N, M, D, like: torch.Tensor, out: Optional[torch.Tensor]) -> torch.Tensor:
-    shape = (B, H, M, D) if op == FLARE_OP_ENCODE else (B, H, N, D)
+    shape = (B, H, M, D) if op in (FLARE_OP_ENCODE, FLARE_OP_PP_QUERIES) else (B, H, N, D)
     if out is None:
         return torch.empty(shape, dtype=like.dtype, device=like.device)
     if tuple(out.shape) != shape or out.dtype != like.dtype or not out.is_contiguous() or not out.is_cuda:
@@ -159,6 +166,11 @@ def flare_forward(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tenso
 def flare_pp_forward(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tensor:
     """Y [B, H, N, D] = FLARE++(Q, K, V)."""
     return _call(FLARE_OP_PP_FORWARD, "flare_pp_forward", Q, K, V, out, stream, workspace)
+
+
+def flare_pp_queries(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Q' [B, H, M, D] = Q + encode(Q, K, V) in the operator dtype: the corrected queries FLARE++ uses."""
+    return _call(FLARE_OP_PP_QUERIES, "flare_pp_queries", Q, K, V, out, stream, workspace)
 
 
 def _call_ex(op: int, name: str, Q, K, V, layout: int, out, stream, workspace):
@@ -286,6 +298,11 @@ def flare_describe_plan(op: int, B: int, H: int, N: int, M: int, D: int, dtype: 
     buf = ctypes.create_string_buffer(512)
     _raise(lib().flare_describe_plan(op, B, H, N, M, D, dtype_code(dtype), buf, 512))
     return buf.value.decode()
+
+
+def flare_set_tuning(key: int, value: int) -> None:
+    """Process-wide launch-plan override (FLARE_TUNE_*); 0 restores the library's choice."""
+    _raise(lib().flare_set_tuning(int(key), int(value)))
 
 
 def flare_timing_enable(on: bool) -> None:

@@ -49,7 +49,8 @@ def fwd_args(q=PQ, k=PK, v=PV, y=PY, B=1, H=2, N=100, M=64, D=64, dt=F.FLARE_BF1
     return (q, k, v, y, B, H, N, M, D, dt)
 
 
-@pytest.mark.parametrize("name", ["flare_encode", "flare_decode", "flare_forward", "flare_pp_forward"])
+@pytest.mark.parametrize("name", ["flare_encode", "flare_decode", "flare_forward", "flare_pp_forward",
+                                  "flare_pp_queries"])
 def test_null_pointers_rejected(name):
     for i in range(4):
         a = list(fwd_args())
@@ -112,10 +113,34 @@ def test_workspace_checks():
     assert call("flare_forward", *fwd_args(), ws=(PW + 16, need)) == INVALID
 
 
-def test_injected_allocation_failure(monkeypatch):
-    monkeypatch.setenv("FLARE_TEST_FAIL_ALLOC", "1")
-    assert call("flare_forward", *fwd_args()) == NOMEM
-    monkeypatch.delenv("FLARE_TEST_FAIL_ALLOC")
+def test_injected_allocation_failure():
+    F.flare_set_tuning(F.FLARE_TUNE_FAIL_ALLOC, 1)
+    try:
+        assert call("flare_forward", *fwd_args()) == NOMEM
+        assert call("flare_pp_queries", *fwd_args()) == NOMEM
+        assert "injected" in F.lib().flare_last_error().decode()
+    finally:
+        F.flare_set_tuning(F.FLARE_TUNE_FAIL_ALLOC, 0)
+
+
+def test_tuning_keys_validated():
+    L = F.lib()
+    assert L.flare_set_tuning(F.FLARE_TUNE_CHUNKS, -1) == INVALID
+    assert L.flare_set_tuning(99, 1) == INVALID
+    assert L.flare_set_tuning(-1, 1) == INVALID
+    # an override changes the plan, and 0 restores the library's own
+    buf = ctypes.create_string_buffer(512)
+    args = (F.FLARE_OP_FORWARD, 4, 8, 65536, 128, 32, F.FLARE_BF16, buf, 512)
+    assert L.flare_describe_plan(*args) == OK
+    default = buf.value.decode()
+    F.flare_set_tuning(F.FLARE_TUNE_CHUNKS, 3)
+    try:
+        assert L.flare_describe_plan(*args) == OK
+        assert "encode grid (3,32)" in buf.value.decode()
+    finally:
+        F.flare_set_tuning(F.FLARE_TUNE_CHUNKS, 0)
+    assert L.flare_describe_plan(*args) == OK
+    assert buf.value.decode() == default
 
 
 def test_status_strings_and_plan():

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from flare_inputs import WORKLOADS, make_inputs, workload_inputs
+from flare_inputs import WORKLOADS, f32_to_bf16_bits, make_inputs, workload_inputs
 from rank_latent_attention_flare_amd import flare as F
 from tests.gpu_util import errors, to_dev, to_host64
 
@@ -87,6 +87,9 @@ SHARP = [
     # q_scale 8 waves of both kinds occur
     (1, 2, 2000, 64, 32, 12.0, 2.0),
     (1, 1, 3000, 100, 64, 8.0, 2.0),
+    # D = 64 with M <= 64 (the statistics kernel forms the dZ partials itself)
+    # and padded latents (M = 50 of 64)
+    (1, 2, 2000, 50, 64, 8.0, 2.0),
 ]
 
 
@@ -100,6 +103,44 @@ def test_backward_sharp_logits(case):
     got = F.flare_backward(to_dev(Q), to_dev(K), to_dev(V), to_dev(dY))
     torch.cuda.synchronize()
     check(got, oracle.backward(Q, K, V, dY), "bf16", f"sharp {case}")
+
+
+@pytest.mark.parametrize("D,M", [(32, 50), (64, 50), (64, 100)])
+def test_backward_negative_logits(D, M):
+    # Every logit near -200 in log2 units (a common component of Q and K
+    # pointing in opposite directions), with padded latents: the exponentials
+    # against the encode's offsets underflow unless every kernel takes its
+    # offsets from the statistics of this head; (64, 50) runs the fused dZ
+    # path, (64, 100) the separate latent pass.
+    rng = np.random.default_rng(1000 + D + M)
+    B, H, N = 1, 2, 1500
+    q = 0.3 * rng.standard_normal((H, M, D), dtype=np.float32)
+    k = 0.3 * rng.standard_normal((B, H, N, D), dtype=np.float32)
+    v = rng.standard_normal((B, H, N, D), dtype=np.float32)
+    g = rng.standard_normal((B, H, N, D), dtype=np.float32)
+    q[..., 0] -= 33.0
+    k[..., 0] += 33.0
+    Q, K, V, dY = (f32_to_bf16_bits(x) for x in (q, k, v, g))
+    print(f"[backward] negative logits D={D} M={M}", flush=True)
+    got = F.flare_backward(to_dev(Q), to_dev(K), to_dev(V), to_dev(dY))
+    torch.cuda.synchronize()
+    want = oracle.backward(Q, K, V, dY)
+    for g, w, name in zip(got, want, ("dQ", "dK", "dV")):
+        print(f"[backward] negative D={D} M={M} {name} {errors(to_host64(g), w)}", flush=True)
+    check_one(got[1], want[1], "bf16", f"negative D={D} M={M} dK")
+    check_one(got[2], want[2], "bf16", f"negative D={D} M={M} dV")
+    # dQ = s dl K. Along d = 0, the direction every key shares (K[n][0] near
+    # 33), the entries are sums whose terms cancel: the encode part of each
+    # row of dl sums to zero exactly, and on this input sum_n |dl[m][n]| is
+    # 100-400 times |sum_n dl[m][n]|. One bf16 rounding of each dl term
+    # (relative 2^-9, the matrix-core operand) then leaves an error up to
+    # s 2^-9 sum_n |dl[m][n]| |K[n][0]| (0.2-0.7 on these inputs, measured
+    # 0.02-0.17), which no element bar on that column can hold. The other
+    # columns carry no shared component and meet the bar; column 0 must be
+    # finite.
+    dq = to_host64(got[0])
+    assert np.isfinite(dq).all()
+    check_one(got[0][..., 1:], want[0][..., 1:], "bf16", f"negative D={D} M={M} dQ[..., 1:]")
 
 
 def test_backward_workspace_variant_is_identical():
