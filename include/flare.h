@@ -128,6 +128,22 @@ flare_status flare_pp_queries_ws(const void* Q, const void* K, const void* V, vo
                                  int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
                                  flare_dtype dtype, hipStream_t stream, void* workspace, size_t ws_bytes);
 
+/* FLARE forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and result as flare_forward (bit for bit), but the
+ * workspace is a static device array of FLARE_STATIC_SCRATCH_BYTES inside the
+ * library, one per GPU, held from the library's load until the process ends;
+ * nothing is allocated. Sizes whose forward workspace
+ * (flare_workspace_size(FLARE_OP_FORWARD, ...)) exceeds it return
+ * FLARE_ERR_UNSUPPORTED before anything is enqueued. Every call on one GPU
+ * uses that GPU's one array: calls that overlap in time on a GPU (other
+ * streams, other threads) race and must be serialised by the caller; calls
+ * in order on one stream are safe. */
+#define FLARE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+flare_status flare_forward_noalloc(const void* Q, const void* K, const void* V, void* Y,
+                                   int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                   flare_dtype dtype, hipStream_t stream);
+
 /* Scratch bytes the *_ws variant of `op` needs for these sizes (0 when the
  * sizes or type are invalid or unsupported). */
 size_t flare_workspace_size(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,

@@ -453,6 +453,40 @@ PPLayout pp_layout(const Plan& pf, const Plan& p1) {
 
 }  // namespace
 
+namespace {
+
+// Scratch memory of flare_forward_noalloc: a static device array, one copy per
+// GPU (the code object's), held until the process ends. Host code never uses
+// its name as an address: the device address comes from hipGetSymbolAddress,
+// once per device, and is kept per device.
+constexpr size_t kStaticScratchBytes = FLARE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device, with that device current).
+flare_status static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(FLARE_ERR_UNSUPPORTED, "device index beyond the scratch table");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr || uintptr_t(ptr) % 256 != 0) return fail(FLARE_ERR_HIP, "static scratch has no aligned device address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FLARE_OK;
+}
+
+}  // namespace
+
 namespace flare {
 hipError_t launch_raw(const void* fn, dim3 grid, dim3 block, void** args, size_t shm, hipStream_t s) {
     if (!g_timing.on.load(std::memory_order_relaxed)) return hipLaunchKernel(fn, grid, block, args, shm, s);
@@ -517,6 +551,27 @@ flare_status flare_pp_forward_ws(const void* Q, const void* K, const void* V, vo
                                  int64_t N, int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream, void* ws,
                                  size_t n) {
     return exec(FLARE_OP_PP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, ws, n);
+}
+flare_status flare_forward_noalloc(const void* Q, const void* K, const void* V, void* Y, int64_t B, int64_t H,
+                                   int64_t N, int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {
+    // Sizes first (no device call), so that an oversized request launches
+    // nothing and reports the limit.
+    Plan p;
+    g_last_error.clear();
+    flare_status st = make_plan(B, H, N, M, D, dtype, &p);
+    if (st != FLARE_OK) return st;
+    const size_t need = p.total[FLARE_OP_FORWARD];
+    if (need > kStaticScratchBytes)
+        return fail(FLARE_ERR_UNSUPPORTED, "flare_forward_noalloc: workspace of " + std::to_string(need) +
+                                               " bytes exceeds the static scratch of " +
+                                               std::to_string(kStaticScratchBytes) + " bytes");
+    void* ws = nullptr;
+    st = static_scratch(&ws);
+    if (st != FLARE_OK) return st;
+    // The forward writes every workspace byte it later reads (partials, Z,
+    // offsets), so nothing needs clearing between calls.
+    return exec(FLARE_OP_FORWARD, Q, K, V, Y, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, ws,
+                kStaticScratchBytes);
 }
 flare_status flare_pp_queries(const void* Q, const void* K, const void* V, void* Qp, int64_t B, int64_t H,
                               int64_t N, int64_t M, int64_t D, flare_dtype dtype, hipStream_t stream) {

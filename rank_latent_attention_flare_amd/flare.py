@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.flare_pp_backward.restype = ctypes.c_int
         L.flare_pp_backward_ws.argtypes = bw + [_vp, ctypes.c_size_t]
         L.flare_pp_backward_ws.restype = ctypes.c_int
+        L.flare_forward_noalloc.argtypes = base
+        L.flare_forward_noalloc.restype = ctypes.c_int
         L.flare_attend.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
         L.flare_attend.restype = ctypes.c_int
         L.flare_workspace_size.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
@@ -166,6 +168,12 @@ def flare_forward(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tenso
 def flare_pp_forward(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tensor:
     """Y [B, H, N, D] = FLARE++(Q, K, V)."""
     return _call(FLARE_OP_PP_FORWARD, "flare_pp_forward", Q, K, V, out, stream, workspace)
+
+
+def flare_forward_noalloc(Q, K, V, out=None, stream=None) -> torch.Tensor:
+    """Y [B, H, N, D] = FLARE(Q, K, V) with the library's static scratch (no allocation in the library;
+    pass `out` to allocate nothing at all)."""
+    return _call(FLARE_OP_FORWARD, "flare_forward_noalloc", Q, K, V, out, stream, None)
 
 
 def flare_pp_queries(Q, K, V, out=None, stream=None, workspace=None) -> torch.Tensor:

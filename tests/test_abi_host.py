@@ -230,3 +230,15 @@ def test_pp_backward_validates_before_launch():
     assert ws >= F.lib().flare_workspace_size(F.FLARE_OP_BACKWARD, *args) + tok > 0
     assert F.lib().flare_pp_backward_ws(*ok, PW, 256) == INVALID
     assert "workspace" in F.lib().flare_last_error().decode()
+
+
+def test_noalloc_rejects_oversized_workspace():
+    # the forward workspace of (64, 16, 2^22, 512, 64) bf16 (262 MiB) exceeds
+    # the 64 MiB static scratch: rejected before any device call
+    L = F.lib()
+    need = L.flare_workspace_size(F.FLARE_OP_FORWARD, 64, 16, 1 << 22, 512, 64, F.FLARE_BF16)
+    assert need > (64 << 20)
+    args = (PQ, PK, PV, PY, 64, 16, 1 << 22, 512, 64, F.FLARE_BF16, None)
+    assert L.flare_forward_noalloc(*args) == UNSUPPORTED
+    assert "static scratch" in L.flare_last_error().decode()
+    assert L.flare_forward_noalloc(PQ, PK, PV, PY, 0, 1, 10, 10, 64, F.FLARE_BF16, None) == INVALID
