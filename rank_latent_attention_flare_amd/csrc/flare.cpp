@@ -315,7 +315,7 @@ int decode_groups(const Plan& p, bool z_f32) {
             cus = 256;
         cus_cache.store(cus, std::memory_order_relaxed);
     }
-    const int per_cu = flare::dec_wgs_per_cu_bf16(int(p.D), p.Mp, p.tb, z_f32);
+    const int per_cu = flare::dec_wgs_per_cu_bf16(int(p.D), int(p.M), p.tb, z_f32);
     const int64_t per_wg = 32 * p.tb * flare::kDecWaves;
     int64_t G = (int64_t(cus) * per_cu + p.BH - 1) / p.BH;
     G = std::max<int64_t>(1, std::min<int64_t>(G, (p.N + per_wg - 1) / per_wg));

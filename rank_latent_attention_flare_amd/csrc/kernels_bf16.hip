@@ -819,7 +819,9 @@ __device__ __forceinline__ int dec_zpos(int m) {
 
 // LONG: M > 256 (more than one group of 8 latent blocks; the group loop costs
 // registers, so the common M <= 256 kernel is built without it).
-template <int D, int TB, typename ZT, bool LONG>
+// MBC > 0: built for exactly M = 32 * MBC latents (no padded block), so that
+// the latent loop has no run-time bounds and its blocks schedule freely.
+template <int D, int TB, typename ZT, bool LONG, int MBC = 0>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(D == 32 && TB == 1 && !LONG ? 4 : 1)))
 void decode_bf16(DecodeArgs a) {
     constexpr int KB = D / 16, DB = D / 32, CH = D / 8, NW = kDecWaves;
@@ -842,6 +844,46 @@ void decode_bf16(DecodeArgs a) {
     const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + (int64_t)b * a.sb + (int64_t)h * a.sh;
     uint16_t* __restrict__ Yb = (uint16_t*)a.Y + (int64_t)b * a.sb + (int64_t)h * a.sh;
 
+    // K rows of one block as MFMA B operands. Rows past the end (the ragged
+    // last block, or a block past the wave's last) load the last token
+    // instead: every column of the logits belongs to one token, so they only
+    // feed outputs that are never stored, and the loads stay unconditional
+    // (a fixed number in flight, which the explicit waits below rely on).
+    // A lane's byte offset from its block's first token row is the same for
+    // every block (when T * sn * 2 bytes fit in 32 bits), so whole blocks are
+    // addressed from a uniform base in scalar registers.
+    const bool fixed_off = sn < (int64_t(1) << 24);
+    uint32_t roff[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) roff[tb] = fixed_off ? (uint32_t)((32 * tb + l32) * (int)sn + 8 * hi) * 2u : 0u;
+    auto kload = [&](int bk, bf16x8 (&dst)[TB][KB]) {
+        const int nb = bk * 32 * TB;
+        if (fixed_off && nb + 32 * TB <= N) {
+            const unsigned char* kg = (const unsigned char*)(Kb + (int64_t)nb * sn);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                uint32_t o = roff[tb];
+                asm volatile("" : "+v"(o));  // keeps the zero extension next to the loads
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) dst[tb][kb] = *(const bf16x8*)(kg + o + 32 * kb);
+            }
+            asm volatile("" ::: "memory");
+        } else {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int n = min(nb + 32 * tb + l32, N - 1);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    dst[tb][kb] = *(const bf16x8*)(Kb + (int64_t)n * sn + 16 * kb + 8 * hi);
+            }
+        }
+    };
+    // This wave's first K block is requested before the staging below, so
+    // that its latency overlaps the staging instead of following it.
+    int blk = blockIdx.x * NW + wave;
+    bf16x8 kA[TB][KB], kB[TB][KB];
+    kload(blk, kA);
+
     // ---- stage Q (bf16, swizzled rows) and Z^T (bf16, permuted latents)
     for (int p = tid; p < Mp * CH; p += 64 * NW) {
         const int m = p / CH, ch = p % CH;
@@ -849,16 +891,27 @@ void decode_bf16(DecodeArgs a) {
         if (m < M) v = *(const u32x4*)(Qb + (int64_t)m * D + ch * 8);
         *(u32x4*)(qs + tile_off<D>(m, ch)) = v;
     }
-    for (int e = tid; e < Mp * D; e += 64 * NW) {
-        const int m = e / D, d = e % D;
-        __bf16 z = (__bf16)0.0f;
+    // four consecutive columns of one latent per thread and step (one 16- or
+    // 8-byte load), written to four Z^T rows
+    for (int e = tid; e < Mp * (D / 4); e += 64 * NW) {
+        const int m = e / (D / 4), d = 4 * (e % (D / 4));
+        float z4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (m < M) {
-            if constexpr (sizeof(ZT) == 4)
-                z = (__bf16)(float)Zb[(int64_t)m * D + d];
-            else
-                z = __builtin_bit_cast(__bf16, (uint16_t)Zb[(int64_t)m * D + d]);
+            if constexpr (sizeof(ZT) == 4) {
+                const f32x4 v = *(const f32x4*)((const float*)Zb + (int64_t)m * D + d);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) z4[i] = v[i];
+            } else {
+                const u32x2 v = *(const u32x2*)((const uint16_t*)Zb + (int64_t)m * D + d);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    z4[2 * i] = __uint_as_float(v[i] << 16);
+                    z4[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+                }
+            }
         }
-        *(__bf16*)(zt + d * zs + 2 * dec_zpos(m)) = z;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(__bf16*)(zt + (d + i) * zs + 2 * dec_zpos(m)) = (__bf16)z4[i];
     }
     __syncthreads();
     // Offsets. With the encode's merged offsets mu*[m] (log2 units), every
@@ -898,40 +951,6 @@ void decode_bf16(DecodeArgs a) {
     const int nblk = (N + 32 * TB - 1) / (32 * TB);
     const int stride = gridDim.x * NW;
 
-    // K rows of one block as MFMA B operands. Rows past the end (the ragged
-    // last block, or a block past the wave's last) load the last token
-    // instead: every column of the logits belongs to one token, so they only
-    // feed outputs that are never stored, and the loads stay unconditional
-    // (a fixed number in flight, which the explicit waits below rely on).
-    // A lane's byte offset from its block's first token row is the same for
-    // every block (when T * sn * 2 bytes fit in 32 bits), so whole blocks are
-    // addressed from a uniform base in scalar registers.
-    const bool fixed_off = sn < (int64_t(1) << 24);
-    uint32_t roff[TB];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) roff[tb] = fixed_off ? (uint32_t)((32 * tb + l32) * (int)sn + 8 * hi) * 2u : 0u;
-    auto kload = [&](int bk, bf16x8 (&dst)[TB][KB]) {
-        const int nb = bk * 32 * TB;
-        if (fixed_off && nb + 32 * TB <= N) {
-            const unsigned char* kg = (const unsigned char*)(Kb + (int64_t)nb * sn);
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                uint32_t o = roff[tb];
-                asm volatile("" : "+v"(o));  // keeps the zero extension next to the loads
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) dst[tb][kb] = *(const bf16x8*)(kg + o + 32 * kb);
-            }
-            asm volatile("" ::: "memory");
-        } else {
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const int n = min(nb + 32 * tb + l32, N - 1);
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    dst[tb][kb] = *(const bf16x8*)(Kb + (int64_t)n * sn + 16 * kb + 8 * hi);
-            }
-        }
-    };
     auto qread = [&](int mb, bf16x8 (&qa)[KB]) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) qa[kb] = *(const bf16x8*)(qs + tile_off<D>(32 * mb + l32, 2 * kb + hi));
@@ -986,7 +1005,7 @@ void decode_bf16(DecodeArgs a) {
             };
             // Full latent blocks first (logits of block mb in SS[mb % 2]), then
             // the padded block when M % 32 != 0, with its own logits.
-            const int MBF = M >> 5;
+            const int MBF = MBC > 0 ? MBC : (M >> 5);
             bf16x8 qa[KB];
             f32x16 SS[2][TB];
 #pragma unroll
@@ -1047,7 +1066,7 @@ void decode_bf16(DecodeArgs a) {
                     }
                 }
             }
-            if (M & 31) {
+            if (MBC == 0 && (M & 31)) {
                 qread(MBF, qa);
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
@@ -1145,9 +1164,6 @@ void decode_bf16(DecodeArgs a) {
     // needs is ever behind a transfer issued in the same step. (A wait on a
     // register set alone would also wait for the later loads and the stores:
     // the counter is shared and the compiler takes the conservative count.)
-    int blk = blockIdx.x * NW + wave;
-    bf16x8 kA[TB][KB], kB[TB][KB];
-    kload(blk, kA);
     while (blk < nblk) {
         wait_vmcnt<0>();
         asm volatile("" ::: "memory");
@@ -1218,9 +1234,19 @@ hipError_t launch_enc_d(const EncodeArgs& a, hipStream_t s) {
 }
 
 template <int D, int TB, typename ZT>
-const void* dec_kernel(int Mp) {
+const void* dec_kernel(int M) {
+    const int Mp = (M + 31) / 32 * 32;
     if constexpr (D <= 64 && TB == 1) {
         if (Mp > 256) return (const void*)decode_bf16<D, TB, ZT, true>;
+        if (M == Mp) {
+            switch (M / 32) {
+                case 1: return (const void*)decode_bf16<D, TB, ZT, false, 1>;
+                case 2: return (const void*)decode_bf16<D, TB, ZT, false, 2>;
+                case 4: return (const void*)decode_bf16<D, TB, ZT, false, 4>;
+                case 8: return (const void*)decode_bf16<D, TB, ZT, false, 8>;
+                default: break;
+            }
+        }
     }
     return (const void*)decode_bf16<D, TB, ZT, false>;
 }
@@ -1250,7 +1276,7 @@ hipError_t allow_dec_lds(const void* fn) {
 template <int D, int TB, typename ZT>
 hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
     const int lds = dec_lds_bytes_bf16(a.Mp, D);
-    const void* fn = dec_kernel<D, TB, ZT>(a.Mp);
+    const void* fn = dec_kernel<D, TB, ZT>(a.M);
     if (lds > 65536) {
         hipError_t e = allow_dec_lds(fn);
         if (e != hipSuccess) return e;
@@ -1287,17 +1313,18 @@ int enc_threads_bf16(EncCfg cfg) { return 64 * (cfg.wm == 0 ? 1 : cfg.wm) * cfg.
 // Resident decode workgroups per CU, from the kernel's occupancy at its LDS
 // size. Computed once per (D, tb, Z type, Mp) and cached: the query and the
 // attribute call cost more than a launch.
-int dec_wgs_per_cu_bf16(int D, int Mp, int tb, bool z_f32) {
+int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32) {
     const int di = D == 32 ? 0 : D == 64 ? 1 : D == 128 ? 2 : -1;
-    if (di < 0 || tb < 1 || tb > 2 || Mp < 32 || Mp > kBf16MaxM || Mp % 32) return 1;
-    static std::atomic<int> cache[3][2][2][kBf16MaxM / 32];
-    std::atomic<int>& slot = cache[di][tb - 1][z_f32 ? 1 : 0][Mp / 32 - 1];
+    const int Mp = (M + 31) / 32 * 32;
+    if (di < 0 || tb < 1 || tb > 2 || M < 1 || Mp > kBf16MaxM) return 1;
+    static std::atomic<int> cache[3][2][2][kBf16MaxM / 32][2];
+    std::atomic<int>& slot = cache[di][tb - 1][z_f32 ? 1 : 0][Mp / 32 - 1][M == Mp ? 1 : 0];
     const int known = slot.load(std::memory_order_relaxed);
     if (known > 0) return known;
     const int lds = dec_lds_bytes_bf16(Mp, D);
     const void* fn = nullptr;
 #define FLARE_DEC_FN(DD, TB)                                                                          \
-    if (D == DD && tb == TB) fn = z_f32 ? dec_kernel<DD, TB, float>(Mp) : dec_kernel<DD, TB, uint16_t>(Mp);
+    if (D == DD && tb == TB) fn = z_f32 ? dec_kernel<DD, TB, float>(M) : dec_kernel<DD, TB, uint16_t>(M);
     FLARE_DEC_FN(32, 1)
     FLARE_DEC_FN(32, 2)
     FLARE_DEC_FN(64, 1)

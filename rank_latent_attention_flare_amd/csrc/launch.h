@@ -131,7 +131,7 @@ constexpr int kBf16MaxM = 512;
 constexpr int kBf16MaxM128 = 256;
 int dec_tb_bf16(int D, int Mp);  // 32-token blocks per wave per step (the library's choice)
 bool dec_tb_built_bf16(int D, int Mp, int tb);  // whether a decode with tb blocks is built for (D, Mp)
-int dec_wgs_per_cu_bf16(int D, int Mp, int tb, bool z_f32);  // resident decode workgroups per CU (cached)
+int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32);  // resident decode workgroups per CU (cached)
 int dec_lds_bytes_bf16(int Mp, int D);
 
 hipError_t launch_encode_bf16(const EncodeArgs& a, hipStream_t s);
