@@ -165,7 +165,7 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     p->C = int(C);
     p->chunk_len = int(chunk);
     // decode workgroups per (b, h)
-    const int64_t per_wg = 32 * p->tb * flare::kDecWaves;
+    const int64_t per_wg = 32 * p->tb * (dt == FLARE_BF16 ? flare::dec_waves_bf16(int(D), int(M), p->tb) : flare::kDecWaves);
     int64_t G = std::max<int64_t>(1, (kTargetDecWgs + p->BH - 1) / p->BH);
     G = std::min<int64_t>(G, (N + per_wg - 1) / per_wg);
     p->G = int(G);
@@ -316,7 +316,7 @@ int decode_groups(const Plan& p, bool z_f32) {
         cus_cache.store(cus, std::memory_order_relaxed);
     }
     const int per_cu = flare::dec_wgs_per_cu_bf16(int(p.D), int(p.M), p.tb, z_f32);
-    const int64_t per_wg = 32 * p.tb * flare::kDecWaves;
+    const int64_t per_wg = 32 * p.tb * flare::dec_waves_bf16(int(p.D), int(p.M), p.tb);
     int64_t G = (int64_t(cus) * per_cu + p.BH - 1) / p.BH;
     G = std::max<int64_t>(1, std::min<int64_t>(G, (p.N + per_wg - 1) / per_wg));
     return int(G);

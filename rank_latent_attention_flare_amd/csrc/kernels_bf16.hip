@@ -790,7 +790,7 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
 // ---------------------------------------------------------------------------
 // K3: decode.
 //
-// Workgroup = kDecWaves waves for one (b, h); Q[h] (or Q'[b,h]) and Z[b,h] are
+// Workgroup = NW waves for one (b, h); Q[h] (or Q'[b,h]) and Z[b,h] are
 // staged once into LDS as bf16 (Z rounded to nearest-even from fp32 when it
 // comes from the fused forward). Each wave then owns blocks of 32*TB tokens:
 // it loads their K rows straight into MFMA B operands (next block in flight),
@@ -821,10 +821,18 @@ __device__ __forceinline__ int dec_zpos(int m) {
 // registers, so the common M <= 256 kernel is built without it).
 // MBC > 0: built for exactly M = 32 * MBC latents (no padded block), so that
 // the latent loop has no run-time bounds and its blocks schedule freely.
-template <int D, int TB, typename ZT, bool LONG, int MBC = 0>
-__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(D == 32 && TB == 1 && !LONG ? 4 : 1)))
+// NW: waves per workgroup, all sharing the workgroup's one LDS copy of Q and
+// Z^T. Where that copy is large (D = 64 with M >= 256) more waves per
+// workgroup give more resident waves per SIMD than more workgroups could.
+// Resident waves per SIMD the register budget is built for.
+constexpr int dec_waves_per_simd(int D, int TB, bool LONG, int NW) {
+    return (D == 32 && TB == 1 && !LONG) ? 4 : (NW == 12 ? 3 : (NW == 8 ? 2 : 1));
+}
+template <int D, int TB, typename ZT, bool LONG, int MBC = 0, int NW = kDecWaves>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(dec_waves_per_simd(D, TB, LONG, NW))))
 void decode_bf16(DecodeArgs a) {
-    constexpr int KB = D / 16, DB = D / 32, CH = D / 8, NW = kDecWaves;
+    constexpr int KB = D / 16, DB = D / 32, CH = D / 8;
+    static_assert(NW >= 1 && NW <= 16, "reduction scratch holds 16 waves");
     const int Mp = a.Mp, MB = Mp / 32;
     const int zs = 2 * Mp + 16;  // bytes per Z^T row (padded)
     extern __shared__ __attribute__((aligned(16))) unsigned char dsm[];
@@ -1237,7 +1245,15 @@ template <int D, int TB, typename ZT>
 const void* dec_kernel(int M) {
     const int Mp = (M + 31) / 32 * 32;
     if constexpr (D <= 64 && TB == 1) {
-        if (Mp > 256) return (const void*)decode_bf16<D, TB, ZT, true>;
+        if (Mp > 256) {
+            if constexpr (D == 64)
+                return (const void*)decode_bf16<D, TB, ZT, true, 0, 8>;
+            else
+                return (const void*)decode_bf16<D, TB, ZT, true>;
+        }
+        if constexpr (D == 64) {
+            if (M == 256) return (const void*)decode_bf16<D, TB, ZT, false, 8, 12>;
+        }
         if (M == Mp) {
             switch (M / 32) {
                 case 1: return (const void*)decode_bf16<D, TB, ZT, false, 1>;
@@ -1283,7 +1299,7 @@ hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
     }
     DecodeArgs arg = a;
     void* args[] = {&arg};
-    return launch_raw(fn, dim3(a.G, a.BH), dim3(64 * kDecWaves), args, lds, s);
+    return launch_raw(fn, dim3(a.G, a.BH), dim3(64 * dec_waves_bf16(D, a.M, TB)), args, lds, s);
 }
 
 template <int D, typename ZT>
@@ -1334,7 +1350,9 @@ int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32) {
     if (!fn) return 1;
     if (lds > 65536 && allow_dec_lds(fn) != hipSuccess) return 1;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * kDecWaves, lds) != hipSuccess || n < 1) return 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * dec_waves_bf16(D, M, tb), lds) != hipSuccess ||
+        n < 1)
+        return 1;
     slot.store(n, std::memory_order_relaxed);
     return n;
 }
@@ -1343,6 +1361,13 @@ int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32) {
 // than two at D = 32, equal or faster at D = 64).
 int dec_tb_bf16(int, int) { return 1; }
 bool dec_tb_built_bf16(int D, int Mp, int tb) { return tb == 1 || (tb == 2 && D <= 64 && Mp <= 256); }
+
+int dec_waves_bf16(int D, int M, int tb) {
+    const int Mp = (M + 31) / 32 * 32;
+    if (D != 64 || tb != 1) return kDecWaves;
+    if (Mp > 256) return 8;
+    return M == 256 ? 12 : kDecWaves;
+}
 
 int dec_lds_bytes_bf16(int Mp, int D) { return Mp * 2 * D + D * (2 * Mp + 16) + 64; }
 

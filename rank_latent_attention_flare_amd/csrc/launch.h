@@ -124,7 +124,7 @@ EncCfg enc_cfg_bf16(int D, int Mb);  // the library's choice for Mb latent block
 int enc_tile_tokens_bf16(EncCfg cfg);
 int enc_threads_bf16(EncCfg cfg);
 
-constexpr int kDecWaves = 4;  // waves per decode workgroup
+constexpr int kDecWaves = 4;  // waves per decode workgroup (fp32; bf16 default)
 // Largest M of the bf16 path: its decode unrolls every latent block. At
 // D = 128 the decode's LDS (Q and Z^T of the head) caps M at 256.
 constexpr int kBf16MaxM = 512;
@@ -133,6 +133,7 @@ int dec_tb_bf16(int D, int Mp);  // 32-token blocks per wave per step (the libra
 bool dec_tb_built_bf16(int D, int Mp, int tb);  // whether a decode with tb blocks is built for (D, Mp)
 int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32);  // resident decode workgroups per CU (cached)
 int dec_lds_bytes_bf16(int Mp, int D);
+int dec_waves_bf16(int D, int M, int tb);  // waves per bf16 decode workgroup
 
 hipError_t launch_encode_bf16(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);

@@ -49,6 +49,10 @@ SMALL = [
     (1, 2, 1500, 300, 64, "bf16"),
     (1, 1, 1000, 512, 32, "bf16"),
     (2, 1, 700, 480, 64, "bf16"),
+    # D = 64 with exactly 256 latents (twelve-wave decode workgroups) and with
+    # 512 (eight-wave workgroups), ragged tokens
+    (1, 2, 3001, 256, 64, "bf16"),
+    (1, 1, 2500, 512, 64, "bf16"),
 ]
 
 
