@@ -61,17 +61,23 @@
 extern "C" {
 #endif
 
-typedef enum { FLARE_F32 = 0, FLARE_BF16 = 1 } flare_dtype;
+/* The enumerated argument types below are fixed 32-bit integers with named
+ * values (not C enums), so that a caller passing a value outside the named
+ * ones gets FLARE_ERR_INVALID_ARG rather than undefined behaviour. */
+typedef int32_t flare_dtype;
+enum { FLARE_F32 = 0, FLARE_BF16 = 1 };
 
-typedef enum {
+typedef int32_t flare_status;
+enum {
     FLARE_OK = 0,
     FLARE_ERR_INVALID_ARG = 1, /* null pointer, size < 1, misaligned or aliased tensors, small workspace */
     FLARE_ERR_UNSUPPORTED = 2, /* (dtype, D, M) outside the supported set */
     FLARE_ERR_NO_MEMORY = 3,   /* scratch allocation failed */
     FLARE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
-} flare_status;
+};
 
-typedef enum {
+typedef int32_t flare_op;
+enum {
     FLARE_OP_ENCODE = 0,
     FLARE_OP_DECODE = 1,
     FLARE_OP_FORWARD = 2,
@@ -79,7 +85,7 @@ typedef enum {
     FLARE_OP_BACKWARD = 4,   /* flare_backward (workspace sizing only) */
     FLARE_OP_PP_BACKWARD = 5, /* flare_pp_backward (workspace sizing only) */
     FLARE_OP_PP_QUERIES = 6   /* flare_pp_queries */
-} flare_op;
+};
 
 /* Encode: Y := Z[B][H][M][D] = softmax_n(s Q K^T) V for every (b, h).
  * FLARE skill page, "2. Implement Encode Stage"; encode half of step 4.
@@ -173,7 +179,8 @@ flare_status flare_pp_forward_ws(const void* Q, const void* K, const void* V, vo
  *                      transpose the FLARE skill page applies after its
  *                      projections and undoes before its output projection
  *                      ("4. Combine Encode-Decode into Attention Layer"). */
-typedef enum { FLARE_LAYOUT_BHND = 0, FLARE_LAYOUT_BNHD = 1 } flare_layout;
+typedef int32_t flare_layout;
+enum { FLARE_LAYOUT_BHND = 0, FLARE_LAYOUT_BNHD = 1 };
 
 /* The four operations with a layout argument. workspace == NULL with
  * ws_bytes == 0 allocates scratch memory as the plain entry points do;
@@ -277,7 +284,8 @@ const char* flare_last_error(void);
  * computed: results differ at most by rounding. A value of 0 restores the
  * library's own choice; negative values and unknown keys return
  * FLARE_ERR_INVALID_ARG. Overrides apply to calls that start after the set. */
-typedef enum {
+typedef int32_t flare_tune;
+enum {
     FLARE_TUNE_CHUNKS = 0,      /* encode: token chunks per (b, h) (capped at N) */
     FLARE_TUNE_ENC_MBW = 1,     /* bf16 encode shape: latent blocks of 32 per wave, */
     FLARE_TUNE_ENC_WM = 2,      /*   waves over latent blocks (0: one wave owns them all), */
@@ -290,7 +298,7 @@ typedef enum {
     FLARE_TUNE_FAIL_ALLOC = 6,  /* 1: the allocating entry points fail with
                                  *   FLARE_ERR_NO_MEMORY (error-path tests) */
     FLARE_TUNE_KEYS = 7
-} flare_tune;
+};
 
 flare_status flare_set_tuning(flare_tune key, int64_t value);
 
