@@ -145,17 +145,19 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
         p->tb = 2;
         p->cfg = flare::EncCfg{0, 0, 0};
         p->Mp = int(M);
-        tile = 64;
+        tile = 32;  // chunk granularity (the kernel's 64-token tiles may be partial)
         const int nth = flare::enc_threads_f32(int(M));
         waves_per_wg = int((M + nth - 1) / nth) * (nth / 64);
     }
     // Split over N: enough workgroups to fill the chip, but chunks long enough
     // that the partials stay a few percent of the K/V bytes (bf16: 32*Mp
-    // tokens; fp32, whose lanes each run a whole latent: 4*Mp, at least one tile).
+    // tokens). fp32, whose lanes each run a whole latent through every token
+    // of their chunk in one serial chain, takes chunks down to 32 tokens: its
+    // time is that chain, and its partials are no burden at the sizes it
+    // serves.
     const int64_t target_wgs = std::max<int64_t>(1, kTargetEncWaves / waves_per_wg);
     int64_t C = std::max<int64_t>(1, (target_wgs + p->BH - 1) / p->BH);
-    const int64_t min_chunk =
-        dt == FLARE_BF16 ? 32 * int64_t(std::min(p->Mp, 256)) : std::max<int64_t>(tile, 4 * int64_t(p->Mp));
+    const int64_t min_chunk = dt == FLARE_BF16 ? 32 * int64_t(std::min(p->Mp, 256)) : 32;
     const int64_t cmax = std::max<int64_t>(1, N / min_chunk);
     C = std::min(C, cmax);
     if (tune(FLARE_TUNE_CHUNKS) > 0) C = std::min<int64_t>(tune(FLARE_TUNE_CHUNKS), N);

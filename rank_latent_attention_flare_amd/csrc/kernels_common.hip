@@ -44,6 +44,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 typedef float f32x4c __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ void combine_store(const CombineArgs& a, int bh, int m, int d, float mx, float den,
+                                              const f32x4c& z);
+
 template <int G>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int bh = blockIdx.y;
@@ -93,6 +96,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     f32x4c z;
 #pragma unroll
     for (int e = 0; e < 4; ++e) z[e] = num[e] / den;
+    combine_store(a, bh, m, d, mx, den, z);
+}
+
+// The combine's outputs for one entry: merged offset and sum (optional), then
+// Z in fp32 or the operator dtype, or Q' = Q + Z.
+__device__ __forceinline__ void combine_store(const CombineArgs& a, int bh, int m, int d, float mx, float den,
+                                              const f32x4c& z) {
+    const int D = a.D;
     const int64_t o = (int64_t)bh * a.M * D + (int64_t)m * D + d;
     if (a.zmu && d == 0) a.zmu[(int64_t)bh * a.M + m] = mx;
     if (a.zsig && d == 0) a.zsig[(int64_t)bh * a.M + m] = den;
@@ -122,13 +133,74 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 // ---------------------------------------------------------------------------
 // fp32 encode partials: grid (C, BH, latent groups of blockDim.x); thread =
 // latent. blockDim.x is M rounded up to 64, at most 256. K/V tiles of 64
-// tokens go through LDS; each thread keeps its latent's exact running maximum,
-// sum and accumulator.
+// tokens go through LDS (16-byte loads); each thread keeps its latent's exact
+// running maximum, sum and accumulator. The dot products run as four
+// independent partial sums (shorter dependency chains; every chunk is short,
+// so the chains, not the loads, set the time).
 // ---------------------------------------------------------------------------
+typedef float f32x4f __attribute__((ext_vector_type(4)));
+
+template <int D>
+__device__ __forceinline__ float dot4(const float* q, const float* k) {
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int d = 0; d < D; d += 4) {
+        const f32x4f kv = *(const f32x4f*)(k + d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = fmaf(q[d + i], kv[i], s[i]);
+    }
+    return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+// Exact online softmax of one query row q against `rows` LDS rows: keys kr,
+// values vr (D floats each), scores c * <q, k>, folded into the running
+// (offset mu, sum, accumulator). Rows go four at a time: their four scores
+// first, then one rescale to the largest, then their terms in row order; a
+// tail of fewer than four goes one at a time. Every rescale is by
+// 2^(mu_old - mu_new), so the ratio acc / sum is the softmax whatever the
+// grouping.
+template <int D>
+__device__ __forceinline__ void online_softmax_rows(const float* q, const float* kr, const float* vr, int rows,
+                                                    float c, float& mu, float& sum, float* acc) {
+    auto rescale = [&](float xm) {
+        if (xm > mu) {
+            const float alpha = (mu == -INFINITY) ? 0.0f : exp2f(mu - xm);
+            sum *= alpha;
+#pragma unroll
+            for (int d = 0; d < D; ++d) acc[d] *= alpha;
+            mu = xm;
+        }
+    };
+    auto add = [&](float x, const float* v) {
+        const float p = exp2f(x - mu);
+        sum += p;
+#pragma unroll
+        for (int d = 0; d < D; d += 4) {
+            const f32x4f vv = *(const f32x4f*)(v + d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[d + i] = fmaf(p, vv[i], acc[d + i]);
+        }
+    };
+    int r = 0;
+    for (; r + 4 <= rows; r += 4) {
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = dot4<D>(q, kr + (r + j) * D) * c;
+        rescale(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) add(x[j], vr + (r + j) * D);
+    }
+    for (; r < rows; ++r) {
+        const float x = dot4<D>(q, kr + r * D) * c;
+        rescale(x);
+        add(x, vr + r * D);
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
     constexpr int T = 64;
-    __shared__ float kt[T * D], vt[T * D];
+    __shared__ __attribute__((aligned(16))) float kt[T * D], vt[T * D];
     const int tid = threadIdx.x, nth = blockDim.x;
     const int chunk = blockIdx.x, bh = blockIdx.y;
     const int m = blockIdx.z * nth + tid;
@@ -149,31 +221,15 @@ __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
     float mu = -INFINITY, sig = 0.0f;
     for (int t0 = n0; t0 < n1; t0 += T) {
         const int nt = min(T, n1 - t0);
-        for (int e = tid; e < nt * D; e += nth) {
-            const int64_t g = (int64_t)(t0 + e / D) * a.sn + e % D;
-            kt[e] = Kb[g];
-            vt[e] = Vb[g];
+        // token rows are D contiguous floats (D a multiple of 8, rows 16-byte aligned)
+        for (int e = tid; e < nt * (D / 4); e += nth) {
+            const int r = e / (D / 4), d = 4 * (e % (D / 4));
+            const int64_t g = (int64_t)(t0 + r) * a.sn + d;
+            *(f32x4f*)(kt + r * D + d) = *(const f32x4f*)(Kb + g);
+            *(f32x4f*)(vt + r * D + d) = *(const f32x4f*)(Vb + g);
         }
         __syncthreads();
-        if (active) {
-            for (int t = 0; t < nt; ++t) {
-                float s = 0.0f;
-#pragma unroll
-                for (int d = 0; d < D; ++d) s = fmaf(q[d], kt[t * D + d], s);
-                const float x = s * c;
-                if (x > mu) {
-                    const float alpha = (mu == -INFINITY) ? 0.0f : exp2f(mu - x);
-                    sig *= alpha;
-#pragma unroll
-                    for (int d = 0; d < D; ++d) acc[d] *= alpha;
-                    mu = x;
-                }
-                const float p = exp2f(x - mu);
-                sig += p;
-#pragma unroll
-                for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vt[t * D + d], acc[d]);
-            }
-        }
+        if (active) online_softmax_rows<D>(q, kt, vt, nt, c, mu, sig, acc);
         __syncthreads();
     }
     if (active) {
@@ -187,47 +243,51 @@ __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // fp32 decode: grid (token blocks of 256, BH); thread = token. Exact online
-// softmax over the latents; Q and Z rows are read with wave-uniform addresses.
+// softmax over the latents, which stream through LDS in tiles of LT (Q and Z
+// rows, 16-byte loads); every lane reads the same latent row at a time
+// (LDS broadcast).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void decode_f32(DecodeArgs a) {
-    const int bh = blockIdx.y;
-    const int n = blockIdx.x * 256 + threadIdx.x;
+    constexpr int LT = D <= 32 ? 64 : 32;
+    __shared__ __attribute__((aligned(16))) float qs[LT * D], zs[LT * D];
+    const int bh = blockIdx.y, tid = threadIdx.x;
+    const int n = blockIdx.x * 256 + tid;
     const int b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M;
-    if (n >= N) return;
+    const bool active = n < N;  // every thread stages the tiles
     const float c = a.c;
     const float* Qb = (const float*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
     const float* Zb = (const float*)a.Z + (int64_t)bh * M * D;
-    const int64_t row = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)n * a.sn;
+    const int64_t row = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)(active ? n : 0) * a.sn;
     const float* kr = (const float*)a.K + row;
     float k[D], y[D];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        k[d] = kr[d];
-        y[d] = 0.0f;
+    for (int d = 0; d < D; d += 4) {
+        const f32x4f kv = active ? *(const f32x4f*)(kr + d) : f32x4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            k[d + i] = kv[i];
+            y[d + i] = 0.0f;
+        }
     }
     float nu = -INFINITY, tau = 0.0f;
-    for (int m = 0; m < M; ++m) {
-        float s = 0.0f;
-#pragma unroll
-        for (int d = 0; d < D; ++d) s = fmaf(Qb[(int64_t)m * D + d], k[d], s);
-        const float x = s * c;
-        if (x > nu) {
-            const float alpha = (nu == -INFINITY) ? 0.0f : exp2f(nu - x);
-            tau *= alpha;
-#pragma unroll
-            for (int d = 0; d < D; ++d) y[d] *= alpha;
-            nu = x;
+    for (int m0 = 0; m0 < M; m0 += LT) {
+        const int lt = min(LT, M - m0);
+        __syncthreads();  // the previous tile has been read
+        for (int e = tid; e < lt * (D / 4); e += 256) {
+            const int64_t g = (int64_t)m0 * D + 4 * e;
+            *(f32x4f*)(qs + 4 * e) = *(const f32x4f*)(Qb + g);
+            *(f32x4f*)(zs + 4 * e) = *(const f32x4f*)(Zb + g);
         }
-        const float p = exp2f(x - nu);
-        tau += p;
-#pragma unroll
-        for (int d = 0; d < D; ++d) y[d] = fmaf(p, Zb[(int64_t)m * D + d], y[d]);
+        __syncthreads();
+        if (active) online_softmax_rows<D>(k, qs, zs, lt, c, nu, tau, y);
     }
-    float* yr = (float*)a.Y + row;
+    if (active) {
+        float* yr = (float*)a.Y + row;
 #pragma unroll
-    for (int d = 0; d < D; ++d) yr[d] = y[d] / tau;
+        for (int d = 0; d < D; ++d) yr[d] = y[d] / tau;
+    }
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
@@ -311,6 +371,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     if (a.D % 4 != 0) return hipErrorInvalidValue;
     dim3 grid((a.M * (a.D / 4) + 255) / 256, a.BH), block(256);
     // groups of 8 chunks when that covers them all (fewer registers), else 16
+    // (measured on MI355X: 32-chunk groups, or four lanes per entry splitting
+    // the chunks, are slower at 32 chunks)
     if (a.C <= 8)
         FLARE_LAUNCH(combine_kernel<8>, grid, block, 0, s, a);
     else

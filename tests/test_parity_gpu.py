@@ -215,8 +215,10 @@ def test_chunk_count_invariance(i, tuning):
     b = F.flare_forward(Qd, Kd, Vd)
     tuning(F.FLARE_TUNE_CHUNKS, 5)
     c = F.flare_forward(Qd, Kd, Vd)
+    tuning(F.FLARE_TUNE_CHUNKS, 40)  # more than 16 chunks: the combine splits each entry over four lanes
+    d = F.flare_forward(Qd, Kd, Vd)
     torch.cuda.synchronize()
-    for x in (b, c):
+    for x in (b, c, d):
         e = errors(x.double().cpu().numpy(), a.double().cpu().numpy())
         assert e["rel_l2"] <= 5e-3, e
 
