@@ -297,7 +297,9 @@ enum {
     FLARE_TUNE_DEC_GROUPS = 5,  /* decode: workgroups per (b, h) */
     FLARE_TUNE_FAIL_ALLOC = 6,  /* 1: the allocating entry points fail with
                                  *   FLARE_ERR_NO_MEMORY (error-path tests) */
-    FLARE_TUNE_KEYS = 7
+    FLARE_TUNE_DEC_HEADS = 7,   /* bf16 decode, token-major layout: heads per workgroup
+                                 *   (1, 2 or 4, a divisor of H, where built) */
+    FLARE_TUNE_KEYS = 8
 };
 
 flare_status flare_set_tuning(flare_tune key, int64_t value);

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
     const int wm = wave % WM, wt = wave / WM;
-    const int chunk = blockIdx.x, bh = blockIdx.y;
+    const int chunk = a.heads_fast ? blockIdx.y : blockIdx.x, bh = a.heads_fast ? blockIdx.x : blockIdx.y;
     const int b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M, Mp = a.Mp;
     const int n0 = chunk * a.chunk_len;
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     }
 
     if (wt == 0) {
-        const int64_t pbase = ((int64_t)bh * gridDim.x + chunk) * Mp;
+        const int64_t pbase = ((int64_t)bh * a.C + chunk) * Mp;
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) {
             const int m = 32 * (wm * MBW + mb) + l32;
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
-    const int chunk = blockIdx.x, bh = blockIdx.y;
+    const int chunk = a.heads_fast ? blockIdx.y : blockIdx.x, bh = a.heads_fast ? blockIdx.x : blockIdx.y;
     const int b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M, Mp = a.Mp;
     const int n0 = chunk * a.chunk_len;
@@ -761,7 +761,7 @@ __global__ __launch_bounds__(64 * NWV) void encode_partial_priv_bf16(EncodeArgs 
         }
     }
     __syncthreads();
-    const int64_t pbase = ((int64_t)bh * gridDim.x + chunk) * Mp;
+    const int64_t pbase = ((int64_t)bh * a.C + chunk) * Mp;
     const int mlim = min(Mp, 32 * MBW);
     for (int e = tid; e < mlim * D; e += 64 * NWV) {
         const int m = e / D, d = e - m * D;
@@ -828,26 +828,34 @@ __device__ __forceinline__ int dec_zpos(int m) {
 constexpr int dec_waves_per_simd(int D, int TB, bool LONG, int NW) {
     return (D == 32 && TB == 1 && !LONG) ? 4 : (NW == 12 ? 3 : (NW == 8 ? 2 : 1));
 }
-template <int D, int TB, typename ZT, bool LONG, int MBC = 0, int NW = kDecWaves>
+// HG: heads per workgroup (a divisor of H). Wave w serves head w % HG of the
+// workgroup's group, so the HG waves of one token slot process the same token
+// block for HG adjacent heads at the same time: in the token-major layout
+// their rows are one contiguous run of HG * D * 2 bytes per token.
+template <int D, int TB, typename ZT, bool LONG, int MBC = 0, int NW = kDecWaves, int HG = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(dec_waves_per_simd(D, TB, LONG, NW))))
 void decode_bf16(DecodeArgs a) {
     constexpr int KB = D / 16, DB = D / 32, CH = D / 8;
     static_assert(NW >= 1 && NW <= 16, "reduction scratch holds 16 waves");
+    static_assert(NW % HG == 0, "every head of the group has the same number of waves");
+    constexpr int WPH = NW / HG;  // waves (token slots) per head
     const int Mp = a.Mp, MB = Mp / 32;
     const int zs = 2 * Mp + 16;  // bytes per Z^T row (padded)
+    const int head_bytes = Mp * 2 * D + D * zs;  // one head's Q and Z^T (a multiple of 16)
     extern __shared__ __attribute__((aligned(16))) unsigned char dsm[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block indices live in scalar registers
+    const int hl = wave % HG, slot = wave / HG;  // this wave's head in the group, and its token slot
     const int hi = lane >> 5, l32 = lane & 31;
-    const int bh = blockIdx.y;
-    const int b = bh / a.H, h = bh - b * a.H;
+    const int ngrp = a.H / HG;
+    const int b = blockIdx.y / ngrp, h0 = (blockIdx.y - b * ngrp) * HG;
+    const int h = h0 + hl, bh = b * a.H + h;
     const int N = a.N, M = a.M;
     const float c = a.c;
-    unsigned char* qs = dsm;                  // [Mp][D] bf16, swizzled
-    unsigned char* zt = dsm + Mp * 2 * D;     // [D][zs bytes]
-    float* red = (float*)(zt + D * zs);       // [NW] reduction scratch
+    unsigned char* qs = dsm + hl * head_bytes;  // [Mp][D] bf16, swizzled
+    unsigned char* zt = qs + Mp * 2 * D;        // [D][zs bytes]
+    float* red = (float*)(dsm + HG * head_bytes);  // [NW] reduction scratch
     const uint16_t* __restrict__ Qb = (const uint16_t*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
-    const ZT* __restrict__ Zb = (const ZT*)a.Z + (int64_t)bh * M * D;
     const int64_t sn = a.sn;
     const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + (int64_t)b * a.sb + (int64_t)h * a.sh;
     uint16_t* __restrict__ Yb = (uint16_t*)a.Y + (int64_t)b * a.sb + (int64_t)h * a.sh;
@@ -888,29 +896,34 @@ void decode_bf16(DecodeArgs a) {
     };
     // This wave's first K block is requested before the staging below, so
     // that its latency overlaps the staging instead of following it.
-    int blk = blockIdx.x * NW + wave;
+    int blk = blockIdx.x * WPH + slot;
     bf16x8 kA[TB][KB], kB[TB][KB];
     kload(blk, kA);
 
-    // ---- stage Q (bf16, swizzled rows) and Z^T (bf16, permuted latents)
-    for (int p = tid; p < Mp * CH; p += 64 * NW) {
-        const int m = p / CH, ch = p % CH;
+    // ---- stage Q (bf16, swizzled rows) and Z^T (bf16, permuted latents) of
+    // every head of the group (all threads take part)
+    for (int p = tid; p < HG * Mp * CH; p += 64 * NW) {
+        const int hh = p / (Mp * CH), r = p - hh * (Mp * CH);
+        const int m = r / CH, ch = r % CH;
+        const uint16_t* Qh = (const uint16_t*)a.Q + (int64_t)b * a.q_bstride + (int64_t)(h0 + hh) * M * D;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (m < M) v = *(const u32x4*)(Qb + (int64_t)m * D + ch * 8);
-        *(u32x4*)(qs + tile_off<D>(m, ch)) = v;
+        if (m < M) v = *(const u32x4*)(Qh + (int64_t)m * D + ch * 8);
+        *(u32x4*)(dsm + hh * head_bytes + tile_off<D>(m, ch)) = v;
     }
     // four consecutive columns of one latent per thread and step (one 16- or
     // 8-byte load), written to four Z^T rows
-    for (int e = tid; e < Mp * (D / 4); e += 64 * NW) {
-        const int m = e / (D / 4), d = 4 * (e % (D / 4));
+    for (int e = tid; e < HG * Mp * (D / 4); e += 64 * NW) {
+        const int hh = e / (Mp * (D / 4)), r = e - hh * (Mp * (D / 4));
+        const int m = r / (D / 4), d = 4 * (r % (D / 4));
+        const ZT* Zh = (const ZT*)a.Z + (int64_t)(b * a.H + h0 + hh) * M * D;
         float z4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (m < M) {
             if constexpr (sizeof(ZT) == 4) {
-                const f32x4 v = *(const f32x4*)((const float*)Zb + (int64_t)m * D + d);
+                const f32x4 v = *(const f32x4*)((const float*)Zh + (int64_t)m * D + d);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) z4[i] = v[i];
             } else {
-                const u32x2 v = *(const u32x2*)((const uint16_t*)Zb + (int64_t)m * D + d);
+                const u32x2 v = *(const u32x2*)((const uint16_t*)Zh + (int64_t)m * D + d);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     z4[2 * i] = __uint_as_float(v[i] << 16);
@@ -918,20 +931,23 @@ void decode_bf16(DecodeArgs a) {
                 }
             }
         }
+        unsigned char* zh = dsm + hh * head_bytes + Mp * 2 * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(__bf16*)(zt + (d + i) * zs + 2 * dec_zpos(m)) = (__bf16)z4[i];
+        for (int i = 0; i < 4; ++i) *(__bf16*)(zh + (d + i) * zs + 2 * dec_zpos(m)) = (__bf16)z4[i];
     }
     __syncthreads();
     // Offsets. With the encode's merged offsets mu*[m] (log2 units), every
     // logit of this (b, h) satisfies c*S <= max_m mu*[m] + 32, one offset for
     // all tokens. Without them, per token: c * max_m |Q[m]| * |K[tok]|
     // (Cauchy-Schwarz); here only max_m |Q[m]|^2 is prepared.
+    // (each head's waves reduce over that head's latents)
     const bool goff = a.zmu != nullptr;
     float red_in = goff ? -INFINITY : 0.0f;
+    const int ht = lane + 64 * slot;  // this thread's index among its head's threads
     if (goff) {
-        for (int m = tid; m < M; m += 64 * NW) red_in = fmaxf(red_in, a.zmu[(int64_t)bh * M + m]);
+        for (int m = ht; m < M; m += 64 * WPH) red_in = fmaxf(red_in, a.zmu[(int64_t)bh * M + m]);
     } else {
-        for (int m = tid; m < M; m += 64 * NW) {
+        for (int m = ht; m < M; m += 64 * WPH) {
             float s2 = 0.0f;
             for (int ch = 0; ch < CH; ++ch) {
                 const bf16x8 v = *(const bf16x8*)(qs + tile_off<D>(m, ch));
@@ -948,16 +964,16 @@ void decode_bf16(DecodeArgs a) {
     for (int off = 32; off >= 1; off >>= 1) red_in = fmaxf(red_in, __shfl_xor(red_in, off, 64));
     if (lane == 0) red[wave] = red_in;
     __syncthreads();
-    float rmax = red[0];
+    float rmax = red[hl];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) rmax = fmaxf(rmax, red[w]);
+    for (int w = hl + HG; w < NW; w += HG) rmax = fmaxf(rmax, red[w]);
     const float cq = goff ? 0.0f : c * sqrtf(rmax);
     const float gnu = goff ? rmax + kSumLimitLog2 : 0.0f;
 
     const bf16x8 csel = colsum_selector(lane);
     const f32x16 zero16 = {};
     const int nblk = (N + 32 * TB - 1) / (32 * TB);
-    const int stride = gridDim.x * NW;
+    const int stride = gridDim.x * WPH;
 
     auto qread = [&](int mb, bf16x8 (&qa)[KB]) {
 #pragma unroll
@@ -1192,14 +1208,14 @@ void decode_bf16(DecodeArgs a) {
 
 template <int D, int MBW, int WM, int WT>
 hipError_t launch_enc(const EncodeArgs& a, hipStream_t s) {
-    dim3 grid(a.C, a.BH), block(64 * WM * WT);
+    dim3 grid(a.heads_fast ? a.BH : a.C, a.heads_fast ? a.C : a.BH), block(64 * WM * WT);
     FLARE_LAUNCH((encode_partial_bf16<D, MBW, WM, WT>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
 template <int D, int MBW, int NWV>
 hipError_t launch_enc_priv(const EncodeArgs& a, hipStream_t s) {
-    dim3 grid(a.C, a.BH), block(64 * NWV);
+    dim3 grid(a.heads_fast ? a.BH : a.C, a.heads_fast ? a.C : a.BH), block(64 * NWV);
     FLARE_LAUNCH((encode_partial_priv_bf16<D, MBW, NWV>), grid, block, 0, s, a);
     return hipGetLastError();
 }
@@ -1242,9 +1258,40 @@ hipError_t launch_enc_d(const EncodeArgs& a, hipStream_t s) {
 }
 
 template <int D, int TB, typename ZT>
-const void* dec_kernel(int M) {
+const void* dec_kernel(int M, int hg) {
     const int Mp = (M + 31) / 32 * 32;
     if constexpr (D <= 64 && TB == 1) {
+        if (hg > 1 && M == Mp) {  // head groups (token-major layout), as dec_heads_bf16 picks them
+            if constexpr (D == 32) {
+                if (hg == 4) {
+                    switch (M / 32) {
+                        case 1: return (const void*)decode_bf16<D, TB, ZT, false, 1, 8, 4>;
+                        case 2: return (const void*)decode_bf16<D, TB, ZT, false, 2, 8, 4>;
+                        case 4: return (const void*)decode_bf16<D, TB, ZT, false, 4, 8, 4>;
+                        default: break;
+                    }
+                } else if (hg == 2 && M == 256) {
+                    return (const void*)decode_bf16<D, TB, ZT, false, 8, 8, 2>;
+                }
+            } else {
+                if (hg == 2) {
+                    switch (M / 32) {
+                        case 1: return (const void*)decode_bf16<D, TB, ZT, false, 1, 4, 2>;
+                        case 2: return (const void*)decode_bf16<D, TB, ZT, false, 2, 4, 2>;
+                        case 4: return (const void*)decode_bf16<D, TB, ZT, false, 4, 4, 2>;
+                        case 8: return (const void*)decode_bf16<D, TB, ZT, false, 8, 12, 2>;
+                        default: break;
+                    }
+                } else if (hg == 4) {
+                    switch (M / 32) {
+                        case 2: return (const void*)decode_bf16<D, TB, ZT, false, 2, 8, 4>;
+                        case 4: return (const void*)decode_bf16<D, TB, ZT, false, 4, 8, 4>;
+                        default: break;
+                    }
+                }
+            }
+            return nullptr;  // not built
+        }
         if (Mp > 256) {
             if constexpr (D == 64)
                 return (const void*)decode_bf16<D, TB, ZT, true, 0, 8>;
@@ -1291,15 +1338,16 @@ hipError_t allow_dec_lds(const void* fn) {
 
 template <int D, int TB, typename ZT>
 hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
-    const int lds = dec_lds_bytes_bf16(a.Mp, D);
-    const void* fn = dec_kernel<D, TB, ZT>(a.M);
+    const int lds = dec_lds_bytes_bf16(a.Mp, D, a.hg);
+    const void* fn = dec_kernel<D, TB, ZT>(a.M, a.hg);
+    if (!fn) return hipErrorInvalidValue;
     if (lds > 65536) {
         hipError_t e = allow_dec_lds(fn);
         if (e != hipSuccess) return e;
     }
     DecodeArgs arg = a;
     void* args[] = {&arg};
-    return launch_raw(fn, dim3(a.G, a.BH), dim3(64 * dec_waves_bf16(D, a.M, TB)), args, lds, s);
+    return launch_raw(fn, dim3(a.G, a.BH / a.hg), dim3(64 * dec_waves_bf16(D, a.M, TB, a.hg)), args, lds, s);
 }
 
 template <int D, typename ZT>
@@ -1329,18 +1377,19 @@ int enc_threads_bf16(EncCfg cfg) { return 64 * (cfg.wm == 0 ? 1 : cfg.wm) * cfg.
 // Resident decode workgroups per CU, from the kernel's occupancy at its LDS
 // size. Computed once per (D, tb, Z type, Mp) and cached: the query and the
 // attribute call cost more than a launch.
-int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32) {
+int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32, int hg) {
     const int di = D == 32 ? 0 : D == 64 ? 1 : D == 128 ? 2 : -1;
+    const int hi = hg == 1 ? 0 : hg == 2 ? 1 : hg == 4 ? 2 : -1;
     const int Mp = (M + 31) / 32 * 32;
-    if (di < 0 || tb < 1 || tb > 2 || M < 1 || Mp > kBf16MaxM) return 1;
-    static std::atomic<int> cache[3][2][2][kBf16MaxM / 32][2];
-    std::atomic<int>& slot = cache[di][tb - 1][z_f32 ? 1 : 0][Mp / 32 - 1][M == Mp ? 1 : 0];
+    if (di < 0 || hi < 0 || tb < 1 || tb > 2 || M < 1 || Mp > kBf16MaxM) return 1;
+    static std::atomic<int> cache[3][2][2][kBf16MaxM / 32][2][3];
+    std::atomic<int>& slot = cache[di][tb - 1][z_f32 ? 1 : 0][Mp / 32 - 1][M == Mp ? 1 : 0][hi];
     const int known = slot.load(std::memory_order_relaxed);
     if (known > 0) return known;
-    const int lds = dec_lds_bytes_bf16(Mp, D);
+    const int lds = dec_lds_bytes_bf16(Mp, D, hg);
     const void* fn = nullptr;
-#define FLARE_DEC_FN(DD, TB)                                                                          \
-    if (D == DD && tb == TB) fn = z_f32 ? dec_kernel<DD, TB, float>(M) : dec_kernel<DD, TB, uint16_t>(M);
+#define FLARE_DEC_FN(DD, TB)                                                                                \
+    if (D == DD && tb == TB) fn = z_f32 ? dec_kernel<DD, TB, float>(M, hg) : dec_kernel<DD, TB, uint16_t>(M, hg);
     FLARE_DEC_FN(32, 1)
     FLARE_DEC_FN(32, 2)
     FLARE_DEC_FN(64, 1)
@@ -1350,7 +1399,7 @@ int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32) {
     if (!fn) return 1;
     if (lds > 65536 && allow_dec_lds(fn) != hipSuccess) return 1;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * dec_waves_bf16(D, M, tb), lds) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * dec_waves_bf16(D, M, tb, hg), lds) != hipSuccess ||
         n < 1)
         return 1;
     slot.store(n, std::memory_order_relaxed);
@@ -1362,14 +1411,41 @@ int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32) {
 int dec_tb_bf16(int, int) { return 1; }
 bool dec_tb_built_bf16(int D, int Mp, int tb) { return tb == 1 || (tb == 2 && D <= 64 && Mp <= 256); }
 
-int dec_waves_bf16(int D, int M, int tb) {
+int dec_waves_bf16(int D, int M, int tb, int hg) {
     const int Mp = (M + 31) / 32 * 32;
+    if (hg == 4) return 8;                  // two token slots of four heads
+    if (hg == 2) return D == 32 ? 8 : (M == 256 ? 12 : kDecWaves);
     if (D != 64 || tb != 1) return kDecWaves;
     if (Mp > 256) return 8;
     return M == 256 ? 12 : kDecWaves;
 }
 
-int dec_lds_bytes_bf16(int Mp, int D) { return Mp * 2 * D + D * (2 * Mp + 16) + 64; }
+// Head groups built (D, exact M -> hg): D = 32: 4 at M <= 128, 2 at 256;
+// D = 64: 2 at M <= 256, 4 at M = 64 and 128.
+bool dec_heads_built_bf16(int D, int M, int hg) {
+    const int Mp = (M + 31) / 32 * 32;
+    if (M != Mp) return hg == 1;
+    if (hg == 1) return true;
+    if (D == 32) return (hg == 4 && Mp <= 128) || (hg == 2 && Mp == 256);
+    if (D == 64) return (hg == 2 && Mp <= 256) || (hg == 4 && (Mp == 64 || Mp == 128));
+    return false;
+}
+
+// Measured on MI355X in the token-major layout (decode us, heads per
+// workgroup 1 / 2 / 4): D = 64, M = 128: 324 / 302 / 275 (FLARE++ workload);
+// D = 64, M = 64: 48.1 / 49.6 / 54.4 (long sequences); D = 32, M = 128:
+// 55.4 / 56.6 / 56.7 (65k mesh). So: four heads at D = 64, M = 128, pairs at
+// D = 64, M = 256 (twelve-wave workgroups), one otherwise.
+int dec_heads_bf16(int D, int M, int H, int tb, bool token_major) {
+    if (!token_major || tb != 1) return 1;
+    int hg = 1;
+    if (D == 64 && M == 128) hg = 4;
+    else if (D == 64 && M == 256) hg = 2;
+    while (hg > 1 && H % hg) hg /= 2;
+    return dec_heads_built_bf16(D, M, hg) ? hg : 1;
+}
+
+int dec_lds_bytes_bf16(int Mp, int D, int hg) { return hg * (Mp * 2 * D + D * (2 * Mp + 16)) + 64; }
 
 hipError_t launch_encode_bf16(const EncodeArgs& a, hipStream_t s) {
     switch (a.D) {

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
     constexpr int T = 64;
     __shared__ __attribute__((aligned(16))) float kt[T * D], vt[T * D];
     const int tid = threadIdx.x, nth = blockDim.x;
-    const int chunk = blockIdx.x, bh = blockIdx.y;
+    const int chunk = a.heads_fast ? blockIdx.y : blockIdx.x, bh = a.heads_fast ? blockIdx.x : blockIdx.y;
     const int m = blockIdx.z * nth + tid;
     const int b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M;
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
         __syncthreads();
     }
     if (active) {
-        const int64_t r = ((int64_t)bh * gridDim.x + chunk) * a.Mp + m;
+        const int64_t r = ((int64_t)bh * a.C + chunk) * a.Mp + m;
         a.out.mu[r] = mu;
         a.out.sig[r] = sig;
 #pragma unroll
@@ -334,7 +334,7 @@ unsigned elementwise_blocks(int64_t n) { return (unsigned)std::min<int64_t>(8192
 template <int D>
 hipError_t enc_f32(const EncodeArgs& a, hipStream_t s) {
     const int nth = enc_threads_f32(a.M);
-    dim3 grid(a.C, a.BH, (a.M + nth - 1) / nth), block(nth);
+    dim3 grid(a.heads_fast ? a.BH : a.C, a.heads_fast ? a.C : a.BH, (a.M + nth - 1) / nth), block(nth);
     FLARE_LAUNCH((encode_partial_f32<D>), grid, block, 0, s, a);
     return hipGetLastError();
 }

@@ -58,6 +58,7 @@ struct EncodeArgs {
     float c;             // (1/sqrt(D)) * log2(e)
     Partials out;
     EncCfg cfg;          // bf16: the workgroup shape (from the plan)
+    bool heads_fast;     // grid (BH, C) instead of (C, BH): adjacent heads' workgroups are dispatched together
 };
 
 // What the combine writes.
@@ -115,8 +116,9 @@ struct DecodeArgs {
     void* Y;             // same layout as K
     int64_t sb, sh, sn;  // K and Y strides in elements: batch, head, token
     int BH, H, N, M, Mp, D;
-    int G;               // workgroups per (b, h)
+    int G;               // workgroups per (b, h) group of hg heads
     int tb;              // bf16: 32-token blocks per wave and step (1 or 2)
+    int hg;              // bf16: heads per workgroup (a divisor of H; 1 unless token-major)
     float c;
 };
 
@@ -131,9 +133,13 @@ constexpr int kBf16MaxM = 512;
 constexpr int kBf16MaxM128 = 256;
 int dec_tb_bf16(int D, int Mp);  // 32-token blocks per wave per step (the library's choice)
 bool dec_tb_built_bf16(int D, int Mp, int tb);  // whether a decode with tb blocks is built for (D, Mp)
-int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32);  // resident decode workgroups per CU (cached)
-int dec_lds_bytes_bf16(int Mp, int D);
-int dec_waves_bf16(int D, int M, int tb);  // waves per bf16 decode workgroup
+int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32, int hg);  // resident decode workgroups per CU (cached)
+int dec_lds_bytes_bf16(int Mp, int D, int hg);
+int dec_waves_bf16(int D, int M, int tb, int hg);  // waves per bf16 decode workgroup
+// Heads per bf16 decode workgroup: groups of 2 or 4 heads in the token-major
+// layout (for the exact latent counts they are built for), 1 otherwise.
+int dec_heads_bf16(int D, int M, int H, int tb, bool token_major);
+bool dec_heads_built_bf16(int D, int M, int hg);
 
 hipError_t launch_encode_bf16(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);

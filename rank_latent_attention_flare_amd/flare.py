@@ -21,7 +21,8 @@ FLARE_OP_PP_BACKWARD = 5
 FLARE_OP_PP_QUERIES = 6
 FLARE_LAYOUT_BHND, FLARE_LAYOUT_BNHD = 0, 1
 FLARE_TUNE_CHUNKS, FLARE_TUNE_ENC_MBW, FLARE_TUNE_ENC_WM, FLARE_TUNE_ENC_WT = 0, 1, 2, 3
-FLARE_TUNE_DEC_TB, FLARE_TUNE_DEC_GROUPS, FLARE_TUNE_FAIL_ALLOC = 4, 5, 6
+FLARE_TUNE_DEC_TB, FLARE_TUNE_DEC_GROUPS, FLARE_TUNE_FAIL_ALLOC, FLARE_TUNE_DEC_HEADS = 4, 5, 6, 7
+FLARE_TUNE_KEYS = 8
 FLARE_KERNEL_KINDS = 4
 KERNEL_KIND_NAMES = ("encode_partial", "combine", "decode", "backward")
 

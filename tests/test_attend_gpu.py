@@ -20,6 +20,9 @@ CASES = [
     (1, 2, 4097, 100, 32, "bf16"),
     (1, 1, 1, 1, 32, "bf16"),
     (2, 2, 777, 33, 128, "bf16"),
+    # exact latent counts with token-major queries: head groups per workgroup
+    (1, 4, 3001, 128, 32, "bf16"),
+    (2, 2, 1999, 64, 64, "bf16"),
     (1, 3, 3000, 40, 8, "f32"),
     (1, 2, 500, 300, 32, "f32"),
 ]

@@ -30,6 +30,16 @@ CASES = [
     (3, 8, 2049, 128, 32, "bf16"),
     (1, 3, 3000, 40, 8, "f32"),
     (2, 2, 999, 17, 64, "f32"),
+    # exact latent counts, ragged tokens: the token-major decode serves four
+    # adjacent heads per workgroup at D = 64, M = 128 and pairs at M = 256
+    # (other head groups are checked below through the tuning key)
+    (2, 4, 3001, 32, 32, "bf16"),
+    (1, 4, 2500, 64, 32, "bf16"),
+    (1, 2, 3001, 256, 32, "bf16"),
+    (2, 4, 1999, 64, 64, "bf16"),
+    (1, 6, 2049, 128, 64, "bf16"),
+    (1, 2, 3001, 256, 64, "bf16"),
+    (1, 3, 1500, 64, 64, "bf16"),  # H odd: one head per workgroup
 ]
 
 
@@ -72,3 +82,25 @@ def test_token_major_equals_plain_layout(op, case):
     want = {"encode": lambda: oracle.encode(Q, K, V), "decode": lambda: oracle.decode(Q, K, V),
             "forward": lambda: oracle.forward(Q, K, V)[0], "pp_forward": lambda: oracle.pp_forward(Q, K, V)[0]}[op]()
     assert_parity(to_host64(out.contiguous()), want, dt, f"{op} token-major {case_id(case)}")
+
+
+@pytest.mark.parametrize("hg,case", [(4, (2, 4, 3001, 32, 32)), (4, (1, 4, 2500, 128, 32)), (2, (1, 2, 3001, 256, 32)),
+                                     (2, (2, 4, 1999, 64, 64)), (4, (1, 4, 1999, 64, 64)), (2, (1, 6, 2049, 128, 64))],
+                         ids=lambda x: str(x))
+def test_head_groups_equal_plain_layout(hg, case):
+    # every built head-group decode (set through the tuning key) against the
+    # plain layout, bit for bit, and the oracle
+    B, H, N, M, D = case
+    Q, K, V = make_inputs(B, H, N, M, D, "bf16", q_scale=0.5, seed=N + hg)
+    q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+    ref = F.flare_forward(q, k, v)
+    F.flare_set_tuning(F.FLARE_TUNE_DEC_HEADS, hg)
+    try:
+        out = F.flare_forward_ex(q, token_major(k), token_major(v), F.FLARE_LAYOUT_BNHD)
+        torch.cuda.synchronize()
+    finally:
+        F.flare_set_tuning(F.FLARE_TUNE_DEC_HEADS, 0)
+    print(f"[layout] head groups {hg} case {case}", flush=True)
+    assert torch.equal(out.transpose(1, 2).contiguous().view(torch.int16), ref.view(torch.int16))
+    assert_parity(to_host64(out.transpose(1, 2).contiguous()), oracle.forward(Q, K, V)[0], "bf16",
+                  f"head groups {hg} {case}")

@@ -203,7 +203,7 @@ def test_bitwise_repeatable(i):
 def tuning():
     """flare_set_tuning for one test; every key is restored to the library's choice afterwards."""
     yield F.flare_set_tuning
-    for key in range(7):
+    for key in range(F.FLARE_TUNE_KEYS):
         F.flare_set_tuning(key, 0)
 
 
