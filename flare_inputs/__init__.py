@@ -69,6 +69,9 @@ WORKLOADS = {
     # the top of the FLARE page's latent range ("Key Hyperparameters": M up
     # to 512): not one of the five headline configurations
     6: Workload("latents-512", 1, 8, 262144, 512, 64, BF16, 0.5, 1.0, "forward", 6),
+    # the same latent count at the widest head (D = 128): the decode's latents
+    # do not fit in one CU's LDS there, so it runs over two latent ranges
+    7: Workload("latents-512-d128", 1, 8, 131072, 512, 128, BF16, 0.5, 1.0, "forward", 7),
 }
 
 

@@ -60,6 +60,8 @@ struct Plan {
     int C, chunk_len;  // encode split over N
     int G;             // decode workgroups per (b, h) (fp32; bf16: decode_groups)
     int tb;            // bf16 decode: 32-token blocks per wave and step
+    bool dsplit;       // bf16 D = 128 with M > 256: the decode runs as two launches over the latents
+    size_t dsplit_bytes, off_dsplit;  // their fp32 state (decode op: at 0; forward ops: at off_dsplit)
     flare::EncCfg cfg; // bf16 encode workgroup shape
     size_t esize;
     size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[7];
@@ -138,7 +140,9 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
                               int(tune(FLARE_TUNE_ENC_WT))};
         if (o.mbw > 0 && o.wt > 0 && o.wm >= 0 && (o.wm == 0 ? o.mbw : o.mbw * o.wm) >= p->Mp / 32) p->cfg = o;
         tile = flare::enc_tile_tokens_bf16(p->cfg);
-        waves_per_wg = flare::enc_threads_bf16(p->cfg) / 64;
+        // waves over all workgroups of one chunk (latent groups on grid z)
+        const int zg = p->cfg.wm == 0 ? 1 : (p->Mp / 32 + p->cfg.mbw * p->cfg.wm - 1) / (p->cfg.mbw * p->cfg.wm);
+        waves_per_wg = flare::enc_threads_bf16(p->cfg) / 64 * zg;
         p->tb = flare::dec_tb_bf16(int(D), p->Mp);
         const int64_t otb = tune(FLARE_TUNE_DEC_TB);
         if (otb > 0 && flare::dec_tb_built_bf16(int(D), p->Mp, int(otb))) p->tb = int(otb);
@@ -184,9 +188,16 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     const size_t fwd_total = off;
     p->off_qp = off;  off = align256(off + size_t(p->BH) * size_t(M) * size_t(D) * p->esize);
     p->total[FLARE_OP_ENCODE] = enc_total;
-    p->total[FLARE_OP_DECODE] = 0;
-    p->total[FLARE_OP_FORWARD] = fwd_total;
-    p->total[FLARE_OP_PP_FORWARD] = off;
+    // split decode state: per token block, 32 * D floats of Y and 32 (max, sum) pairs
+    p->dsplit = dt == FLARE_BF16 && D == 128 && p->Mp > flare::kDecSplitM128;
+    const size_t nblk = size_t((N + 31) / 32);
+    p->dsplit_bytes = p->dsplit ? align256(size_t(p->BH) * nblk * 32 * size_t(D) * 4) +
+                                      align256(size_t(p->BH) * nblk * 32 * 2 * 4)
+                                : 0;
+    p->off_dsplit = off;  // after every forward section (FLARE++'s Q' included)
+    p->total[FLARE_OP_DECODE] = p->dsplit_bytes;
+    p->total[FLARE_OP_FORWARD] = p->dsplit ? off + p->dsplit_bytes : fwd_total;
+    p->total[FLARE_OP_PP_FORWARD] = off + p->dsplit_bytes;
     p->total[FLARE_OP_PP_QUERIES] = enc_total;
     // backward: the forward's sections (encode partials, reused for the dZ and
     // dQ partials; Z and mu*), then sig*, the per-token decode statistics, dZ
@@ -322,8 +333,9 @@ int dec_heads(const Plan& p) {
 
 // Decode workgroups per group of heads: one resident wave of workgroups over
 // the whole chip (from the kernel's occupancy), each looping over token blocks.
-int decode_groups(const Plan& p, bool z_f32) {
+int decode_groups(const Plan& p, bool z_f32, int m_range = 0, int split = 0) {
     if (tune(FLARE_TUNE_DEC_GROUPS) > 0) return int(std::min<int64_t>(tune(FLARE_TUNE_DEC_GROUPS), 1 << 20));
+    const int Mr = m_range > 0 ? m_range : int(p.M);  // latents of this launch
     if (p.dt != FLARE_BF16) return p.G;
     static std::atomic<int> cus_cache{0};
     int cus = cus_cache.load(std::memory_order_relaxed);
@@ -336,9 +348,9 @@ int decode_groups(const Plan& p, bool z_f32) {
             cus = 256;
         cus_cache.store(cus, std::memory_order_relaxed);
     }
-    const int hg = dec_heads(p);
-    const int per_cu = flare::dec_wgs_per_cu_bf16(int(p.D), int(p.M), p.tb, z_f32, hg);
-    const int64_t per_wg = 32 * p.tb * (flare::dec_waves_bf16(int(p.D), int(p.M), p.tb, hg) / hg);
+    const int hg = split ? 1 : dec_heads(p);
+    const int per_cu = flare::dec_wgs_per_cu_bf16(int(p.D), Mr, p.tb, z_f32, hg, split);
+    const int64_t per_wg = 32 * p.tb * (flare::dec_waves_bf16(int(p.D), Mr, p.tb, hg) / hg);
     const int64_t groups = p.BH / hg;
     int64_t G = (int64_t(cus) * per_cu + groups - 1) / groups;
     G = std::max<int64_t>(1, std::min<int64_t>(G, (p.N + per_wg - 1) / per_wg));
@@ -346,7 +358,30 @@ int decode_groups(const Plan& p, bool z_f32) {
 }
 
 hipError_t run_decode(const Plan& p, const void* Q, int64_t q_bstride, const void* K, const void* Z, bool z_f32,
-                      void* Y, hipStream_t s, const float* zmu = nullptr) {
+                      void* Y, hipStream_t s, const float* zmu = nullptr, char* split_ws = nullptr) {
+    if (p.dsplit) {
+        // two launches over latents [0, 256) and [256, M), each against its
+        // exact per-token maxima, the second merging the first's state
+        if (!split_ws) return hipErrorInvalidValue;
+        DecodeArgs a{};
+        a.Q = Q; a.q_bstride = q_bstride; a.K = K; a.Z = Z; a.z_f32 = z_f32; a.zmu = nullptr; a.Y = Y;
+        a.sb = p.sb; a.sh = p.sh; a.sn = p.sn;
+        a.BH = p.BH; a.H = int(p.H); a.N = int(p.N); a.D = int(p.D);
+        a.tb = 1; a.hg = 1; a.c = p.c; a.Mtot = int(p.M);
+        const size_t nblk = size_t((p.N + 31) / 32);
+        a.part_y = (float*)split_ws;
+        a.part_nt = (float*)(split_ws + align256(size_t(p.BH) * nblk * 32 * size_t(p.D) * 4));
+        hipError_t e = hipSuccess;
+        for (int part = 1; part <= 2 && e == hipSuccess; ++part) {
+            a.split = part;
+            a.m_off = part == 1 ? 0 : flare::kDecSplitM128;
+            a.M = part == 1 ? flare::kDecSplitM128 : int(p.M) - flare::kDecSplitM128;
+            a.Mp = (a.M + 31) / 32 * 32;
+            a.G = decode_groups(p, z_f32, a.M, part);
+            e = timed(2, s, [&] { return flare::launch_decode_bf16(a, s); });
+        }
+        return e;
+    }
     DecodeArgs a{};
     a.Q = Q;
     a.q_bstride = q_bstride;
@@ -401,7 +436,7 @@ flare_status exec(flare_op op, const void* Q, const void* K, const void* V, void
             if (e == hipSuccess) e = run_combine(p, flare::COMBINE_Z_DTYPE, Q, Y, ws, s);
             break;
         case FLARE_OP_DECODE:
-            e = run_decode(p, Q, 0, K, V, dt == FLARE_F32, Y, s);
+            e = run_decode(p, Q, 0, K, V, dt == FLARE_F32, Y, s, nullptr, ws);
             break;
         case FLARE_OP_PP_QUERIES:
             // the first two launches of pp_forward, with Q' written to the output
@@ -412,7 +447,8 @@ flare_status exec(flare_op op, const void* Q, const void* K, const void* V, void
             e = run_encode_partial(p, Q, 0, K, V, ws, s);
             if (e == hipSuccess)
                 e = run_combine(p, flare::COMBINE_Z_F32, Q, ws + p.off_z, ws, s, (float*)(ws + p.off_zmu));
-            if (e == hipSuccess) e = run_decode(p, Q, 0, K, ws + p.off_z, true, Y, s, (const float*)(ws + p.off_zmu));
+            if (e == hipSuccess)
+                e = run_decode(p, Q, 0, K, ws + p.off_z, true, Y, s, (const float*)(ws + p.off_zmu), ws + p.off_dsplit);
             break;
         case FLARE_OP_PP_FORWARD: {
             void* qp = ws + p.off_qp;
@@ -423,7 +459,8 @@ flare_status exec(flare_op op, const void* Q, const void* K, const void* V, void
             if (e == hipSuccess)
                 e = run_combine(p, flare::COMBINE_Z_F32, Q, ws + p.off_z, ws, s, (float*)(ws + p.off_zmu));
             if (e == hipSuccess)
-                e = run_decode(p, qp, qstride, K, ws + p.off_z, true, Y, s, (const float*)(ws + p.off_zmu));
+                e = run_decode(p, qp, qstride, K, ws + p.off_z, true, Y, s, (const float*)(ws + p.off_zmu),
+                               ws + p.off_dsplit);
             break;
         }
     }
@@ -835,7 +872,19 @@ flare_status flare_attend(const void* q, const void* Z, void* Y, int64_t B, int6
     // operand of the logits (batch-strided, as FLARE++'s Q') and the values;
     // the token queries take the place of K. No encode offsets: the
     // per-token Cauchy-Schwarz bound.
-    hipError_t e = run_decode(p, Z, H * M * D, q, Z, dtype == FLARE_F32, Y, stream);
+    // (the split decode needs scratch memory for its state: stream-ordered,
+    // as in the plain entry points)
+    void* ws = nullptr;
+    if (p.dsplit) {
+        if (tune(FLARE_TUNE_FAIL_ALLOC) == 1) return fail(FLARE_ERR_NO_MEMORY, "allocation failure injected (FLARE_TUNE_FAIL_ALLOC)");
+        hipError_t ea = hipMallocAsync(&ws, p.dsplit_bytes, stream);
+        if (ea != hipSuccess || !ws) return fail(FLARE_ERR_NO_MEMORY, std::string("hipMallocAsync: ") + hipGetErrorString(ea));
+    }
+    hipError_t e = run_decode(p, Z, H * M * D, q, Z, dtype == FLARE_F32, Y, stream, nullptr, (char*)ws);
+    if (ws) {
+        hipError_t ef = hipFreeAsync(ws, stream);
+        if (e == hipSuccess && ef != hipSuccess) return hip_fail(ef, "hipFreeAsync");
+    }
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     return FLARE_OK;
 }

@@ -232,11 +232,14 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     const uint16_t* __restrict__ Vb = (const uint16_t*)a.V + kvoff;
     const uint16_t* __restrict__ Qb = (const uint16_t*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
 
-    // This wave's latent queries as MFMA B operands (column m, k = d).
+    // This wave's latent queries as MFMA B operands (column m, k = d). A
+    // workgroup covers 32 * WM * MBW latents; grid z selects which (when M
+    // needs more than one workgroup's worth).
+    const int mgrp = 32 * WM * MBW * blockIdx.z;
     bf16x8 qop[MBW][KB];
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
-        const int m = 32 * (wm * MBW + mb) + l32;
+        const int m = mgrp + 32 * (wm * MBW + mb) + l32;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
             qop[mb][kb] = (m < M) ? *(const bf16x8*)(Qb + (int64_t)m * D + 16 * kb + 8 * hi) : zero8();
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
         const int64_t pbase = ((int64_t)bh * a.C + chunk) * Mp;
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) {
-            const int m = 32 * (wm * MBW + mb) + l32;
+            const int m = mgrp + 32 * (wm * MBW + mb) + l32;
             const float sig = ps[mb];
             if (m < Mp) {
                 if (hi == 0) {
@@ -832,12 +835,20 @@ constexpr int dec_waves_per_simd(int D, int TB, bool LONG, int NW) {
 // workgroup's group, so the HG waves of one token slot process the same token
 // block for HG adjacent heads at the same time: in the token-major layout
 // their rows are one contiguous run of HG * D * 2 bytes per token.
-template <int D, int TB, typename ZT, bool LONG, int MBC = 0, int NW = kDecWaves, int HG = 1>
+// SPLIT (1 or 2): one of the two launches of a decode whose latents do not fit
+// in LDS. Each covers the latent range [m_off, m_off + M) of the full a.Mtot,
+// against the exact per-token maximum over that range. Launch 1 stores every
+// token's (maximum, sum, unnormalised Y) in fp32; launch 2 merges its own
+// state with it by the log-sum-exp rule (an exact rescaling by powers of two)
+// and writes Y.
+template <int D, int TB, typename ZT, bool LONG, int MBC = 0, int NW = kDecWaves, int HG = 1, int SPLIT = 0>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(dec_waves_per_simd(D, TB, LONG, NW))))
 void decode_bf16(DecodeArgs a) {
     constexpr int KB = D / 16, DB = D / 32, CH = D / 8;
     static_assert(NW >= 1 && NW <= 16, "reduction scratch holds 16 waves");
     static_assert(NW % HG == 0, "every head of the group has the same number of waves");
+    static_assert(SPLIT == 0 || (TB == 1 && HG == 1 && MBC == 0), "the split decode is built for one token block");
+    const int Mt = SPLIT ? a.Mtot : a.M;  // latents per head in Q and Z (their row stride)
     constexpr int WPH = NW / HG;  // waves (token slots) per head
     const int Mp = a.Mp, MB = Mp / 32;
     const int zs = 2 * Mp + 16;  // bytes per Z^T row (padded)
@@ -855,7 +866,6 @@ void decode_bf16(DecodeArgs a) {
     unsigned char* qs = dsm + hl * head_bytes;  // [Mp][D] bf16, swizzled
     unsigned char* zt = qs + Mp * 2 * D;        // [D][zs bytes]
     float* red = (float*)(dsm + HG * head_bytes);  // [NW] reduction scratch
-    const uint16_t* __restrict__ Qb = (const uint16_t*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
     const int64_t sn = a.sn;
     const uint16_t* __restrict__ Kb = (const uint16_t*)a.K + (int64_t)b * a.sb + (int64_t)h * a.sh;
     uint16_t* __restrict__ Yb = (uint16_t*)a.Y + (int64_t)b * a.sb + (int64_t)h * a.sh;
@@ -905,7 +915,8 @@ void decode_bf16(DecodeArgs a) {
     for (int p = tid; p < HG * Mp * CH; p += 64 * NW) {
         const int hh = p / (Mp * CH), r = p - hh * (Mp * CH);
         const int m = r / CH, ch = r % CH;
-        const uint16_t* Qh = (const uint16_t*)a.Q + (int64_t)b * a.q_bstride + (int64_t)(h0 + hh) * M * D;
+        const uint16_t* Qh = (const uint16_t*)a.Q + (int64_t)b * a.q_bstride + (int64_t)(h0 + hh) * Mt * D +
+                             (int64_t)a.m_off * D;
         u32x4 v = {0u, 0u, 0u, 0u};
         if (m < M) v = *(const u32x4*)(Qh + (int64_t)m * D + ch * 8);
         *(u32x4*)(dsm + hh * head_bytes + tile_off<D>(m, ch)) = v;
@@ -915,7 +926,7 @@ void decode_bf16(DecodeArgs a) {
     for (int e = tid; e < HG * Mp * (D / 4); e += 64 * NW) {
         const int hh = e / (Mp * (D / 4)), r = e - hh * (Mp * (D / 4));
         const int m = r / (D / 4), d = 4 * (r % (D / 4));
-        const ZT* Zh = (const ZT*)a.Z + (int64_t)(b * a.H + h0 + hh) * M * D;
+        const ZT* Zh = (const ZT*)a.Z + (int64_t)(b * a.H + h0 + hh) * Mt * D + (int64_t)a.m_off * D;
         float z4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (m < M) {
             if constexpr (sizeof(ZT) == 4) {
@@ -1105,12 +1116,9 @@ void decode_bf16(DecodeArgs a) {
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) tau[tb] = tacc[tb][0];
         };
-        run(nu);
-        bool low = false;
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) low |= !(tau[tb] >= kTauFloor);
-        if (wave_any(low)) {
-            // Exact per-token maxima over the latents, then recompute.
+        // Exact per-token maxima over the latents, then the sums against them.
+        float ex[TB];
+        auto exact_run = [&]() {
             float mx[TB];
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) mx[tb] = -INFINITY;
@@ -1128,10 +1136,59 @@ void decode_bf16(DecodeArgs a) {
                     for (int i = 0; i < 16; ++i) mx[tb] = fmaxf(mx[tb], S[i]);
                 }
             }
-            float ex[TB];
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) ex[tb] = pair_max(mx[tb]) * c;
             run(ex);
+        };
+        if constexpr (SPLIT > 0) {
+            exact_run();
+            // state of token l32 of block bk, in the accumulator's register layout
+            const int64_t pb = (int64_t)bh * nblk + bk;
+            float* py = a.part_y + pb * (32 * D) + 4 * lane;
+            float* pnt = a.part_nt + (pb * 32 + l32) * 2;
+            if constexpr (SPLIT == 1) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const f32x4 v = {yac[0][db][4 * g4], yac[0][db][4 * g4 + 1], yac[0][db][4 * g4 + 2],
+                                         yac[0][db][4 * g4 + 3]};
+                        *(f32x4*)(py + (db * 4 + g4) * 256) = v;
+                    }
+                if (hi == 0) {
+                    const f32x2 v = {ex[0], tau[0]};
+                    *(f32x2*)pnt = v;
+                }
+                return;
+            } else {
+                const f32x2 st = *(const f32x2*)pnt;
+                const float nm = fmaxf(st[0], ex[0]);
+                const float wa = exp2_fast(st[0] - nm), wb = exp2_fast(ex[0] - nm);
+                const float inv = __builtin_amdgcn_rcpf(fmaf(wa, st[1], wb * tau[0]));
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const f32x4 v = *(const f32x4*)(py + (db * 4 + g4) * 256);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = 4 * g4 + i;
+                            const float y = fmaf(wa, v[i], wb * yac[0][db][r]) * inv;
+                            if (r < 8)
+                                ypk[0][2 * db][r] = (__bf16)y;
+                            else
+                                ypk[0][2 * db + 1][r - 8] = (__bf16)y;
+                        }
+                    }
+                ypend = bk;
+                return;
+            }
+        } else {
+            run(nu);
+            bool low = false;
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) low |= !(tau[tb] >= kTauFloor);
+            if (wave_any(low)) exact_run();
         }
         // normalise and round; stored during the next block
 #pragma unroll
@@ -1208,7 +1265,8 @@ void decode_bf16(DecodeArgs a) {
 
 template <int D, int MBW, int WM, int WT>
 hipError_t launch_enc(const EncodeArgs& a, hipStream_t s) {
-    dim3 grid(a.heads_fast ? a.BH : a.C, a.heads_fast ? a.C : a.BH), block(64 * WM * WT);
+    const int z = (a.Mp / 32 + MBW * WM - 1) / (MBW * WM);  // latent groups
+    dim3 grid(a.heads_fast ? a.BH : a.C, a.heads_fast ? a.C : a.BH, z), block(64 * WM * WT);
     FLARE_LAUNCH((encode_partial_bf16<D, MBW, WM, WT>), grid, block, 0, s, a);
     return hipGetLastError();
 }
@@ -1336,10 +1394,26 @@ hipError_t allow_dec_lds(const void* fn) {
     return e;
 }
 
+// The two launches of the split decode (D = 128, M > 256).
+template <typename ZT>
+const void* dec_split_kernel(int split) {
+    if (split == 1) return (const void*)decode_bf16<128, 1, ZT, false, 0, kDecWaves, 1, 1>;
+    return (const void*)decode_bf16<128, 1, ZT, false, 0, kDecWaves, 1, 2>;
+}
+
+template <int D, int TB, typename ZT>
+const void* dec_fn(int M, int hg, int split) {
+    if constexpr (D == 128 && TB == 1) {
+        if (split) return dec_split_kernel<ZT>(split);
+    }
+    if (split) return nullptr;
+    return dec_kernel<D, TB, ZT>(M, hg);
+}
+
 template <int D, int TB, typename ZT>
 hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
     const int lds = dec_lds_bytes_bf16(a.Mp, D, a.hg);
-    const void* fn = dec_kernel<D, TB, ZT>(a.M, a.hg);
+    const void* fn = dec_fn<D, TB, ZT>(a.M, a.hg, a.split);
     if (!fn) return hipErrorInvalidValue;
     if (lds > 65536) {
         hipError_t e = allow_dec_lds(fn);
@@ -1377,19 +1451,20 @@ int enc_threads_bf16(EncCfg cfg) { return 64 * (cfg.wm == 0 ? 1 : cfg.wm) * cfg.
 // Resident decode workgroups per CU, from the kernel's occupancy at its LDS
 // size. Computed once per (D, tb, Z type, Mp) and cached: the query and the
 // attribute call cost more than a launch.
-int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32, int hg) {
+int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32, int hg, int split) {
     const int di = D == 32 ? 0 : D == 64 ? 1 : D == 128 ? 2 : -1;
     const int hi = hg == 1 ? 0 : hg == 2 ? 1 : hg == 4 ? 2 : -1;
     const int Mp = (M + 31) / 32 * 32;
-    if (di < 0 || hi < 0 || tb < 1 || tb > 2 || M < 1 || Mp > kBf16MaxM) return 1;
-    static std::atomic<int> cache[3][2][2][kBf16MaxM / 32][2][3];
-    std::atomic<int>& slot = cache[di][tb - 1][z_f32 ? 1 : 0][Mp / 32 - 1][M == Mp ? 1 : 0][hi];
+    if (di < 0 || hi < 0 || tb < 1 || tb > 2 || M < 1 || Mp > kBf16MaxM || split < 0 || split > 2) return 1;
+    static std::atomic<int> cache[3][2][2][kBf16MaxM / 32][2][3][3];
+    std::atomic<int>& slot = cache[di][tb - 1][z_f32 ? 1 : 0][Mp / 32 - 1][M == Mp ? 1 : 0][hi][split];
     const int known = slot.load(std::memory_order_relaxed);
     if (known > 0) return known;
     const int lds = dec_lds_bytes_bf16(Mp, D, hg);
     const void* fn = nullptr;
-#define FLARE_DEC_FN(DD, TB)                                                                                \
-    if (D == DD && tb == TB) fn = z_f32 ? dec_kernel<DD, TB, float>(M, hg) : dec_kernel<DD, TB, uint16_t>(M, hg);
+#define FLARE_DEC_FN(DD, TB)                                                                          \
+    if (D == DD && tb == TB)                                                                          \
+        fn = z_f32 ? dec_fn<DD, TB, float>(M, hg, split) : dec_fn<DD, TB, uint16_t>(M, hg, split);
     FLARE_DEC_FN(32, 1)
     FLARE_DEC_FN(32, 2)
     FLARE_DEC_FN(64, 1)

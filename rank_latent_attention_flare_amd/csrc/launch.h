@@ -119,6 +119,12 @@ struct DecodeArgs {
     int G;               // workgroups per (b, h) group of hg heads
     int tb;              // bf16: 32-token blocks per wave and step (1 or 2)
     int hg;              // bf16: heads per workgroup (a divisor of H; 1 unless token-major)
+    // Split decode (bf16, D = 128, M > 256): this launch's latent range
+    // [m_off, m_off + M) of Mtot, and the fp32 state between the two launches
+    int split;           // 0: whole range; 1: first launch; 2: second launch
+    int m_off, Mtot;
+    float* part_y;       // [BH][ceil(N/32)][32 * D] unnormalised Y of the first range
+    float* part_nt;      // [BH][ceil(N/32) * 32][2] its per-token (maximum, sum)
     float c;
 };
 
@@ -130,10 +136,13 @@ constexpr int kDecWaves = 4;  // waves per decode workgroup (fp32; bf16 default)
 // Largest M of the bf16 path: its decode unrolls every latent block. At
 // D = 128 the decode's LDS (Q and Z^T of the head) caps M at 256.
 constexpr int kBf16MaxM = 512;
-constexpr int kBf16MaxM128 = 256;
+constexpr int kBf16MaxM128 = 512;
+// At D = 128 the decode's LDS holds Q and Z^T for at most 256 latents; above
+// that it runs in two launches over the two latent ranges (split decode).
+constexpr int kDecSplitM128 = 256;
 int dec_tb_bf16(int D, int Mp);  // 32-token blocks per wave per step (the library's choice)
 bool dec_tb_built_bf16(int D, int Mp, int tb);  // whether a decode with tb blocks is built for (D, Mp)
-int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32, int hg);  // resident decode workgroups per CU (cached)
+int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32, int hg, int split);  // resident decode workgroups per CU (cached)
 int dec_lds_bytes_bf16(int Mp, int D, int hg);
 int dec_waves_bf16(int D, int M, int tb, int hg);  // waves per bf16 decode workgroup
 // Heads per bf16 decode workgroup: groups of 2 or 4 heads in the token-major

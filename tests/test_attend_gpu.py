@@ -23,6 +23,7 @@ CASES = [
     # exact latent counts with token-major queries: head groups per workgroup
     (1, 4, 3001, 128, 32, "bf16"),
     (2, 2, 1999, 64, 64, "bf16"),
+    (1, 2, 1200, 320, 128, "bf16"),  # split decode (D = 128, M > 256)
     (1, 3, 3000, 40, 8, "f32"),
     (1, 2, 500, 300, 32, "f32"),
 ]

@@ -40,6 +40,7 @@ CASES = [
     (1, 6, 2049, 128, 64, "bf16"),
     (1, 2, 3001, 256, 64, "bf16"),
     (1, 3, 1500, 64, 64, "bf16"),  # H odd: one head per workgroup
+    (1, 2, 1000, 400, 128, "bf16"),  # split decode (D = 128, M > 256)
 ]
 
 

@@ -53,6 +53,10 @@ SMALL = [
     # 512 (eight-wave workgroups), ragged tokens
     (1, 2, 3001, 256, 64, "bf16"),
     (1, 1, 2500, 512, 64, "bf16"),
+    # D = 128 beyond 256 latents: encode workgroups over two latent groups,
+    # decode in two launches over the latent ranges (the second ragged at 300)
+    (1, 2, 1500, 512, 128, "bf16"),
+    (2, 1, 777, 300, 128, "bf16"),
 ]
 
 
