@@ -236,10 +236,11 @@ flare_status flare_attend(const void* q, const void* Z, void* Y,
  * Q, Z and dZ being rounded to nearest-even bf16 where they become MFMA
  * operands; other bf16 heads run fp32 arithmetic on the widened inputs.
  * It recomputes the forward's encode internally; nothing N x M is stored.
- * Supported for D in {8, 16, 24, 32, 48, 64} (bf16: 32 and 64) with the
- * forward's M range; otherwise FLARE_ERR_UNSUPPORTED. Outputs may not overlap inputs or each
- * other. The _ws variant takes flare_workspace_size(FLARE_OP_BACKWARD, ...)
- * bytes of caller-owned scratch memory. */
+ * Supported for D in {8, 16, 24, 32, 48, 64, 96, 128} (bf16: 32, 64 and
+ * 128) with the forward's M range; otherwise FLARE_ERR_UNSUPPORTED. Outputs
+ * may not overlap inputs or each other. The _ws variant takes
+ * flare_workspace_size(FLARE_OP_BACKWARD, ...) bytes of caller-owned
+ * scratch memory. */
 flare_status flare_backward(const void* Q, const void* K, const void* V, const void* dY,
                             void* dQ, void* dK, void* dV,
                             int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
@@ -248,6 +249,19 @@ flare_status flare_backward_ws(const void* Q, const void* K, const void* V, cons
                                void* dQ, void* dK, void* dV,
                                int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
                                flare_dtype dtype, hipStream_t stream, void* workspace, size_t ws_bytes);
+
+/* flare_backward with a token layout: K, V, dY, dK and dV are [B][H][N][D]
+ * (FLARE_LAYOUT_BHND) or token-major [B][N][H][D] (FLARE_LAYOUT_BNHD); Q
+ * and dQ stay [H][M][D]. Same kernels with token rows addressed through the
+ * layout's stride, so the gradients equal flare_backward's on the same
+ * values bit for bit. workspace == NULL with ws_bytes == 0: the library
+ * allocates (stream-ordered); otherwise flare_workspace_size(
+ * FLARE_OP_BACKWARD, ...) bytes, as for flare_backward_ws. */
+flare_status flare_backward_ex(const void* Q, const void* K, const void* V, const void* dY,
+                               void* dQ, void* dK, void* dV,
+                               int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                               flare_dtype dtype, flare_layout layout, hipStream_t stream,
+                               void* workspace, size_t ws_bytes);
 
 /* Backward of flare_pp_forward (FLARE++ skill page, "Core Mechanism"; FLARE++
  * abstract: Q' = Q + encode(Q, K, V), then the FLARE forward with Q'). The
@@ -270,6 +284,13 @@ flare_status flare_pp_backward_ws(const void* Q, const void* K, const void* V, c
                                   int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
                                   flare_dtype dtype, hipStream_t stream,
                                   void* workspace, size_t workspace_bytes);
+/* flare_pp_backward with a token layout, as flare_backward_ex (workspace:
+ * flare_workspace_size(FLARE_OP_PP_BACKWARD, ...) bytes, or NULL and 0). */
+flare_status flare_pp_backward_ex(const void* Q, const void* K, const void* V, const void* dY,
+                                  void* dQ, void* dK, void* dV,
+                                  int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                  flare_dtype dtype, flare_layout layout, hipStream_t stream,
+                                  void* workspace, size_t ws_bytes);
 
 /* Static text for a status code. */
 const char* flare_status_string(flare_status s);

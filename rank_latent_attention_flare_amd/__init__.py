@@ -6,14 +6,14 @@ script and the Python binding with the same entry-point names.
 """
 from .flare import (FLARE_BF16, FLARE_F32, FLARE_LAYOUT_BHND, FLARE_LAYOUT_BNHD, FLARE_OP_BACKWARD,
                     FLARE_OP_DECODE, FLARE_OP_ENCODE, FLARE_OP_FORWARD, FLARE_OP_PP_BACKWARD, FLARE_OP_PP_FORWARD,
-                    FLARE_OP_PP_QUERIES, FlareError, flare_attend, flare_backward, flare_copy_kernel, flare_decode,
+                    FLARE_OP_PP_QUERIES, FlareError, flare_attend, flare_backward, flare_backward_ex, flare_copy_kernel, flare_decode,
                     flare_decode_ex, flare_describe_plan, flare_encode, flare_encode_ex, flare_forward,
-                    flare_forward_ex, flare_pp_backward, flare_pp_forward, flare_pp_forward_ex, flare_pp_queries,
+                    flare_forward_ex, flare_pp_backward, flare_pp_backward_ex, flare_pp_forward, flare_pp_forward_ex, flare_pp_queries,
                     flare_timing_enable, flare_timing_read, flare_workspace_size, lib, workspace_for)
 
 __all__ = ["FLARE_BF16", "FLARE_F32", "FLARE_LAYOUT_BHND", "FLARE_LAYOUT_BNHD", "FLARE_OP_BACKWARD",
            "FLARE_OP_DECODE", "FLARE_OP_ENCODE", "FLARE_OP_FORWARD", "FLARE_OP_PP_BACKWARD", "FLARE_OP_PP_FORWARD",
-           "FLARE_OP_PP_QUERIES", "FlareError", "flare_attend", "flare_backward", "flare_copy_kernel", "flare_decode",
+           "FLARE_OP_PP_QUERIES", "FlareError", "flare_attend", "flare_backward", "flare_backward_ex", "flare_copy_kernel", "flare_decode",
            "flare_decode_ex", "flare_describe_plan", "flare_encode", "flare_encode_ex", "flare_forward",
-           "flare_forward_ex", "flare_pp_backward", "flare_pp_forward", "flare_pp_forward_ex", "flare_pp_queries",
+           "flare_forward_ex", "flare_pp_backward", "flare_pp_backward_ex", "flare_pp_forward", "flare_pp_forward_ex", "flare_pp_queries",
            "flare_timing_enable", "flare_timing_read", "flare_workspace_size", "lib", "workspace_for"]

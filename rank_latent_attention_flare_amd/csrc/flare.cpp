@@ -661,6 +661,7 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
                         (float*)(ws + p.off_zsig));
     flare::BackwardArgs a{};
     a.Q = Q; a.K = K; a.V = V; a.dY = dY; a.dQ = dQ; a.dK = dK; a.dV = dV;
+    a.sb = p.sb; a.sh = p.sh; a.sn = p.sn;
     a.Z = (const float*)(ws + p.off_z);
     a.zmu = (const float*)(ws + p.off_zmu);
     a.zsig = (const float*)(ws + p.off_zsig);
@@ -765,16 +766,16 @@ flare_status finish(flare_status res, hipError_t e, bool alloc, void* wsv, hipSt
 }
 
 flare_status backward(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK, void* dV,
-                      int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dt, hipStream_t s,
-                      void* wsv, size_t ws_bytes, bool alloc) {
+                      int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dt, flare_layout layout,
+                      hipStream_t s, void* wsv, size_t ws_bytes, bool alloc) {
     Plan p;
     g_last_error.clear();
     flare_status st = make_plan(B, H, N, M, D, dt, &p);
     if (st != FLARE_OK) return st;
-    st = set_layout(&p, FLARE_LAYOUT_BHND);
+    st = set_layout(&p, layout);
     if (st != FLARE_OK) return st;
     if (!flare::backward_supports(int(D)))
-        return fail(FLARE_ERR_UNSUPPORTED, "the backward supports D in {8, 16, 24, 32, 48, 64}");
+        return fail(FLARE_ERR_UNSUPPORTED, "the backward supports D in {8, 16, 24, 32, 48, 64, 96, 128}");
     st = check_backward_ptrs(p, Q, K, V, dY, dQ, dK, dV);
     if (st != FLARE_OK) return st;
     st = get_workspace(p.total[FLARE_OP_BACKWARD], s, wsv, ws_bytes, alloc);
@@ -784,18 +785,17 @@ flare_status backward(const void* Q, const void* K, const void* V, const void* d
 }
 
 flare_status pp_backward(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK, void* dV,
-                         int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dt, hipStream_t s,
-                         void* wsv, size_t ws_bytes, bool alloc) {
+                         int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dt, flare_layout layout,
+                         hipStream_t s, void* wsv, size_t ws_bytes, bool alloc) {
     Plan pf, p1;
     g_last_error.clear();
     flare_status st = make_plan(B, H, N, M, D, dt, &pf);
     if (st != FLARE_OK) return st;
     st = make_plan(1, H, N, M, D, dt, &p1);
     if (st != FLARE_OK) return st;
-    if ((st = set_layout(&pf, FLARE_LAYOUT_BHND)) != FLARE_OK || (st = set_layout(&p1, FLARE_LAYOUT_BHND)) != FLARE_OK)
-        return st;
+    if ((st = set_layout(&pf, layout)) != FLARE_OK || (st = set_layout(&p1, layout)) != FLARE_OK) return st;
     if (!flare::backward_supports(int(D)))
-        return fail(FLARE_ERR_UNSUPPORTED, "the backward supports D in {8, 16, 24, 32, 48, 64}");
+        return fail(FLARE_ERR_UNSUPPORTED, "the backward supports D in {8, 16, 24, 32, 48, 64, 96, 128}");
     st = check_backward_ptrs(pf, Q, K, V, dY, dQ, dK, dV);
     if (st != FLARE_OK) return st;
     const PPLayout L = pp_layout(pf, p1);
@@ -803,7 +803,8 @@ flare_status pp_backward(const void* Q, const void* K, const void* V, const void
     if (st != FLARE_OK) return st;
     char* ws = (char*)wsv;
     const bool bf = dt == FLARE_BF16;
-    const size_t e = pf.esize, qm = size_t(H) * M * D, tok = size_t(H) * N * D;  // per batch entry
+    // per batch entry (one entry's token rows are contiguous in both layouts)
+    const size_t e = pf.esize, qm = size_t(H) * M * D, tok = size_t(H) * N * D;
     // Q' = Q + encode(Q, K, V) for every batch entry
     hipError_t err = run_encode_partial(pf, Q, 0, K, V, ws, s);
     if (err == hipSuccess) err = run_combine(pf, flare::COMBINE_QPRIME, Q, ws + L.qp, ws, s);
@@ -833,25 +834,41 @@ extern "C" {
 flare_status flare_backward(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK,
                             void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
                             hipStream_t stream) {
-    return backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, stream, nullptr, 0, true);
+    return backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, nullptr, 0, true);
 }
 
 flare_status flare_backward_ws(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK,
                                void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
                                hipStream_t stream, void* workspace, size_t ws_bytes) {
-    return backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, stream, workspace, ws_bytes, false);
+    return backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, workspace, ws_bytes,
+                    false);
 }
 
 flare_status flare_pp_backward(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK,
                                void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
                                hipStream_t stream) {
-    return pp_backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, stream, nullptr, 0, true);
+    return pp_backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, nullptr, 0, true);
 }
 
 flare_status flare_pp_backward_ws(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK,
                                   void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
                                   hipStream_t stream, void* workspace, size_t ws_bytes) {
-    return pp_backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, stream, workspace, ws_bytes, false);
+    return pp_backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, FLARE_LAYOUT_BHND, stream, workspace, ws_bytes,
+                       false);
+}
+
+flare_status flare_backward_ex(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK,
+                               void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
+                               flare_layout layout, hipStream_t stream, void* workspace, size_t ws_bytes) {
+    const bool alloc = !workspace && ws_bytes == 0;
+    return backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, layout, stream, workspace, ws_bytes, alloc);
+}
+
+flare_status flare_pp_backward_ex(const void* Q, const void* K, const void* V, const void* dY, void* dQ, void* dK,
+                                  void* dV, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, flare_dtype dtype,
+                                  flare_layout layout, hipStream_t stream, void* workspace, size_t ws_bytes) {
+    const bool alloc = !workspace && ws_bytes == 0;
+    return pp_backward(Q, K, V, dY, dQ, dK, dV, B, H, N, M, D, dtype, layout, stream, workspace, ws_bytes, alloc);
 }
 
 flare_status flare_attend(const void* q, const void* Z, void* Y, int64_t B, int64_t H, int64_t N, int64_t M,

@@ -72,6 +72,14 @@ __device__ __forceinline__ float half_dot(const float (&a)[H2], const float* b) 
     return s;
 }
 
+// Element offset of head bh's token 0 in K, V, dY, dK and dV (token rows
+// are a.sn elements apart: D in the [B][H][N][D] layout, H * D in the
+// token-major [B][N][H][D] one).
+__device__ __forceinline__ int64_t head_base(const BackwardArgs& a, int bh) {
+    const int b = bh / a.H;
+    return b * a.sb + (bh - b * a.H) * a.sh;
+}
+
 constexpr int kTokPerBlock = 128;  // token kernels: 256 threads, a lane pair per token
 constexpr int kTile = 64;          // latent kernels: tokens staged per LDS tile
 
@@ -90,8 +98,9 @@ __global__ __launch_bounds__(256) void bw_stats(BackwardArgs a) {
     const int nn = min(n, N - 1);
     const T* Qh = (const T*)a.Q + (int64_t)h * M * D + half * H2;
     const float* Zb = a.Z + (int64_t)bh * M * D + half * H2;
-    const T* kr = (const T*)a.K + ((int64_t)bh * N + nn) * D + half * H2;
-    const T* gr = (const T*)a.dY + ((int64_t)bh * N + nn) * D + half * H2;
+    const int64_t row = head_base(a, bh) + nn * a.sn + half * H2;
+    const T* kr = (const T*)a.K + row;
+    const T* gr = (const T*)a.dY + row;
     float k[H2], g[H2];
 #pragma unroll
     for (int i = 0; i < H2; ++i) {
@@ -128,14 +137,15 @@ __global__ __launch_bounds__(256) void bw_stats(BackwardArgs a) {
 
 // ---------------------------------------------------------------------------
 // Latent kernels: grid (chunks C, B*H, latent groups of 128). The chunk's
-// tokens pass through LDS in tiles of 64: K and dY (and V for dQ) as fp32
-// rows, with the per-token statistics. A lane pair owns one latent.
+// tokens pass through LDS in tiles of 64 (32 above D = 64): K and dY (and V
+// for dQ) as fp32 rows, with the per-token statistics. A lane pair owns one
+// latent.
 // ---------------------------------------------------------------------------
 template <int D, typename T, bool DQ>
 __global__ __launch_bounds__(256) void bw_latent(BackwardArgs a) {
-    constexpr int H2 = D / 2;
-    __shared__ float kt[kTile * D], gt[kTile * D], vt[DQ ? kTile * D : 1];
-    __shared__ float snu[kTile], stau[kTile], sdel[kTile];
+    constexpr int H2 = D / 2, TL = D > 64 ? kTile / 2 : kTile;  // at most 48 KB of tiles
+    __shared__ float kt[TL * D], gt[TL * D], vt[DQ ? TL * D : 1];
+    __shared__ float snu[TL], stau[TL], sdel[TL];
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
     const int chunk = blockIdx.x, bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M;
@@ -164,11 +174,11 @@ __global__ __launch_bounds__(256) void bw_latent(BackwardArgs a) {
         sig = a.zsig[r];
         gam = a.gam[r];
     }
-    const int64_t tok0 = (int64_t)bh * N;
-    for (int t0 = n0; t0 < n1; t0 += kTile) {
-        const int nt = min(kTile, n1 - t0);
+    const int64_t tok0 = (int64_t)bh * N, hb = head_base(a, bh);
+    for (int t0 = n0; t0 < n1; t0 += TL) {
+        const int nt = min(TL, n1 - t0);
         for (int e = tid; e < nt * D; e += 256) {
-            const int64_t g = (tok0 + t0) * D + e;
+            const int64_t g = hb + (t0 + e / D) * a.sn + e % D;
             kt[e] = ld<T>((const T*)a.K + g);
             gt[e] = ld<T>((const T*)a.dY + g);
             if constexpr (DQ) vt[e] = ld<T>((const T*)a.V + g);
@@ -209,25 +219,26 @@ __global__ __launch_bounds__(256) void bw_latent(BackwardArgs a) {
 }
 
 // dZ = sum over chunks of the partials, and gam[m] = <dZ[m], Z[m]>.
-// One wave per (b, h, m): lane d sums the chunks of column d (all chunks'
-// loads in flight together), then the wave reduces gam.
+// One wave per (b, h, m): lane d sums the chunks of columns d, d + 64, ...
+// (all chunks' loads in flight together), then the wave reduces gam.
 __global__ __launch_bounds__(256) void bw_dz_combine(BackwardArgs a) {
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // bh * M + m
-    const int d = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63;
     if (r >= (int64_t)a.BH * a.M) return;
     const int bh = (int)(r / a.M), m = (int)(r - (int64_t)bh * a.M);
     const int D = a.D, C = a.C;
-    float s = 0.0f, gz = 0.0f;
-    if (d < D) {
+    float gz = 0.0f;
+    for (int d = lane; d < D; d += 64) {
+        float s = 0.0f;
         const float* p = a.part + ((int64_t)bh * C * a.M + m) * D + d;
         const int64_t step = (int64_t)a.M * D;
         for (int ch = 0; ch < C; ++ch) s += p[ch * step];
         a.dZ[r * D + d] = s;
-        gz = s * a.Z[r * D + d];
+        gz = fmaf(s, a.Z[r * D + d], gz);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) gz += __shfl_xor(gz, off, 64);
-    if (d == 0) a.gam[r] = gz;
+    if (lane == 0) a.gam[r] = gz;
 }
 
 // dQ[h] = sum over the batch and the chunks of the partials (already scaled
@@ -267,7 +278,7 @@ __global__ __launch_bounds__(256) void bw_dkdv(BackwardArgs a) {
     const int n = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6) * 32 + (lane & 31);
     const int N = a.N, M = a.M;
     const int nn = min(n, N - 1);
-    const int64_t row = ((int64_t)bh * N + nn) * D + half * H2;
+    const int64_t row = head_base(a, bh) + nn * a.sn + half * H2;
     float k[H2], v[H2], g[H2], dk[H2], dv[H2];
 #pragma unroll
     for (int i = 0; i < H2; ++i) {
@@ -384,8 +395,9 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
     if (lane == 0) red[wave] = mz;
     __syncthreads();
     const float nub = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) + 32.0f;
-    const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
-    const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
+    const int64_t sn = a.sn;
+    const uint16_t* Kb = (const uint16_t*)a.K + head_base(a, bh);
+    const uint16_t* Gb = (const uint16_t*)a.dY + head_base(a, bh);
     const int nblk = (N + 31) / 32, bstep = gridDim.x * 4;
     int blk = blockIdx.x * 4 + wave;
     if (!FDZ && blk >= nblk) return;  // no barrier follows (FDZ: the waves merge at the end)
@@ -397,8 +409,8 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
         const int nn = min(bk * 32 + l32, N - 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            ko[kb] = *(const bf16x8*)(Kb + (int64_t)nn * D + 16 * kb + 8 * hi);
-            go[kb] = *(const bf16x8*)(Gb + (int64_t)nn * D + 16 * kb + 8 * hi);
+            ko[kb] = *(const bf16x8*)(Kb + nn * sn + 16 * kb + 8 * hi);
+            go[kb] = *(const bf16x8*)(Gb + nn * sn + 16 * kb + 8 * hi);
         }
     };
     load(min(blk, nblk - 1), kpf, gpf);
@@ -636,9 +648,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1
         gam[m] = m < M ? a.gam[r] : 0.0f;
     }
     __syncthreads();
-    const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
-    const uint16_t* Vb = (const uint16_t*)a.V + (int64_t)bh * N * D;
-    const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
+    const int64_t sn = a.sn, hb = head_base(a, bh);
+    const uint16_t* Kb = (const uint16_t*)a.K + hb;
+    const uint16_t* Vb = (const uint16_t*)a.V + hb;
+    const uint16_t* Gb = (const uint16_t*)a.dY + hb;
     const int g = lane >> 4, gi = lane & 15;
     const int prow = enc_row_token(l32);
     const int nblk = (N + 31) / 32, bstep = gridDim.x * 4;
@@ -659,7 +672,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1
         const int nn = min(bk * 32 + l32, N - 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const int64_t o = (int64_t)nn * D + 16 * kb + 8 * hi;
+            const int64_t o = nn * sn + 16 * kb + 8 * hi;
             kpf[kb] = *(const bf16x8*)(Kb + o);
             vpf[kb] = *(const bf16x8*)(Vb + o);
             if constexpr (!ENC) gpf[kb] = *(const bf16x8*)(Gb + o);
@@ -691,7 +704,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1
                 for (int i = 0; i < D / 16; ++i) {
                     const int byte = i * 1024 + 16 * lane;
                     const int row = byte / (2 * D), col = byte % (2 * D);
-                    const int64_t go = ((int64_t)bh * N + min(blk * 32 + row, N - 1)) * 2 * D + col;
+                    const int64_t go = (hb + min(blk * 32 + row, N - 1) * sn) * 2 + col;
                     __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.dK + go),
                                                      (void*)(oldk + i * 1024), 16, 0, 0);
                     __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.dV + go),
@@ -817,8 +830,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1
         // values, so the stores are unconditional and the next wait stays
         // exact
         {
-            uint16_t* dK = (uint16_t*)a.dK + ((int64_t)bh * N + nn) * D;
-            uint16_t* dV = (uint16_t*)a.dV + ((int64_t)bh * N + nn) * D;
+            uint16_t* dK = (uint16_t*)a.dK + hb + nn * sn;
+            uint16_t* dV = (uint16_t*)a.dV + hb + nn * sn;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -961,9 +974,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[j][db] = f32x16{};
     }
-    const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)bh * N * D;
-    const uint16_t* Vb = (const uint16_t*)a.V + (int64_t)bh * N * D;
-    const uint16_t* Gb = (const uint16_t*)a.dY + (int64_t)bh * N * D;
+    const int64_t sn = a.sn;
+    const uint16_t* Kb = (const uint16_t*)a.K + head_base(a, bh);
+    const uint16_t* Vb = (const uint16_t*)a.V + head_base(a, bh);
+    const uint16_t* Gb = (const uint16_t*)a.dY + head_base(a, bh);
     const float* nub = a.nu + (int64_t)bh * N;
     const float* delb = a.del + (int64_t)bh * N;
     const int prow = enc_row_token(l32);
@@ -982,7 +996,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         const int nv = n1 - t, tn = t + min(prow, nv - 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const int64_t o = (int64_t)tn * D + 16 * kb + 8 * hi;
+            const int64_t o = tn * sn + 16 * kb + 8 * hi;
             kP[kb] = *(const bf16x8*)(Kb + o);
             if constexpr (!ENC) gP[kb] = *(const bf16x8*)(Gb + o);
             if constexpr (DQ) vP[kb] = *(const bf16x8*)(Vb + o);
@@ -1146,6 +1160,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         case 32: return FN<32>(a, s);    \
         case 48: return FN<48>(a, s);    \
         case 64: return FN<64>(a, s);    \
+        case 96: return FN<96>(a, s);    \
+        case 128: return FN<128>(a, s);  \
         default: return hipErrorInvalidValue; \
     }
 
@@ -1282,7 +1298,9 @@ hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-bool backward_supports(int D) { return D == 8 || D == 16 || D == 24 || D == 32 || D == 48 || D == 64; }
+bool backward_supports(int D) {
+    return D == 8 || D == 16 || D == 24 || D == 32 || D == 48 || D == 64 || D == 96 || D == 128;
+}
 
 hipError_t launch_bw_stats(const BackwardArgs& a, hipStream_t s) { FLARE_BW_DISPATCH(stats_d, a, s) }
 hipError_t launch_bw_dz(const BackwardArgs& a, hipStream_t s) { FLARE_BW_DISPATCH(dz_d, a, s) }

@@ -79,16 +79,17 @@ struct CombineArgs {
     float* zsig;         // optional [BH][M]: merged sums sig* against mu*
 };
 
-// Backward of the FLARE forward ([B][H][N][D] layout). Storage of Q, K, V,
-// dY, dQ, dK, dV is the operator dtype; everything else is fp32 workspace.
+// Backward of the FLARE forward. Storage of Q, K, V, dY, dQ, dK, dV is the
+// operator dtype; everything else is fp32 workspace.
 struct BackwardArgs {
     const void* Q;       // [H][M][D]
-    const void* K;       // [B][H][N][D]
+    const void* K;       // [B][H][N][D] or [B][N][H][D] (strides below)
     const void* V;
     const void* dY;
     void* dQ;            // [H][M][D]
-    void* dK;            // [B][H][N][D]
+    void* dK;            // same layout as K
     void* dV;
+    int64_t sb, sh, sn;  // K, V, dY, dK, dV strides in elements: batch, head, token
     const float* Z;      // [BH][M][D] forward encode output
     const float* zmu;    // [BH][M] its offsets mu* (log2 units)
     const float* zsig;   // [BH][M] and sums sig*

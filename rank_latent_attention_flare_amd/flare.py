@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.flare_pp_backward.restype = ctypes.c_int
         L.flare_pp_backward_ws.argtypes = bw + [_vp, ctypes.c_size_t]
         L.flare_pp_backward_ws.restype = ctypes.c_int
+        for name in ("flare_backward_ex", "flare_pp_backward_ex"):
+            getattr(L, name).argtypes = bw[:13] + [ctypes.c_int, _vp, _vp, ctypes.c_size_t]
+            getattr(L, name).restype = ctypes.c_int
         L.flare_forward_noalloc.argtypes = base
         L.flare_forward_noalloc.restype = ctypes.c_int
         L.flare_attend.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
@@ -289,6 +292,41 @@ def flare_pp_backward(Q, K, V, dY, stream=None, workspace=None, out=None):
     else:
         _raise(lib().flare_pp_backward_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size()))
     return dQ, dK, dV
+
+
+def _backward_ex(name: str, Q, K, V, dY, layout: int, stream, workspace, out):
+    if layout == FLARE_LAYOUT_BHND:
+        B, H, N, M, D = _dims(FLARE_OP_FORWARD, Q, K, V)
+        tok = (B, H, N, D)
+    else:
+        if Q.dim() != 3 or K.dim() != 4:
+            raise ValueError("expected Q [H, M, D] and K, V, dY [B, N, H, D]")
+        H, M, D = Q.shape
+        B, N = K.shape[:2]
+        tok = (B, N, H, D)
+    for t in (K, V, dY):
+        if tuple(t.shape) != tok or t.dtype != Q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"K, V and dY must be contiguous {Q.dtype} device tensors of shape {tok}")
+    if not Q.is_cuda or not Q.is_contiguous():
+        raise ValueError("Q must be a contiguous device tensor")
+    if out is None:
+        out = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    dQ, dK, dV = out
+    ws, nws = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    _raise(getattr(lib(), name)(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dY.data_ptr(), dQ.data_ptr(),
+                                dK.data_ptr(), dV.data_ptr(), B, H, N, M, D, dtype_code(Q.dtype), layout,
+                                _stream(stream), ws, nws))
+    return dQ, dK, dV
+
+
+def flare_backward_ex(Q, K, V, dY, layout, stream=None, workspace=None, out=None):
+    """flare_backward with K, V, dY (and dK, dV) in `layout` ([B, N, H, D] with FLARE_LAYOUT_BNHD)."""
+    return _backward_ex("flare_backward_ex", Q, K, V, dY, layout, stream, workspace, out)
+
+
+def flare_pp_backward_ex(Q, K, V, dY, layout, stream=None, workspace=None, out=None):
+    """flare_pp_backward with K, V, dY (and dK, dV) in `layout`."""
+    return _backward_ex("flare_pp_backward_ex", Q, K, V, dY, layout, stream, workspace, out)
 
 
 def flare_workspace_size(op: int, B: int, H: int, N: int, M: int, D: int, dtype: torch.dtype) -> int:

@@ -206,11 +206,20 @@ def test_backward_validates_before_launch():
     assert fn(*a) == INVALID and "null" in F.lib().flare_last_error().decode()
     a = list(ok); a[5] = PK  # dK aliases K
     assert fn(*a) == INVALID and "overlap" in F.lib().flare_last_error().decode()
-    a = list(ok); a[11] = 128  # D = 128: no backward
+    a = list(ok); a[11] = 256  # D = 256: neither forward nor backward
+    assert fn(*a) == UNSUPPORTED
+    a = list(ok); a[11] = 96  # bf16 has no D = 96
     assert fn(*a) == UNSUPPORTED
     ws = F.lib().flare_workspace_size(F.FLARE_OP_BACKWARD, 1, 2, 100, 64, 32, F.FLARE_BF16)
     assert ws >= F.lib().flare_workspace_size(F.FLARE_OP_FORWARD, 1, 2, 100, 64, 32, F.FLARE_BF16) > 0
     assert F.lib().flare_backward_ws(*ok, PW, 256) == INVALID
+    # the layout variant: a bad layout, and the same checks as the plain entry
+    ex = F.lib().flare_backward_ex
+    assert ex(*ok[:13], 7, None, None, 0) == INVALID and "layout" in F.lib().flare_last_error().decode()
+    a = list(ok); a[5] = PK
+    assert ex(*a[:13], F.FLARE_LAYOUT_BNHD, None, None, 0) == INVALID
+    assert ex(*ok[:13], F.FLARE_LAYOUT_BNHD, None, PW, 256) == INVALID
+    assert "workspace" in F.lib().flare_last_error().decode()
 
 
 def test_pp_backward_validates_before_launch():
@@ -221,8 +230,12 @@ def test_pp_backward_validates_before_launch():
     assert fn(*a) == INVALID and "null" in F.lib().flare_last_error().decode()
     a = list(ok); a[4] = PQ + 64  # dQ overlaps Q
     assert fn(*a) == INVALID and "overlap" in F.lib().flare_last_error().decode()
-    a = list(ok); a[11] = 128  # D = 128: no backward
+    a = list(ok); a[11] = 256  # D = 256: neither forward nor backward
     assert fn(*a) == UNSUPPORTED
+    ex = F.lib().flare_pp_backward_ex
+    assert ex(*ok[:13], 7, None, None, 0) == INVALID and "layout" in F.lib().flare_last_error().decode()
+    a = list(ok); a[4] = PQ + 64
+    assert ex(*a[:13], F.FLARE_LAYOUT_BNHD, None, None, 0) == INVALID
     # its workspace holds a FLARE backward's plus Q', dQ', a zero dY and the first stage's dQ
     args = (2, 2, 100, 64, 32, F.FLARE_BF16)
     ws = F.lib().flare_workspace_size(F.FLARE_OP_PP_BACKWARD, *args)

@@ -105,3 +105,46 @@ def test_head_groups_equal_plain_layout(hg, case):
     assert torch.equal(out.transpose(1, 2).contiguous().view(torch.int16), ref.view(torch.int16))
     assert_parity(to_host64(out.transpose(1, 2).contiguous()), oracle.forward(Q, K, V)[0], "bf16",
                   f"head groups {hg} {case}")
+
+
+BW_CASES = [
+    # B, H, N, M, D, dtype: the matrix-core kernels (D = 32 with the fused
+    # latent partials, D = 64), bf16 on the fp32 kernels (M = 300 at D = 64,
+    # D = 128), and fp32 storage
+    (2, 3, 1000, 64, 32, "bf16"),
+    (1, 2, 777, 33, 64, "bf16"),
+    (2, 2, 900, 200, 64, "bf16"),
+    (1, 2, 500, 300, 64, "bf16"),
+    (1, 2, 400, 40, 128, "bf16"),
+    (2, 3, 500, 17, 16, "f32"),
+    (1, 2, 300, 24, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("pp", [False, True], ids=["flare", "flare_pp"])
+@pytest.mark.parametrize("case", BW_CASES, ids=case_id)
+def test_backward_token_major_equals_plain_layout(pp, case):
+    B, H, N, M, D, dt = case
+    seed = zlib.crc32(repr(("layout-backward", pp) + case).encode()) % 100000
+    Q, K, V = make_inputs(B, H, N, M, D, dt, q_scale=0.5, seed=seed)
+    dY = make_inputs(B, H, N, M, D, dt, seed=seed + 1)[2]
+    print(f"[layout] backward pp={pp} case={case_id(case)} seed={seed}", flush=True)
+    q, k, v, g = to_dev(Q), to_dev(K), to_dev(V), to_dev(dY)
+    plain = F.flare_pp_backward if pp else F.flare_backward
+    ex = F.flare_pp_backward_ex if pp else F.flare_backward_ex
+    ref = plain(q, k, v, g)
+    got = ex(q, token_major(k), token_major(v), token_major(g), F.FLARE_LAYOUT_BNHD)
+    op = F.FLARE_OP_PP_BACKWARD if pp else F.FLARE_OP_BACKWARD
+    ws = torch.empty(F.flare_workspace_size(op, B, H, N, M, D, q.dtype), dtype=torch.uint8, device="cuda")
+    got_ws = ex(q, token_major(k), token_major(v), token_major(g), F.FLARE_LAYOUT_BNHD, workspace=ws)
+    same = ex(q, k, v, g, F.FLARE_LAYOUT_BHND)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dt == "bf16" else torch.int32
+    assert torch.equal(got[0].view(bits), ref[0].view(bits)), "dQ"
+    for i, name in ((1, "dK"), (2, "dV")):
+        assert tuple(got[i].shape) == (B, N, H, D)
+        assert torch.equal(got[i].transpose(1, 2).contiguous().view(bits), ref[i].view(bits)), name
+    for x, y in zip(got_ws, got):
+        assert torch.equal(x, y)
+    for x, y in zip(same, ref):
+        assert torch.equal(x, y)
