@@ -684,10 +684,10 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     // skip the decode term and need no per-token statistics; the fp32
     // kernels compute the full formula with the caller's dY = 0.
     a.enc_only = mc && dz_given;
-    // bf16 at D = 32 (M <= 128), and for dZ also at D = 64 (M <= 64): the
-    // token-side kernels also form the latent-side partials (dZ in the
-    // statistics kernel, dQ in the dK/dV kernel), one per workgroup, in fz
-    // and fq chunk slots
+    // bf16 at D = 32 (M <= 128) and D = 64 (M <= 64): the token-side
+    // kernels also form the latent-side partials (dZ in the statistics
+    // kernel, dQ in the dK/dV kernel), one per workgroup, in fz and fq chunk
+    // slots
     const int fz = mc ? flare::bw_fused_dz_groups(a) : 0;
     const int fq = mc ? flare::bw_fused_dq_groups(a) : 0;
     if (e == hipSuccess && !a.enc_only)

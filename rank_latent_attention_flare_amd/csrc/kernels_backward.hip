@@ -595,9 +595,10 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
 // are exactly the k-slots of the B operand of the accumulations dK^T += Q^T dl
 // and dV^T += dZ^T A, whose A operands are read transposed from the natural
 // row-major LDS rows.
-// FDQ (bf16, D = 32, M <= 128): the same kernel also forms dQ's partial sums,
-// dQ^T[d][m] += K^T[d][n] dl[m][n] over the workgroup's tokens, so that no
-// separate latent-side pass over K, V and dY is needed for dQ.
+// FDQ (bf16, M <= 32 MBX: 128 at D = 32, 64 at D = 64): the same kernel
+// also forms dQ's partial sums, dQ^T[d][m] += K^T[d][n] dl[m][n] over the
+// workgroup's tokens, so that no separate latent-side pass over K, V and dY
+// is needed for dQ.
 // 8 bytes from LDS in inline asm that waits for its own result (the data
 // came by a global->LDS transfer the compiler cannot track).
 __device__ __forceinline__ u32x2 lds_u32x2(const unsigned char* p) {
@@ -608,9 +609,10 @@ __device__ __forceinline__ u32x2 lds_u32x2(const unsigned char* p) {
 
 // ENC: the encode's backward alone (first stage of the FLARE++ backward):
 // dl = A (dZ V^T - gam), no decode weights, no dY.
-template <int D, bool ENC = false, bool FDQ = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1))) void bw_dkdv_bf16(BackwardArgs a) {
-    static_assert(!(FDQ && (ENC || D != 32)), "dQ fused at D = 32 with the full formula only");
+template <int D, bool ENC = false, bool FDQ = false, int MBX = 4>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D == 32 ? 2 : 1))) void bw_dkdv_bf16(
+    BackwardArgs a) {
+    static_assert(!(FDQ && ENC), "dQ fused with the full formula only");
     constexpr int KB = D / 16, DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
     const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
@@ -633,7 +635,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1
     // registers, for up to MBX latent blocks
     unsigned char* ktile = (unsigned char*)(gam + Mp) + wave * (32 * 2 * D + 32 * 64);
     unsigned char* ptile = ktile + 32 * 2 * D;
-    constexpr int MBX = 4, MBU = FDQ ? MBX : 1;
+    constexpr int MBU = FDQ ? MBX : 1;
     f32x16 dq[FDQ ? MBX : 1][DB];
 #pragma unroll
     for (int j = 0; j < (FDQ ? MBX : 1); ++j)
@@ -661,11 +663,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1
     // block's are loaded while this one is processed (clamped to the last
     // block, so the loads are unconditional and the compiler's wait before
     // the first use covers exactly them)
-    // (at D = 64 the second set of rows would cost occupancy, and with ENC
-    // the LDS reads after the global->LDS transfers make the compiler wait
-    // for every load in flight: there each block's rows are loaded at its
-    // start)
-    constexpr bool PF = D <= 32 && !ENC && !FDQ;
+    // (with ENC the LDS reads after the global->LDS transfers make the
+    // compiler wait for every load in flight, and FDQ holds its dQ sums in
+    // the registers a second set would take (at D = 32 at two waves per
+    // SIMD; at D = 64 prefetching there measured 4% slower): there each
+    // block's rows are loaded at its start)
+    constexpr bool PF = !ENC && !FDQ;
     bf16x8 kop[KB], vop[KB], gop[KB], kpf[KB], vpf[KB], gpf[KB];
     float nu, del, nupf = 0.0f, delpf = 0.0f;
     auto load = [&](int bk) {
@@ -722,11 +725,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1
         }
         // FDQ: K^T operands of this block (rows d, k = tokens), transposed
         // reads of the K tile; rows past N are zero, so their dl adds nothing
-        auto tr_addr = [&](const unsigned char* t, int row0, int kp, int db, int second) {
+        // (W: the tile's row width in elements, D for K rows, 32 for dl rows)
+        auto tr_addr = [&](auto W, const unsigned char* t, int row0, int kp, int db, int second) {
             const int row = row0 + 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
             const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
-            return t + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+            return t + tile_off<decltype(W)::value>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
         };
+        const std::integral_constant<int, D> WK{};
+        const std::integral_constant<int, 32> WP{};
         bf16x8 kt[2][DB];
         if constexpr (FDQ) {
 #pragma unroll
@@ -734,8 +740,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1
                 *(bf16x8*)(ktile + tile_off<D>(l32, 2 * kb + hi)) = n < N ? kop[kb] : zero8();
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                lds_tr_op2(tr_addr(ktile, 0, 0, db, 0), tr_addr(ktile, 0, 0, db, 1), tr_addr(ktile, 0, 1, db, 0),
-                           tr_addr(ktile, 0, 1, db, 1), kt[0][db], kt[1][db]);
+                lds_tr_op2(tr_addr(WK, ktile, 0, 0, db, 0), tr_addr(WK, ktile, 0, 0, db, 1),
+                           tr_addr(WK, ktile, 0, 1, db, 0), tr_addr(WK, ktile, 0, 1, db, 1), kt[0][db], kt[1][db]);
         }
         // (FDQ: unrolled, so that each latent block's dQ sums stay in registers)
 #pragma unroll MBU
@@ -811,8 +817,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ ? 2 : 1
                 *(bf16x8*)(ptile + tile_off<32>(l32, hi)) = pl[0];
                 *(bf16x8*)(ptile + tile_off<32>(l32, 2 + hi)) = pl[1];
                 bf16x8 pt0, pt1;
-                lds_tr_op2(tr_addr(ptile, 0, 0, 0, 0), tr_addr(ptile, 0, 0, 0, 1), tr_addr(ptile, 0, 1, 0, 0),
-                           tr_addr(ptile, 0, 1, 0, 1), pt0, pt1);
+                lds_tr_op2(tr_addr(WP, ptile, 0, 0, 0, 0), tr_addr(WP, ptile, 0, 0, 0, 1),
+                           tr_addr(WP, ptile, 0, 1, 0, 0), tr_addr(WP, ptile, 0, 1, 0, 1), pt0, pt1);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     dqb[db] = mfma(kt[0][db], pt0, dqb[db]);
@@ -986,10 +992,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     // lane, spread to the register layout by lane permutes); the next
     // sub-block's are loaded while this one is processed (clamped to this
     // one at the chunk's end, so the loads are unconditional and the
-    // compiler's wait before the first use covers exactly them). At D = 64
-    // the second set of rows would cost occupancy: there each sub-block's
-    // rows are loaded at its start and the statistics where they are used.
-    constexpr bool PF = D <= 32;
+    // compiler's wait before the first use covers exactly them). The D = 64
+    // dZ form runs three waves per SIMD, which a second set of rows would
+    // cost: there each sub-block's rows are loaded at its start and the
+    // statistics where they are used.
+    constexpr bool PF = D <= 32 || DQ;
     bf16x8 kA[KB], gA[KB], vA[KB], kP[KB], gP[KB], vP[KB];
     float nuP = 0.0f, deP = 0.0f;
     auto load = [&](int t) {
@@ -1231,7 +1238,9 @@ hipError_t launch_bw_tok(F fn, const BackwardArgs& a, int lds, hipStream_t s, in
 
 int bw_fused_dq_groups(const BackwardArgs& a) {
     const int Mp = (a.M + 31) / 32 * 32;
-    if (!a.bf16 || a.enc_only || a.D != 32 || Mp > 128 || a.C < 1) return 0;
+    // (D = 64: two latent blocks, whose sums fill the registers of the one
+    // wave per SIMD the kernel runs at)
+    if (!a.bf16 || a.enc_only || !((a.D == 32 && Mp <= 128) || (a.D == 64 && Mp <= 64)) || a.C < 1) return 0;
     return std::min(tok_groups(a), a.C);
 }
 
@@ -1289,9 +1298,11 @@ hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
     }
     if (const int fg = bw_fused_dq_groups(a)) {
         // dQ fused in: per-wave K and dl tiles, and the four waves' sums
-        // merged through LDS at the end
-        const int lds_f = std::max(lds + 4 * (32 * 2 * a.D + 32 * 64), 3 * 4 * (a.D / 32) * 16 * 64 * 4);
-        return launch_bw_tok(bw_dkdv_bf16<32, false, true>, a, lds_f, s, fg);
+        // (mbx latent blocks) merged through LDS at the end
+        const int mbx = a.D == 64 ? 2 : 4;
+        const int lds_f = std::max(lds + 4 * (32 * 2 * a.D + 32 * 64), 3 * mbx * (a.D / 32) * 16 * 64 * 4);
+        if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32, false, true>, a, lds_f, s, fg);
+        return launch_bw_tok(bw_dkdv_bf16<64, false, true, 2>, a, lds_f, s, fg);
     }
     if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32>, a, lds, s);
     if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64>, a, lds, s);
