@@ -93,3 +93,21 @@ __device__ __forceinline__ void lds_tr_op2(const unsigned char* p1, const unsign
     o2 = __builtin_bit_cast(bf16x8, b);
 }
 
+// The same reads through the compiler builtin, for kernels that move no data
+// by global->LDS transfers: the compiler then places the waits itself and can
+// keep several of these reads in flight.
+__device__ __forceinline__ void lds_tr_op2_c(const unsigned char* p1, const unsigned char* p2,
+                                             const unsigned char* p3, const unsigned char* p4, bf16x8& o1,
+                                             bf16x8& o2) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    auto rd = [](const unsigned char* p) {
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                             (lds_s16x4*)(const __attribute__((address_space(3))) unsigned char*)p));
+    };
+    const u32x2 w1 = rd(p1), w2 = rd(p2), w3 = rd(p3), w4 = rd(p4);
+    const u32x4 a = {w1[0], w1[1], w2[0], w2[1]};
+    const u32x4 b = {w3[0], w3[1], w4[0], w4[1]};
+    o1 = __builtin_bit_cast(bf16x8, a);
+    o2 = __builtin_bit_cast(bf16x8, b);
+}
+

@@ -509,8 +509,8 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
             bf16x8 gt[2][DB];
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                lds_tr_op2(tr_addr(wd, gtile, 0, db, 0), tr_addr(wd, gtile, 0, db, 1), tr_addr(wd, gtile, 1, db, 0),
-                           tr_addr(wd, gtile, 1, db, 1), gt[0][db], gt[1][db]);
+                lds_tr_op2_c(tr_addr(wd, gtile, 0, db, 0), tr_addr(wd, gtile, 0, db, 1), tr_addr(wd, gtile, 1, db, 0),
+                             tr_addr(wd, gtile, 1, db, 1), gt[0][db], gt[1][db]);
 #pragma unroll MBU
             for (int mb = 0; mb < MBX; ++mb) {
                 if (mb >= MB) continue;
@@ -531,8 +531,8 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
                     *(u32x2*)(btile + tile_off<32>(l32, q) + 8 * hi) = w;
                 }
                 bf16x8 bt0, bt1;
-                lds_tr_op2(tr_addr(wb, btile, 0, 0, 0), tr_addr(wb, btile, 0, 0, 1), tr_addr(wb, btile, 1, 0, 0),
-                           tr_addr(wb, btile, 1, 0, 1), bt0, bt1);
+                lds_tr_op2_c(tr_addr(wb, btile, 0, 0, 0), tr_addr(wb, btile, 0, 0, 1), tr_addr(wb, btile, 1, 0, 0),
+                             tr_addr(wb, btile, 1, 0, 1), bt0, bt1);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     dz[mb][db] = mfma(gt[0][db], bt0, dz[mb][db]);
@@ -740,8 +740,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
                 *(bf16x8*)(ktile + tile_off<D>(l32, 2 * kb + hi)) = n < N ? kop[kb] : zero8();
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                lds_tr_op2(tr_addr(WK, ktile, 0, 0, db, 0), tr_addr(WK, ktile, 0, 0, db, 1),
-                           tr_addr(WK, ktile, 0, 1, db, 0), tr_addr(WK, ktile, 0, 1, db, 1), kt[0][db], kt[1][db]);
+                lds_tr_op2_c(tr_addr(WK, ktile, 0, 0, db, 0), tr_addr(WK, ktile, 0, 0, db, 1),
+                             tr_addr(WK, ktile, 0, 1, db, 0), tr_addr(WK, ktile, 0, 1, db, 1), kt[0][db], kt[1][db]);
         }
         // (FDQ: unrolled, so that each latent block's dQ sums stay in registers)
 #pragma unroll MBU
@@ -801,9 +801,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 bf16x8 qt0, qt1, zt0, zt1;
-                lds_tr_op2(taddr(qs, 0, db, 0), taddr(qs, 0, db, 1), taddr(qs, 1, db, 0), taddr(qs, 1, db, 1), qt0, qt1);
-                lds_tr_op2(taddr(dzs, 0, db, 0), taddr(dzs, 0, db, 1), taddr(dzs, 1, db, 0), taddr(dzs, 1, db, 1), zt0,
-                           zt1);
+                lds_tr_op2_c(taddr(qs, 0, db, 0), taddr(qs, 0, db, 1), taddr(qs, 1, db, 0), taddr(qs, 1, db, 1), qt0,
+                             qt1);
+                lds_tr_op2_c(taddr(dzs, 0, db, 0), taddr(dzs, 0, db, 1), taddr(dzs, 1, db, 0), taddr(dzs, 1, db, 1),
+                             zt0, zt1);
                 dk[db] = mfma(qt0, pl[0], dk[db]);
                 dk[db] = mfma(qt1, pl[1], dk[db]);
                 dv[db] = mfma(zt0, pe[0], dv[db]);
@@ -817,8 +818,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
                 *(bf16x8*)(ptile + tile_off<32>(l32, hi)) = pl[0];
                 *(bf16x8*)(ptile + tile_off<32>(l32, 2 + hi)) = pl[1];
                 bf16x8 pt0, pt1;
-                lds_tr_op2(tr_addr(WP, ptile, 0, 0, 0, 0), tr_addr(WP, ptile, 0, 0, 0, 1),
-                           tr_addr(WP, ptile, 0, 1, 0, 0), tr_addr(WP, ptile, 0, 1, 0, 1), pt0, pt1);
+                lds_tr_op2_c(tr_addr(WP, ptile, 0, 0, 0, 0), tr_addr(WP, ptile, 0, 0, 0, 1),
+                             tr_addr(WP, ptile, 0, 1, 0, 0), tr_addr(WP, ptile, 0, 1, 0, 1), pt0, pt1);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     dqb[db] = mfma(kt[0][db], pt0, dqb[db]);
@@ -941,7 +942,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
 // ENC (with DQ): the encode's backward alone, dl = A (dZ V^T - gam), for the
 // first stage of the FLARE++ backward: no decode weights, no dY.
 template <int D, bool DQ, int MBW, bool ENC = false>  // MBW: latent blocks per wave at most
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && !DQ ? 3 : 1))) void bw_lat_bf16(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && !DQ ? 2 : 1))) void bw_lat_bf16(
     BackwardArgs a) {
     constexpr int KB = D / 16, DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
@@ -992,11 +993,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     // lane, spread to the register layout by lane permutes); the next
     // sub-block's are loaded while this one is processed (clamped to this
     // one at the chunk's end, so the loads are unconditional and the
-    // compiler's wait before the first use covers exactly them). The D = 64
-    // dZ form runs three waves per SIMD, which a second set of rows would
-    // cost: there each sub-block's rows are loaded at its start and the
-    // statistics where they are used.
-    constexpr bool PF = D <= 32 || DQ;
+    // compiler's wait before the first use covers exactly them). (Loading
+    // each sub-block's rows at its start instead, which lets the D = 64 dZ
+    // form run three waves per SIMD, measured 7% slower on MI355X.)
     bf16x8 kA[KB], gA[KB], vA[KB], kP[KB], gP[KB], vP[KB];
     float nuP = 0.0f, deP = 0.0f;
     auto load = [&](int t) {
@@ -1008,17 +1007,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
             if constexpr (!ENC) gP[kb] = *(const bf16x8*)(Gb + o);
             if constexpr (DQ) vP[kb] = *(const bf16x8*)(Vb + o);
         }
-        if constexpr (!ENC && PF) {
+        if constexpr (!ENC) {
             const int tc = t + min(l32, nv - 1);
             nuP = nub[tc];
             if constexpr (DQ) deP = delb[tc];
         }
     };
     int t0 = n0 + 32 * ts;
-    if (PF && nmb > 0 && t0 < n1) load(t0);
+    if (nmb > 0 && t0 < n1) load(t0);
     for (; nmb > 0 && t0 < n1; t0 += 32 * TS) {
         const int nv = n1 - t0;  // valid tokens in this sub-block (>= 1)
-        if constexpr (!PF) load(t0);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             kA[kb] = kP[kb];
@@ -1026,7 +1024,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
             vA[kb] = vP[kb];
         }
         const float nuc = nuP, dec = deP;
-        if constexpr (PF) load(t0 + 32 * TS < n1 ? t0 + 32 * TS : t0);
+        load(t0 + 32 * TS < n1 ? t0 + 32 * TS : t0);
         // the accumulation's source rows (K for dQ, dY for dZ) in natural
         // order into this wave's tile; rows past the chunk are zero, so their
         // (finite) weights add nothing
@@ -1040,14 +1038,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int tk = 16 * (i >> 3) + 8 * hi + (i & 7);
-                if constexpr (PF) {
-                    nur[i] = __shfl(nuc, tk, 64);
-                    der[i] = DQ ? __shfl(dec, tk, 64) : 0.0f;
-                } else {
-                    const int tc = t0 + min(tk, nv - 1);
-                    nur[i] = nub[tc];
-                    der[i] = DQ ? delb[tc] : 0.0f;
-                }
+                nur[i] = __shfl(nuc, tk, 64);
+                der[i] = DQ ? __shfl(dec, tk, 64) : 0.0f;
             }
         }
         // the transposed operands of this sub-block (same for every latent block)
@@ -1059,7 +1051,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         bf16x8 tA[2][DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            lds_tr_op2(taddr(0, db, 0), taddr(0, db, 1), taddr(1, db, 0), taddr(1, db, 1), tA[0][db], tA[1][db]);
+            lds_tr_op2_c(taddr(0, db, 0), taddr(0, db, 1), taddr(1, db, 0), taddr(1, db, 1), tA[0][db],
+                         tA[1][db]);
 #pragma unroll
         for (int j = 0; j < MBW; ++j) {
             if (j >= nmb) break;
