@@ -103,6 +103,80 @@ def trace_summary(path: str, steps: int, cold: bool) -> str:
     return "\n".join(out)
 
 
+def kernel_kind(name: str) -> str | None:
+    """The library's kernel kind of a kernel symbol (None for other kernels)."""
+    for kind, tag in (("encode_partial", "encode_partial"), ("decode", "decode_"), ("combine", "combine_kernel"),
+                      ("copy", "copy_kernel")):
+        if tag in name:
+            return kind
+    return None
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, workload, layout: str, variant: str, copy_mib: int,
+                kernel_trace_csv: str | None, bench_args: str = "") -> list:
+    """HBM traffic per launch of the forward kernels from two rocprofv3 --pmc
+    runs of a default bench.py run (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch), each scaled so that the same counter over the library's plain
+    copy kernel (copy_mib MiB each way, launched once before the timed steps)
+    reads copy_mib MiB. Returns one record per kernel kind (averages over all
+    its dispatches), with the hash of its source."""
+    import csv
+
+    def per_dispatch(path: str, counter: str) -> dict:
+        vals, names = {}, {}
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                d = r["Dispatch_Id"]
+                vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+                names[d] = r["Kernel_Name"]
+        return {d: (names[d], v) for d, v in vals.items()}
+
+    fetch, write = per_dispatch(fetch_csv, "FETCH_SIZE"), per_dispatch(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib << 20
+
+    def scale(table):
+        c = [v for n, v in table.values() if kernel_kind(n) == "copy"]
+        if not c:
+            raise SystemExit("no copy-kernel dispatch in the counter run (run bench.py with --calib-copy-mib > 0)")
+        return copy_bytes / (c[0] * 1024.0)
+
+    fs, ws = scale(fetch), scale(write)
+    dur = {}
+    if kernel_trace_csv:
+        with open(kernel_trace_csv, newline="") as f:
+            for r in csv.DictReader(f):
+                k = kernel_kind(r["Kernel_Name"])
+                if k:
+                    dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    e = 2 if workload.dtype == "bf16" else 4
+    alg = {"encode_partial": 2 * workload.B * workload.H * workload.N * workload.D * e,
+           "decode": 2 * workload.B * workload.H * workload.N * workload.D * e}
+    out = []
+    for kind in ("encode_partial", "combine", "decode"):
+        fv = [(n, v) for n, v in fetch.values() if kernel_kind(n) == kind]
+        wv = [v for n, v in write.values() if kernel_kind(n) == kind]
+        if not fv or not wv:
+            continue
+        rd = sum(v for _, v in fv) / len(fv) * 1024.0 * fs
+        wr = sum(wv) / len(wv) * 1024.0 * ws
+        lay = ("" if layout == "bhnd" else "_bnhd") + ("" if variant == "flare" else "_" + variant)
+        rec = {"kernel": kind,
+               "kernel_symbol": fv[0][0].replace("void ", "").replace("flare::(anonymous namespace)::", "").split("(")[0],
+               "workload": workload.name + lay, "source": KERNEL_SOURCES[kind], "source_hash": source_hash(kind),
+               "avg_duration_us": round(sum(dur[kind]) / len(dur[kind]), 2) if kind in dur else None,
+               "launches": len(fv), "hbm_read_bytes_per_launch": int(rd), "hbm_write_bytes_per_launch": int(wr),
+               "hbm_bytes_per_launch": int(rd + wr), "alg_bytes_per_launch": alg.get(kind),
+               "calibration": {"copy_bytes": copy_bytes, "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
+               "commands": [f"rocprofv3 --pmc {c} -d <out> -o {o} --output-format csv -- python3 bench.py {bench_args}"
+                            for c, o in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))]
+               + ([f"rocprofv3 --kernel-trace --stats -d <out> -o kt --output-format csv -- python3 bench.py "
+                   f"{bench_args}"] if kernel_trace_csv else [])}
+        out.append(rec)
+    return out
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -132,6 +206,10 @@ def parse():
     p.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                    help="print the per-pass kernel summary of a rocprofv3 kernel trace of a default run of this "
                         "script with the same --steps and --cold-mib, and exit")
+    p.add_argument("--pmc-summary", nargs="+", metavar="CSV",
+                   help="FETCH_CSV WRITE_CSV [KERNEL_TRACE_CSV]: write profiles/<kernel>_<workload>_pmc.json (the "
+                        "traffic the roofline reports) from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of "
+                        "this script with the same --workload, --layout and --variant, and exit")
     p.add_argument("--ramp-seconds", type=float, default=1.0,
                    help="run the step back to back for this long before the warmup steps, so that the GPU "
                         "reaches its steady clocks (a cold MI355X needs ~0.1-0.2 s); 0 disables")
@@ -140,6 +218,27 @@ def parse():
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        from flare_inputs import WORKLOADS
+        if len(args.pmc_summary) not in (2, 3):
+            raise SystemExit("--pmc-summary takes FETCH_CSV WRITE_CSV [KERNEL_TRACE_CSV]")
+        w = WORKLOADS[args.workload]
+        bench_args = f"--workload {args.workload} --no-cpu-baseline" + \
+            ("" if args.layout == "bhnd" else f" --layout {args.layout}") + \
+            ("" if args.variant == "flare" else f" --variant {args.variant}") + \
+            ("" if args.steps == 200 else f" --steps {args.steps}") + \
+            ("" if args.warmup == 20 else f" --warmup {args.warmup}") + \
+            ("" if args.ramp_seconds == 1.0 else f" --ramp-seconds {args.ramp_seconds:g}")
+        recs = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], w, args.layout, args.variant,
+                           args.calib_copy_mib, args.pmc_summary[2] if len(args.pmc_summary) == 3 else None,
+                           bench_args)
+        for rec in recs:
+            path = os.path.join(ROOT, "profiles", f"{rec['kernel']}_{rec['workload']}_pmc.json")
+            with open(path, "w") as f:
+                json.dump(rec, f, indent=1)
+                f.write("\n")
+            print(path, rec["hbm_bytes_per_launch"], rec["alg_bytes_per_launch"])
+        return
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.steps, args.cold_mib > 0))
         return
@@ -182,20 +281,27 @@ def main():
         sys.exit(2)
     if args.variant == "backward":
         # the backward of the workload's operator: flare_backward, or
-        # flare_pp_backward on the FLARE++ workload
-        if args.layout != "bhnd":
-            print("--variant backward takes the [B,H,N,D] layout", file=sys.stderr)
-            sys.exit(2)
+        # flare_pp_backward on the FLARE++ workload (their _ex forms in the
+        # token-major layout)
         pp = op == F.FLARE_OP_PP_FORWARD
         bw_op = F.FLARE_OP_PP_BACKWARD if pp else F.FLARE_OP_BACKWARD
         bw_fn = F.flare_pp_backward if pp else F.flare_backward
+        bw_ex = F.flare_pp_backward_ex if pp else F.flare_backward_ex
         ws = torch.empty(F.flare_workspace_size(bw_op, w.B, w.H, w.N, w.M, w.D, Q.dtype),
                          dtype=torch.uint8, device=Q.device)
         dYt = V.flip(2).contiguous()  # upstream gradient: the values in reverse token order
-        grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+        if args.layout == "bnhd":
+            dYt = dYt.transpose(1, 2).contiguous()
+        grads = None
 
         def fn(Q, K, V, out=None, workspace=None, stream=None):
-            bw_fn(Q, K, V, dYt, stream=stream, workspace=workspace, out=grads)
+            nonlocal grads
+            if grads is None:
+                grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+            if args.layout == "bnhd":
+                bw_ex(Q, K, V, dYt, F.FLARE_LAYOUT_BNHD, stream=stream, workspace=workspace, out=grads)
+            else:
+                bw_fn(Q, K, V, dYt, stream=stream, workspace=workspace, out=grads)
             return grads[1]
     if args.variant == "skill":
         ws = F.workspace_for(F.FLARE_OP_ENCODE, Q, K)
@@ -324,8 +430,14 @@ def main():
         if cnt:
             kern[kind] = {"avg_us": 1e3 * ms / cnt, "launches_per_step": cnt / args.steps,
                           "share_of_step": ms / total_ms}
-    # algorithmic bytes per launch: encode reads K and V; decode reads K and writes Y
-    alg_bytes = {"encode_partial": 2 * kv_bytes, "decode": 2 * kv_bytes}
+    # Algorithmic work per launch. Each encode launch is a full pass: it reads
+    # K and V once. The decode reads K and writes Y once per step, over its
+    # launches per step (two when its latent range is split in halves). Both
+    # contract 4*M*N*D flops per (b, h) per pass.
+    dec_launches = kern["decode"]["launches_per_step"] if "decode" in kern else 1.0
+    pass_flops = 4 * w.B * w.H * w.N * w.M * w.D
+    alg_bytes = {"encode_partial": 2 * kv_bytes, "decode": int(round(2 * kv_bytes / dec_launches))}
+    alg_flops = {"encode_partial": pass_flops, "decode": int(round(pass_flops / dec_launches))}
     if args.variant == "backward":
         # contraction work of the backward kernels per (b, h): logits and the products and
         # accumulations of each kernel (stats 6, dZ 4, dK/dV 10, dQ 8) x M*N*D flops; on the
@@ -348,10 +460,25 @@ def main():
         if "encode_partial" in kern and "decode" in kern:
             dominant = max(("encode_partial", "decode"),
                            key=lambda k: kern[k]["avg_us"] * kern[k]["launches_per_step"])
-            achieved = alg_bytes[dominant] / (kern[dominant]["avg_us"] * 1e-6) / 1e9
+            dur_s = kern[dominant]["avg_us"] * 1e-6
         else:  # no per-kernel events: attribute the step to one kernel (lower bound)
             dominant = "decode"
-            achieved = alg_bytes[dominant] / (ms_step * 1e-3) / 1e9
+            dur_s = ms_step * 1e-3
+        # The bound: whichever takes longer at the published peaks, the
+        # kernel's HBM bytes or its matrix-core work (bf16 only; the fp32 path
+        # runs on the VALU with M*N*D far below the HBM balance). A decode or
+        # encode pass does 2M/e flops per byte, so bf16 turns matrix-core bound
+        # above M = 312.
+        on_mfma = w.dtype == "bf16" and (alg_flops[dominant] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+                                         > alg_bytes[dominant] / (HBM_PEAK_GBS * 1e9))
+
+        def position(seconds):
+            if on_mfma:
+                a = alg_flops[dominant] / seconds / 1e12
+                return a, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+            a = alg_bytes[dominant] / seconds / 1e9
+            return a, HBM_PEAK_GBS, "GB/s"
+        achieved, peak, unit = position(dur_s)
         traffic = None
         lay = ("" if args.layout == "bhnd" else "_bnhd") + ("" if args.variant == "flare" else "_" + args.variant)
         pmc_path = os.path.join(ROOT, "profiles", f"{dominant}_{w.name}{lay}_pmc.json")
@@ -361,15 +488,15 @@ def main():
             if pmc.get("source_hash") == source_hash(dominant):
                 traffic = pmc.get("hbm_bytes_per_launch")
         if cold and dominant in cold["kernels"]:
-            cold_gbs = alg_bytes[dominant] / (cold["kernels"][dominant]["avg_us"] * 1e-6) / 1e9
-            cold["roofline"] = {"kernel": dominant, "achieved": round(cold_gbs, 1),
-                                "frac": round(cold_gbs / HBM_PEAK_GBS, 4),
+            cold_a, _, _ = position(cold["kernels"][dominant]["avg_us"] * 1e-6)
+            cold["roofline"] = {"kernel": dominant, "bound": "mfma" if on_mfma else "hbm",
+                                "achieved": round(cold_a, 1), "unit": unit, "frac": round(cold_a / peak, 4),
                                 "hbm_frac_step": round((4 if passes == 1 else 6) * kv_bytes
                                                        / (cold["ms_per_step_median"] * 1e-3) / 1e9
                                                        / HBM_PEAK_GBS, 4)}
-        roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "alg_bytes_per_launch": alg_bytes[dominant],
+        roofline = {"bound": "mfma" if on_mfma else "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                    "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+                    "alg_bytes_per_launch": alg_bytes[dominant], "alg_flops_per_launch": alg_flops[dominant],
                     "mfma_tflops_step": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
                     "mfma_frac_step": round(flops_step / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                     "hbm_frac_step": round((4 if passes == 1 else 6) * kv_bytes / (ms_step * 1e-3) / 1e9
@@ -382,7 +509,10 @@ def main():
         bw_n = min(w.N, 16384)
         t0 = time.perf_counter()
         done = 0
-        for (b, h) in heads:
+        # whole heads in order, cycling over the workload's heads again when all
+        # are done before the budget is spent (a small workload is repeated)
+        while True:
+            b, h = heads[done % len(heads)]
             q = Qh[h]
             if args.variant == "backward" and op == F.FLARE_OP_PP_FORWARD:
                 oracle.pp_backward_head(oracle.widen(q), oracle.widen(Kh[b, h, :bw_n]),
@@ -406,10 +536,10 @@ def main():
         el = time.perf_counter() - t0
         ntok = bw_n if args.variant == "backward" else w.N
         cores = 1 if args.variant == "backward" else oracle.threads()  # the fp64 backward is one loop nest
+        sample = (f"{done} heads ({done / len(heads):.2f} passes over the {len(heads)} heads) of {w.name}, "
+                  f"N={ntok} of {w.N}, fp64 {w.op if args.variant == 'flare' else args.variant}, {el:.1f} s")
         cpu = {"value": round(done * ntok / el, 1), "unit": "tokens*heads/s", "cores": cores,
-               "cpu_model": cpu_model(), "kind": "oracle", "sample": f"{done} of {len(heads)} heads of {w.name}, N={ntok} of {w.N}, "
-                                            f"fp64 {w.op if args.variant == 'flare' else args.variant}, "
-                                            f"{el:.1f} s"}
+               "cpu_model": cpu_model(), "kind": "oracle", "sample": sample}
 
     line = {
         "metric": "FLARE fwd tokens*heads/s (N=65536, M=128) + roofline fraction",

@@ -116,7 +116,7 @@ def heads_to_check(w):
     return [(0, 0), (w.B - 1, w.H - 1)] if w.B * w.H > 1 else [(0, 0)]
 
 
-@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5, 6, 7])
 def test_workload_matches_oracle_on_sampled_tokens(i):
     w, Q, K, V, Qd, Kd, Vd = workload(i)
     op = w.op
