@@ -151,8 +151,9 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
         p->cfg = flare::EncCfg{0, 0, 0};
         p->Mp = int(M);
         tile = 32;  // chunk granularity (the kernel's 64-token tiles may be partial)
-        const int nth = flare::enc_threads_f32(int(M));
-        waves_per_wg = int((M + nth - 1) / nth) * (nth / 64);
+        const int nth = flare::enc_threads_f32(int(M), int(D));
+        const int per = nth / flare::f32_lanes_enc(int(M), int(D));
+        waves_per_wg = int((M + per - 1) / per) * (nth / 64);
     }
     // Split over N: enough workgroups to fill the chip, but chunks long enough
     // that the partials stay a few percent of the K/V bytes (bf16: 32*Mp
@@ -998,12 +999,14 @@ flare_status flare_describe_plan(flare_op op, int64_t B, int64_t H, int64_t N, i
               std::to_string(cfg.wm) + "x" + std::to_string(cfg.wt) + " latent-blocks/wave " + std::to_string(cfg.mbw) +
               " tile " + std::to_string(flare::enc_tile_tokens_bf16(cfg));
     } else {
-        const int nth = flare::enc_threads_f32(int(M));
-        enc = "encode grid (" + std::to_string(p.C) + "," + std::to_string(p.BH) + "," + std::to_string((M + nth - 1) / nth) +
-              ") threads " + std::to_string(nth);
+        const int nth = flare::enc_threads_f32(int(M), int(D)), lanes = flare::f32_lanes_enc(int(M), int(D));
+        enc = "encode grid (" + std::to_string(p.C) + "," + std::to_string(p.BH) + "," +
+              std::to_string((M + nth / lanes - 1) / (nth / lanes)) + ") threads " + std::to_string(nth) +
+              " lanes/latent " + std::to_string(lanes);
     }
     // the launched decode grid (bf16: sized from the device's occupancy)
-    const int dec_g = dtype == FLARE_BF16 ? decode_groups(p, op != FLARE_OP_DECODE) : int((N + 255) / 256);
+    const int dec_tpb = 256 / flare::f32_lanes_dec(N * p.BH, int(D));  // fp32: tokens per workgroup
+    const int dec_g = dtype == FLARE_BF16 ? decode_groups(p, op != FLARE_OP_DECODE) : int((N + dec_tpb - 1) / dec_tpb);
     std::string txt = enc + " chunk " + std::to_string(p.chunk_len) + "; decode grid (" + std::to_string(dec_g) + "," +
                       std::to_string(p.BH) + "); workspace " + std::to_string(p.total[op]) + " bytes";
     std::snprintf(buf, len, "%s", txt.c_str());

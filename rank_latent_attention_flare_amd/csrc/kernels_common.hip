@@ -131,43 +131,49 @@ __device__ __forceinline__ void combine_store(const CombineArgs& a, int bh, int 
 }
 
 // ---------------------------------------------------------------------------
-// fp32 encode partials: grid (C, BH, latent groups of blockDim.x); thread =
-// latent. blockDim.x is M rounded up to 64, at most 256. K/V tiles of 64
-// tokens go through LDS (16-byte loads); each thread keeps its latent's exact
-// running maximum, sum and accumulator. The dot products run as four
-// independent partial sums (shorter dependency chains; every chunk is short,
-// so the chains, not the loads, set the time).
+// fp32 encode partials: grid (C, BH, latent groups); L consecutive lanes per
+// latent, each holding D/L of its columns (L = 1, 2 or 4: more lanes when
+// there are few latents, so that short chunks still fill a wave). K/V tiles
+// of 64 tokens go through LDS (16-byte loads); each latent keeps its exact
+// running maximum, sum and accumulator (the scalars in all L lanes). The dot
+// products run as four independent partial sums over the lane's columns,
+// closed across the L lanes by xor shuffles (shorter dependency chains;
+// every chunk is short, so the chains, not the loads, set the time).
 // ---------------------------------------------------------------------------
 typedef float f32x4f __attribute__((ext_vector_type(4)));
 
-template <int D>
+template <int DL, int L>
 __device__ __forceinline__ float dot4(const float* q, const float* k) {
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int d = 0; d < D; d += 4) {
+    for (int d = 0; d < DL; d += 4) {
         const f32x4f kv = *(const f32x4f*)(k + d);
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[i] = fmaf(q[d + i], kv[i], s[i]);
     }
-    return (s[0] + s[1]) + (s[2] + s[3]);
+    float r = (s[0] + s[1]) + (s[2] + s[3]);
+#pragma unroll
+    for (int o = 1; o < L; o <<= 1) r += __shfl_xor(r, o, 64);
+    return r;
 }
 
-// Exact online softmax of one query row q against `rows` LDS rows: keys kr,
-// values vr (D floats each), scores c * <q, k>, folded into the running
-// (offset mu, sum, accumulator). Rows go four at a time: their four scores
-// first, then one rescale to the largest, then their terms in row order; a
-// tail of fewer than four goes one at a time. Every rescale is by
-// 2^(mu_old - mu_new), so the ratio acc / sum is the softmax whatever the
-// grouping.
-template <int D>
+// Exact online softmax of one query row q (this lane's DL columns) against
+// `rows` LDS rows of D floats: keys kr, values vr (both already offset to
+// this lane's columns), scores c * <q, k>, folded into the running (offset
+// mu, sum, accumulator). Rows go four at a time: their four scores first,
+// then one rescale to the largest, then their terms in row order; a tail of
+// fewer than four goes one at a time. Every rescale is by 2^(mu_old - mu_new),
+// so the ratio acc / sum is the softmax whatever the grouping.
+template <int D, int L>
 __device__ __forceinline__ void online_softmax_rows(const float* q, const float* kr, const float* vr, int rows,
                                                     float c, float& mu, float& sum, float* acc) {
+    constexpr int DL = D / L;
     auto rescale = [&](float xm) {
         if (xm > mu) {
             const float alpha = (mu == -INFINITY) ? 0.0f : exp2f(mu - xm);
             sum *= alpha;
 #pragma unroll
-            for (int d = 0; d < D; ++d) acc[d] *= alpha;
+            for (int d = 0; d < DL; ++d) acc[d] *= alpha;
             mu = xm;
         }
     };
@@ -175,7 +181,7 @@ __device__ __forceinline__ void online_softmax_rows(const float* q, const float*
         const float p = exp2f(x - mu);
         sum += p;
 #pragma unroll
-        for (int d = 0; d < D; d += 4) {
+        for (int d = 0; d < DL; d += 4) {
             const f32x4f vv = *(const f32x4f*)(v + d);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[d + i] = fmaf(p, vv[i], acc[d + i]);
@@ -185,25 +191,25 @@ __device__ __forceinline__ void online_softmax_rows(const float* q, const float*
     for (; r + 4 <= rows; r += 4) {
         float x[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = dot4<D>(q, kr + (r + j) * D) * c;
+        for (int j = 0; j < 4; ++j) x[j] = dot4<DL, L>(q, kr + (r + j) * D) * c;
         rescale(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
 #pragma unroll
         for (int j = 0; j < 4; ++j) add(x[j], vr + (r + j) * D);
     }
     for (; r < rows; ++r) {
-        const float x = dot4<D>(q, kr + r * D) * c;
+        const float x = dot4<DL, L>(q, kr + r * D) * c;
         rescale(x);
         add(x, vr + r * D);
     }
 }
 
-template <int D>
+template <int D, int L>
 __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
-    constexpr int T = 64;
+    constexpr int T = 64, DL = D / L;
     __shared__ __attribute__((aligned(16))) float kt[T * D], vt[T * D];
-    const int tid = threadIdx.x, nth = blockDim.x;
+    const int tid = threadIdx.x, nth = blockDim.x, j = tid % L;
     const int chunk = a.heads_fast ? blockIdx.y : blockIdx.x, bh = a.heads_fast ? blockIdx.x : blockIdx.y;
-    const int m = blockIdx.z * nth + tid;
+    const int m = blockIdx.z * (nth / L) + tid / L;
     const int b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M;
     const int n0 = chunk * a.chunk_len, n1 = min(N, n0 + a.chunk_len);
@@ -211,11 +217,11 @@ __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
     const float* Kb = (const float*)a.K + (int64_t)b * a.sb + (int64_t)h * a.sh;
     const float* Vb = (const float*)a.V + (int64_t)b * a.sb + (int64_t)h * a.sh;
     const float* Qb = (const float*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
-    const bool active = m < M;
-    float q[D], acc[D];
+    const bool active = m < M;  // the same for the L lanes of a latent
+    float q[DL], acc[DL];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        q[d] = active ? Qb[(int64_t)m * D + d] : 0.0f;
+    for (int d = 0; d < DL; ++d) {
+        q[d] = active ? Qb[(int64_t)m * D + j * DL + d] : 0.0f;
         acc[d] = 0.0f;
     }
     float mu = -INFINITY, sig = 0.0f;
@@ -229,41 +235,44 @@ __global__ __launch_bounds__(256) void encode_partial_f32(EncodeArgs a) {
             *(f32x4f*)(vt + r * D + d) = *(const f32x4f*)(Vb + g);
         }
         __syncthreads();
-        if (active) online_softmax_rows<D>(q, kt, vt, nt, c, mu, sig, acc);
+        if (active) online_softmax_rows<D, L>(q, kt + j * DL, vt + j * DL, nt, c, mu, sig, acc);
         __syncthreads();
     }
     if (active) {
         const int64_t r = ((int64_t)bh * a.C + chunk) * a.Mp + m;
-        a.out.mu[r] = mu;
-        a.out.sig[r] = sig;
+        if (j == 0) {
+            a.out.mu[r] = mu;
+            a.out.sig[r] = sig;
+        }
 #pragma unroll
-        for (int d = 0; d < D; ++d) a.out.acc[r * D + d] = acc[d];
+        for (int d = 0; d < DL; ++d) a.out.acc[r * D + j * DL + d] = acc[d];
     }
 }
 
 // ---------------------------------------------------------------------------
-// fp32 decode: grid (token blocks of 256, BH); thread = token. Exact online
-// softmax over the latents, which stream through LDS in tiles of LT (Q and Z
-// rows, 16-byte loads); every lane reads the same latent row at a time
-// (LDS broadcast).
+// fp32 decode: grid (token blocks of 256 / L, BH); L consecutive lanes per
+// token, each holding D/L of its columns. Exact online softmax over the
+// latents, which stream through LDS in tiles of LT (Q and Z rows, 16-byte
+// loads); the lanes of a group read the same latent row at a time (LDS
+// broadcast).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int L>
 __global__ __launch_bounds__(256) void decode_f32(DecodeArgs a) {
-    constexpr int LT = D <= 32 ? 64 : 32;
+    constexpr int LT = D <= 32 ? 64 : 32, DL = D / L, TPB = 256 / L;
     __shared__ __attribute__((aligned(16))) float qs[LT * D], zs[LT * D];
-    const int bh = blockIdx.y, tid = threadIdx.x;
-    const int n = blockIdx.x * 256 + tid;
+    const int bh = blockIdx.y, tid = threadIdx.x, j = tid % L;
+    const int n = blockIdx.x * TPB + tid / L;
     const int b = bh / a.H, h = bh - b * a.H;
     const int N = a.N, M = a.M;
-    const bool active = n < N;  // every thread stages the tiles
+    const bool active = n < N;  // every thread stages the tiles; the same for the L lanes of a token
     const float c = a.c;
     const float* Qb = (const float*)a.Q + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
     const float* Zb = (const float*)a.Z + (int64_t)bh * M * D;
-    const int64_t row = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)(active ? n : 0) * a.sn;
+    const int64_t row = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)(active ? n : 0) * a.sn + j * DL;
     const float* kr = (const float*)a.K + row;
-    float k[D], y[D];
+    float k[DL], y[DL];
 #pragma unroll
-    for (int d = 0; d < D; d += 4) {
+    for (int d = 0; d < DL; d += 4) {
         const f32x4f kv = active ? *(const f32x4f*)(kr + d) : f32x4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -281,12 +290,12 @@ __global__ __launch_bounds__(256) void decode_f32(DecodeArgs a) {
             *(f32x4f*)(zs + 4 * e) = *(const f32x4f*)(Zb + g);
         }
         __syncthreads();
-        if (active) online_softmax_rows<D>(k, qs, zs, lt, c, nu, tau, y);
+        if (active) online_softmax_rows<D, L>(k, qs + j * DL, zs + j * DL, lt, c, nu, tau, y);
     }
     if (active) {
         float* yr = (float*)a.Y + row;
 #pragma unroll
-        for (int d = 0; d < D; ++d) yr[d] = y[d] / tau;
+        for (int d = 0; d < DL; ++d) yr[d] = y[d] / tau;
     }
 }
 
@@ -331,19 +340,40 @@ __global__ __launch_bounds__(256) void batch_sum_kernel(T* __restrict__ dst, con
 
 unsigned elementwise_blocks(int64_t n) { return (unsigned)std::min<int64_t>(8192, std::max<int64_t>(1, (n + 255) / 256)); }
 
+template <int D, int L>
+hipError_t enc_f32_l(const EncodeArgs& a, hipStream_t s) {
+    const int nth = enc_threads_f32(a.M, D);
+    const int per = nth / L;  // latents per workgroup
+    dim3 grid(a.heads_fast ? a.BH : a.C, a.heads_fast ? a.C : a.BH, (a.M + per - 1) / per), block(nth);
+    FLARE_LAUNCH((encode_partial_f32<D, L>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t enc_f32(const EncodeArgs& a, hipStream_t s) {
-    const int nth = enc_threads_f32(a.M);
-    dim3 grid(a.heads_fast ? a.BH : a.C, a.heads_fast ? a.C : a.BH, (a.M + nth - 1) / nth), block(nth);
-    FLARE_LAUNCH((encode_partial_f32<D>), grid, block, 0, s, a);
+    switch (f32_lanes_enc(a.M, D)) {
+        case 1: return enc_f32_l<D, 1>(a, s);
+        case 2: if constexpr (D % 8 == 0) return enc_f32_l<D, 2>(a, s); break;
+        case 4: if constexpr (D % 16 == 0) return enc_f32_l<D, 4>(a, s); break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D, int L>
+hipError_t dec_f32_l(const DecodeArgs& a, hipStream_t s) {
+    dim3 grid((a.N + 256 / L - 1) / (256 / L), a.BH), block(256);
+    FLARE_LAUNCH((decode_f32<D, L>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t dec_f32(const DecodeArgs& a, hipStream_t s) {
-    dim3 grid((a.N + 255) / 256, a.BH), block(256);
-    FLARE_LAUNCH((decode_f32<D>), grid, block, 0, s, a);
-    return hipGetLastError();
+    switch (f32_lanes_dec(int64_t(a.N) * a.BH, D)) {
+        case 1: return dec_f32_l<D, 1>(a, s);
+        case 2: if constexpr (D % 8 == 0) return dec_f32_l<D, 2>(a, s); break;
+        case 4: if constexpr (D % 16 == 0) return dec_f32_l<D, 4>(a, s); break;
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -362,7 +392,21 @@ hipError_t dec_f32(const DecodeArgs& a, hipStream_t s) {
         default: return hipErrorInvalidValue; \
     }
 
-int enc_threads_f32(int M) { return M >= 256 ? 256 : (M + 63) / 64 * 64; }
+// Lanes per latent (encode) or per token (decode): the largest of 4, 2, 1
+// that divides D into 4-column groups, when it is worth it. The encode
+// spreads few latents over more lanes (at most 64 / M lanes each); the decode
+// does so when the tokens of all heads fill less than about 4096 wavefronts.
+static int f32_lanes_fit(int want, int D) {
+    int l = want >= 4 ? 4 : want >= 2 ? 2 : 1;
+    while (l > 1 && D % (4 * l) != 0) l /= 2;
+    return l;
+}
+int f32_lanes_enc(int M, int D) { return f32_lanes_fit(M <= 16 ? 4 : M <= 32 ? 2 : 1, D); }
+int f32_lanes_dec(int64_t tokens, int D) { return f32_lanes_fit(tokens <= (int64_t(1) << 18) ? 4 : 1, D); }
+int enc_threads_f32(int M, int D) {
+    const int t = M * f32_lanes_enc(M, D);
+    return t >= 256 ? 256 : (t + 63) / 64 * 64;
+}
 
 hipError_t launch_encode_f32(const EncodeArgs& a, hipStream_t s) { FLARE_F32_DISPATCH(enc_f32, a, s) }
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { FLARE_F32_DISPATCH(dec_f32, a, s) }

@@ -153,7 +153,9 @@ bool dec_heads_built_bf16(int D, int M, int hg);
 
 hipError_t launch_encode_bf16(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
-int enc_threads_f32(int M);     // threads per fp32 encode workgroup (latents per group)
+int enc_threads_f32(int M, int D);  // threads per fp32 encode workgroup
+int f32_lanes_enc(int M, int D);    // fp32 lanes per latent (encode)
+int f32_lanes_dec(int64_t tokens, int D);  // fp32 lanes per token (decode; tokens = N * B * H)
 hipError_t launch_encode_f32(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -35,6 +35,14 @@ SMALL = [
     (1, 3, 3000, 40, 8, "f32"),
     (2, 2, 1, 1, 64, "f32"),
     (1, 1, 2500, 300, 32, "f32"),
+    # fp32 lanes per latent / token: 2 and 4 lanes (few latents or tokens),
+    # D = 24 (2 lanes at most), D = 96 and 128, and one lane per token in a
+    # decode of more than 2^18 token rows
+    (2, 1, 900, 12, 24, "f32"),
+    (1, 2, 600, 16, 128, "f32"),
+    (1, 1, 500, 70, 48, "f32"),
+    (1, 1, 300, 20, 96, "f32"),
+    (1, 2, 140000, 24, 32, "f32"),
     (2, 3, 1000, 64, 64, "bf16"),
     (1, 2, 4097, 100, 32, "bf16"),
     (1, 1, 1, 1, 32, "bf16"),
