@@ -35,21 +35,24 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-KERNEL_SOURCES = {
-    "encode_partial": ["rank_latent_attention_flare_amd/csrc/kernels_bf16.hip",
-                       "rank_latent_attention_flare_amd/csrc/gfx950_ops.h"],
-    "decode": ["rank_latent_attention_flare_amd/csrc/kernels_bf16.hip",
-               "rank_latent_attention_flare_amd/csrc/gfx950_ops.h"],
-    "combine": ["rank_latent_attention_flare_amd/csrc/kernels_common.hip"],
-}
+_BF16_SRC = ["rank_latent_attention_flare_amd/csrc/kernels_bf16.hip", "rank_latent_attention_flare_amd/csrc/gfx950_ops.h"]
+_COMMON_SRC = ["rank_latent_attention_flare_amd/csrc/kernels_common.hip"]
 
 
-def source_hash(kind: str) -> str:
+def kernel_sources(kind: str, dtype: str = "bf16") -> list:
+    """The sources that define a kernel kind for a storage type (the fp32
+    encode and decode live with the combine)."""
+    if kind == "combine" or dtype != "bf16":
+        return _COMMON_SRC
+    return _BF16_SRC
+
+
+def source_hash(kind: str, dtype: str = "bf16") -> str:
     """Hash of the code (comments and blank space removed) of the sources that
     define a kernel: recorded with its hardware counters, so that counters taken
     on an older version of the kernel are not reported against the current one."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kind]:
+    for rel in kernel_sources(kind, dtype):
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -164,7 +167,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload, layout: str, variant: 
         lay = ("" if layout == "bhnd" else "_bnhd") + ("" if variant == "flare" else "_" + variant)
         rec = {"kernel": kind,
                "kernel_symbol": fv[0][0].replace("void ", "").replace("flare::(anonymous namespace)::", "").split("(")[0],
-               "workload": workload.name + lay, "source": KERNEL_SOURCES[kind], "source_hash": source_hash(kind),
+               "workload": workload.name + lay, "source": kernel_sources(kind, workload.dtype),
+               "source_hash": source_hash(kind, workload.dtype),
                "avg_duration_us": round(sum(dur[kind]) / len(dur[kind]), 2) if kind in dur else None,
                "launches": len(fv), "hbm_read_bytes_per_launch": int(rd), "hbm_write_bytes_per_launch": int(wr),
                "hbm_bytes_per_launch": int(rd + wr), "alg_bytes_per_launch": alg.get(kind),
@@ -485,7 +489,7 @@ def main():
         if os.path.exists(pmc_path):
             with open(pmc_path) as f:
                 pmc = json.load(f)
-            if pmc.get("source_hash") == source_hash(dominant):
+            if pmc.get("source_hash") == source_hash(dominant, w.dtype):
                 traffic = pmc.get("hbm_bytes_per_launch")
         if cold and dominant in cold["kernels"]:
             cold_a, _, _ = position(cold["kernels"][dominant]["avg_us"] * 1e-6)

@@ -63,3 +63,11 @@ def test_trace_summary_splits_passes(tmp_path):
     out = bench.trace_summary(str(path), 3, False)
     rows = [r for r in out.splitlines() if r.startswith("| a ")]
     assert rows == ["| a | 8 | 2.12 | 2.00 | 3.00 |"]  # all: 17 us / 8
+
+
+def test_fp32_kernels_hash_their_own_source():
+    # the fp32 encode and decode are defined with the combine, not with the
+    # bf16 kernels: counters taken on one must not validate the other
+    assert bench.kernel_sources("encode_partial", "f32") == bench.kernel_sources("combine")
+    assert bench.source_hash("decode", "f32") != bench.source_hash("decode", "bf16")
+    assert bench.source_hash("encode_partial", "f32") == bench.source_hash("combine")
