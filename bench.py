@@ -207,6 +207,8 @@ def parse():
                    help="how the cold pass evicts the caches: read the flush buffer (default) or write it")
     p.add_argument("--calib-copy-mib", type=int, default=512,
                    help="size of the plain copy kernel run once before the timed steps (counter calibration)")
+    p.add_argument("--no-calibrate", action="store_true",
+                   help="skip the in-run peak calibration (a timed copy and the MFMA and exp probes)")
     p.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                    help="print the per-pass kernel summary of a rocprofv3 kernel trace of a default run of this "
                         "script with the same --steps and --cold-mib, and exit")
@@ -345,6 +347,37 @@ def main():
     for _ in range(args.warmup):
         fn(Q, K, V, out=Y, workspace=ws)
     torch.cuda.synchronize()
+
+    # In-run peak calibration, at the clocks the warm GPU runs at: the plain
+    # copy kernel (1:1 read/write HBM traffic), the bf16 MFMA probe and the
+    # v_exp_f32 probe, each launched once untimed and once timed with events.
+    calib = None
+    if not args.no_calibrate:
+        def timed_once(launch):
+            launch()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            r = launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e-3, r
+        nb = max(args.calib_copy_mib, 64) << 20
+        ca = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        cb = torch.empty_like(ca)
+        t_copy, _ = timed_once(lambda: F.flare_copy_kernel(ca, cb))
+        probe_out = torch.empty(F.flare_probe_lanes(), dtype=torch.float32, device="cuda")
+        t_read, _ = timed_once(lambda: F.flare_read_kernel(ca, probe_out))
+        del ca, cb
+        t_mfma, mfma_work = timed_once(lambda: F.flare_probe_peak(F.FLARE_PROBE_MFMA_BF16, 2000, probe_out))
+        t_exp, exp_work = timed_once(lambda: F.flare_probe_peak(F.FLARE_PROBE_EXP, 4000, probe_out))
+        calib = {"read_gbs": round(nb / t_read / 1e9, 1), "copy_gbs": round(2 * nb / t_copy / 1e9, 1),
+                 "copy_mib": nb >> 20,
+                 "mfma_bf16_tflops": round(mfma_work / t_mfma / 1e12, 1),
+                 "exp_per_s": float(f"{exp_work / t_exp:.4g}"),
+                 "note": "rates this GPU sustained during the run: a streaming read, a plain copy (bytes read "
+                         "+ written), independent v_mfma_f32_32x32x16_bf16 chains and independent v_exp_f32 "
+                         "chains, four waves per SIMD"}
 
     # Timed region: exactly K steps, no instrumentation between the launches.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -505,6 +538,13 @@ def main():
                     "mfma_frac_step": round(flops_step / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                     "hbm_frac_step": round((4 if passes == 1 else 6) * kv_bytes / (ms_step * 1e-3) / 1e9
                                            / HBM_PEAK_GBS, 4)}
+        if calib:
+            # the same position against what this GPU sustained in the run:
+            # the MFMA probe, or for a bandwidth-bound kernel the streaming
+            # read (encode: reads only) or the copy (decode: reads K, writes Y)
+            ref = calib["mfma_bf16_tflops"] if on_mfma else (calib["read_gbs"] if dominant == "encode_partial"
+                                                             else calib["copy_gbs"])
+            roofline["frac_of_calibrated"] = round(achieved / ref, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -558,6 +598,7 @@ def main():
                    "plan": F.flare_describe_plan(op, w.B, w.H, w.N, w.M, w.D, Q.dtype)},
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kern.items()},
         "roofline": roofline,
+        "calibration": calib,
         "cold": cold,
         "cpu_baseline": cpu,
     }

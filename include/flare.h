@@ -347,6 +347,29 @@ flare_status flare_timing_read(double* ms, int64_t* count);
  * hardware memory counters to bytes. */
 flare_status flare_copy_kernel(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
+/* Peak probes for measurement: fixed instruction streams of known size,
+ * launched over the whole chip (four waves per SIMD on 256 compute units)
+ * on `stream`, for the caller to time with events; their rate is what the
+ * GPU sustains at its clock of the moment.
+ *   FLARE_PROBE_MFMA_BF16: each wave issues iters x 4 independent
+ *     v_mfma_f32_32x32x16_bf16 (32768 flops each);
+ *   FLARE_PROBE_EXP: each lane evaluates iters x 16 independent v_exp_f32.
+ * `out` (device memory, at least flare_probe_lanes() floats) receives one
+ * value per lane so that nothing is elided. *work (host) receives the work
+ * launched: flops, or exponentials. 1 <= iters <= 2^20, else
+ * FLARE_ERR_INVALID_ARG; an unknown kind is FLARE_ERR_INVALID_ARG. */
+typedef int32_t flare_probe;
+enum { FLARE_PROBE_MFMA_BF16 = 0, FLARE_PROBE_EXP = 1 };
+size_t flare_probe_lanes(void);
+flare_status flare_probe_peak(flare_probe kind, int64_t iters, float* out, size_t out_floats, double* work,
+                              hipStream_t stream);
+
+/* Streaming read of `bytes` bytes (multiple of 16, 16-byte aligned) by a
+ * grid of flare_probe_lanes() lanes, each folding what it reads into one
+ * float of `out` (at least flare_probe_lanes() floats): a read-only kernel
+ * of known traffic, to calibrate streaming-read bandwidth. */
+flare_status flare_read_kernel(const void* src, size_t bytes, float* out, size_t out_floats, hipStream_t stream);
+
 /* Launch plan the library would use (for logs): writes a short text into
  * buf (up to len bytes incl. the terminator). */
 flare_status flare_describe_plan(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,

@@ -984,6 +984,32 @@ flare_status flare_copy_kernel(const void* src, void* dst, size_t bytes, hipStre
     return FLARE_OK;
 }
 
+size_t flare_probe_lanes(void) { return size_t(flare::kProbeLanes); }
+
+flare_status flare_read_kernel(const void* src, size_t bytes, float* out, size_t out_floats, hipStream_t stream) {
+    g_last_error.clear();
+    if (!src || !out) return fail(FLARE_ERR_INVALID_ARG, "null pointer");
+    if (bytes % 16 || uintptr_t(src) % 16) return fail(FLARE_ERR_INVALID_ARG, "read needs a 16-byte aligned pointer and size");
+    if (out_floats < size_t(flare::kProbeLanes)) return fail(FLARE_ERR_INVALID_ARG, "out holds fewer than flare_probe_lanes() floats");
+    const hipError_t e = flare::launch_read(src, bytes, out, stream);
+    if (e != hipSuccess) return hip_fail(e, "read kernel");
+    return FLARE_OK;
+}
+
+flare_status flare_probe_peak(flare_probe kind, int64_t iters, float* out, size_t out_floats, double* work,
+                              hipStream_t stream) {
+    g_last_error.clear();
+    if (kind != FLARE_PROBE_MFMA_BF16 && kind != FLARE_PROBE_EXP) return fail(FLARE_ERR_INVALID_ARG, "bad probe kind");
+    if (iters < 1 || iters > (int64_t(1) << 20)) return fail(FLARE_ERR_INVALID_ARG, "iters must be in [1, 2^20]");
+    if (!out || !work) return fail(FLARE_ERR_INVALID_ARG, "null pointer");
+    if (out_floats < size_t(flare::kProbeLanes)) return fail(FLARE_ERR_INVALID_ARG, "out holds fewer than flare_probe_lanes() floats");
+    const double lanes = double(flare::kProbeLanes);
+    *work = kind == FLARE_PROBE_MFMA_BF16 ? lanes / 64.0 * double(iters) * 4.0 * 32768.0 : lanes * double(iters) * 16.0;
+    const hipError_t e = flare::launch_probe(int(kind), int(iters), out, stream);
+    if (e != hipSuccess) return hip_fail(e, "probe kernel");
+    return FLARE_OK;
+}
+
 flare_status flare_describe_plan(flare_op op, int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
                                  flare_dtype dtype, char* buf, size_t len) {
     g_last_error.clear();

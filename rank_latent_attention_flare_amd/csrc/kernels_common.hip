@@ -305,6 +305,58 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
         dst[i] = src[i];
 }
 
+// Peak probes: fixed instruction streams of known size over the whole chip,
+// for the measurement harness to time. Each lane writes one float (the
+// chains' results) so that nothing is elided.
+typedef __bf16 bf16x8p __attribute__((ext_vector_type(8)));
+typedef float f32x16p __attribute__((ext_vector_type(16)));
+
+// Four independent chains of v_mfma_f32_32x32x16_bf16 per wave.
+__global__ __launch_bounds__(256) void probe_mfma_kernel(float* __restrict__ out, int iters) {
+    const int lane = threadIdx.x & 63;
+    bf16x8p a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(1e-3f * (lane + i));
+        b[i] = (__bf16)(1e-3f * (lane - i));
+    }
+    f32x16p c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+    }
+    out[blockIdx.x * 256 + threadIdx.x] = c0[0] + c1[5] + c2[10] + c3[15];
+}
+
+// Sixteen independent chains x <- 2^(-x) of v_exp_f32 per lane (values stay
+// in [0.5, 1]; the negation is an operand modifier).
+__global__ __launch_bounds__(256) void probe_exp_kernel(float* __restrict__ out, int iters) {
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = 0.5f + 0.03f * j + 1e-5f * threadIdx.x;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = __builtin_amdgcn_exp2f(-x[j]);
+    }
+    float r = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r += x[j];
+    out[blockIdx.x * 256 + threadIdx.x] = r;
+}
+
+// Streaming read of n16 16-byte vectors (grid-stride): each lane sums what it
+// read into one float of `out`, so the loads are not elided.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, float* __restrict__ out, size_t n16) {
+    uint32_t acc = 0;
+    for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
+        const u32x4 v = src[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    out[blockIdx.x * 256 + threadIdx.x] = (float)(acc & 0xffff);
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* __restrict__ dst, size_t n16) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) dst[i] = z;
@@ -449,6 +501,24 @@ hipError_t launch_batch_sum(void* dst, const void* base, const void* add, int B,
     else
         FLARE_LAUNCH(batch_sum_kernel<float>, dim3(elementwise_blocks(n)), dim3(256), 0, s, (float*)dst,
                            (const float*)base, (const float*)add, B, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe(int kind, int iters, float* out, hipStream_t s) {
+    const dim3 grid(kProbeLanes / 256), block(256);
+    if (kind == 0)
+        FLARE_LAUNCH(probe_mfma_kernel, grid, block, 0, s, out, iters);
+    else if (kind == 1)
+        FLARE_LAUNCH(probe_exp_kernel, grid, block, 0, s, out, iters);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_read(const void* src, size_t bytes, float* out, hipStream_t s) {
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return hipSuccess;
+    FLARE_LAUNCH(read_kernel, dim3(kProbeLanes / 256), dim3(256), 0, s, (const u32x4*)src, out, n16);
     return hipGetLastError();
 }
 

@@ -159,6 +159,12 @@ int f32_lanes_dec(int64_t tokens, int D);  // fp32 lanes per token (decode; toke
 hipError_t launch_encode_f32(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+// Peak probes over the whole chip (kind 0: bf16 MFMA, 1: v_exp_f32); one
+// float per lane to `out` (kProbeLanes lanes: four waves per SIMD of 256 CUs).
+constexpr int kProbeLanes = 256 * 4 * 4 * 64;
+hipError_t launch_probe(int kind, int iters, float* out, hipStream_t s);
+// Streaming read of `bytes` (one float per probe lane to `out`).
+hipError_t launch_read(const void* src, size_t bytes, float* out, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // elementwise helpers (bf16 or fp32 storage; sums in fp32, rounded once)
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s);  // bytes % 16 == 0

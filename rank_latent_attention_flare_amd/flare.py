@@ -90,6 +90,12 @@ def lib() -> ctypes.CDLL:
         L.flare_timing_read.restype = ctypes.c_int
         L.flare_copy_kernel.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
         L.flare_copy_kernel.restype = ctypes.c_int
+        L.flare_read_kernel.argtypes = [_vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _vp]
+        L.flare_read_kernel.restype = ctypes.c_int
+        L.flare_probe_lanes.argtypes = []
+        L.flare_probe_lanes.restype = ctypes.c_size_t
+        L.flare_probe_peak.argtypes = [ctypes.c_int, _i64, _vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double), _vp]
+        L.flare_probe_peak.restype = ctypes.c_int
         L.flare_describe_plan.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                           ctypes.c_char_p, ctypes.c_size_t]
         L.flare_describe_plan.restype = ctypes.c_int
@@ -362,6 +368,31 @@ def flare_timing_read():
     cnt = (_i64 * FLARE_KERNEL_KINDS)()
     _raise(lib().flare_timing_read(ms, cnt))
     return {KERNEL_KIND_NAMES[i]: (ms[i], cnt[i]) for i in range(FLARE_KERNEL_KINDS)}
+
+
+FLARE_PROBE_MFMA_BF16, FLARE_PROBE_EXP = 0, 1
+
+
+def flare_probe_peak(kind: int, iters: int, out: torch.Tensor, stream=None) -> float:
+    """Launch a peak probe (FLARE_PROBE_MFMA_BF16 or FLARE_PROBE_EXP) on the stream; returns the work
+    launched (flops, or exponentials). `out` is a float32 device tensor of at least flare_probe_lanes()."""
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 device tensor")
+    work = ctypes.c_double(0.0)
+    _raise(lib().flare_probe_peak(kind, iters, out.data_ptr(), out.numel(), ctypes.byref(work), _stream(stream)))
+    return work.value
+
+
+def flare_read_kernel(src: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """Streaming read of all of src's bytes (a calibration kernel); out: float32, >= flare_probe_lanes()."""
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 device tensor")
+    _raise(lib().flare_read_kernel(src.data_ptr(), src.numel() * src.element_size(), out.data_ptr(), out.numel(),
+                                   _stream(stream)))
+
+
+def flare_probe_lanes() -> int:
+    return int(lib().flare_probe_lanes())
 
 
 def flare_copy_kernel(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

@@ -255,3 +255,27 @@ def test_noalloc_rejects_oversized_workspace():
     assert L.flare_forward_noalloc(*args) == UNSUPPORTED
     assert "static scratch" in L.flare_last_error().decode()
     assert L.flare_forward_noalloc(PQ, PK, PV, PY, 0, 1, 10, 10, 64, F.FLARE_BF16, None) == INVALID
+
+
+def test_probe_validates_before_launch():
+    import ctypes
+    L = F.lib()
+    n = L.flare_probe_lanes()
+    assert n == 256 * 4 * 4 * 64
+    work = ctypes.c_double(0.0)
+    fn = L.flare_probe_peak
+    assert fn(7, 10, PY, n, ctypes.byref(work), None) == INVALID and "kind" in L.flare_last_error().decode()
+    assert fn(F.FLARE_PROBE_MFMA_BF16, 0, PY, n, ctypes.byref(work), None) == INVALID
+    assert fn(F.FLARE_PROBE_EXP, (1 << 20) + 1, PY, n, ctypes.byref(work), None) == INVALID
+    assert fn(F.FLARE_PROBE_EXP, 10, None, n, ctypes.byref(work), None) == INVALID
+    assert fn(F.FLARE_PROBE_EXP, 10, PY, n - 1, ctypes.byref(work), None) == INVALID
+    assert fn(F.FLARE_PROBE_EXP, 10, PY, n, None, None) == INVALID
+
+
+def test_read_kernel_validates_before_launch():
+    L = F.lib()
+    n = L.flare_probe_lanes()
+    assert L.flare_read_kernel(None, 1024, PY, n, None) == INVALID
+    assert L.flare_read_kernel(PK, 1000, PY, n, None) == INVALID  # not a multiple of 16
+    assert L.flare_read_kernel(PK + 8, 1024, PY, n, None) == INVALID
+    assert L.flare_read_kernel(PK, 1024, PY, n - 1, None) == INVALID
