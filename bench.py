@@ -348,37 +348,6 @@ def main():
         fn(Q, K, V, out=Y, workspace=ws)
     torch.cuda.synchronize()
 
-    # In-run peak calibration, at the clocks the warm GPU runs at: the plain
-    # copy kernel (1:1 read/write HBM traffic), the bf16 MFMA probe and the
-    # v_exp_f32 probe, each launched once untimed and once timed with events.
-    calib = None
-    if not args.no_calibrate:
-        def timed_once(launch):
-            launch()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            r = launch()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e-3, r
-        nb = max(args.calib_copy_mib, 64) << 20
-        ca = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        cb = torch.empty_like(ca)
-        t_copy, _ = timed_once(lambda: F.flare_copy_kernel(ca, cb))
-        probe_out = torch.empty(F.flare_probe_lanes(), dtype=torch.float32, device="cuda")
-        t_read, _ = timed_once(lambda: F.flare_read_kernel(ca, probe_out))
-        del ca, cb
-        t_mfma, mfma_work = timed_once(lambda: F.flare_probe_peak(F.FLARE_PROBE_MFMA_BF16, 2000, probe_out))
-        t_exp, exp_work = timed_once(lambda: F.flare_probe_peak(F.FLARE_PROBE_EXP, 4000, probe_out))
-        calib = {"read_gbs": round(nb / t_read / 1e9, 1), "copy_gbs": round(2 * nb / t_copy / 1e9, 1),
-                 "copy_mib": nb >> 20,
-                 "mfma_bf16_tflops": round(mfma_work / t_mfma / 1e12, 1),
-                 "exp_per_s": float(f"{exp_work / t_exp:.4g}"),
-                 "note": "rates this GPU sustained during the run: a streaming read, a plain copy (bytes read "
-                         "+ written), independent v_mfma_f32_32x32x16_bf16 chains and independent v_exp_f32 "
-                         "chains, four waves per SIMD"}
-
     # Timed region: exactly K steps, no instrumentation between the launches.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if args.graph:
@@ -450,6 +419,39 @@ def main():
                 "value_median": round(w.B * w.H * w.N / (med * 1e-3), 1),
                 "kernels": {k: {"avg_us": round(1e3 * ms / cnt, 3), "launches_per_step": cnt / args.steps}
                             for k, (ms, cnt) in kt_cold.items() if cnt}}
+    # In-run peak calibration, after the timed passes (so that the probes'
+    # heat and power do not reach them), at the clocks the warm GPU runs at:
+    # a streaming read and the plain copy kernel (1:1 read/write HBM traffic),
+    # the bf16 MFMA probe and the v_exp_f32 probe, each launched once untimed
+    # and once timed with events.
+    calib = None
+    if not args.no_calibrate:
+        def timed_once(launch):
+            launch()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            r = launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e-3, r
+        nb = max(args.calib_copy_mib, 64) << 20
+        ca = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        cb = torch.empty_like(ca)
+        t_copy, _ = timed_once(lambda: F.flare_copy_kernel(ca, cb))
+        probe_out = torch.empty(F.flare_probe_lanes(), dtype=torch.float32, device="cuda")
+        t_read, _ = timed_once(lambda: F.flare_read_kernel(ca, probe_out))
+        del ca, cb
+        t_mfma, mfma_work = timed_once(lambda: F.flare_probe_peak(F.FLARE_PROBE_MFMA_BF16, 2000, probe_out))
+        t_exp, exp_work = timed_once(lambda: F.flare_probe_peak(F.FLARE_PROBE_EXP, 4000, probe_out))
+        calib = {"read_gbs": round(nb / t_read / 1e9, 1), "copy_gbs": round(2 * nb / t_copy / 1e9, 1),
+                 "copy_mib": nb >> 20,
+                 "mfma_bf16_tflops": round(mfma_work / t_mfma / 1e12, 1),
+                 "exp_per_s": float(f"{exp_work / t_exp:.4g}"),
+                 "note": "rates this GPU sustained during the run: a streaming read, a plain copy (bytes read "
+                         "+ written), independent v_mfma_f32_32x32x16_bf16 chains and independent v_exp_f32 "
+                         "chains, four waves per SIMD"}
+
     outs = grads if args.variant == "backward" else (Y,)
     if not all(torch.isfinite(t.float()).all() for t in outs):
         print("non-finite output", file=sys.stderr)
