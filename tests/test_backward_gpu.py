@@ -40,6 +40,9 @@ CASES = [
     (2, 128, 777, 50, 64, "bf16"),
     # bf16 heads whose Q, Z and dZ do not fit in LDS take the fp32 VALU kernels
     (1, 1, 600, 300, 64, "bf16"),
+    # D = 64 with 256 latents (padded from 250): the latent kernels with four
+    # latent blocks per wave and two token streams
+    (1, 2, 1500, 250, 64, "bf16"),
     # D = 96 and 128: the fp32 VALU kernels (bf16 storage widened), token
     # tiles of 32 in the latent kernels, two columns per lane in the dZ merge
     (1, 2, 500, 40, 128, "f32"),
@@ -193,6 +196,7 @@ PP_CASES = [
     (1, 1, 1, 1, 32, "bf16"),
     (2, 1, 400, 48, 128, "bf16"),
     (1, 2, 300, 20, 96, "f32"),
+    (1, 1, 900, 256, 64, "bf16"),  # encode-only latent kernel with four latent blocks per wave
 ]
 
 
