@@ -599,19 +599,12 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
 // also forms dQ's partial sums, dQ^T[d][m] += K^T[d][n] dl[m][n] over the
 // workgroup's tokens, so that no separate latent-side pass over K, V and dY
 // is needed for dQ.
-// Four 8-byte LDS reads at p, p + 16, p + 32 and p + 48, in inline asm that
-// waits once for all four (the data came by global->LDS transfers the
-// compiler cannot track, so it must not see these reads).
-__device__ __forceinline__ void lds_u32x2_x4(const unsigned char* p, u32x2 (&r)[4]) {
-    asm volatile(
-        "ds_read_b64 %0, %4\n\t"
-        "ds_read_b64 %1, %4 offset:16\n\t"
-        "ds_read_b64 %2, %4 offset:32\n\t"
-        "ds_read_b64 %3, %4 offset:48\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(lds_addr(p))
-        : "memory");
+// 8 bytes from LDS in inline asm that waits for its own result (the data
+// came by a global->LDS transfer the compiler cannot track).
+__device__ __forceinline__ u32x2 lds_u32x2(const unsigned char* p) {
+    u32x2 r;
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(lds_addr(p)) : "memory");
+    return r;
 }
 
 // ENC: the encode's backward alone (first stage of the FLARE++ backward):
@@ -846,20 +839,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
         {
             uint16_t* dK = (uint16_t*)a.dK + hb + nn * sn;
             uint16_t* dV = (uint16_t*)a.dV + hb + nn * sn;
-            // ENC with accum: this lane's stored dK and dV values from the
-            // wave's LDS copy (transfers waited for above), all requested
-            // before one wait: columns d0 = 32 db + 8 g4 + 4 hi sit at byte
-            // 2 d0 = 64 db + 16 g4 + 8 hi of the token's row
-            u32x2 okr[DB][4], ovr[DB][4];
-            if constexpr (ENC) {
-                if (a.accum) {
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        lds_u32x2_x4(oldk + l32 * 2 * D + 8 * hi + 64 * db, okr[db]);
-                        lds_u32x2_x4(oldv + l32 * 2 * D + 8 * hi + 64 * db, ovr[db]);
-                    }
-                }
-            }
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -875,8 +854,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
                     if (a.accum) {  // added to what dK, dV hold (fp32 sum, rounded once)
                         u32x2 ok, ov;
                         if constexpr (ENC) {
-                            ok = okr[db][g4];
-                            ov = ovr[db][g4];
+                            // from this wave's LDS copy (transfers waited for above)
+                            ok = lds_u32x2(oldk + l32 * 2 * D + 2 * d0);
+                            ov = lds_u32x2(oldv + l32 * 2 * D + 2 * d0);
                         } else {
                             ok = *(const u32x2*)(dK + d0);
                             ov = *(const u32x2*)(dV + d0);
