@@ -351,7 +351,7 @@ int decode_groups(const Plan& p, bool z_f32, int m_range = 0, int split = 0) {
     }
     const int hg = split ? 1 : dec_heads(p);
     const int per_cu = flare::dec_wgs_per_cu_bf16(int(p.D), Mr, p.tb, z_f32, hg, split);
-    const int64_t per_wg = 32 * p.tb * (flare::dec_waves_bf16(int(p.D), Mr, p.tb, hg) / hg);
+    const int64_t per_wg = 32 * p.tb * (flare::dec_waves_bf16(int(p.D), Mr, p.tb, hg, split) / hg);
     const int64_t groups = p.BH / hg;
     int64_t G = (int64_t(cus) * per_cu + groups - 1) / groups;
     G = std::max<int64_t>(1, std::min<int64_t>(G, (p.N + per_wg - 1) / per_wg));
@@ -365,7 +365,7 @@ hipError_t run_decode(const Plan& p, const void* Q, int64_t q_bstride, const voi
         // exact per-token maxima, the second merging the first's state
         if (!split_ws) return hipErrorInvalidValue;
         DecodeArgs a{};
-        a.Q = Q; a.q_bstride = q_bstride; a.K = K; a.Z = Z; a.z_f32 = z_f32; a.zmu = nullptr; a.Y = Y;
+        a.Q = Q; a.q_bstride = q_bstride; a.K = K; a.Z = Z; a.z_f32 = z_f32; a.zmu = zmu; a.Y = Y;
         a.sb = p.sb; a.sh = p.sh; a.sn = p.sn;
         a.BH = p.BH; a.H = int(p.H); a.N = int(p.N); a.D = int(p.D);
         a.tb = 1; a.hg = 1; a.c = p.c; a.Mtot = int(p.M);

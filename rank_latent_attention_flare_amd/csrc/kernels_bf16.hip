@@ -837,10 +837,12 @@ constexpr int dec_waves_per_simd(int D, int TB, bool LONG, int NW) {
 // their rows are one contiguous run of HG * D * 2 bytes per token.
 // SPLIT (1 or 2): one of the two launches of a decode whose latents do not fit
 // in LDS. Each covers the latent range [m_off, m_off + M) of the full a.Mtot,
-// against the exact per-token maximum over that range. Launch 1 stores every
-// token's (maximum, sum, unnormalised Y) in fp32; launch 2 merges its own
-// state with it by the log-sum-exp rule (an exact rescaling by powers of two)
-// and writes Y.
+// against the same kind of offset as the other decodes (the encode's merged
+// offsets over that range, else the per-token Cauchy-Schwarz bound), or the
+// exact per-token maximum over the range where a sum falls below the floor.
+// Launch 1 stores every token's (offset, sum, unnormalised Y) in fp32; launch
+// 2 merges its own state with it by the log-sum-exp rule (each side scaled by
+// 2^(its offset - the larger offset)) and writes Y.
 template <int D, int TB, typename ZT, bool LONG, int MBC = 0, int NW = kDecWaves, int HG = 1, int SPLIT = 0>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(dec_waves_per_simd(D, TB, LONG, NW))))
 void decode_bf16(DecodeArgs a) {
@@ -956,7 +958,7 @@ void decode_bf16(DecodeArgs a) {
     float red_in = goff ? -INFINITY : 0.0f;
     const int ht = lane + 64 * slot;  // this thread's index among its head's threads
     if (goff) {
-        for (int m = ht; m < M; m += 64 * WPH) red_in = fmaxf(red_in, a.zmu[(int64_t)bh * M + m]);
+        for (int m = ht; m < M; m += 64 * WPH) red_in = fmaxf(red_in, a.zmu[(int64_t)bh * Mt + a.m_off + m]);
     } else {
         for (int m = ht; m < M; m += 64 * WPH) {
             float s2 = 0.0f;
@@ -1141,7 +1143,14 @@ void decode_bf16(DecodeArgs a) {
             run(ex);
         };
         if constexpr (SPLIT > 0) {
-            exact_run();
+            // against the bound first (as below), with exact maxima only when
+            // a sum falls below the floor; the state records the offset used
+            run(nu);
+            float off0 = nu[0];
+            if (wave_any(!(tau[0] >= kTauFloor))) {
+                exact_run();
+                off0 = ex[0];
+            }
             // state of token l32 of block bk, in the accumulator's register layout
             const int64_t pb = (int64_t)bh * nblk + bk;
             float* py = a.part_y + pb * (32 * D) + 4 * lane;
@@ -1156,14 +1165,14 @@ void decode_bf16(DecodeArgs a) {
                         *(f32x4*)(py + (db * 4 + g4) * 256) = v;
                     }
                 if (hi == 0) {
-                    const f32x2 v = {ex[0], tau[0]};
+                    const f32x2 v = {off0, tau[0]};
                     *(f32x2*)pnt = v;
                 }
                 return;
             } else {
                 const f32x2 st = *(const f32x2*)pnt;
-                const float nm = fmaxf(st[0], ex[0]);
-                const float wa = exp2_fast(st[0] - nm), wb = exp2_fast(ex[0] - nm);
+                const float nm = fmaxf(st[0], off0);
+                const float wa = exp2_fast(st[0] - nm), wb = exp2_fast(off0 - nm);
                 const float inv = __builtin_amdgcn_rcpf(fmaf(wa, st[1], wb * tau[0]));
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
@@ -1394,11 +1403,14 @@ hipError_t allow_dec_lds(const void* fn) {
     return e;
 }
 
-// The two launches of the split decode (D = 128, M > 256).
+// The two launches of the split decode (D = 128, M > 256), in workgroups of
+// eight waves that share one LDS copy of Q and Z^T (two waves per SIMD where a
+// workgroup of four would leave one).
+constexpr int kDecSplitWaves = 8;
 template <typename ZT>
 const void* dec_split_kernel(int split) {
-    if (split == 1) return (const void*)decode_bf16<128, 1, ZT, false, 0, kDecWaves, 1, 1>;
-    return (const void*)decode_bf16<128, 1, ZT, false, 0, kDecWaves, 1, 2>;
+    if (split == 1) return (const void*)decode_bf16<128, 1, ZT, false, 0, kDecSplitWaves, 1, 1>;
+    return (const void*)decode_bf16<128, 1, ZT, false, 0, kDecSplitWaves, 1, 2>;
 }
 
 template <int D, int TB, typename ZT>
@@ -1421,7 +1433,7 @@ hipError_t launch_dec_tb(const DecodeArgs& a, hipStream_t s) {
     }
     DecodeArgs arg = a;
     void* args[] = {&arg};
-    return launch_raw(fn, dim3(a.G, a.BH / a.hg), dim3(64 * dec_waves_bf16(D, a.M, TB, a.hg)), args, lds, s);
+    return launch_raw(fn, dim3(a.G, a.BH / a.hg), dim3(64 * dec_waves_bf16(D, a.M, TB, a.hg, a.split)), args, lds, s);
 }
 
 template <int D, typename ZT>
@@ -1474,7 +1486,7 @@ int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32, int hg, int split) {
     if (!fn) return 1;
     if (lds > 65536 && allow_dec_lds(fn) != hipSuccess) return 1;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * dec_waves_bf16(D, M, tb, hg), lds) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * dec_waves_bf16(D, M, tb, hg, split), lds) != hipSuccess ||
         n < 1)
         return 1;
     slot.store(n, std::memory_order_relaxed);
@@ -1486,8 +1498,9 @@ int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32, int hg, int split) {
 int dec_tb_bf16(int, int) { return 1; }
 bool dec_tb_built_bf16(int D, int Mp, int tb) { return tb == 1 || (tb == 2 && D <= 64 && Mp <= 256); }
 
-int dec_waves_bf16(int D, int M, int tb, int hg) {
+int dec_waves_bf16(int D, int M, int tb, int hg, int split) {
     const int Mp = (M + 31) / 32 * 32;
+    if (split) return kDecSplitWaves;
     if (hg == 4) return 8;                  // two token slots of four heads
     if (hg == 2) return D == 32 ? 8 : (M == 256 ? 12 : kDecWaves);
     if (D != 64 || tb != 1) return kDecWaves;

@@ -113,7 +113,7 @@ struct DecodeArgs {
     const void* K;       // [B][H][N][D] or [B][N][H][D] (strides below)
     const void* Z;       // [BH][M][D], fp32 or operator dtype
     bool z_f32;
-    const float* zmu;    // optional [BH][M] merged encode offsets; null: per-token bound
+    const float* zmu;    // optional [BH][M] (split: [BH][Mtot]) merged encode offsets; null: per-token bound
     void* Y;             // same layout as K
     int64_t sb, sh, sn;  // K and Y strides in elements: batch, head, token
     int BH, H, N, M, Mp, D;
@@ -125,7 +125,7 @@ struct DecodeArgs {
     int split;           // 0: whole range; 1: first launch; 2: second launch
     int m_off, Mtot;
     float* part_y;       // [BH][ceil(N/32)][32 * D] unnormalised Y of the first range
-    float* part_nt;      // [BH][ceil(N/32) * 32][2] its per-token (maximum, sum)
+    float* part_nt;      // [BH][ceil(N/32) * 32][2] its per-token (offset, sum)
     float c;
 };
 
@@ -145,7 +145,7 @@ int dec_tb_bf16(int D, int Mp);  // 32-token blocks per wave per step (the libra
 bool dec_tb_built_bf16(int D, int Mp, int tb);  // whether a decode with tb blocks is built for (D, Mp)
 int dec_wgs_per_cu_bf16(int D, int M, int tb, bool z_f32, int hg, int split);  // resident decode workgroups per CU (cached)
 int dec_lds_bytes_bf16(int Mp, int D, int hg);
-int dec_waves_bf16(int D, int M, int tb, int hg);  // waves per bf16 decode workgroup
+int dec_waves_bf16(int D, int M, int tb, int hg, int split = 0);  // waves per bf16 decode workgroup
 // Heads per bf16 decode workgroup: groups of 2 or 4 heads in the token-major
 // layout (for the exact latent counts they are built for), 1 otherwise.
 int dec_heads_bf16(int D, int M, int H, int tb, bool token_major);
