@@ -197,7 +197,8 @@ struct EncShape {
     static constexpr int NW = WM * WT;
     static constexpr int T = 64;
     static constexpr int SB = T / (32 * WT);
-    static constexpr int SBYTES = 2 * T * RB;  // K tile then V tile
+    static constexpr int TBY = T * RB;         // one tensor's tile
+    static constexpr int SBYTES = 2 * TBY;     // K and V of one stage
     // ring depth: 4 stages of 8 KB tiles (D = 32; measured best on MI355X),
     // otherwise as many stages as fit in 64 KB, at least 3
     static constexpr int NS = SBYTES <= 8192 ? 4 : ((65536 / SBYTES) < 3 ? 3 : ((65536 / SBYTES) > 8 ? 8 : (65536 / SBYTES)));
@@ -205,6 +206,9 @@ struct EncShape {
     static constexpr int IPW = PIECES >= NW ? PIECES / NW : 1;  // per issuing wave
     static constexpr int NWI = PIECES / IPW;       // issuing waves: the first NWI
     static constexpr int MERGE_BYTES = (WT - 1) * WM * MBW * (16 * DB + 2) * 64 * 4;
+    // LDS: the K tiles of all NS stages, then the V tiles of all stages (so
+    // that a stage's offset within either ring fits the 16-bit LDS instruction
+    // offset at D = 128 too)
     static constexpr int SMEM = NS * SBYTES > MERGE_BYTES ? NS * SBYTES : MERGE_BYTES;
     static_assert(SB >= 1 && SB * 32 * WT == T, "tile split");
     static_assert(IPW * NWI == PIECES && NWI <= NW, "tile transfer split");
@@ -214,7 +218,7 @@ template <int D, int MBW, int WM, int WT>
 __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a) {
     using Sh = EncShape<D, MBW, WM, WT>;
     constexpr int KB = Sh::KB, DB = Sh::DB, CH = Sh::CH, RB = Sh::RB, NW = Sh::NW, T = Sh::T, SB = Sh::SB;
-    constexpr int NS = Sh::NS, IPW = Sh::IPW, NWI = Sh::NWI, SBYTES = Sh::SBYTES;
+    constexpr int NS = Sh::NS, IPW = Sh::IPW, NWI = Sh::NWI, TBY = Sh::TBY;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Sh::SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     auto issue = [&](int tile, int stage) __attribute__((always_inline)) {
         if (wave >= NWI) return;
         const int t0 = n0 + tile * T;
-        unsigned char* st = smem + stage * SBYTES;
+        unsigned char* st = smem + stage * TBY;  // K; V at st + NS * TBY
         if (fixed_off && t0 + T <= n1) {
             const unsigned char* kg = (const unsigned char*)(Kb + (int64_t)t0 * a.sn);
             const unsigned char* vg = (const unsigned char*)(Vb + (int64_t)t0 * a.sn);
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
                 // compiler does not merge these loads with the clamped ones)
                 uint32_t po = poff[i];
                 asm volatile("" : "+v"(po));
-                dma16<true>(vg + po, st + T * RB + pc * 1024);
+                dma16<true>(vg + po, st + NS * TBY + pc * 1024);
                 dma16<KNT>(kg + po, st + pc * 1024);
             }
             asm volatile("" ::: "memory");
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
                 const int n = min(t0 + row, n1 - 1);
                 const int64_t g = (int64_t)n * a.sn + ch * 8;
                 dma16<KNT>(Kb + g, st + pc * 1024);
-                dma16<true>(Vb + g, st + T * RB + pc * 1024);
+                dma16<true>(Vb + g, st + NS * TBY + pc * 1024);
             }
         }
     };
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
 
     // LDS byte offsets of this lane's operands in stage 0, sub-block 0 of its
     // token group. Stage s, sub-block j and (for V) k-half kp add
-    // s*SBYTES + 32*j*RB + 16*kp*RB: the row swizzle repeats every 16 rows,
+    // s*TBY + 32*j*RB + 16*kp*RB: the row swizzle repeats every 16 rows,
     // so those are constants (instruction offsets in the unrolled loop).
     // K rows as A operands of S^T = K Q^T; V^T operands (A of acc^T += V^T
     // P^T; k = 16 tokens) read transposed from the row-major V tile: lane i of
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             for (int second = 0; second < 2; ++second) {
                 const int row = r0 + 8 * (g >> 1) + (gi >> 2) + 4 * second;
                 const int dcol = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
-                vofs[db][second] = lds_addr(smem) + T * RB + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
+                vofs[db][second] = lds_addr(smem) + NS * TBY + tile_off<D>(row, dcol >> 3) + ((dcol >> 2) & 1) * 8;
             }
     }
 
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
         const int valid = n1 - (n0 + it * T);
         static_for<0, SB>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
-            constexpr int SOFF = S * SBYTES + 32 * j * RB;  // stage and sub-block
+            constexpr int SOFF = S * TBY + 32 * j * RB;  // stage and sub-block
             const int nv = valid - 32 * (wt * SB + j);     // valid tokens in this sub-block
             if (tail && nv <= 0) return;
             // S^T for the 32 tokens x (32 * MBW) latents.
@@ -461,8 +465,8 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     };
     int it = 0;
     // Full tiles NS at a time, each stage's offsets constant (they fit the
-    // 16-bit instruction offset for D <= 64); then the rest one at a time.
-    constexpr bool kImm = (NS - 1) * SBYTES + (SB - 1) * 32 * RB + 16 * RB < 65536;
+    // 16-bit instruction offset); then the rest one at a time.
+    constexpr bool kImm = (NS - 1) * TBY + (SB - 1) * 32 * RB + 16 * RB < 65536;
     if constexpr (kImm) {
         for (; it + NS <= nfull; it += NS)
             static_for<0, NS>([&](auto sc) __attribute__((always_inline)) {
@@ -472,7 +476,7 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
     }
     for (; it < ntiles; ++it) {
         sync_issue(it);
-        tile(it, it == nfull, std::integral_constant<int, 0>{}, (it % NS) * SBYTES);
+        tile(it, it == nfull, std::integral_constant<int, 0>{}, (it % NS) * TBY);
     }
 
     // Merge the WT token waves of each latent group (tile buffers are free
