@@ -361,23 +361,43 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             }
     }
 
+    constexpr bool kLogitsFirst = MBW == 1 && SB > 1 && D == 128;
     // Tile `it` in LDS stage S (a constant) plus sro bytes (0 in the unrolled
     // loop; the stage offset otherwise). tail: the chunk's last, ragged tile,
     // whose sub-blocks may be partial or empty.
     auto tile = [&](int it, bool tail, auto stage_c, int sro) __attribute__((always_inline)) {
         constexpr int S = decltype(stage_c)::value;
         const int valid = n1 - (n0 + it * T);
-        static_for<0, SB>([&](auto jc) __attribute__((always_inline)) {
+        // Logits S^T of sub-block j: 32 tokens x (32 * MBW) latents (bf16
+        // products, fp32 accumulation), padded tokens masked.
+        auto logits = [&](auto jc, f32x16 (&Sx)[MBW]) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
             constexpr int SOFF = S * TBY + 32 * j * RB;  // stage and sub-block
             const int nv = valid - 32 * (wt * SB + j);     // valid tokens in this sub-block
-            if (tail && nv <= 0) return;
-            // S^T for the 32 tokens x (32 * MBW) latents.
             bf16x8 ka[KB];
             uint32_t kad[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) kad[kb] = kofs[kb] + sro;
             lds_b128<KB, SOFF>(kad, ka);
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb) {
+                Sx[mb] = mfma(ka[0], qop[mb][0], f32x16{});
+#pragma unroll
+                for (int kb = 1; kb < KB; ++kb) Sx[mb] = mfma(ka[kb], qop[mb][kb], Sx[mb]);
+                if (tail) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int tok = 16 * (i >> 3) + 8 * hi + (i & 7);
+                        if (tok >= nv) Sx[mb][i] = -INFINITY;
+                    }
+                }
+            }
+        };
+        // Softmax of sub-block j against the running offsets, then
+        // acc^T += V^T P^T.
+        auto update = [&](auto jc, f32x16 (&Sx)[MBW]) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int SOFF = S * TBY + 32 * j * RB;
             constexpr int NOP = 2 * DB;
             bf16x8 va[NOP];
             auto read_v = [&]() __attribute__((always_inline)) {
@@ -389,27 +409,11 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
                         va[o + 1]);
                 });
             };
-            // At D >= 64 the reads are issued here, so their latency overlaps
-            // the logits and the softmax (measured 3-4% faster on MI355X); at
-            // D = 32 after the softmax (faster there).
+            // At D >= 64 the reads are issued first, so their latency overlaps
+            // the softmax (measured 3-4% faster on MI355X); at D = 32 after
+            // the softmax (faster there).
             constexpr bool kVEarly = D >= 64;
             if constexpr (kVEarly) read_v();
-            auto mask = [&](f32x16& X) __attribute__((always_inline)) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int tok = 16 * (i >> 3) + 8 * hi + (i & 7);
-                    if (tok >= nv) X[i] = -INFINITY;
-                }
-            };
-            // logits S (bf16 products, fp32 accumulation)
-            f32x16 Sx[MBW];
-#pragma unroll
-            for (int mb = 0; mb < MBW; ++mb) {
-                Sx[mb] = mfma(ka[0], qop[mb][0], f32x16{});
-#pragma unroll
-                for (int kb = 1; kb < KB; ++kb) Sx[mb] = mfma(ka[kb], qop[mb][kb], Sx[mb]);
-                if (tail) mask(Sx[mb]);
-            }
             bf16x8 pb[MBW][2];
             float ts[MBW];
             bool bad = false;
@@ -440,7 +444,6 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
             }
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) ps[mb] += ts[mb];
-            // acc^T += V^T P^T
             if constexpr (!kVEarly) read_v();
 #pragma unroll
             for (int o = 0; o < NOP; ++o) {
@@ -448,7 +451,27 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
 #pragma unroll
                 for (int mb = 0; mb < MBW; ++mb) acc[mb][db] = mfma(va[o], pb[mb][kp], acc[mb][db]);
             }
-        });
+        };
+        auto live = [&](int j) __attribute__((always_inline)) { return !tail || valid - 32 * (wt * SB + j) > 0; };
+        if constexpr (kLogitsFirst) {
+            // With one latent block per wave, the logits of every sub-block
+            // go to the matrix core before the first softmax, which then runs
+            // on the VALU while they complete.
+            f32x16 Sx[SB][MBW];
+            static_for<0, SB>([&](auto jc) __attribute__((always_inline)) {
+                if (live(decltype(jc)::value)) logits(jc, Sx[decltype(jc)::value]);
+            });
+            static_for<0, SB>([&](auto jc) __attribute__((always_inline)) {
+                if (live(decltype(jc)::value)) update(jc, Sx[decltype(jc)::value]);
+            });
+        } else {
+            static_for<0, SB>([&](auto jc) __attribute__((always_inline)) {
+                if (!live(decltype(jc)::value)) return;
+                f32x16 Sx[MBW];
+                logits(jc, Sx);
+                update(jc, Sx);
+            });
+        }
     };
     const bool ragged = (n1 - n0) % T != 0;
     const int nfull = ragged ? ntiles - 1 : ntiles;
