@@ -379,11 +379,16 @@ __global__ __launch_bounds__(64 * WM * WT) void encode_partial_bf16(EncodeArgs a
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) kad[kb] = kofs[kb] + sro;
             lds_b128<KB, SOFF>(kad, ka);
+            // At D = 32 the wave issues its logit MFMAs at raised priority, so
+            // the arbiter takes them ahead of other waves' softmax work
+            // (measured 6% faster on MI355X; slower at D = 64).
+            if constexpr (D == 32) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
                 Sx[mb] = mfma(ka[0], qop[mb][0], f32x16{});
 #pragma unroll
                 for (int kb = 1; kb < KB; ++kb) Sx[mb] = mfma(ka[kb], qop[mb][kb], Sx[mb]);
+                if constexpr (D == 32) { if (mb == MBW - 1) __builtin_amdgcn_s_setprio(0); }
                 if (tail) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
