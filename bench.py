@@ -116,13 +116,15 @@ def kernel_kind(name: str) -> str | None:
 
 
 def pmc_summary(fetch_csv: str, write_csv: str, workload, layout: str, variant: str, copy_mib: int,
-                kernel_trace_csv: str | None, bench_args: str = "") -> list:
+                kernel_trace_csv: str | None, bench_args: str = "", trace_args: str = "") -> list:
     """HBM traffic per launch of the forward kernels from two rocprofv3 --pmc
-    runs of a default bench.py run (FETCH_SIZE, then WRITE_SIZE; KiB per
-    dispatch), each scaled so that the same counter over the library's plain
-    copy kernel (copy_mib MiB each way, launched once before the timed steps)
-    reads copy_mib MiB. Returns one record per kernel kind (averages over all
-    its dispatches), with the hash of its source."""
+    runs of bench.py (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, with the
+    arguments bench_args), each scaled so that the same counter over the
+    library's plain copy kernel (copy_mib MiB each way, launched once before
+    the timed steps) reads copy_mib MiB. The optional kernel trace (of a run
+    with the arguments trace_args) gives each kernel's average duration.
+    Returns one record per kernel kind (averages over all its dispatches),
+    with the hash of its source."""
     import csv
 
     def per_dispatch(path: str, counter: str) -> dict:
@@ -176,7 +178,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload, layout: str, variant: 
                "commands": [f"rocprofv3 --pmc {c} -d <out> -o {o} --output-format csv -- python3 bench.py {bench_args}"
                             for c, o in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))]
                + ([f"rocprofv3 --kernel-trace --stats -d <out> -o kt --output-format csv -- python3 bench.py "
-                   f"{bench_args}"] if kernel_trace_csv else [])}
+                   f"{trace_args or bench_args}"] if kernel_trace_csv else [])}
         out.append(rec)
     return out
 
@@ -215,7 +217,9 @@ def parse():
     p.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                    help="FETCH_CSV WRITE_CSV [KERNEL_TRACE_CSV]: write profiles/<kernel>_<workload>_pmc.json (the "
                         "traffic the roofline reports) from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of "
-                        "this script with the same --workload, --layout and --variant, and exit")
+                        "this script with the same --workload, --layout, --variant, --steps, --warmup and "
+                        "--ramp-seconds (the kernel trace: of a run with the same --workload, --layout and --variant "
+                        "and the default steps), and exit")
     p.add_argument("--ramp-seconds", type=float, default=1.0,
                    help="run the step back to back for this long before the warmup steps, so that the GPU "
                         "reaches its steady clocks (a cold MI355X needs ~0.1-0.2 s); 0 disables")
@@ -235,9 +239,12 @@ def main():
             ("" if args.steps == 200 else f" --steps {args.steps}") + \
             ("" if args.warmup == 20 else f" --warmup {args.warmup}") + \
             ("" if args.ramp_seconds == 1.0 else f" --ramp-seconds {args.ramp_seconds:g}")
+        trace_args = f"--workload {args.workload} --no-cpu-baseline" + \
+            ("" if args.layout == "bhnd" else f" --layout {args.layout}") + \
+            ("" if args.variant == "flare" else f" --variant {args.variant}")
         recs = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], w, args.layout, args.variant,
                            args.calib_copy_mib, args.pmc_summary[2] if len(args.pmc_summary) == 3 else None,
-                           bench_args)
+                           bench_args, trace_args)
         for rec in recs:
             path = os.path.join(ROOT, "profiles", f"{rec['kernel']}_{rec['workload']}_pmc.json")
             with open(path, "w") as f:
