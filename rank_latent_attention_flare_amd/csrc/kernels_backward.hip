@@ -686,7 +686,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
         }
     };
     if constexpr (PF) load(blk);
-    const bool padded = M != Mp;
     for (; blk < nblk; blk += bstep) {
         const int n = blk * 32 + l32, nn = min(n, N - 1);
         if constexpr (!PF) load(blk);
@@ -781,10 +780,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
                     const float p_e = exp2_fast(xe);
                     float dl = p_e * (GV[i] - gj);
                     if constexpr (!ENC) {
-                        // p_dec <= 1 for real latents; the clamp keeps padded
-                        // latents (zero rows, last block only) finite
-                        float xd = fmaf(S[i], c, -nu);
-                        if (padded && mb == MB - 1) xd = fminf(xd, 0.0f);
+                        // p_dec <= 1 for real latents (nu is their log2-sum-
+                        // exp2); the clamp keeps padded latents (zero rows,
+                        // last block only) finite. Applied to every block:
+                        // one v_min, where a run-time condition cost three
+                        // instructions per score.
+                        const float xd = fminf(fmaf(S[i], c, -nu), 0.0f);
                         dl = fmaf(exp2_fast(xd), GY[i] - del, dl);
                     }
                     pe[kp][j] = (__bf16)p_e;
