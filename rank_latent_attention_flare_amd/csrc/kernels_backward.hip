@@ -599,13 +599,6 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
 // also forms dQ's partial sums, dQ^T[d][m] += K^T[d][n] dl[m][n] over the
 // workgroup's tokens, so that no separate latent-side pass over K, V and dY
 // is needed for dQ.
-// 8 bytes from LDS in inline asm that waits for its own result (the data
-// came by a global->LDS transfer the compiler cannot track).
-__device__ __forceinline__ u32x2 lds_u32x2(const unsigned char* p) {
-    u32x2 r;
-    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(lds_addr(p)) : "memory");
-    return r;
-}
 
 // ENC: the encode's backward alone (first stage of the FLARE++ backward):
 // dl = A (dZ V^T - gam), no decode weights, no dY.
@@ -625,10 +618,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
     unsigned char* dzs = zs + (ENC ? 0 : Mp * 2 * D);
     float* lam = (float*)(dzs + Mp * 2 * D);  // [Mp] mu* + log2 sig* (+inf for padding)
     float* gam = lam + Mp;                     // [Mp]
-    // ENC with accum: this wave's 32 rows of the old dK and dV, brought in at
-    // the start of each token block (global->LDS transfers, no registers)
-    unsigned char* oldk = (unsigned char*)(gam + Mp) + wave * 2 * (32 * 2 * D);
-    unsigned char* oldv = oldk + 32 * 2 * D;
     // FDQ (dQ fused in): this wave's K rows of the block (zero past N) and
     // its dl tile [token][latent] of the current latent block, bf16 rows
     // (swizzled); the head's dQ^T sums over this wave's tokens stay in
@@ -663,12 +652,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
     // block's are loaded while this one is processed (clamped to the last
     // block, so the loads are unconditional and the compiler's wait before
     // the first use covers exactly them)
-    // (with ENC the LDS reads after the global->LDS transfers make the
-    // compiler wait for every load in flight, and FDQ holds its dQ sums in
-    // the registers a second set would take (at D = 32 at two waves per
-    // SIMD; at D = 64 prefetching there measured 4% slower): there each
-    // block's rows are loaded at its start)
-    constexpr bool PF = !ENC && !FDQ;
+    // (FDQ holds its dQ sums in the registers a second set would take (at
+    // D = 32 at two waves per SIMD; at D = 64 prefetching there measured 4%
+    // slower): there each block's rows are loaded at its start)
+    constexpr bool PF = !FDQ;
     bf16x8 kop[KB], vop[KB], gop[KB], kpf[KB], vpf[KB], gpf[KB];
     float nu, del, nupf = 0.0f, delpf = 0.0f;
     auto load = [&](int bk) {
@@ -697,25 +684,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
         }
         nu = nupf;
         del = delpf;
+        if constexpr (PF) load(min(blk + bstep, nblk - 1));
+        // ENC with accum: this block's old dK and dV (the second stage's
+        // gradients), in the store layout, requested now so that their
+        // latency overlaps the block's work
+        u32x2 okr[ENC ? DB : 1][4], ovr[ENC ? DB : 1][4];
         if constexpr (ENC) {
             if (a.accum) {
-                // 1 KB per transfer: lane l of transfer i fills bytes
-                // i*1024 + 16*l of the row-major [32][D] tile (rows past N
-                // repeat the last token)
+                const uint16_t* oK = (const uint16_t*)a.dK + hb + nn * sn;
+                const uint16_t* oV = (const uint16_t*)a.dV + hb + nn * sn;
 #pragma unroll
-                for (int i = 0; i < D / 16; ++i) {
-                    const int byte = i * 1024 + 16 * lane;
-                    const int row = byte / (2 * D), col = byte % (2 * D);
-                    const int64_t go = (hb + min(blk * 32 + row, N - 1) * sn) * 2 + col;
-                    __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.dK + go),
-                                                     (void*)(oldk + i * 1024), 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds((const void*)((const unsigned char*)a.dV + go),
-                                                     (void*)(oldv + i * 1024), 16, 0, 0);
-                }
-                asm volatile("" ::: "memory");  // the transfers stay ahead of the next block's loads
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int d0 = 32 * db + 8 * g4 + 4 * hi;
+                        okr[db][g4] = *(const u32x2*)(oK + d0);
+                        ovr[db][g4] = *(const u32x2*)(oV + d0);
+                    }
             }
         }
-        if constexpr (PF) load(min(blk + bstep, nblk - 1));
         f32x16 dk[DB], dv[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -829,11 +816,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
             }
         }
         // register r of lane l: d = 32 db + 8 (r/4) + 4 hi + r%4, token l32
-        if constexpr (ENC) {
-            // this block's transfers landed (only the next block's 2 KB
-            // loads, if any, were issued after them)
-            if (a.accum) wait_vmcnt<PF ? 2 * KB : 0>();
-        }
         // every lane stores: lanes past N repeat token N - 1's rows and
         // values, so the stores are unconditional and the next wait stays
         // exact
@@ -855,9 +837,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
                     if (a.accum) {  // added to what dK, dV hold (fp32 sum, rounded once)
                         u32x2 ok, ov;
                         if constexpr (ENC) {
-                            // from this wave's LDS copy (transfers waited for above)
-                            ok = lds_u32x2(oldk + l32 * 2 * D + 2 * d0);
-                            ov = lds_u32x2(oldv + l32 * 2 * D + 2 * d0);
+                            ok = okr[db][g4];
+                            ov = ovr[db][g4];
                         } else {
                             ok = *(const u32x2*)(dK + d0);
                             ov = *(const u32x2*)(dV + d0);
@@ -1290,7 +1271,7 @@ hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
 
 hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
     const int Mp = (a.M + 31) / 32 * 32;
-    const int lds = (a.enc_only ? 2 : 3) * Mp * 2 * a.D + 8 * Mp + (a.enc_only && a.accum ? 4 * 2 * 32 * 2 * a.D : 0);
+    const int lds = (a.enc_only ? 2 : 3) * Mp * 2 * a.D + 8 * Mp;
     if (a.enc_only) {
         if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32, true>, a, lds, s);
         if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64, true>, a, lds, s);
