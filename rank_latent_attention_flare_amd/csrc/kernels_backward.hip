@@ -375,13 +375,14 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
     // <= 1 everywhere; a token whose sum falls below 2^-90 is redone against
     // its exact maximum.
     float* red = (float*)(zs + Mp * 2 * D);
-    // FDZ (dZ fused in): this wave's dY rows of the block (zero past N) and
-    // its Bt tile [token][latent] of the current latent block, bf16 rows
+    // FDZ (dZ fused in): this wave's dY rows of the block, scaled by the
+    // token's 1/tau (zero past N), and its tiles [token][latent] of the
+    // sweep's weights 2^(c l - nu) for each latent block, bf16 rows
     // (swizzled); the head's dZ^T sums over this wave's tokens stay in
     // registers, for up to MBX latent blocks
-    unsigned char* gtile = (unsigned char*)(red + 4) + wave * (32 * 2 * D + 32 * 64);
-    unsigned char* btile = gtile + 32 * 2 * D;
     constexpr int DB = D / 32, MBX = 4 / DB, MBU = FDZ ? MBX : 1;  // 64 accumulator registers
+    unsigned char* gtile = (unsigned char*)(red + 4) + wave * (32 * 2 * D + MBX * 32 * 64);
+    unsigned char* btile = gtile + 32 * 2 * D;
     f32x16 dz[FDZ ? MBX : 1][DB];
 #pragma unroll
     for (int j = 0; j < (FDZ ? MBX : 1); ++j)
@@ -429,7 +430,9 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
             gop[kb] = gpf[kb];
         }
         load(min(blk + bstep, nblk - 1), kpf, gpf);
-        // sums of 2^(c l - nu) and of those weights times <dY, Z[m]>
+        // sums of 2^(c l - nu) and of those weights times <dY, Z[m]>; FDZ:
+        // the weights also go to the wave's tiles, rounded to bf16 (register
+        // i: latent 32 mb + 8 (i/4) + 4 hi + i%4 -> 8 bytes per 4)
         auto sweep = [&](float nu, float& tau, float& pg) {
             tau = 0.0f;
             pg = 0.0f;
@@ -444,19 +447,26 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
                     S = mfma(qa[kb], kop[kb], S);
                     G = mfma(za[kb], gop[kb], G);
                 }
+                float p[16];
                 if (padded && mb == MB - 1) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float p = valid(mb, i) ? exp2_fast(fmaf(S[i], c, -nu)) : 0.0f;
-                        tau += p;
-                        pg = fmaf(p, G[i], pg);
-                    }
+                    for (int i = 0; i < 16; ++i) p[i] = valid(mb, i) ? exp2_fast(fmaf(S[i], c, -nu)) : 0.0f;
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float p = exp2_fast(fmaf(S[i], c, -nu));
-                        tau += p;
-                        pg = fmaf(p, G[i], pg);
+                    for (int i = 0; i < 16; ++i) p[i] = exp2_fast(fmaf(S[i], c, -nu));
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    tau += p[i];
+                    pg = fmaf(p[i], G[i], pg);
+                }
+                if constexpr (FDZ) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const bf16x2 w01 = {(__bf16)p[4 * q], (__bf16)p[4 * q + 1]};
+                        const bf16x2 w23 = {(__bf16)p[4 * q + 2], (__bf16)p[4 * q + 3]};
+                        const u32x2 w = {__builtin_bit_cast(uint32_t, w01), __builtin_bit_cast(uint32_t, w23)};
+                        *(u32x2*)(btile + mb * (32 * 64) + tile_off<32>(l32, q) + 8 * hi) = w;
                     }
                 }
             }
@@ -489,11 +499,12 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
         a.tau[o] = 1.0f;
         a.del[o] = pg / tau;
         if constexpr (FDZ) {
-            // dZ^T[d][m] += sum over tokens dY^T[d][n] Bt[n][m], Bt = 2^(c l - nu'):
-            // the dY rows and, per latent block, Bt go through the wave's
-            // tiles (rows = tokens), and transposed reads give dY^T (rows d,
-            // k = tokens) and Bt (k = tokens, columns = latents). Padding
-            // latents only touch their own (unwritten) columns.
+            // dZ^T[d][m] += sum over tokens dY^T[d][n] Bt[n][m], with
+            // Bt[n][m] = 2^(c l - nu') = 2^(c l - nu) / tau: the sweep's
+            // weights are in the tiles, and the token's 1/tau goes with its
+            // dY row (rounded to bf16 once scaled). Transposed reads of the
+            // tiles give dY^T (rows d, k = tokens) and the weights (k =
+            // tokens, columns = latents); padding latents have weight 0.
             // W: the tile's row width in bf16 (D for dY, 32 latents for Bt)
             auto tr_addr = [&](auto W, const unsigned char* t, int kp, int db, int second) {
                 const int row = 16 * kp + 8 * (g >> 1) + (gi >> 2) + 4 * second;
@@ -503,9 +514,16 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
             const std::integral_constant<int, D> wd;
             const std::integral_constant<int, 32> wb;
             const int n = blk * 32 + l32;
+            const float rt = 1.0f / tau;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                *(bf16x8*)(gtile + tile_off<D>(l32, 2 * kb + hi)) = n < N ? gop[kb] : zero8();
+            for (int kb = 0; kb < KB; ++kb) {
+                bf16x8 v = zero8();
+                if (n < N) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[j] = (__bf16)((float)gop[kb][j] * rt);
+                }
+                *(bf16x8*)(gtile + tile_off<D>(l32, 2 * kb + hi)) = v;
+            }
             bf16x8 gt[2][DB];
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -514,25 +532,10 @@ __global__ __launch_bounds__(256) void bw_stats_bf16(BackwardArgs a) {
 #pragma unroll MBU
             for (int mb = 0; mb < MBX; ++mb) {
                 if (mb >= MB) continue;
-                bf16x8 qa[KB];
-                rows(qs, mb, qa);
-                f32x16 S = mfma(qa[0], kop[0], f32x16{});
-#pragma unroll
-                for (int kb = 1; kb < KB; ++kb) S = mfma(qa[kb], kop[kb], S);
-                // register i: latent 32 mb + 8 (i/4) + 4 hi + i%4 -> 8 bytes per 4
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float bt[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) bt[j] = exp2_fast(fmaf(S[4 * q + j], c, -nup));
-                    const bf16x2 w01 = {(__bf16)bt[0], (__bf16)bt[1]};
-                    const bf16x2 w23 = {(__bf16)bt[2], (__bf16)bt[3]};
-                    const u32x2 w = {__builtin_bit_cast(uint32_t, w01), __builtin_bit_cast(uint32_t, w23)};
-                    *(u32x2*)(btile + tile_off<32>(l32, q) + 8 * hi) = w;
-                }
+                const unsigned char* bt = btile + mb * (32 * 64);
                 bf16x8 bt0, bt1;
-                lds_tr_op2_c(tr_addr(wb, btile, 0, 0, 0), tr_addr(wb, btile, 0, 0, 1), tr_addr(wb, btile, 1, 0, 0),
-                             tr_addr(wb, btile, 1, 0, 1), bt0, bt1);
+                lds_tr_op2_c(tr_addr(wb, bt, 0, 0, 0), tr_addr(wb, bt, 0, 0, 1), tr_addr(wb, bt, 1, 0, 0),
+                             tr_addr(wb, bt, 1, 0, 1), bt0, bt1);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     dz[mb][db] = mfma(gt[0][db], bt0, dz[mb][db]);
@@ -607,6 +610,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
     BackwardArgs a) {
     static_assert(!(FDQ && ENC), "dQ fused with the full formula only");
     constexpr int KB = D / 16, DB = D / 32;
+    // the -del start of the Z dY^T products is a 16-register broadcast held
+    // through the latent loop: not where the dQ sums take those registers
+    constexpr bool kDelInit = !FDQ;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
     const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -617,12 +623,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
     unsigned char* zs = qs + Mp * 2 * D;               // Z rows (not with ENC)
     unsigned char* dzs = zs + (ENC ? 0 : Mp * 2 * D);
     float* lam = (float*)(dzs + Mp * 2 * D);  // [Mp] mu* + log2 sig* (+inf for padding)
-    float* gam = lam + Mp;                     // [Mp]
+    float* gam = lam + Mp;                     // [Mp] -gam (negated: the dZ V^T products start from it)
+    float* sbias = gam + Mp;                   // [Mp] 0, or -1e30 for padding (the logits' start)
     // FDQ (dQ fused in): this wave's K rows of the block (zero past N) and
     // its dl tile [token][latent] of the current latent block, bf16 rows
     // (swizzled); the head's dQ^T sums over this wave's tokens stay in
     // registers, for up to MBX latent blocks
-    unsigned char* ktile = (unsigned char*)(gam + Mp) + wave * (32 * 2 * D + 32 * 64);
+    unsigned char* ktile = (unsigned char*)(sbias + Mp) + wave * (32 * 2 * D + 32 * 64);
     unsigned char* ptile = ktile + 32 * 2 * D;
     constexpr int MBU = FDQ ? MBX : 1;
     f32x16 dq[FDQ ? MBX : 1][DB];
@@ -636,7 +643,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
     for (int m = tid; m < Mp; m += 256) {
         const int64_t r = (int64_t)bh * M + m;
         lam[m] = m < M ? a.zmu[r] + __log2f(a.zsig[r]) : INFINITY;
-        gam[m] = m < M ? a.gam[r] : 0.0f;
+        gam[m] = m < M ? -a.gam[r] : 0.0f;
+        sbias[m] = m < M ? 0.0f : -1e30f;
     }
     __syncthreads();
     const int64_t sn = a.sn, hb = head_base(a, bh);
@@ -646,6 +654,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
     const int g = lane >> 4, gi = lane & 15;
     const int prow = enc_row_token(l32);
     const int nblk = (N + 31) / 32, bstep = gridDim.x * 4;
+    const bool padded = M != Mp;
     int blk = blockIdx.x * 4 + wave;
     if (!FDQ && blk >= nblk) return;  // no barrier follows (FDQ: the waves merge at the end)
     // this block's K, V (and dY) rows and per-token statistics; the next
@@ -685,6 +694,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
         nu = nupf;
         del = delpf;
         if constexpr (PF) load(min(blk + bstep, nblk - 1));
+        f32x16 ndel;
+        if constexpr (kDelInit) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ndel[r] = -del;
+        }
         // ENC with accum: this block's old dK and dV (the second stage's
         // gradients), in the store layout, requested now so that their
         // latency overlaps the block's work
@@ -742,10 +756,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
                 if constexpr (!ENC) za[kb] = *(const bf16x8*)(zs + off);
                 dza[kb] = *(const bf16x8*)(dzs + off);
             }
-            f32x16 S = mfma(qa[0], kop[0], f32x16{});
-            f32x16 GV = mfma(dza[0], vop[0], f32x16{});
+            // The dZ V^T products start from -gam of their latents (and,
+            // without FDQ, the Z dY^T products from -del of the token), so
+            // that the matrix core leaves dZ.V - gam (and dY.Z - del):
+            // register 8 kp + j of a lane holds latent 32 mb + 16 kp + 8 hi + j
+            // of token l32. The logits of padded latents (zero rows, last
+            // block only) start from -1e30, so that both their weights are 0:
+            // the decode weight 2^(c l - nu) of a zero row would otherwise
+            // overflow where nu < -128, and the dK sum over the latents would
+            // take its inf times the zero Q row.
+            auto rowvec = [&](const float* t) __attribute__((always_inline)) {
+                f32x16 v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 x = *(const f32x4*)(t + 32 * mb + 16 * (q >> 1) + 8 * hi + 4 * (q & 1));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+                }
+                return v;
+            };
+            f32x16 s0 = f32x16{};
+            if (!ENC && padded && mb == MB - 1) s0 = rowvec(sbias);
+            f32x16 S = mfma(qa[0], kop[0], s0);
+            f32x16 GV = mfma(dza[0], vop[0], rowvec(gam));
             f32x16 GY;
-            if constexpr (!ENC) GY = mfma(za[0], gop[0], f32x16{});
+            if constexpr (!ENC) GY = mfma(za[0], gop[0], kDelInit ? ndel : f32x16{});
 #pragma unroll
             for (int kb = 1; kb < KB; ++kb) {
                 S = mfma(qa[kb], kop[kb], S);
@@ -757,24 +792,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FDQ && D ==
             for (int kp = 0; kp < 2; ++kp) {
                 const int m0 = 32 * mb + 16 * kp + 8 * hi;
                 const f32x4 l0 = *(const f32x4*)(lam + m0), l1 = *(const f32x4*)(lam + m0 + 4);
-                const f32x4 g0 = *(const f32x4*)(gam + m0), g1 = *(const f32x4*)(gam + m0 + 4);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int i = 8 * kp + j;
                     const float lj = j < 4 ? l0[j] : l1[j - 4];
-                    const float gj = j < 4 ? g0[j] : g1[j - 4];
-                    const float xe = fmaf(S[i], c, -lj);
-                    const float p_e = exp2_fast(xe);
-                    float dl = p_e * (GV[i] - gj);
-                    if constexpr (!ENC) {
-                        // p_dec <= 1 for real latents (nu is their log2-sum-
-                        // exp2); the clamp keeps padded latents (zero rows,
-                        // last block only) finite. Applied to every block:
-                        // one v_min, where a run-time condition cost three
-                        // instructions per score.
-                        const float xd = fminf(fmaf(S[i], c, -nu), 0.0f);
-                        dl = fmaf(exp2_fast(xd), GY[i] - del, dl);
-                    }
+                    const float p_e = exp2_fast(fmaf(S[i], c, -lj));
+                    float dl = p_e * GV[i];
+                    if constexpr (!ENC) dl = fmaf(exp2_fast(fmaf(S[i], c, -nu)), kDelInit ? GY[i] : GY[i] - del, dl);
                     pe[kp][j] = (__bf16)p_e;
                     pl[kp][j] = (__bf16)dl;
                 }
@@ -1013,15 +1037,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
             *(bf16x8*)(tt + tile_off<D>(prow, 2 * kb + hi)) = prow < nv ? (DQ ? kA[kb] : gA[kb]) : zero8();
-        // per token (register i: token 16 (i/8) + 8 hi + i%8): nu' and del
-        // (past the chunk: the last token's, with zero rows above)
-        float nur[16], der[16];
+        // per token (register i: token 16 (i/8) + 8 hi + i%8): nu' and -del
+        // (past the chunk: the last token's, with zero rows above); the
+        // Z dY^T products start from -del, so the matrix core leaves
+        // dY.Z - del
+        float nur[16];
+        f32x16 nder;
         if constexpr (!ENC) {
+            const float ndec = -dec;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int tk = 16 * (i >> 3) + 8 * hi + (i & 7);
                 nur[i] = __shfl(nuc, tk, 64);
-                der[i] = DQ ? __shfl(dec, tk, 64) : 0.0f;
+                nder[i] = DQ ? __shfl(ndec, tk, 64) : 0.0f;
             }
         }
         // the transposed operands of this sub-block (same for every latent block)
@@ -1058,25 +1086,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 #pragma unroll
                 for (int kb = 1; kb < KB; ++kb) GV = mfma(vA[kb], dzB[kb], GV);
                 if constexpr (!ENC) {
-                    GY = mfma(gA[0], zB[0], f32x16{});
+                    GY = mfma(gA[0], zB[0], nder);
 #pragma unroll
                     for (int kb = 1; kb < KB; ++kb) GY = mfma(gA[kb], zB[kb], GY);
                 }
             }
             bf16x8 pw[2];
+            // The decode weight of a padded latent (zero row) can overflow
+            // where nu' < -128; no clamp is applied: its weights only reach
+            // the padded latent's own output column, which is not stored.
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 float w;
                 if constexpr (ENC) {
                     w = exp2_fast(fmaf(S[i], c, -lam[j])) * (GV[i] - gm[j]);
                 } else {
-                    // decode weight Bt[n][m] (0 past the chunk); clamp: padded
-                    // latents (zero rows) stay finite
-                    const float p_d = exp2_fast(fminf(fmaf(S[i], c, -nur[i]), 0.0f));
+                    // decode weight Bt[n][m] (0 past the chunk)
+                    const float p_d = exp2_fast(fmaf(S[i], c, -nur[i]));
                     w = p_d;
                     if constexpr (DQ) {
                         const float p_e = exp2_fast(fmaf(S[i], c, -lam[j]));
-                        w = p_e * (GV[i] - gm[j]) + p_d * (GY[i] - der[i]);
+                        w = fmaf(p_d, GY[i], p_e * (GV[i] - gm[j]));
                     }
                 }
                 pw[i >> 3][i & 7] = (__bf16)w;
@@ -1190,7 +1220,7 @@ bool bw_bf16_fits(int M, int D) {
     // Q, Z and dZ of the head (and small per-latent or per-wave buffers) in
     // one CU's LDS; at D = 64 up to M = 256
     const int Mp = (M + 31) / 32 * 32;
-    return (D == 32 || (D == 64 && Mp <= 256)) && 3 * Mp * 2 * D + 4 * 32 * 2 * D + 8 * Mp <= 163840;
+    return (D == 32 || (D == 64 && Mp <= 256)) && 3 * Mp * 2 * D + 4 * 32 * 2 * D + 12 * Mp <= 163840;
 }
 
 namespace {
@@ -1230,7 +1260,8 @@ hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s) {
     if (const int fg = bw_fused_dz_groups(a)) {
         // dZ fused in: per-wave dY and Bt tiles, and the four waves' sums
         // (64 registers each) merged through LDS at the end
-        const int lds_f = std::max(lds + 4 * (32 * 2 * a.D + 32 * 64), 3 * 16 * 64 * 64 * 4 / 16);
+        const int mbx = a.D == 64 ? 2 : 4;
+        const int lds_f = std::max(lds + 4 * (32 * 2 * a.D + mbx * 32 * 64), 3 * 16 * 64 * 64 * 4 / 16);
         if (a.D == 32) return launch_bw_tok(bw_stats_bf16<32, true>, a, lds_f, s, fg);
         return launch_bw_tok(bw_stats_bf16<64, true>, a, lds_f, s, fg);
     }
@@ -1271,7 +1302,7 @@ hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
 
 hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
     const int Mp = (a.M + 31) / 32 * 32;
-    const int lds = (a.enc_only ? 2 : 3) * Mp * 2 * a.D + 8 * Mp;
+    const int lds = (a.enc_only ? 2 : 3) * Mp * 2 * a.D + 12 * Mp;  // rows, then lam, -gam and the logits' start
     if (a.enc_only) {
         if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32, true>, a, lds, s);
         if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64, true>, a, lds, s);
