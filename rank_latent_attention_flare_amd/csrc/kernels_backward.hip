@@ -618,8 +618,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu((FDQ &
     constexpr int NT = 64 * NWV;
     constexpr int KB = D / 16, DB = D / 32;
     // the -del start of the Z dY^T products is a 16-register broadcast held
-    // through the latent loop: not where the dQ sums take those registers
-    constexpr bool kDelInit = !FDQ && NWV == 4;
+    // through the latent loop: not in the eight-wave form, which has no
+    // registers to spare
+    constexpr bool kDelInit = NWV == 4;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
     const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -764,7 +765,7 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu((FDQ &
                 dza[kb] = *(const bf16x8*)(dzs + off);
             }
             // The dZ V^T products start from -gam of their latents (and,
-            // without FDQ, the Z dY^T products from -del of the token), so
+            // with kDelInit, the Z dY^T products from -del of the token), so
             // that the matrix core leaves dZ.V - gam (and dY.Z - del):
             // register 8 kp + j of a lane holds latent 32 mb + 16 kp + 8 hi + j
             // of token l32. The logits of padded latents (zero rows, last
