@@ -99,6 +99,13 @@ SHARP = [
     # D = 64 with M <= 64 (the statistics kernel forms the dZ partials itself)
     # and padded latents (M = 50 of 64)
     (1, 2, 2000, 50, 64, 8.0, 2.0),
+    # padded last latent block whose logits start from -1e30 in the dK/dV
+    # kernel: the eight-wave form (D = 64, M > 128), the four-wave form at
+    # D = 32 with separate latent passes, and the D = 32 form with dQ and dZ
+    # fused in
+    (1, 1, 2500, 250, 64, 8.0, 2.0),
+    (1, 1, 2000, 300, 32, 12.0, 2.0),
+    (1, 2, 2000, 100, 32, 12.0, 2.0),
 ]
 
 
