@@ -106,6 +106,72 @@ def trace_summary(path: str, steps: int, cold: bool) -> str:
     return "\n".join(out)
 
 
+SQ_SETS = (
+    "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_SALU SQ_INSTS_LDS SQ_WAVE_CYCLES "
+    "SQ_BUSY_CYCLES",
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY SQ_VALU_MFMA_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY "
+    "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_MISC",
+    "SQ_INSTS_VALU_FMA_F32 SQ_INSTS_VALU_CVT SQ_INSTS_VALU_MUL_F32 SQ_INSTS_VALU_ADD_F32 SQ_INSTS_VALU_INT32 "
+    "SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_BRANCH",
+    "GRBM_GUI_ACTIVE GRBM_COUNT SQ_CYCLES SQ_BUSY_CU_CYCLES",
+)
+
+
+def sq_summary(paths: list, workload) -> str:
+    """Markdown table of the SQ and GRBM counter passes (rocprofv3 --pmc with
+    each of SQ_SETS, one run each, in that order) of this script on one
+    workload: per kernel that works on score tiles (encodes, decodes and the
+    backward's token and latent kernels), averages over all its dispatches of
+      shader clock = GRBM_GUI_ACTIVE / 8 XCDs / duration,
+      MFMA busy    = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8),
+    instruction counts per 32x32 tile of scores (B*H*N*M/1024 per launch),
+    and SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES."""
+    import csv
+    import statistics
+
+    vals, names, dur = {}, {}, {}
+    for path in paths:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                key = (path, r["Dispatch_Id"])
+                names[key] = r["Kernel_Name"]
+                c = vals.setdefault(key, {})
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                    dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    blocks = workload.B * workload.H * workload.N * workload.M / 1024.0
+    per = {}  # kernel -> counter -> list of per-dispatch values
+    for key, c in vals.items():
+        short = names[key].replace("void ", "").replace("flare::(anonymous namespace)::", "").split("(")[0]
+        if not any(t in short for t in ("encode_partial", "decode_", "bw_")) or "combine" in short:
+            continue
+        k = per.setdefault(short, {})
+        for cn, v in c.items():
+            k.setdefault(cn, []).append(v)
+        if key in dur:
+            k.setdefault("_us", []).append(dur[key])
+    out = ["| kernel | avg us (counter runs) | shader clock GHz | MFMA busy | MFMA / block | VALU / block "
+           "| of which exp, fma, cvt | LDS / block | LDS bank-conflict cycles / block "
+           "| SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+
+    def m(k, cn):
+        return statistics.mean(k[cn]) if cn in k and k[cn] else float("nan")
+
+    for short, k in sorted(per.items(), key=lambda kv: -m(kv[1], "GRBM_GUI_ACTIVE")):
+        us = m(k, "_us")
+        gui = m(k, "GRBM_GUI_ACTIVE")
+        clock = gui / 8 / (us * 1e3) if us == us else float("nan")
+        busy = m(k, "SQ_VALU_MFMA_BUSY_CYCLES") / (1024 * gui / 8)
+        out.append(
+            f"| {short} | {us:.1f} | {clock:.2f} | {100 * busy:.0f}% | {m(k, 'SQ_INSTS_MFMA') / blocks:.2f} "
+            f"| {m(k, 'SQ_INSTS_VALU') / blocks:.1f} | {m(k, 'SQ_INSTS_VALU_TRANS_F32') / blocks:.1f}, "
+            f"{m(k, 'SQ_INSTS_VALU_FMA_F32') / blocks:.1f}, {m(k, 'SQ_INSTS_VALU_CVT') / blocks:.1f} "
+            f"| {m(k, 'SQ_INSTS_LDS') / blocks:.2f} | {m(k, 'SQ_LDS_BANK_CONFLICT') / blocks:.2f} "
+            f"| {m(k, 'SQ_WAIT_INST_ANY') / m(k, 'SQ_WAVE_CYCLES'):.2f} |")
+    return "\n".join(out)
+
+
 def kernel_kind(name: str) -> str | None:
     """The library's kernel kind of a kernel symbol (None for other kernels)."""
     for kind, tag in (("encode_partial", "encode_partial"), ("decode", "decode_"), ("combine", "combine_kernel"),
@@ -220,6 +286,9 @@ def parse():
                         "this script with the same --workload, --layout, --variant, --steps, --warmup and "
                         "--ramp-seconds (the kernel trace: of a run with the same --workload, --layout and --variant "
                         "and the default steps), and exit")
+    p.add_argument("--sq-summary", nargs=4, metavar="CSV",
+                   help="print the SQ/GRBM counter table from four rocprofv3 --pmc runs of this script with the "
+                        "counter sets of SQ_SETS, in order, on the same --workload, and exit")
     p.add_argument("--ramp-seconds", type=float, default=1.0,
                    help="run the step back to back for this long before the warmup steps, so that the GPU "
                         "reaches its steady clocks (a cold MI355X needs ~0.1-0.2 s); 0 disables")
@@ -254,6 +323,10 @@ def main():
         return
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.steps, args.cold_mib > 0))
+        return
+    if args.sq_summary:
+        from flare_inputs import WORKLOADS
+        print(sq_summary(args.sq_summary, WORKLOADS[args.workload]))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this "

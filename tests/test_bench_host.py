@@ -71,3 +71,32 @@ def test_fp32_kernels_hash_their_own_source():
     assert bench.kernel_sources("encode_partial", "f32") == bench.kernel_sources("combine")
     assert bench.source_hash("decode", "f32") != bench.source_hash("decode", "bf16")
     assert bench.source_hash("encode_partial", "f32") == bench.source_hash("combine")
+
+
+def test_sq_summary_per_block_counts_clock_and_busy(tmp_path):
+    # one decode dispatch per pass, 50 us long; 2.0 GHz means GRBM_GUI_ACTIVE
+    # = 8 XCDs x 2.0e9 x 50e-6; MFMA busy 30% of the SIMD cycles
+    w = WORKLOADS[2]
+    blocks = w.B * w.H * w.N * w.M / 1024
+    dec = "void flare::(anonymous namespace)::decode_bf16<32, 1, float, false>(flare::DecodeArgs)"
+    gui = 8 * 2.0e9 * 50e-6
+    counts = {"SQ_INSTS_MFMA": 6 * blocks, "SQ_INSTS_VALU": 61 * blocks, "SQ_INSTS_VALU_TRANS_F32": 16 * blocks,
+              "SQ_INSTS_VALU_FMA_F32": 16 * blocks, "SQ_INSTS_VALU_CVT": 10 * blocks, "SQ_INSTS_LDS": 4.5 * blocks,
+              "SQ_LDS_BANK_CONFLICT": 1.5 * blocks, "SQ_WAIT_INST_ANY": 45.0, "SQ_WAVE_CYCLES": 100.0,
+              "SQ_VALU_MFMA_BUSY_CYCLES": 0.3 * 1024 * gui / 8, "GRBM_GUI_ACTIVE": gui}
+    paths = []
+    for i, names in enumerate(s.split() for s in bench.SQ_SETS):
+        path = str(tmp_path / f"p{i + 1}.csv")
+        with open(path, "w", newline="") as f:
+            wr = csv.DictWriter(f, fieldnames=COUNTER_COLS + ["Start_Timestamp", "End_Timestamp"])
+            wr.writeheader()
+            for cn in names:
+                wr.writerow({"Correlation_Id": 0, "Dispatch_Id": 0, "Agent_Id": 1, "Kernel_Name": dec,
+                             "Counter_Name": cn, "Counter_Value": counts.get(cn, 1.0),
+                             "Start_Timestamp": 1000, "End_Timestamp": 51000})
+        paths.append(path)
+    table = bench.sq_summary(paths, w).splitlines()
+    assert len(table) == 3
+    cells = [c.strip() for c in table[2].strip("|").split("|")]
+    assert cells == ["decode_bf16<32, 1, float, false>", "50.0", "2.00", "30%", "6.00", "61.0", "16.0, 16.0, 10.0",
+                     "4.50", "1.50", "0.45"]
