@@ -50,6 +50,7 @@ int64_t tune(flare_tune k) { return g_tune[k].load(std::memory_order_relaxed); }
 constexpr int kTargetEncWaves = 2048;  // waves over all encode workgroups
 constexpr int kTargetDecWgs = 1024;    // decode workgroups
 constexpr int64_t kMaxGridY = 65535;
+constexpr int kBwRange = 256;  // latents per range of the split matrix-core backward
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -66,6 +67,8 @@ struct Plan {
     size_t esize;
     size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[7];
     size_t off_zsig, off_nu, off_tau, off_del, off_dz, off_gam;  // backward
+    bool bsplit;       // backward over latent ranges of at most kBwRange (bf16, D = 64, 256 < Mp <= 512)
+    size_t off_bs_q, off_bs_z, off_bs_dz, off_bs_mu, off_bs_sig, off_bs_gam, off_bs_dq;  // one range's latent arrays
     float c;
     int64_t sb, sh, sn;  // element strides of K, V and Y: batch, head, token
 };
@@ -211,6 +214,21 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     p->off_del = off;  off = align256(off + tok);
     p->off_dz = off;   off = align256(off + lat * size_t(D));
     p->off_gam = off;  off = align256(off + lat);
+    // bf16 at D = 64 with more latents than one compute unit's LDS holds Q, Z
+    // and dZ of (256 < Mp <= 512): the latent-side and dK/dV kernels run over
+    // latent ranges of at most kBwRange, each on compact copies of the range's
+    // latent arrays (the per-token statistics still take every latent)
+    p->bsplit = dt == FLARE_BF16 && D == 64 && p->Mp > kBwRange && p->Mp <= 2 * kBwRange;
+    if (p->bsplit) {
+        const size_t r = kBwRange;
+        p->off_bs_q = off;   off = align256(off + size_t(p->H) * r * size_t(D) * p->esize);
+        p->off_bs_z = off;   off = align256(off + size_t(p->BH) * r * size_t(D) * 4);
+        p->off_bs_dz = off;  off = align256(off + size_t(p->BH) * r * size_t(D) * 4);
+        p->off_bs_mu = off;  off = align256(off + size_t(p->BH) * r * 4);
+        p->off_bs_sig = off; off = align256(off + size_t(p->BH) * r * 4);
+        p->off_bs_gam = off; off = align256(off + size_t(p->BH) * r * 4);
+        p->off_bs_dq = off;  off = align256(off + size_t(p->H) * r * size_t(D) * p->esize);
+    }
     p->total[FLARE_OP_BACKWARD] = off;
     p->total[FLARE_OP_PP_BACKWARD] = 0;  // sized by pp_layout
     return FLARE_OK;
@@ -678,9 +696,11 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     a.c = p.c;
     a.bf16 = p.dt == FLARE_BF16;
     a.accum = accum_kv;
-    // bf16 heads whose Q, Z and dZ fit in LDS: the per-token kernels on the
-    // matrix core; otherwise (and for fp32) the fp32 VALU kernels
-    const bool mc = a.bf16 && flare::bw_bf16_fits(int(p.M), int(p.D));
+    // bf16 heads whose Q, Z and dZ fit in LDS, whole or in latent ranges: the
+    // per-token kernels on the matrix core; otherwise (and for fp32) the fp32
+    // VALU kernels
+    const bool split = p.bsplit;
+    const bool mc = a.bf16 && (split || flare::bw_bf16_fits(int(p.M), int(p.D)));
     // With dZ given (the encode's backward alone), the matrix-core kernels
     // skip the decode term and need no per-token statistics; the fp32
     // kernels compute the full formula with the caller's dY = 0.
@@ -689,8 +709,8 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     // kernels also form the latent-side partials (dZ in the statistics
     // kernel, dQ in the dK/dV kernel), one per workgroup, in fz and fq chunk
     // slots
-    const int fz = mc ? flare::bw_fused_dz_groups(a) : 0;
-    const int fq = mc ? flare::bw_fused_dq_groups(a) : 0;
+    const int fz = mc && !split ? flare::bw_fused_dz_groups(a) : 0;
+    const int fq = mc && !split ? flare::bw_fused_dq_groups(a) : 0;
     if (e == hipSuccess && !a.enc_only)
         e = timed(3, s, [&] { return mc ? flare::launch_bw_stats_bf16(a, s) : flare::launch_bw_stats(a, s); });
     if (dz_given) {
@@ -701,20 +721,63 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
         flare::BackwardArgs one = a;
         one.C = 1;
         if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(one, s); });
-    } else {
+    } else if (!split) {
         if (e == hipSuccess && fz == 0)
             e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, false, s) : flare::launch_bw_dz(a, s); });
         flare::BackwardArgs dza = a;
         if (fz > 0) dza.C = fz;
         if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(dza, s); });
     }
-    if (e == hipSuccess)
-        e = timed(3, s, [&] { return mc ? flare::launch_bw_dkdv_bf16(a, s) : flare::launch_bw_dkdv(a, s); });
-    if (e == hipSuccess && fq == 0)
-        e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, true, s) : flare::launch_bw_dq(a, s); });
-    flare::BackwardArgs dqa = a;
-    if (fq > 0) dqa.C = fq;
-    if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(dqa, s); });
+    if (!split) {
+        if (e == hipSuccess)
+            e = timed(3, s, [&] { return mc ? flare::launch_bw_dkdv_bf16(a, s) : flare::launch_bw_dkdv(a, s); });
+        if (e == hipSuccess && fq == 0)
+            e = timed(3, s, [&] { return mc ? flare::launch_bw_lat_bf16(a, true, s) : flare::launch_bw_dq(a, s); });
+        flare::BackwardArgs dqa = a;
+        if (fq > 0) dqa.C = fq;
+        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(dqa, s); });
+        return e;
+    }
+    // Latent ranges: the range's rows of Q, Z, mu*, sig* (and of a given dZ
+    // and its gam) are copied to compact arrays [.][mr][.], the latent-side
+    // kernels and the dK/dV kernel run on them as for a head of mr latents
+    // (dK and dV of later ranges added to what the earlier ones wrote), and
+    // the range's dQ is copied back into its rows.
+    const int64_t M = p.M, D = p.D, H = p.H, BH = p.BH, es = int64_t(p.esize);
+    auto rows = [&](void* dst, const void* src, int64_t n, int64_t bytes, int64_t sp, int64_t dp) {
+        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_copy_rows(dst, src, n, bytes, sp, dp, s); });
+    };
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += kBwRange) {
+        const int64_t mr = std::min<int64_t>(kBwRange, M - m0);
+        flare::BackwardArgs ar = a;
+        ar.M = int(mr);
+        ar.Q = ws + p.off_bs_q;
+        ar.Z = (const float*)(ws + p.off_bs_z);
+        ar.dZ = (float*)(ws + p.off_bs_dz);
+        ar.zmu = (const float*)(ws + p.off_bs_mu);
+        ar.zsig = (const float*)(ws + p.off_bs_sig);
+        ar.gam = (float*)(ws + p.off_bs_gam);
+        ar.dQ = ws + p.off_bs_dq;
+        ar.accum = accum_kv || m0 > 0;
+        rows((void*)ar.Q, (const char*)Q + m0 * D * es, H, mr * D * es, M * D * es, mr * D * es);
+        rows((void*)ar.Z, a.Z + m0 * D, BH, mr * D * 4, M * D * 4, mr * D * 4);
+        rows((void*)ar.zmu, a.zmu + m0, BH, mr * 4, M * 4, mr * 4);
+        rows((void*)ar.zsig, a.zsig + m0, BH, mr * 4, M * 4, mr * 4);
+        if (dz_given) {
+            rows(ar.dZ, a.dZ + m0 * D, BH, mr * D * 4, M * D * 4, mr * D * 4);
+            rows(ar.gam, a.gam + m0, BH, mr * 4, M * 4, mr * 4);
+        } else {
+            if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_lat_bf16(ar, false, s); });
+            if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(ar, s); });
+        }
+        const int fqr = flare::bw_fused_dq_groups(ar);
+        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dkdv_bf16(ar, s); });
+        if (e == hipSuccess && fqr == 0) e = timed(3, s, [&] { return flare::launch_bw_lat_bf16(ar, true, s); });
+        flare::BackwardArgs dqa = ar;
+        if (fqr > 0) dqa.C = fqr;
+        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(dqa, s); });
+        rows((char*)dQ + m0 * D * es, ar.dQ, H, mr * D * es, mr * D * es, M * D * es);
+    }
     return e;
 }
 
@@ -819,7 +882,7 @@ flare_status pp_backward(const void* Q, const void* K, const void* V, const void
     // dY = 0 and dZ given); its dK, dV are added to the second stage's in the
     // kernel (fp32 sum, rounded once), its dQ goes to a buffer
     // (the zero dY is read by the fp32 kernels only)
-    if (err == hipSuccess && !(bf && flare::bw_bf16_fits(int(M), int(D))))
+    if (err == hipSuccess && !(bf && (pf.bsplit || flare::bw_bf16_fits(int(M), int(D)))))
         err = flare::launch_fill_zero(ws + L.dy0, size_t(B) * tok * e, s);
     if (err == hipSuccess)
         err = backward_core(pf, Q, K, V, ws + L.dy0, ws + L.dq1, dK, dV, ws + L.bw, s, ws + L.dqp, true);

@@ -357,6 +357,16 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
     out[blockIdx.x * 256 + threadIdx.x] = (float)(acc & 0xffff);
 }
 
+// rows x words 4-byte words, row r of src at src + r * sp, of dst at dst + r * dp (pitches in words)
+__global__ __launch_bounds__(256) void copy_rows_kernel(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src,
+                                                        int64_t rows, int64_t words, int64_t sp, int64_t dp) {
+    const int64_t n = rows * words;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+        const int64_t r = e / words, w = e - r * words;
+        dst[r * dp + w] = src[r * sp + w];
+    }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* __restrict__ dst, size_t n16) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) dst[i] = z;
@@ -481,6 +491,16 @@ hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s) {
     const size_t n16 = bytes / 16;
     if (n16 == 0) return hipSuccess;
     FLARE_LAUNCH(fill_zero_kernel, dim3(elementwise_blocks((int64_t)n16)), dim3(256), 0, s, (u32x4*)dst, n16);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(void* dst, const void* src, int64_t rows, int64_t row_bytes, int64_t src_pitch,
+                            int64_t dst_pitch, hipStream_t s) {
+    if (row_bytes % 4 || src_pitch % 4 || dst_pitch % 4 || uintptr_t(dst) % 4 || uintptr_t(src) % 4)
+        return hipErrorInvalidValue;
+    if (rows <= 0 || row_bytes <= 0) return hipSuccess;
+    FLARE_LAUNCH(copy_rows_kernel, dim3(elementwise_blocks(rows * (row_bytes / 4))), dim3(256), 0, s, (uint32_t*)dst,
+                 (const uint32_t*)src, rows, row_bytes / 4, src_pitch / 4, dst_pitch / 4);
     return hipGetLastError();
 }
 

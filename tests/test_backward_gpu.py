@@ -38,8 +38,11 @@ CASES = [
     # the same at D = 64 with padded latents (the statistics kernel forms the
     # dZ partials there)
     (2, 128, 777, 50, 64, "bf16"),
-    # bf16 heads whose Q, Z and dZ do not fit in LDS take the fp32 VALU kernels
+    # D = 64 with more than 256 latents: the matrix-core kernels over latent
+    # ranges of at most 256 (the second ragged, or a full 256, or padded)
     (1, 1, 600, 300, 64, "bf16"),
+    (2, 1, 700, 480, 64, "bf16"),
+    (1, 1, 500, 512, 64, "bf16"),
     # D = 64 with 256 latents (padded from 250): the latent kernels with four
     # latent blocks per wave and two token streams
     (1, 2, 1500, 250, 64, "bf16"),
@@ -106,6 +109,8 @@ SHARP = [
     (1, 1, 2500, 250, 64, 8.0, 2.0),
     (1, 1, 2000, 300, 32, 12.0, 2.0),
     (1, 2, 2000, 100, 32, 12.0, 2.0),
+    # latent ranges at D = 64 (256 + 44, the second padded)
+    (1, 1, 1500, 300, 64, 8.0, 2.0),
 ]
 
 
@@ -195,6 +200,7 @@ def test_backward_full_size_one_head_group():
 
 PP_CASES = [
     # B, H, N, M, D, dtype
+    (2, 1, 600, 400, 64, "bf16"),  # latent ranges in both stages (the first with dZ given)
     (2, 2, 300, 40, 32, "f32"),
     (1, 1, 500, 17, 16, "f32"),
     (2, 2, 1000, 64, 64, "bf16"),
