@@ -229,9 +229,10 @@ flare_status flare_attend(const void* q, const void* Z, void* Y,
  *   dQ = s dl K (summed over the batch, Q being shared),  dK = s dl^T Q.
  * Inputs Q [H][M][D], K, V, dY [B][H][N][D]; outputs dQ [H][M][D], dK, dV
  * [B][H][N][D], in the operator dtype. Precision follows the forward's:
- * FLARE_F32 computes in fp32 throughout; FLARE_BF16 heads at D = 32, and
- * at D = 64 (above 256 latents over latent ranges of at most 256) run on
- * bf16 MFMA with fp32 accumulation, the probabilities, dl and the staged
+ * FLARE_F32 computes in fp32 throughout; FLARE_BF16 heads at D = 32, at
+ * D = 64 (above 256 latents over latent ranges of at most 256) and at
+ * D = 128 with M <= 288 (above 128 latents over ranges of at most 128) run
+ * on bf16 MFMA with fp32 accumulation, the probabilities, dl and the staged
  * Q, Z and dZ being rounded to nearest-even bf16 where they become MFMA
  * operands (where the dZ partials are formed with the token statistics,
  * D = 32 with M <= 128 or D = 64 with M <= 64, also dY scaled by the

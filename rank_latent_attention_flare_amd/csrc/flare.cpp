@@ -50,7 +50,6 @@ int64_t tune(flare_tune k) { return g_tune[k].load(std::memory_order_relaxed); }
 constexpr int kTargetEncWaves = 2048;  // waves over all encode workgroups
 constexpr int kTargetDecWgs = 1024;    // decode workgroups
 constexpr int64_t kMaxGridY = 65535;
-constexpr int kBwRange = 256;  // latents per range of the split matrix-core backward
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -67,7 +66,8 @@ struct Plan {
     size_t esize;
     size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[7];
     size_t off_zsig, off_nu, off_tau, off_del, off_dz, off_gam;  // backward
-    bool bsplit;       // backward over latent ranges of at most kBwRange (bf16, D = 64, 256 < Mp <= 512)
+    bool bsplit;       // backward over latent ranges of bw_range (bf16: D = 64, 256 < Mp <= 512; D = 128, 128 < Mp <= 288)
+    int bw_range;      // latents per range (256 at D = 64, 128 at D = 128)
     size_t off_bs_q, off_bs_z, off_bs_dz, off_bs_mu, off_bs_sig, off_bs_gam, off_bs_dq;  // one range's latent arrays
     float c;
     int64_t sb, sh, sn;  // element strides of K, V and Y: batch, head, token
@@ -214,13 +214,15 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     p->off_del = off;  off = align256(off + tok);
     p->off_dz = off;   off = align256(off + lat * size_t(D));
     p->off_gam = off;  off = align256(off + lat);
-    // bf16 at D = 64 with more latents than one compute unit's LDS holds Q, Z
-    // and dZ of (256 < Mp <= 512): the latent-side and dK/dV kernels run over
-    // latent ranges of at most kBwRange, each on compact copies of the range's
-    // latent arrays (the per-token statistics still take every latent)
-    p->bsplit = dt == FLARE_BF16 && D == 64 && p->Mp > kBwRange && p->Mp <= 2 * kBwRange;
+    // bf16 with more latents than one compute unit's LDS holds Q, Z and dZ of
+    // (D = 64: 256 < Mp <= 512; D = 128: 128 < Mp <= 288): the latent-side and
+    // dK/dV kernels run over latent ranges of at most bw_range, each on
+    // compact copies of the range's latent arrays (the per-token statistics
+    // still take every latent: Q and Z of the head in LDS)
+    p->bw_range = D == 128 ? 128 : 256;
+    p->bsplit = dt == FLARE_BF16 && ((D == 64 && p->Mp > 256 && p->Mp <= 512) || (D == 128 && p->Mp > 128 && p->Mp <= 288));
     if (p->bsplit) {
-        const size_t r = kBwRange;
+        const size_t r = size_t(p->bw_range);
         p->off_bs_q = off;   off = align256(off + size_t(p->H) * r * size_t(D) * p->esize);
         p->off_bs_z = off;   off = align256(off + size_t(p->BH) * r * size_t(D) * 4);
         p->off_bs_dz = off;  off = align256(off + size_t(p->BH) * r * size_t(D) * 4);
@@ -747,8 +749,8 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     auto rows = [&](void* dst, const void* src, int64_t n, int64_t bytes, int64_t sp, int64_t dp) {
         if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_copy_rows(dst, src, n, bytes, sp, dp, s); });
     };
-    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += kBwRange) {
-        const int64_t mr = std::min<int64_t>(kBwRange, M - m0);
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += p.bw_range) {
+        const int64_t mr = std::min<int64_t>(p.bw_range, M - m0);
         flare::BackwardArgs ar = a;
         ar.M = int(mr);
         ar.Q = ws + p.off_bs_q;

@@ -619,8 +619,8 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu((FDQ &
     constexpr int KB = D / 16, DB = D / 32;
     // the -del start of the Z dY^T products is a 16-register broadcast held
     // through the latent loop: not in the eight-wave form, which has no
-    // registers to spare
-    constexpr bool kDelInit = NWV == 4;
+    // registers to spare, nor at D = 128
+    constexpr bool kDelInit = NWV == 4 && D != 128;
     extern __shared__ __attribute__((aligned(16))) unsigned char bsm[];
     const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -672,7 +672,7 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu((FDQ &
     // (FDQ holds its dQ sums in the registers a second set would take (at
     // D = 32 at two waves per SIMD; at D = 64 prefetching there measured 4%
     // slower): there each block's rows are loaded at its start)
-    constexpr bool PF = !FDQ && NWV == 4;
+    constexpr bool PF = !FDQ && NWV == 4 && D != 128;  // (D = 128: 460 registers without, no spills)
     bf16x8 kop[KB], vop[KB], gop[KB], kpf[KB], vpf[KB], gpf[KB];
     float nu, del, nupf = 0.0f, delpf = 0.0f;
     auto load = [&](int bk) {
@@ -1226,9 +1226,10 @@ hipError_t dkdv_d(const BackwardArgs& a, hipStream_t s) {
 
 bool bw_bf16_fits(int M, int D) {
     // Q, Z and dZ of the head (and small per-latent or per-wave buffers) in
-    // one CU's LDS; at D = 64 up to M = 256
+    // one CU's LDS; at D = 64 up to M = 256, at D = 128 up to M = 128
     const int Mp = (M + 31) / 32 * 32;
-    return (D == 32 || (D == 64 && Mp <= 256)) && 3 * Mp * 2 * D + 4 * 32 * 2 * D + 12 * Mp <= 163840;
+    return (D == 32 || (D == 64 && Mp <= 256) || (D == 128 && Mp <= 128)) &&
+           3 * Mp * 2 * D + 4 * 32 * 2 * D + 12 * Mp <= 163840;
 }
 
 namespace {
@@ -1275,6 +1276,7 @@ hipError_t launch_bw_stats_bf16(const BackwardArgs& a, hipStream_t s) {
     }
     if (a.D == 32) return launch_bw_tok(bw_stats_bf16<32>, a, lds, s);
     if (a.D == 64) return launch_bw_tok(bw_stats_bf16<64>, a, lds, s);
+    if (a.D == 128) return launch_bw_tok(bw_stats_bf16<128>, a, lds, s);
     return hipErrorInvalidValue;
 }
 
@@ -1300,11 +1302,13 @@ hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s) {
         if (a.D == 32) return go(bw_lat_bf16<32, true, 4, true>);
         if (a.D == 64 && Mp == 256) return go(bw_lat_bf16<64, true, 4, true>);
         if (a.D == 64 && Mp <= 256) return go(bw_lat_bf16<64, true, 2, true>);
+        if (a.D == 128 && Mp <= 128) return go(bw_lat_bf16<128, true, 2, true>);
         return hipErrorInvalidValue;
     }
     if (a.D == 32) return dq ? go(bw_lat_bf16<32, true, 4>) : go(bw_lat_bf16<32, false, 4>);
     if (a.D == 64 && Mp == 256) return dq ? go(bw_lat_bf16<64, true, 4>) : go(bw_lat_bf16<64, false, 4>);
     if (a.D == 64 && Mp <= 256) return dq ? go(bw_lat_bf16<64, true, 2>) : go(bw_lat_bf16<64, false, 2>);
+    if (a.D == 128 && Mp <= 128) return dq ? go(bw_lat_bf16<128, true, 2>) : go(bw_lat_bf16<128, false, 2>);
     return hipErrorInvalidValue;
 }
 
@@ -1315,6 +1319,7 @@ hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
         if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32, true>, a, lds, s);
         if (a.D == 64 && Mp > 128) return launch_bw_tok(bw_dkdv_bf16<64, true, false, 4, 8>, a, lds, s, 0, 8);
         if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64, true>, a, lds, s);
+        if (a.D == 128 && Mp <= 128) return launch_bw_tok(bw_dkdv_bf16<128, true>, a, lds, s);
         return hipErrorInvalidValue;
     }
     if (const int fg = bw_fused_dq_groups(a)) {
@@ -1328,6 +1333,7 @@ hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
     if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32>, a, lds, s);
     if (a.D == 64 && Mp > 128) return launch_bw_tok(bw_dkdv_bf16<64, false, false, 4, 8>, a, lds, s, 0, 8);
     if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64>, a, lds, s);
+    if (a.D == 128 && Mp <= 128) return launch_bw_tok(bw_dkdv_bf16<128>, a, lds, s);
     return hipErrorInvalidValue;
 }
 

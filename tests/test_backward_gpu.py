@@ -52,6 +52,11 @@ CASES = [
     (2, 1, 333, 70, 96, "f32"),
     (1, 2, 700, 64, 128, "bf16"),
     (1, 1, 300, 400, 128, "bf16"),
+    # bf16 at D = 128 on the matrix core: a whole head of 128 latents, and
+    # latent ranges of 128 (two full, or the second ragged)
+    (1, 2, 800, 128, 128, "bf16"),
+    (1, 1, 500, 256, 128, "bf16"),
+    (2, 1, 600, 200, 128, "bf16"),
 ]
 
 
@@ -109,8 +114,10 @@ SHARP = [
     (1, 1, 2500, 250, 64, 8.0, 2.0),
     (1, 1, 2000, 300, 32, 12.0, 2.0),
     (1, 2, 2000, 100, 32, 12.0, 2.0),
-    # latent ranges at D = 64 (256 + 44, the second padded)
+    # latent ranges at D = 64 (256 + 44, the second padded) and D = 128
+    # (128 + 72)
     (1, 1, 1500, 300, 64, 8.0, 2.0),
+    (1, 1, 1500, 200, 128, 8.0, 2.0),
 ]
 
 
@@ -201,6 +208,7 @@ def test_backward_full_size_one_head_group():
 PP_CASES = [
     # B, H, N, M, D, dtype
     (2, 1, 600, 400, 64, "bf16"),  # latent ranges in both stages (the first with dZ given)
+    (1, 1, 500, 250, 128, "bf16"),  # the same at D = 128
     (2, 2, 300, 40, 32, "f32"),
     (1, 1, 500, 17, 16, "f32"),
     (2, 2, 1000, 64, 64, "bf16"),
