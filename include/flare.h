@@ -231,13 +231,12 @@ flare_status flare_attend(const void* q, const void* Z, void* Y,
  * [B][H][N][D], in the operator dtype. Precision follows the forward's:
  * FLARE_F32 computes in fp32 throughout; FLARE_BF16 heads at D = 32, at
  * D = 64 (above 256 latents over latent ranges of at most 256) and at
- * D = 128 with M <= 288 (above 128 latents over ranges of at most 128) run
- * on bf16 MFMA with fp32 accumulation, the probabilities, dl and the staged
+ * D = 128 (above 128 latents over ranges of at most 128) run on bf16 MFMA
+ * with fp32 accumulation, the probabilities, dl and the staged
  * Q, Z and dZ being rounded to nearest-even bf16 where they become MFMA
  * operands (where the dZ partials are formed with the token statistics,
  * D = 32 with M <= 128 or D = 64 with M <= 64, also dY scaled by the
- * token's inverse decode sum); other bf16 heads run fp32 arithmetic on the
- * widened inputs.
+ * token's inverse decode sum).
  * It recomputes the forward's encode internally; nothing N x M is stored.
  * Supported for D in {8, 16, 24, 32, 48, 64, 96, 128} (bf16: 32, 64 and
  * 128) with the forward's M range; otherwise FLARE_ERR_UNSUPPORTED. Outputs

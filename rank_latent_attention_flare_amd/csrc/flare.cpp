@@ -66,8 +66,10 @@ struct Plan {
     size_t esize;
     size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[7];
     size_t off_zsig, off_nu, off_tau, off_del, off_dz, off_gam;  // backward
-    bool bsplit;       // backward over latent ranges of bw_range (bf16: D = 64, 256 < Mp <= 512; D = 128, 128 < Mp <= 288)
+    bool bsplit;       // backward over latent ranges of bw_range (bf16: D = 64, 256 < Mp <= 512; D = 128, 128 < Mp <= 512)
     int bw_range;      // latents per range (256 at D = 64, 128 at D = 128)
+    int stats_range;   // > 0: the per-token statistics too, over ranges of this many latents (D = 128, Mp > 256)
+    size_t off_bs_nu2, off_bs_del2;  // a later statistics range's per-token results
     size_t off_bs_q, off_bs_z, off_bs_dz, off_bs_mu, off_bs_sig, off_bs_gam, off_bs_dq;  // one range's latent arrays
     float c;
     int64_t sb, sh, sn;  // element strides of K, V and Y: batch, head, token
@@ -215,14 +217,16 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     p->off_dz = off;   off = align256(off + lat * size_t(D));
     p->off_gam = off;  off = align256(off + lat);
     // bf16 with more latents than one compute unit's LDS holds Q, Z and dZ of
-    // (D = 64: 256 < Mp <= 512; D = 128: 128 < Mp <= 288): the latent-side and
+    // (D = 64: 256 < Mp <= 512; D = 128: 128 < Mp <= 512): the latent-side and
     // dK/dV kernels run over latent ranges of at most bw_range, each on
-    // compact copies of the range's latent arrays (the per-token statistics
-    // still take every latent: Q and Z of the head in LDS)
+    // compact copies of the range's latent arrays. The per-token statistics
+    // take every latent at once where Q and Z of the head fit in LDS, else
+    // (D = 128 above 256 latents) ranges of 256 merged per token.
     p->bw_range = D == 128 ? 128 : 256;
-    p->bsplit = dt == FLARE_BF16 && ((D == 64 && p->Mp > 256 && p->Mp <= 512) || (D == 128 && p->Mp > 128 && p->Mp <= 288));
+    p->bsplit = dt == FLARE_BF16 && ((D == 64 && p->Mp > 256 && p->Mp <= 512) || (D == 128 && p->Mp > 128 && p->Mp <= 512));
+    p->stats_range = p->bsplit && D == 128 && p->Mp > 256 ? 256 : 0;
     if (p->bsplit) {
-        const size_t r = size_t(p->bw_range);
+        const size_t r = size_t(std::max(p->bw_range, p->stats_range));
         p->off_bs_q = off;   off = align256(off + size_t(p->H) * r * size_t(D) * p->esize);
         p->off_bs_z = off;   off = align256(off + size_t(p->BH) * r * size_t(D) * 4);
         p->off_bs_dz = off;  off = align256(off + size_t(p->BH) * r * size_t(D) * 4);
@@ -230,6 +234,10 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
         p->off_bs_sig = off; off = align256(off + size_t(p->BH) * r * 4);
         p->off_bs_gam = off; off = align256(off + size_t(p->BH) * r * 4);
         p->off_bs_dq = off;  off = align256(off + size_t(p->H) * r * size_t(D) * p->esize);
+        if (p->stats_range > 0) {
+            p->off_bs_nu2 = off;  off = align256(off + tok);
+            p->off_bs_del2 = off; off = align256(off + tok);
+        }
     }
     p->total[FLARE_OP_BACKWARD] = off;
     p->total[FLARE_OP_PP_BACKWARD] = 0;  // sized by pp_layout
@@ -713,8 +721,38 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     // slots
     const int fz = mc && !split ? flare::bw_fused_dz_groups(a) : 0;
     const int fq = mc && !split ? flare::bw_fused_dq_groups(a) : 0;
-    if (e == hipSuccess && !a.enc_only)
-        e = timed(3, s, [&] { return mc ? flare::launch_bw_stats_bf16(a, s) : flare::launch_bw_stats(a, s); });
+    const int64_t M = p.M, D = p.D, H = p.H, BH = p.BH, es = int64_t(p.esize);
+    auto rows = [&](void* dst, const void* src, int64_t n, int64_t bytes, int64_t sp, int64_t dp) {
+        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_copy_rows(dst, src, n, bytes, sp, dp, s); });
+    };
+    if (e == hipSuccess && !a.enc_only) {
+        if (split && p.stats_range > 0) {
+            // statistics over latent ranges (compact copies of Q, Z and mu*),
+            // the later ones into spare per-token arrays merged into the first
+            for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += p.stats_range) {
+                const int64_t mr = std::min<int64_t>(p.stats_range, M - m0);
+                flare::BackwardArgs sr = a;
+                sr.M = int(mr);
+                sr.Q = ws + p.off_bs_q;
+                sr.Z = (const float*)(ws + p.off_bs_z);
+                sr.zmu = (const float*)(ws + p.off_bs_mu);
+                if (m0 > 0) {
+                    sr.nu = (float*)(ws + p.off_bs_nu2);
+                    sr.del = (float*)(ws + p.off_bs_del2);
+                }
+                rows((void*)sr.Q, (const char*)Q + m0 * D * es, H, mr * D * es, M * D * es, mr * D * es);
+                rows((void*)sr.Z, a.Z + m0 * D, BH, mr * D * 4, M * D * 4, mr * D * 4);
+                rows((void*)sr.zmu, a.zmu + m0, BH, mr * 4, M * 4, mr * 4);
+                if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_stats_bf16(sr, s); });
+                if (e == hipSuccess && m0 > 0)
+                    e = timed(3, s, [&] {
+                        return flare::launch_bw_stats_merge(a.nu, a.del, sr.nu, sr.del, BH * int64_t(p.N), s);
+                    });
+            }
+        } else {
+            e = timed(3, s, [&] { return mc ? flare::launch_bw_stats_bf16(a, s) : flare::launch_bw_stats(a, s); });
+        }
+    }
     if (dz_given) {
         // dZ given: one "chunk" of partials holding it, merged as usual
         // (which also forms gam = <dZ, Z>)
@@ -745,10 +783,6 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     // kernels and the dK/dV kernel run on them as for a head of mr latents
     // (dK and dV of later ranges added to what the earlier ones wrote), and
     // the range's dQ is copied back into its rows.
-    const int64_t M = p.M, D = p.D, H = p.H, BH = p.BH, es = int64_t(p.esize);
-    auto rows = [&](void* dst, const void* src, int64_t n, int64_t bytes, int64_t sp, int64_t dp) {
-        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_copy_rows(dst, src, n, bytes, sp, dp, s); });
-    };
     for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += p.bw_range) {
         const int64_t mr = std::min<int64_t>(p.bw_range, M - m0);
         flare::BackwardArgs ar = a;

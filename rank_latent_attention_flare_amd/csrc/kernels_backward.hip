@@ -1346,6 +1346,29 @@ hipError_t launch_bw_dz(const BackwardArgs& a, hipStream_t s) { FLARE_BW_DISPATC
 hipError_t launch_bw_dq(const BackwardArgs& a, hipStream_t s) { FLARE_BW_DISPATCH(dq_d, a, s) }
 hipError_t launch_bw_dkdv(const BackwardArgs& a, hipStream_t s) { FLARE_BW_DISPATCH(dkdv_d, a, s) }
 
+// Per token: merge two latent ranges' statistics, each a log2-sum nu_r of
+// 2^(c l) over its latents and del_r = <dY, Y_r> with Y_r normalised over
+// the range: nu = log2(2^nu_a + 2^nu_b), del = (2^nu_a del_a + 2^nu_b del_b)
+// / 2^nu (exact log-sum-exp merge), into the first pair.
+__global__ __launch_bounds__(256) void bw_stats_merge_kernel(float* __restrict__ nu, float* __restrict__ del,
+                                                             const float* __restrict__ nu2,
+                                                             const float* __restrict__ del2, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const float a = nu[i], b = nu2[i], m = fmaxf(a, b);
+        const float wa = exp2f(a - m), wb = exp2f(b - m), w = wa + wb;
+        nu[i] = m + log2f(w);
+        del[i] = (wa * del[i] + wb * del2[i]) / w;
+    }
+}
+
+hipError_t launch_bw_stats_merge(float* nu, float* del, const float* nu2, const float* del2, int64_t n,
+                                 hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const unsigned blocks = (unsigned)std::min<int64_t>(8192, (n + 255) / 256);
+    FLARE_LAUNCH(bw_stats_merge_kernel, dim3(blocks), dim3(256), 0, s, nu, del, nu2, del2, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_bw_dz_combine(const BackwardArgs& a, hipStream_t s) {
     const int64_t n = (int64_t)a.BH * a.M;  // one wave each, four per workgroup
     FLARE_LAUNCH(bw_dz_combine, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, a);

@@ -196,5 +196,9 @@ hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s);
 int bw_fused_dz_groups(const BackwardArgs& a);
 int bw_fused_dq_groups(const BackwardArgs& a);
 hipError_t launch_bw_lat_bf16(const BackwardArgs& a, bool dq, hipStream_t s);  // dZ (dq false) or dQ partials
+// per token (n of them): merge a second latent range's statistics (nu2, del2)
+// into the first's (nu, del), by the log-sum-exp rule
+hipError_t launch_bw_stats_merge(float* nu, float* del, const float* nu2, const float* del2, int64_t n,
+                                 hipStream_t s);
 
 }  // namespace flare

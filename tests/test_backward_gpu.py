@@ -57,6 +57,9 @@ CASES = [
     (1, 2, 800, 128, 128, "bf16"),
     (1, 1, 500, 256, 128, "bf16"),
     (2, 1, 600, 200, 128, "bf16"),
+    # D = 128 above 256 latents: the per-token statistics over two ranges of
+    # up to 256 too, merged per token
+    (1, 1, 400, 512, 128, "bf16"),
 ]
 
 
@@ -118,6 +121,7 @@ SHARP = [
     # (128 + 72)
     (1, 1, 1500, 300, 64, 8.0, 2.0),
     (1, 1, 1500, 200, 128, 8.0, 2.0),
+    (1, 1, 1000, 300, 128, 8.0, 2.0),  # and statistics over two ranges
 ]
 
 
@@ -209,6 +213,7 @@ PP_CASES = [
     # B, H, N, M, D, dtype
     (2, 1, 600, 400, 64, "bf16"),  # latent ranges in both stages (the first with dZ given)
     (1, 1, 500, 250, 128, "bf16"),  # the same at D = 128
+    (1, 1, 300, 400, 128, "bf16"),  # and with statistics over ranges (second stage)
     (2, 2, 300, 40, 32, "f32"),
     (1, 1, 500, 17, 16, "f32"),
     (2, 2, 1000, 64, 64, "bf16"),
