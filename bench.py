@@ -560,13 +560,13 @@ def main():
     if args.variant == "backward":
         # contraction work of the backward kernels per (b, h): logits and the products and
         # accumulations of each kernel (stats 6, dZ 4, dK/dV 10, dQ 8) x M*N*D flops; on the
-        # bf16 matrix core for bf16 heads at D = 32 and D = 64 (above 256 latents over latent
-        # ranges), else fp32 VALU
+        # bf16 matrix core for bf16 heads (over latent ranges where Q, Z and dZ of the head do
+        # not fit in LDS), fp32 VALU for fp32 storage
         # FLARE++: the second stage's 28, plus the first stage's: on the matrix core its
         # encode-only dK/dV (8: logits, dl from dZ V^T, and the dK and dV products) and dQ
         # (6: logits, dZ V^T, dl K) kernels, with no statistics kernel; the fp32 kernels
         # compute the full formula with dY = 0 (statistics 6, dK/dV 10, dQ 8)
-        on_mfma = w.dtype == "bf16" and (w.D == 32 or (w.D == 64 and w.M <= 512))
+        on_mfma = w.dtype == "bf16"
         pp_first = 14 if on_mfma else 24
         bw_flops = ((28 + pp_first) if op == F.FLARE_OP_PP_FORWARD else 28) * w.B * w.H * w.N * w.M * w.D
         bw_ms = kt.get("backward", (0.0, 0))[0] / args.steps if kt else ms_step
