@@ -46,8 +46,9 @@ CASES = [
     # D = 64 with 256 latents (padded from 250): the latent kernels with four
     # latent blocks per wave and two token streams
     (1, 2, 1500, 250, 64, "bf16"),
-    # D = 96 and 128: the fp32 VALU kernels (bf16 storage widened), token
-    # tiles of 32 in the latent kernels, two columns per lane in the dZ merge
+    # D = 96 and 128 in fp32: the fp32 VALU kernels, token tiles of 32 in the
+    # latent kernels, two columns per lane in the dZ merge; bf16 at D = 128:
+    # the matrix core (M = 400 over latent and statistics ranges)
     (1, 2, 500, 40, 128, "f32"),
     (2, 1, 333, 70, 96, "f32"),
     (1, 2, 700, 64, 128, "bf16"),

@@ -109,8 +109,8 @@ def test_head_groups_equal_plain_layout(hg, case):
 
 BW_CASES = [
     # B, H, N, M, D, dtype: the matrix-core kernels (D = 32 with the fused
-    # latent partials, D = 64, and D = 64 over latent ranges at M = 300), bf16
-    # on the fp32 kernels (D = 128), and fp32 storage
+    # latent partials, D = 64, D = 64 over latent ranges at M = 300, and
+    # D = 128), and fp32 storage on the fp32 kernels
     (2, 3, 1000, 64, 32, "bf16"),
     (1, 2, 777, 33, 64, "bf16"),
     (2, 2, 900, 200, 64, "bf16"),
