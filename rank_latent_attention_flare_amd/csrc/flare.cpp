@@ -67,7 +67,8 @@ struct Plan {
     size_t off_acc, off_mu, off_sig, off_z, off_zmu, off_qp, total[7];
     size_t off_zsig, off_nu, off_tau, off_del, off_dz, off_gam;  // backward
     bool bsplit;       // backward over latent ranges of bw_range (bf16: D = 64, 256 < Mp <= 512; D = 128, 128 < Mp <= 512)
-    int bw_range;      // latents per range (256 at D = 64, 128 at D = 128)
+    int bw_range;      // latents per range of the latent-side kernels (256 at D = 64, 128 at D = 128)
+    int kv_range;      // latents per range of the dK/dV kernel (its LDS holds more at D = 128: 192)
     int stats_range;   // > 0: the per-token statistics too, over ranges of this many latents (D = 128, Mp > 256)
     size_t off_bs_nu2, off_bs_del2;  // a later statistics range's per-token results
     size_t off_bs_q, off_bs_z, off_bs_dz, off_bs_mu, off_bs_sig, off_bs_gam, off_bs_dq;  // one range's latent arrays
@@ -223,10 +224,14 @@ flare_status make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, fl
     // take every latent at once where Q and Z of the head fit in LDS, else
     // (D = 128 above 256 latents) ranges of 256 merged per token.
     p->bw_range = D == 128 ? 128 : 256;
+    // (192 at D = 128 where that takes fewer dK/dV passes than ranges of 128:
+    // each pass reads every token's rows again; A/B on MI355X at M = 512,
+    // 6.00 -> 5.69 ms; at M = 256 the extra copies made it 1% slower)
+    p->kv_range = D == 128 && (p->Mp + 191) / 192 < (p->Mp + 127) / 128 ? 192 : p->bw_range;
     p->bsplit = dt == FLARE_BF16 && ((D == 64 && p->Mp > 256 && p->Mp <= 512) || (D == 128 && p->Mp > 128 && p->Mp <= 512));
     p->stats_range = p->bsplit && D == 128 && p->Mp > 256 ? 256 : 0;
     if (p->bsplit) {
-        const size_t r = size_t(std::max(p->bw_range, p->stats_range));
+        const size_t r = size_t(std::max(std::max(p->bw_range, p->kv_range), p->stats_range));
         p->off_bs_q = off;   off = align256(off + size_t(p->H) * r * size_t(D) * p->esize);
         p->off_bs_z = off;   off = align256(off + size_t(p->BH) * r * size_t(D) * 4);
         p->off_bs_dz = off;  off = align256(off + size_t(p->BH) * r * size_t(D) * 4);
@@ -782,9 +787,12 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     // and its gam) are copied to compact arrays [.][mr][.], the latent-side
     // kernels and the dK/dV kernel run on them as for a head of mr latents
     // (dK and dV of later ranges added to what the earlier ones wrote), and
-    // the range's dQ is copied back into its rows.
-    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += p.bw_range) {
-        const int64_t mr = std::min<int64_t>(p.bw_range, M - m0);
+    // the range's dQ is copied back into its rows. Where the dK/dV kernel
+    // takes larger ranges than the latent kernels (D = 128), the latent loop
+    // writes each range's dZ and gam back into the head's arrays, and the
+    // dK/dV kernel runs over its own ranges afterwards.
+    const bool kv_sep = p.kv_range != p.bw_range;
+    auto range_args = [&](int64_t m0, int64_t mr) {
         flare::BackwardArgs ar = a;
         ar.M = int(mr);
         ar.Q = ws + p.off_bs_q;
@@ -799,20 +807,36 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
         rows((void*)ar.Z, a.Z + m0 * D, BH, mr * D * 4, M * D * 4, mr * D * 4);
         rows((void*)ar.zmu, a.zmu + m0, BH, mr * 4, M * 4, mr * 4);
         rows((void*)ar.zsig, a.zsig + m0, BH, mr * 4, M * 4, mr * 4);
+        return ar;
+    };
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += p.bw_range) {
+        const int64_t mr = std::min<int64_t>(p.bw_range, M - m0);
+        const flare::BackwardArgs ar = range_args(m0, mr);
         if (dz_given) {
             rows(ar.dZ, a.dZ + m0 * D, BH, mr * D * 4, M * D * 4, mr * D * 4);
             rows(ar.gam, a.gam + m0, BH, mr * 4, M * 4, mr * 4);
         } else {
             if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_lat_bf16(ar, false, s); });
             if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(ar, s); });
+            if (kv_sep) {
+                rows(a.dZ + m0 * D, ar.dZ, BH, mr * D * 4, mr * D * 4, M * D * 4);
+                rows(a.gam + m0, ar.gam, BH, mr * 4, mr * 4, M * 4);
+            }
         }
-        const int fqr = flare::bw_fused_dq_groups(ar);
-        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dkdv_bf16(ar, s); });
+        const int fqr = kv_sep ? 0 : flare::bw_fused_dq_groups(ar);
+        if (e == hipSuccess && !kv_sep) e = timed(3, s, [&] { return flare::launch_bw_dkdv_bf16(ar, s); });
         if (e == hipSuccess && fqr == 0) e = timed(3, s, [&] { return flare::launch_bw_lat_bf16(ar, true, s); });
         flare::BackwardArgs dqa = ar;
         if (fqr > 0) dqa.C = fqr;
         if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(dqa, s); });
         rows((char*)dQ + m0 * D * es, ar.dQ, H, mr * D * es, mr * D * es, M * D * es);
+    }
+    for (int64_t m0 = 0; kv_sep && m0 < M && e == hipSuccess; m0 += p.kv_range) {
+        const int64_t mr = std::min<int64_t>(p.kv_range, M - m0);
+        const flare::BackwardArgs ar = range_args(m0, mr);
+        rows(ar.dZ, a.dZ + m0 * D, BH, mr * D * 4, M * D * 4, mr * D * 4);
+        rows(ar.gam, a.gam + m0, BH, mr * 4, M * 4, mr * 4);
+        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dkdv_bf16(ar, s); });
     }
     return e;
 }

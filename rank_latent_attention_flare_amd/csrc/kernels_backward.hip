@@ -1319,7 +1319,7 @@ hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
         if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32, true>, a, lds, s);
         if (a.D == 64 && Mp > 128) return launch_bw_tok(bw_dkdv_bf16<64, true, false, 4, 8>, a, lds, s, 0, 8);
         if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64, true>, a, lds, s);
-        if (a.D == 128 && Mp <= 128) return launch_bw_tok(bw_dkdv_bf16<128, true>, a, lds, s);
+        if (a.D == 128 && Mp <= 192) return launch_bw_tok(bw_dkdv_bf16<128, true>, a, lds, s);
         return hipErrorInvalidValue;
     }
     if (const int fg = bw_fused_dq_groups(a)) {
@@ -1333,7 +1333,7 @@ hipError_t launch_bw_dkdv_bf16(const BackwardArgs& a, hipStream_t s) {
     if (a.D == 32) return launch_bw_tok(bw_dkdv_bf16<32>, a, lds, s);
     if (a.D == 64 && Mp > 128) return launch_bw_tok(bw_dkdv_bf16<64, false, false, 4, 8>, a, lds, s, 0, 8);
     if (a.D == 64) return launch_bw_tok(bw_dkdv_bf16<64>, a, lds, s);
-    if (a.D == 128 && Mp <= 128) return launch_bw_tok(bw_dkdv_bf16<128>, a, lds, s);
+    if (a.D == 128 && Mp <= 192) return launch_bw_tok(bw_dkdv_bf16<128>, a, lds, s);  // 146 KB of LDS at 192
     return hipErrorInvalidValue;
 }
 
