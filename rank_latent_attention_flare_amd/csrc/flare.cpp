@@ -727,8 +727,16 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
     const int fz = mc && !split ? flare::bw_fused_dz_groups(a) : 0;
     const int fq = mc && !split ? flare::bw_fused_dq_groups(a) : 0;
     const int64_t M = p.M, D = p.D, H = p.H, BH = p.BH, es = int64_t(p.esize);
+    // row copies are collected and issued together, one launch per batch
+    flare::CopyRows cp[flare::kMaxCopies];
+    int ncp = 0;
     auto rows = [&](void* dst, const void* src, int64_t n, int64_t bytes, int64_t sp, int64_t dp) {
-        if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_copy_rows(dst, src, n, bytes, sp, dp, s); });
+        if (ncp == flare::kMaxCopies && e == hipSuccess) e = hipErrorInvalidValue;
+        if (ncp < flare::kMaxCopies) cp[ncp++] = {dst, src, n, bytes, sp, dp};
+    };
+    auto flush = [&] {
+        if (e == hipSuccess && ncp > 0) e = timed(3, s, [&] { return flare::launch_copy_rows(cp, ncp, s); });
+        ncp = 0;
     };
     if (e == hipSuccess && !a.enc_only) {
         if (split && p.stats_range > 0) {
@@ -748,6 +756,7 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
                 rows((void*)sr.Q, (const char*)Q + m0 * D * es, H, mr * D * es, M * D * es, mr * D * es);
                 rows((void*)sr.Z, a.Z + m0 * D, BH, mr * D * 4, M * D * 4, mr * D * 4);
                 rows((void*)sr.zmu, a.zmu + m0, BH, mr * 4, M * 4, mr * 4);
+                flush();
                 if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_stats_bf16(sr, s); });
                 if (e == hipSuccess && m0 > 0)
                     e = timed(3, s, [&] {
@@ -784,7 +793,8 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
         return e;
     }
     // Latent ranges: the range's rows of Q, Z, mu*, sig* (and of a given dZ
-    // and its gam) are copied to compact arrays [.][mr][.], the latent-side
+    // and its gam) are copied to compact arrays [.][mr][.] (one launch per
+    // range for all of its copies), the latent-side
     // kernels and the dK/dV kernel run on them as for a head of mr latents
     // (dK and dV of later ranges added to what the earlier ones wrote), and
     // the range's dQ is copied back into its rows. Where the dK/dV kernel
@@ -815,7 +825,9 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
         if (dz_given) {
             rows(ar.dZ, a.dZ + m0 * D, BH, mr * D * 4, M * D * 4, mr * D * 4);
             rows(ar.gam, a.gam + m0, BH, mr * 4, M * 4, mr * 4);
-        } else {
+        }
+        flush();
+        if (!dz_given) {
             if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_lat_bf16(ar, false, s); });
             if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dz_combine(ar, s); });
             if (kv_sep) {
@@ -829,13 +841,16 @@ hipError_t backward_core(const Plan& p, const void* Q, const void* K, const void
         flare::BackwardArgs dqa = ar;
         if (fqr > 0) dqa.C = fqr;
         if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dq_combine(dqa, s); });
+        // (with kv_sep, the dZ and gam write-back goes in the same launch)
         rows((char*)dQ + m0 * D * es, ar.dQ, H, mr * D * es, mr * D * es, M * D * es);
+        flush();
     }
     for (int64_t m0 = 0; kv_sep && m0 < M && e == hipSuccess; m0 += p.kv_range) {
         const int64_t mr = std::min<int64_t>(p.kv_range, M - m0);
         const flare::BackwardArgs ar = range_args(m0, mr);
         rows(ar.dZ, a.dZ + m0 * D, BH, mr * D * 4, M * D * 4, mr * D * 4);
         rows(ar.gam, a.gam + m0, BH, mr * 4, M * 4, mr * 4);
+        flush();
         if (e == hipSuccess) e = timed(3, s, [&] { return flare::launch_bw_dkdv_bf16(ar, s); });
     }
     return e;

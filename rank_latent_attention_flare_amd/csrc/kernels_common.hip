@@ -357,13 +357,23 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
     out[blockIdx.x * 256 + threadIdx.x] = (float)(acc & 0xffff);
 }
 
-// rows x words 4-byte words, row r of src at src + r * sp, of dst at dst + r * dp (pitches in words)
-__global__ __launch_bounds__(256) void copy_rows_kernel(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src,
-                                                        int64_t rows, int64_t words, int64_t sp, int64_t dp) {
-    const int64_t n = rows * words;
+// Row copies in 4-byte words: copy i moves rows x words words, row r of src
+// at src + r * sp, of dst at dst + r * dp (pitches in words). blockIdx.y
+// selects the copy.
+struct WordCopy {
+    uint32_t* dst;
+    const uint32_t* src;
+    int64_t rows, words, sp, dp;
+};
+struct WordCopies {
+    WordCopy c[kMaxCopies];
+};
+__global__ __launch_bounds__(256) void copy_rows_kernel(WordCopies b) {
+    const WordCopy c = b.c[blockIdx.y];
+    const int64_t n = c.rows * c.words;
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
-        const int64_t r = e / words, w = e - r * words;
-        dst[r * dp + w] = src[r * sp + w];
+        const int64_t r = e / c.words, w = e - r * c.words;
+        c.dst[r * c.dp + w] = c.src[r * c.sp + w];
     }
 }
 
@@ -494,13 +504,22 @@ hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_copy_rows(void* dst, const void* src, int64_t rows, int64_t row_bytes, int64_t src_pitch,
-                            int64_t dst_pitch, hipStream_t s) {
-    if (row_bytes % 4 || src_pitch % 4 || dst_pitch % 4 || uintptr_t(dst) % 4 || uintptr_t(src) % 4)
-        return hipErrorInvalidValue;
-    if (rows <= 0 || row_bytes <= 0) return hipSuccess;
-    FLARE_LAUNCH(copy_rows_kernel, dim3(elementwise_blocks(rows * (row_bytes / 4))), dim3(256), 0, s, (uint32_t*)dst,
-                 (const uint32_t*)src, rows, row_bytes / 4, src_pitch / 4, dst_pitch / 4);
+hipError_t launch_copy_rows(const CopyRows* c, int n, hipStream_t s) {
+    if (n < 0 || n > kMaxCopies) return hipErrorInvalidValue;
+    WordCopies b{};
+    int k = 0;
+    int64_t most = 0;
+    for (int i = 0; i < n; ++i) {
+        const CopyRows& x = c[i];
+        if (x.row_bytes % 4 || x.src_pitch % 4 || x.dst_pitch % 4 || uintptr_t(x.dst) % 4 || uintptr_t(x.src) % 4)
+            return hipErrorInvalidValue;
+        if (x.rows <= 0 || x.row_bytes <= 0) continue;
+        b.c[k++] = {(uint32_t*)x.dst, (const uint32_t*)x.src, x.rows, x.row_bytes / 4, x.src_pitch / 4,
+                    x.dst_pitch / 4};
+        most = std::max(most, x.rows * (x.row_bytes / 4));
+    }
+    if (k == 0) return hipSuccess;
+    FLARE_LAUNCH(copy_rows_kernel, dim3(elementwise_blocks(most), k), dim3(256), 0, s, b);
     return hipGetLastError();
 }
 

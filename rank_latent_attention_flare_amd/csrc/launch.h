@@ -168,10 +168,17 @@ hipError_t launch_read(const void* src, size_t bytes, float* out, hipStream_t s)
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // elementwise helpers (bf16 or fp32 storage; sums in fp32, rounded once)
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s);  // bytes % 16 == 0
-// rows of row_bytes from src (rows src_pitch bytes apart) to dst (dst_pitch
-// apart); every size and address a multiple of 4 bytes
-hipError_t launch_copy_rows(void* dst, const void* src, int64_t rows, int64_t row_bytes, int64_t src_pitch,
-                            int64_t dst_pitch, hipStream_t s);
+// One row copy: rows of row_bytes from src (rows src_pitch bytes apart) to
+// dst (dst_pitch apart); every size and address a multiple of 4 bytes.
+struct CopyRows {
+    void* dst;
+    const void* src;
+    int64_t rows, row_bytes, src_pitch, dst_pitch;
+};
+constexpr int kMaxCopies = 8;
+// n (<= kMaxCopies) independent row copies in one launch (none may overlap
+// another's destination)
+hipError_t launch_copy_rows(const CopyRows* c, int n, hipStream_t s);
 hipError_t launch_widen(const void* src, float* dst, int64_t n, bool bf16, hipStream_t s);
 hipError_t launch_batch_sum(void* dst, const void* base, const void* add, int B, int64_t n, bool bf16, hipStream_t s);
 
